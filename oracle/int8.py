@@ -1,0 +1,115 @@
+"""Oracle: int8-GEMM variant of the encoder layer (quantise -> int8 GEMM -> int32 -> dequantise).
+
+Test infrastructure only (see oracle/__init__.py). Page keys as listed there.
+
+[SW] section 3, INT8 quantisation paragraph: inputs and weights are quantised to
+INT8, the product is accumulated in INT32, and a dequantisation step returns
+FP32/FP16 values; in FasterTransformer's int8 flow every GEMM has a quantise
+node before it and a dequantise node after it, while bias, residual and
+LayerNorm stay in floating point. Readings where the page is silent:
+  * symmetric codes in [-127, 127], round-half-to-even, clamp;
+  * weights per output channel: s_w[n] = max_k |W[n, k]| / 127 (1 if the row is 0);
+  * activations per tensor with a static scale from calibration (PTQ, named on
+    the page): a = max-abs of that GEMM's input on a calibration batch,
+    s = a / 127, inv = 127 / a, both float32;
+  * the GEMM output is INT32 (the INT8-output form is a later variant);
+  * QK^T and PV stay in floating point on the dequantised Q, K, V.
+Where a floating-point value decides a code, the decision is taken in float32
+exactly as stated here (the activation first rounded to the fp16 it is stored
+in), so that both implementations make the same decision.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import encoder as enc
+
+__all__ = ["quantize_weight", "quantize_act", "int8_matmul", "dequantize", "calibrate",
+           "act_scale", "encoder_layer_int8", "encoder_stack_int8"]
+
+
+def _rne_clamp(v32: np.ndarray) -> np.ndarray:
+    return np.clip(np.rint(v32), -127, 127).astype(np.int8)
+
+
+def quantize_weight(w: np.ndarray):
+    """Per-output-channel symmetric int8 weights: returns (Wq int8 [N, K], s_w float32 [N]).
+
+    s_w[n] = max_k |W[n,k]| / 127 in float32 (1 when the row is all zero);
+    Wq = clamp(rne(W / s_w[n]), -127, 127) with the division in float32.
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w32).max(axis=1)
+    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = _rne_clamp((w32 / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def act_scale(amax: float):
+    """Per-tensor activation scale from a calibration max-abs: (s, inv) in float32."""
+    a = np.float32(amax)
+    if not a > 0:
+        return np.float32(1.0), np.float32(1.0)
+    return np.float32(a / np.float32(127.0)), np.float32(np.float32(127.0) / a)
+
+
+def quantize_act(x_storage: np.ndarray, inv: np.float32) -> np.ndarray:
+    """q = clamp(rne(float32(x) * inv), -127, 127): one float32 multiply, then
+    round-half-to-even. ``x_storage`` holds the stored (e.g. fp16) activation."""
+    x32 = np.asarray(x_storage, dtype=np.float32)
+    return _rne_clamp((x32 * np.float32(inv)).astype(np.float32))
+
+
+def int8_matmul(q: np.ndarray, wq: np.ndarray) -> np.ndarray:
+    """acc[t, n] = sum_k q[t, k] * Wq[n, k], exact in int64."""
+    return np.asarray(q, np.int64) @ np.asarray(wq, np.int64).T
+
+
+def dequantize(acc: np.ndarray, s_a: np.float32, s_w: np.ndarray, bias) -> np.ndarray:
+    """y = acc * (s_a * s_w[n]) + b[n]; the scale product is formed in float32,
+    the rest in float64."""
+    scale = (np.float32(s_a) * np.asarray(s_w, np.float32)).astype(np.float32)
+    return np.asarray(acc, np.float64) * scale.astype(np.float64) + np.asarray(bias, np.float64)
+
+
+def calibrate(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float) -> list:
+    """Max-abs of the inputs of the four GEMMs (QKV, O, FFN1, FFN2) in a float64 run of
+    the floating-point layer on a calibration batch (static PTQ scales)."""
+    _, mid = enc.encoder_layer(x, cu_seqlens, w, heads, eps, return_intermediates=True)
+    return [float(np.abs(np.asarray(x, np.float64)).max()), float(np.abs(mid["ctx"]).max()),
+            float(np.abs(mid["h1"]).max()), float(np.abs(mid["f"]).max())]
+
+
+def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float,
+                       amax: list, storage=np.float16):
+    """Post-LN encoder layer with the four projection GEMMs in int8.
+
+    ``w`` holds the floating-point weights; they are quantised here per
+    quantize_weight. ``amax`` are the four calibration max-abs values.
+    ``storage`` is the type activations are stored in before quantisation.
+    """
+    scales = [act_scale(a) for a in amax]
+
+    def qlinear(a, wname, bname, g):
+        wq, sw = quantize_weight(w[wname])
+        s, inv = scales[g]
+        q = quantize_act(np.asarray(a, np.float64).astype(storage), inv)
+        return dequantize(int8_matmul(q, wq), s, sw, w[bname])
+
+    x = np.asarray(x, np.float64)
+    qkv = qlinear(x, "w_qkv", "b_qkv", 0)
+    ctx = enc.attention(qkv, cu_seqlens, heads)
+    h1 = enc.layer_norm(qlinear(ctx, "w_o", "b_o", 1) + x, w["ln1_g"], w["ln1_b"], eps)
+    f = enc.gelu(qlinear(h1, "w_1", "b_1", 2))
+    return enc.layer_norm(qlinear(f, "w_2", "b_2", 3) + h1, w["ln2_g"], w["ln2_b"], eps)
+
+
+def encoder_stack_int8(x, cu_seqlens, layers: list, amaxes: list, heads: int, eps: float,
+                       storage=np.float16):
+    """Layers in order, each with its own calibration max-abs list; the output of
+    every layer is rounded to ``storage`` as the stored activation."""
+    y = np.asarray(x, np.float64)
+    for w, a in zip(layers, amaxes):
+        y = encoder_layer_int8(y, cu_seqlens, w, heads, eps, a, storage)
+        y = y.astype(storage).astype(np.float64)
+    return y

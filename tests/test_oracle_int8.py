@@ -1,0 +1,92 @@
+"""Pins of oracle/int8.py: brute force on tiny inputs, rounding rules, exactness and
+error bounds. CPU only."""
+import numpy as np
+
+import tel_inputs as ti
+from oracle import encoder as enc
+from oracle import int8 as q8
+from tests import brute
+
+EPS = ti.LN_EPS
+
+
+def test_weight_quantization_rules():
+    rng = np.random.default_rng(0)
+    w = (rng.standard_normal((9, 33)) * 0.02).astype(np.float16)
+    w[3] = 0
+    wq, s = q8.quantize_weight(w)
+    assert wq.dtype == np.int8 and s.dtype == np.float32
+    assert s[3] == 1.0 and not wq[3].any()
+    for n in range(9):
+        if n == 3:
+            continue
+        k = np.abs(w[n].astype(np.float32)).argmax()
+        assert abs(int(wq[n, k])) == 127                          # the row's max maps to +-127
+        err = np.abs(w[n].astype(np.float64) / np.float64(s[n]) - wq[n])
+        assert err.max() <= 0.5 + 1e-5                             # rounding error <= half a step
+    assert np.abs(wq.astype(int)).max() <= 127
+
+
+def test_activation_quantization_ties_and_clamp():
+    x = np.array([2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 200.0, -200.0, 0.0], dtype=np.float16)
+    q = q8.quantize_act(x, np.float32(1.0))
+    assert q.tolist() == [2, 4, -2, -4, 0, 2, 127, -127, 0]        # half to even, clamp at 127
+
+
+def test_activation_scale():
+    s, inv = q8.act_scale(254.0)
+    assert s == np.float32(2.0) and inv == np.float32(0.5)
+    assert q8.act_scale(0.0) == (1.0, 1.0)
+
+
+def test_int8_matmul_brute_force_and_bound():
+    a, b = ti.int8_operands(5, 7, 40, seed=1)
+    acc = q8.int8_matmul(a, b)
+    for i in range(5):
+        for j in range(7):
+            assert acc[i, j] == sum(int(a[i, k]) * int(b[j, k]) for k in range(40))
+    worst = q8.int8_matmul(np.full((1, 3072), -127, np.int8), np.full((1, 3072), -127, np.int8))
+    assert worst[0, 0] == 3072 * 127 * 127 < 2 ** 31
+
+
+def test_quantized_linear_is_exact_on_the_grid():
+    """When x is an integer multiple of s_a and each weight row an integer multiple of its
+    scale, quantise -> int GEMM -> dequantise reproduces x W^T + b."""
+    rng = np.random.default_rng(2)
+    qx = rng.integers(-127, 128, size=(4, 16))
+    qw = rng.integers(-127, 128, size=(6, 16))
+    qw[:, 0] = 127                                                # row max is exactly 127 codes
+    s_a = np.float32(0.125)
+    sw = np.float32(2.0) ** -rng.integers(6, 10, size=6).astype(np.float32)
+    x = (qx * s_a).astype(np.float16)
+    w = (qw * sw[:, None]).astype(np.float16)
+    b = rng.standard_normal(6)
+    wq, s = q8.quantize_weight(w)
+    assert np.array_equal(wq, qw) and np.array_equal(s, sw)
+    y = q8.dequantize(q8.int8_matmul(q8.quantize_act(x, np.float32(1) / s_a), wq), s_a, s, b)
+    assert np.abs(y - enc.linear(x, w, b)).max() <= 1e-12
+
+
+def test_int8_layer_matches_brute_force_tiny():
+    cfg = ti.custom_encoder_config(2, 6, [6, 4], 32, 2, 64, dtype="f16", seed=3)
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets(lens, 6)
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    amax = q8.calibrate(xp, cu, w, 2, EPS)
+    y = q8.encoder_layer_int8(xp, cu, w, 2, EPS, amax)
+    ref = brute.encoder_layer_int8_padded(x, lens, w, 2, EPS, amax)
+    assert np.abs(enc.remove_padding(ref, lens) - y).max() <= 1e-9
+
+
+def test_int8_layer_close_to_float_layer():
+    cfg = ti.ENCODER_CONFIGS["tiny"]
+    cfg = dict(cfg, dtype="f16")
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets(lens, 8)
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    amax = q8.calibrate(xp, cu, w, 4, EPS)
+    y8 = q8.encoder_layer_int8(xp, cu, w, 4, EPS, amax)
+    y = enc.encoder_layer(xp, cu, w, 4, EPS)
+    assert np.linalg.norm(y8 - y) / np.linalg.norm(y) < 0.05
