@@ -1,0 +1,233 @@
+"""Benchmark: valid tokens/s per encoder layer (BERT-base-shaped stack, fp16) on one MI355X.
+
+One step = one pass of the whole path over one seeded synthetic batch: offsets, padding
+removal, the 12 encoder layers, padding rebuild (tel_encoder_forward). Inputs and
+prepared weights are resident in HBM before the timed region. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload bert_base] [--no-cpu]
+
+Also measured here, each with HIP events on the stream its kernel is launched on:
+the average duration of every kernel of one layer (same shapes, launched through the
+kernel-level entry points) and the roofline fraction of the dominant one; and the CPU
+oracle timed on a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bert_base")
+    ap.add_argument("--dtype", default=None, help="override storage type (f16, bf16)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the encoder "
+              "forward shards by sequence with no collectives, and this build measures one "
+              "GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tel_inputs as ti
+    import transformer_encoder_remove_amd as tel
+
+    cfg = dict(ti.ENCODER_CONFIGS[args.workload])
+    if args.dtype:
+        cfg["dtype"] = args.dtype
+    dt = cfg["dtype"]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
+    B, S, H, nh, F, NL = (cfg["batch"], cfg["max_seq"], cfg["hidden"], cfg["heads"], cfg["ffn"],
+                          cfg["layers"])
+    torch.cuda.set_device(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).cuda().to(tdt)
+
+    lens, x_pad = ti.encoder_input(cfg)
+    T, max_len = int(lens.sum()), int(lens.max())
+    log(f"[bench] workload {args.workload}: B={B} S={S} T={T} H={H} heads={nh} F={F} layers={NL} {dt}")
+    desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS)
+    psize = tel.tel_encoder_packed_size(desc)
+    packed, layer_w = [], []
+    for i in range(NL):
+        w = ti.encoder_layer_weights(cfg, i)
+        dw = {k: dev(v) for k, v in w.items()}
+        p = tel.alloc_bytes(psize)
+        tel.tel_encoder_prepare(desc, dw, p)
+        packed.append(p)
+        if i == 0:
+            layer_w = dw
+    x = dev(x_pad)
+    y = torch.empty_like(x)
+    lens_d = torch.from_numpy(lens).cuda()
+    ws = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tel.tel_encoder_forward(desc, packed, x, y, lens_d, T, max_len, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+    value = T * NL / (ms_per_step / 1e3)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}),"
+        f" {value / 1e6:.2f} M valid tokens/s per layer")
+
+    # ---------------------------------------------------------------- per-kernel timing
+    # Each kernel of one layer, same shapes and launch configuration as inside the stack,
+    # timed with HIP events on the stream it is launched on.
+    qkv = torch.randn(3 * T * H, device="cuda").to(tdt)
+    hid = torch.randn(T, H, device="cuda").to(tdt)
+    ctx = torch.empty(T, H, device="cuda", dtype=tdt)
+    pre = torch.empty(T, H, device="cuda", dtype=tdt)
+    ffn = torch.randn(T, F, device="cuda").to(tdt)
+    ffo = torch.empty(T, F, device="cuda", dtype=tdt)
+    qkv_o = torch.empty(3 * T * H, device="cuda", dtype=tdt)
+    bias = {n: torch.zeros(n, device="cuda", dtype=torch.float32) for n in (H, 3 * H, F)}
+    b32 = lambda n: bias[n]
+    g32 = torch.ones(H, device="cuda", dtype=torch.float32)
+    cu = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
+    Lbar = float((lens.astype(np.float64) ** 2).sum() / lens.sum())
+    kernels = {
+        "gemm_qkv": (lambda: tel.tel_gemm(tel.TEL_EPI_QKV_SPLIT, hid, layer_w["w_qkv"], b32(3 * H),
+                                          qkv_o, heads=nh, stream=stream),
+                     2.0 * T * H * 3 * H, 2.0 * (T * H + 3 * H * H + 3 * T * H)),
+        "attention": (lambda: tel.tel_attention_varlen(qkv, ctx, cu, T, max_len, nh, H // nh,
+                                                       stream=stream),
+                      4.0 * T * H * Lbar, 2.0 * 4 * T * H),
+        "gemm_o_resid": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, ctx, layer_w["w_o"], b32(H),
+                                              pre, resid=hid, stream=stream),
+                         2.0 * T * H * H, 2.0 * (3 * T * H + H * H)),
+        "layernorm": (lambda: tel.tel_layernorm(pre, hid, g32, b32(H), ti.LN_EPS, stream=stream),
+                      0.0, 2.0 * 2 * T * H),
+        "gemm_ffn1_gelu": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_GELU, hid, layer_w["w_1"], b32(F),
+                                                ffo, stream=stream),
+                           2.0 * T * H * F, 2.0 * (T * H + F * H + T * F)),
+        "gemm_ffn2_resid": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, ffn, layer_w["w_2"],
+                                                 b32(H), pre, resid=hid, stream=stream),
+                            2.0 * T * H * F, 2.0 * (T * F + F * H + 2 * T * H)),
+    }
+    per_kernel = {}
+    for name, (fn, flops, nbytes) in kernels.items():
+        fn()
+        torch.cuda.synchronize()
+        # A spin kernel holds the GPU while the host enqueues every (event, kernel, event)
+        # triple, so each pair of events brackets one kernel and no host launch latency.
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
+        torch.cuda._sleep(50_000_000)
+        for i in range(args.kernel_reps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])) * 1e3
+        per_kernel[name] = dict(us=us, tflops=flops / us / 1e6, gbs=nbytes / us / 1e3,
+                                flops=flops, bytes=nbytes)
+        log(f"[bench] kernel {name:16s} {us:9.2f} us  {flops / us / 1e6:8.1f} TFLOP/s"
+            f"  {nbytes / us / 1e3:8.1f} GB/s")
+    gemms = {k: v for k, v in per_kernel.items() if k.startswith("gemm")}
+    dom = max(gemms, key=lambda k: gemms[k]["us"])
+    d = per_kernel[dom]
+    peak = PEAK_FP32_TFLOPS if dt == "f32" else PEAK_FP16_TFLOPS
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4), "traffic": None,
+                "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
+    # one layer launches every kernel above once, and the LayerNorm twice
+    layer_sum_us = sum(v["us"] for v in per_kernel.values()) + per_kernel["layernorm"]["us"]
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, lens, x_pad, args.cpu_seconds)
+
+    out = {
+        "metric": "valid tokens/sec per encoder layer (BERT-base fp16) + % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "valid tokens/s per layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload}: {NL}-layer post-LN encoder, offsets + padding "
+                               f"removal + layers + rebuild", "batch": B, "max_seq": S,
+                   "valid_tokens": T, "max_len": max_len, "hidden": H, "heads": nh, "ffn": F,
+                   "layers": NL, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},
+        "layer_kernel_sum_us": round(layer_sum_us, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, lens, x_pad, seconds):
+    """The oracle as it stands (float64 NumPy), on the host cores: layers of the same
+    workload on the full batch, run one after another until `seconds` have passed."""
+    import tel_inputs as ti
+    from oracle import encoder as enc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    S = cfg["max_seq"]
+    cu, _ = enc.offsets(lens, S)
+    xp = enc.remove_padding(x_pad.astype(np.float64), lens)
+    T = int(lens.sum())
+    weights = [ti.encoder_layer_weights(cfg, i) for i in range(cfg["layers"])]
+    elapsed, done = 0.0, 0
+    while elapsed < seconds:
+        w = weights[done % len(weights)]
+        t0 = time.perf_counter()
+        xp = enc.encoder_layer(xp, cu, w, cfg["heads"], ti.LN_EPS)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    cores = blas_threads or len(os.sched_getaffinity(0))
+    log(f"[bench] cpu oracle: {done} layers x {T} tokens in {elapsed:.1f} s on {cores} threads")
+    return {"value": round(T * done / elapsed, 1), "unit": "valid tokens/s per layer",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} layer(s) of the same workload on the full batch ({T} valid "
+                      f"tokens), float64 NumPy, {elapsed:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

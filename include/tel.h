@@ -1,0 +1,184 @@
+/*
+ * tel.h - C ABI of libtel.so: inference forward of a Transformer encoder layer with
+ * padding removal and fused kernels, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these web pages (cited by title and figure/section):
+ *   [KS]  Kuaishou heterogeneous-computing article "GPU底层优化 | 如何让Transformer在GPU上
+ *         跑得更快？" (How to make Transformer run faster on GPU): Fig. 6 (fused
+ *         self-attention and FFN kernels), Fig. 7 (FP16 precision per kernel), Fig. 8
+ *         (memory management), Fig. 9 (padding removal with an offset mask, padded and
+ *         packed sequences convertible both ways), Fig. 10 (which kernels can run
+ *         without padding), Fig. 11 (GEMM configuration).
+ *   [SW]  NVIDIA talk on Swin Transformer "大規模なビジュアル モデルを使用してトレーニングと
+ *         推論を高速化するにはどうすればよいですか?" (How to accelerate training and inference
+ *         of large visual models): section 1 (attention, multi-head, BERT as a stack of
+ *         encoders, window attention, window shift, relative position bias); section 3
+ *         (inference: preprocessing done once, GEMM + bias / + activation epilogues,
+ *         separating the bias from a GEMM whose post-op is LayerNorm, hand-written
+ *         LayerNorm and shift-window-partition kernels, fMHA, QKV GEMM+bias with
+ *         re-laid-out weights, INT8 GEMM with INT32 accumulation and dequantisation).
+ *
+ * Conventions (every entry point):
+ *   - Pointers are DEVICE pointers unless marked [host]. The caller owns every buffer
+ *     (inputs, outputs, packed weights, workspace); the library never allocates or
+ *     frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only enqueues
+ *     work on it and returns; there is no hidden synchronisation. Buffers must stay
+ *     valid until the stream has consumed them. Outputs must not alias inputs.
+ *   - Return value: a tel_status. Arguments are validated on the host before any
+ *     launch; on failure nothing is enqueued. TEL_EDEVICE reports a launch error from
+ *     the HIP runtime.
+ *   - Layouts are row-major. Weights use the nn.Linear layout W[out][in]. Activation
+ *     and weight storage type is TEL_F32, TEL_F16 or TEL_BF16; accumulation,
+ *     softmax, LayerNorm statistics and GELU are float32.
+ *   - Caller obligations not checked on the device: 0 <= seq_lens[b] <= max_seq,
+ *     total_tokens == sum(seq_lens), max_len >= max(seq_lens).
+ *   - Thread safety: calls on different streams may run concurrently; there is no
+ *     global mutable state.
+ */
+#ifndef TEL_H
+#define TEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TEL_OK = 0,
+  TEL_EINVAL = 1,        /* null/misaligned pointer, negative or inconsistent size      */
+  TEL_EUNSUPPORTED = 2,  /* valid but unsupported shape or type (e.g. head_dim 48)      */
+  TEL_EWORKSPACE = 3,    /* workspace or packed buffer smaller than required            */
+  TEL_EDEVICE = 4        /* the HIP runtime reported an error                           */
+} tel_status;
+
+typedef enum { TEL_F32 = 0, TEL_F16 = 1, TEL_BF16 = 2, TEL_I8 = 3 } tel_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* tel_status_str(int status);
+/* Library version string (static). */
+const char* tel_version(void);
+
+/* ------------------------------------------------------------------ offsets, padding */
+
+/* Offset mask of padding removal ([KS] Fig. 9).
+ *   seq_lens        [batch] int32, valid length of each right-padded sequence.
+ *   cu_seqlens      [batch+1] int32 out: exclusive prefix sum, cu[0] = 0, cu[b+1] = cu[b] + len[b].
+ *   padding_offset  [>= total tokens] int32 out: for packed token t of sequence b,
+ *                   padding_offset[t] = b * max_seq - cu[b], so its padded row is
+ *                   t + padding_offset[t].
+ * batch >= 1, max_seq >= 1. Two launches (a single-workgroup scan, then a fill). */
+int tel_build_offsets(const int32_t* seq_lens, int batch, int max_seq, int32_t* cu_seqlens,
+                      int32_t* padding_offset, void* stream);
+
+/* Padding removal ([KS] Figs. 9-10): x_packed[t][:] = x_pad[t + padding_offset[t]][:].
+ *   x_pad [batch*max_seq][width], x_packed [total_tokens][width], element type `dtype`
+ *   (TEL_F32/F16/BF16). width * element size must be a multiple of 16 bytes and both
+ *   pointers 16-byte aligned. total_tokens == 0 is a no-op. */
+int tel_remove_padding(const void* x_pad, void* x_packed, const int32_t* padding_offset,
+                       int total_tokens, int width, int dtype, void* stream);
+
+/* Padding rebuild ([KS] Fig. 9), inverse of tel_remove_padding:
+ *   x_pad[b*max_seq + i][:] = x_packed[cu[b] + i][:] for i < len[b], and 0 for the pad rows.
+ *   Same type/alignment rules as tel_remove_padding. */
+int tel_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu_seqlens,
+                        int batch, int max_seq, int width, int dtype, void* stream);
+
+/* ------------------------------------------------------------------ encoder layer */
+
+/* Post-LN BERT encoder layer ([SW] section 1; [KS] Fig. 6):
+ *   qkv = x W_qkv^T + b_qkv ; ctx = MHA(qkv) within each sequence, scale 1/sqrt(head_dim)
+ *   h1  = LN(ctx W_o^T + b_o + x) ; f = GELU(h1 W_1^T + b_1)   (exact erf GELU)
+ *   y   = LN(f W_2^T + b_2 + h1)  ; LN: biased variance, eps = ln_eps. */
+typedef struct {
+  int hidden;      /* H, multiple of 8                                         */
+  int heads;       /* H % heads == 0; head_dim = H / heads in {16, 32, 64, 128} */
+  int ffn;         /* F, multiple of 8                                         */
+  int dtype;       /* storage type of activations and weights                 */
+  int int8_gemm;   /* 1: the four projection GEMMs run in int8 (dtype TEL_F16) */
+  float ln_eps;
+} tel_encoder_desc;
+
+/* Canonical weights of one layer, storage type desc->dtype, device pointers:
+ * W_qkv [3H][H] with rows [Q heads | K heads | V heads], b_qkv [3H], W_o [H][H], b_o [H],
+ * ln1 gamma/beta [H], W_1 [F][H], b_1 [F], W_2 [H][F], b_2 [H], ln2 gamma/beta [H]. */
+typedef struct {
+  const void *w_qkv, *b_qkv, *w_o, *b_o, *ln1_g, *ln1_b;
+  const void *w_1, *b_1, *w_2, *b_2, *ln2_g, *ln2_b;
+  /* [host] int8 only: calibration max-abs of the inputs of the QKV, O, FFN1 and FFN2
+   * GEMMs (static per-tensor activation scales a/127). Ignored otherwise. */
+  float act_amax[4];
+} tel_encoder_weights;
+
+/* Bytes of the packed (preprocessed) form of one layer's weights. 0 on a bad desc. */
+size_t tel_encoder_packed_size(const tel_encoder_desc* desc);
+
+/* One-time preprocessing of one layer's weights ([SW] section 3: work that needs doing
+ * once is done ahead of inference): copies weights into the GEMM operand layout, widens
+ * biases and LayerNorm parameters to float32, and for int8 quantises the weights per
+ * output channel (codes rne(W / s) clamped to +-127, s = max|W[n,:]| / 127) and stores
+ * the per-column dequantisation scales. `packed` (>= tel_encoder_packed_size bytes,
+ * 256-byte aligned) is written on `stream`. */
+int tel_encoder_prepare(const tel_encoder_desc* desc, const tel_encoder_weights* w,
+                        void* packed, size_t packed_bytes, void* stream);
+
+/* Workspace bytes tel_encoder_layer_forward needs for up to max_tokens packed tokens. */
+size_t tel_encoder_workspace_size(const tel_encoder_desc* desc, int max_tokens);
+
+/* One layer on packed tokens: x [total_tokens][H] -> y [total_tokens][H].
+ * cu_seqlens [batch+1] from tel_build_offsets; max_len [host] >= longest sequence.
+ * workspace: >= tel_encoder_workspace_size(desc, total_tokens) bytes, 256-byte aligned. */
+int tel_encoder_layer_forward(const tel_encoder_desc* desc, const void* packed,
+                              const void* x, void* y, const int32_t* cu_seqlens, int batch,
+                              int total_tokens, int max_len, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* Workspace bytes of tel_encoder_forward for a batch of `batch` x `max_seq`. */
+size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* desc, int batch, int max_seq);
+
+/* Whole stack on a padded batch ([KS] Figs. 9-10): offsets, padding removal, n_layers
+ * layers on the packed tokens, padding rebuild (pad rows of y_pad are 0).
+ *   packed_layers [host] array of n_layers device pointers (tel_encoder_prepare output).
+ *   x_pad, y_pad [batch][max_seq][H]; seq_lens [batch] int32 (device).
+ *   total_tokens, max_len [host]: sum and max of seq_lens. */
+int tel_encoder_forward(const tel_encoder_desc* desc, const void* const* packed_layers,
+                        int n_layers, const void* x_pad, void* y_pad, const int32_t* seq_lens,
+                        int batch, int max_seq, int total_tokens, int max_len,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ kernel-level entry points
+ * The same kernels the layer uses, exposed so that tests and per-kernel measurements can
+ * localise a result to one kernel. */
+
+/* GEMM epilogue selector for tel_gemm. */
+typedef enum {
+  TEL_EPI_BIAS = 0,        /* C = A W^T + b                                               */
+  TEL_EPI_BIAS_GELU = 1,   /* C = GELU(A W^T + b)                                         */
+  TEL_EPI_BIAS_RESID = 2,  /* C = A W^T + b + R       (R [M][N])                          */
+  TEL_EPI_QKV_SPLIT = 3    /* C = A W^T + b written head-split as [3][heads][M][N/(3*heads)] */
+} tel_epilogue;
+
+/* C = epilogue(A [M][K] x W[N][K]^T), storage type `dtype`, float32 accumulation; bias is
+ * float32 [N]; resid (TEL_EPI_BIAS_RESID) has C's type and shape; `heads` is used by
+ * TEL_EPI_QKV_SPLIT only. K % 8 == 0, N % 4 == 0, 16-byte aligned pointers. */
+int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
+             const void* resid, void* C, int M, int N, int K, int heads, void* stream);
+
+/* Variable-length multi-head attention ([SW] section 3, fMHA: batched GEMM, softmax and
+ * batched GEMM in one kernel). qkv_split [3][heads][total_tokens][head_dim] (the
+ * TEL_EPI_QKV_SPLIT layout); ctx [total_tokens][heads*head_dim]; query i of sequence b
+ * attends to keys cu[b] .. cu[b+1]-1 only; scale 1/sqrt(head_dim). */
+int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,
+                         int total_tokens, int max_len, int heads, int head_dim, int dtype,
+                         void* stream);
+
+/* y[r][:] = LN(x[r][:]) * gamma + beta over rows of width `width` (float32 gamma/beta). */
+int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,
+                  int width, float eps, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TEL_H */

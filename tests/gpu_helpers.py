@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: run the library through its C ABI on seeded inputs
+and compare with the oracle at the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import tel_inputs as ti
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# fp16/bf16 outputs vs the float64 oracle: max-abs 2e-2 and relative Frobenius 5e-3.
+# fp32 outputs (float32 storage, float32 MFMA accumulation): 1e-4 and 1e-5.
+TOL = {"f16": (2e-2, 5e-3), "bf16": (2e-2, 5e-3), "f32": (1e-4, 1e-5)}
+
+
+def errors(out: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.isfinite(out).all(), "non-finite output"
+    diff = out - ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(out, ref, dtype: str, what: str = ""):
+    max_abs, rel = errors(out, ref)
+    tmax, trel = TOL[dtype]
+    assert max_abs <= tmax and rel <= trel, \
+        f"{what}: max_abs={max_abs:.3e} (tol {tmax:.0e}) rel_frob={rel:.3e} (tol {trel:.0e})"
+    return max_abs, rel
+
+
+def dev(a: np.ndarray, dtype: str | torch.dtype) -> torch.Tensor:
+    """Host array -> device tensor of the storage type (exact: values already rounded)."""
+    dt = TORCH_DT[dtype] if isinstance(dtype, str) else dtype
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).to("cuda").to(dt)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).to("cuda")
+
+
+def prepare_layers(tel, desc, layer_weights: list, dtype: str) -> list:
+    packed = []
+    n = tel.tel_encoder_packed_size(desc)
+    assert n > 0
+    for w in layer_weights:
+        dw = {k: dev(v, dtype) for k, v in w.items()}
+        p = tel.alloc_bytes(n)
+        tel.tel_encoder_prepare(desc, dw, p)
+        packed.append(p)
+    torch.cuda.synchronize()
+    return packed
+
+
+def gpu_encoder_forward(tel, cfg: dict, lens, x_pad, layer_weights: list) -> np.ndarray:
+    """Whole stack (offsets, remove, layers, rebuild) on the GPU; returns y_pad (float64)."""
+    dt = cfg["dtype"]
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT[dt], ti.LN_EPS)
+    packed = prepare_layers(tel, desc, layer_weights, dt)
+    B, S, H = x_pad.shape
+    x = dev(x_pad, dt)
+    y = torch.full_like(x, float("nan"))
+    lens_d = torch.from_numpy(np.asarray(lens, np.int32)).to("cuda")
+    ws = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
+    T, max_len = int(np.sum(lens)), int(np.max(lens))
+    tel.tel_encoder_forward(desc, packed, x, y, lens_d, T, max_len, ws)
+    torch.cuda.synchronize()
+    return host(y)

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/tel.h declares, and validates
+arguments on the host before touching the GPU. CPU only: no call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tel.h")
+
+tel = pytest.importorskip("transformer_encoder_remove_amd",
+                          reason="libtel.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tel_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(tel.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(tel.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in tel.tel_version()
+    assert tel.tel_status_str(0) == "TEL_OK"
+    assert "TEL_EINVAL" in tel.tel_status_str(1)
+    assert "unknown" in tel.tel_status_str(99)
+
+
+L = tel.lib
+FAKE = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 2)
+
+
+def test_offsets_validation():
+    assert L.tel_build_offsets(None, 2, 8, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets(FAKE, 0, 8, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets(FAKE, 2, 0, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets(FAKE, 1 << 20, 1 << 12, FAKE, FAKE, None) == tel.TEL_EUNSUPPORTED
+
+
+def test_padding_validation():
+    f16 = tel.TEL_F16
+    assert L.tel_remove_padding(FAKE, FAKE, FAKE, -1, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_remove_padding(FAKE, FAKE, FAKE, 0, 64, f16, None) == tel.TEL_OK   # no-op
+    assert L.tel_remove_padding(None, FAKE, FAKE, 3, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_remove_padding(FAKE_ODD, FAKE, FAKE, 3, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_remove_padding(FAKE, FAKE, FAKE, 3, 12, f16, None) == tel.TEL_EUNSUPPORTED
+    assert L.tel_remove_padding(FAKE, FAKE, FAKE, 3, 64, 9, None) == tel.TEL_EINVAL
+    assert L.tel_rebuild_padding(FAKE, FAKE, FAKE, 0, 8, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_rebuild_padding(FAKE, FAKE, None, 2, 8, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_rebuild_padding(FAKE, FAKE, FAKE, 2, 8, 4, f16, None) == tel.TEL_EUNSUPPORTED
+
+
+def desc(**kw):
+    d = dict(hidden=768, heads=12, ffn=3072, dtype=tel.TEL_F16, int8_gemm=0, ln_eps=1e-5)
+    d.update(kw)
+    return tel.tel_encoder_desc(**d)
+
+
+def test_encoder_desc_validation_and_sizes():
+    good = desc()
+    assert tel.tel_encoder_packed_size(good) > 2 * (12 * 768 * 768)
+    assert tel.tel_encoder_packed_size(desc(heads=7)) == 0            # 768 % 7
+    assert tel.tel_encoder_packed_size(desc(hidden=96, heads=2)) == 0  # head_dim 48
+    assert tel.tel_encoder_workspace_size(good, 2560) >= 2 * 2560 * (6 * 768 + 3072)
+    assert tel.tel_encoder_workspace_size(good, 0) == 0
+    assert tel.tel_encoder_forward_workspace_size(good, 32, 128) > \
+        tel.tel_encoder_workspace_size(good, 32 * 128)
+
+
+def test_layer_forward_validation():
+    d = desc()
+    ws_need = tel.tel_encoder_workspace_size(d, 100)
+    args = lambda **kw: dict(dict(packed=FAKE, x=FAKE, y=ctypes.c_void_p(2 << 20), cu=FAKE,
+                                  batch=2, T=100, max_len=64, ws=FAKE, wsb=ws_need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.tel_encoder_layer_forward(ctypes.byref(kw.get("d", d)), a["packed"], a["x"],
+                                           a["y"], a["cu"], a["batch"], a["T"], a["max_len"],
+                                           a["ws"], a["wsb"], None)
+    assert call(T=0) == tel.TEL_OK
+    assert call(batch=0) == tel.TEL_EINVAL
+    assert call(T=-1) == tel.TEL_EINVAL
+    assert call(max_len=0) == tel.TEL_EINVAL
+    assert call(x=None) == tel.TEL_EINVAL
+    assert call(y=FAKE) == tel.TEL_EINVAL                               # aliasing
+    assert call(ws=FAKE_ODD) == tel.TEL_EINVAL                          # misaligned
+    assert call(wsb=ws_need - 1) == tel.TEL_EWORKSPACE
+    assert call(d=desc(dtype=tel.TEL_I8)) == tel.TEL_EUNSUPPORTED
+    assert call(d=desc(hidden=0)) == tel.TEL_EINVAL
+
+
+def test_kernel_entry_validation():
+    f16 = tel.TEL_F16
+    assert L.tel_gemm(0, f16, FAKE, FAKE, FAKE, None, FAKE, 16, 64, 12, 1, None) == \
+        tel.TEL_EUNSUPPORTED                                            # K % 8
+    assert L.tel_gemm(2, f16, FAKE, FAKE, FAKE, None, FAKE, 16, 64, 64, 1, None) == tel.TEL_EINVAL
+    assert L.tel_gemm(9, f16, FAKE, FAKE, FAKE, None, FAKE, 16, 64, 64, 1, None) == tel.TEL_EINVAL
+    assert L.tel_gemm(3, f16, FAKE, FAKE, FAKE, None, FAKE, 16, 96, 64, 5, None) == \
+        tel.TEL_EUNSUPPORTED
+    assert L.tel_gemm(0, f16, FAKE, FAKE, FAKE, None, FAKE, 0, 64, 64, 1, None) == tel.TEL_OK
+    assert L.tel_attention_varlen(FAKE, FAKE, FAKE, 2, 10, 8, 2, 48, f16, None) == \
+        tel.TEL_EUNSUPPORTED
+    assert L.tel_attention_varlen(FAKE, FAKE, FAKE, 2, 10, 0, 2, 64, f16, None) == tel.TEL_EINVAL
+    assert L.tel_layernorm(FAKE, FAKE, FAKE, FAKE, 4, 20, 1e-5, f16, None) == tel.TEL_EUNSUPPORTED
+    assert L.tel_layernorm(FAKE, FAKE, FAKE, FAKE, 4, 64, -1.0, f16, None) == tel.TEL_EINVAL

@@ -1,0 +1,97 @@
+"""GPU parity of the whole path (offsets, padding removal, encoder layers, rebuild) through
+tel_encoder_forward, against the float64 oracle, on the seeded workloads."""
+import numpy as np
+import pytest
+
+import tel_inputs as ti
+from oracle import encoder as enc
+from tests.gpu_helpers import assert_close, errors, gpu_encoder_forward
+
+pytestmark = pytest.mark.gpu
+
+tel = pytest.importorskip("transformer_encoder_remove_amd")
+EPS = ti.LN_EPS
+
+
+def _oracle(cfg, lens, x, ws):
+    return enc.encoder_forward(x, lens, ws, cfg["heads"], EPS)
+
+
+@pytest.mark.parametrize("variant", [False, True])
+def test_tiny_fp32(variant):
+    cfg = ti.ENCODER_CONFIGS["tiny"]
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, 0, variant)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    assert_close(y, _oracle(cfg, lens, x, ws), "f32", "tiny fp32")
+    assert not y[0, lens[0]:].any()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("variant", [False, True])
+def test_bert_base_one_layer_full_batch(dtype, variant):
+    """One BERT-base layer on the full seeded batch (B 32, S 128, lengths U{32..128})."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base"], dtype=dtype)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, 0, variant)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    ref = _oracle(cfg, lens, x, ws)
+    assert_close(enc.remove_padding(y, lens), enc.remove_padding(ref, lens), dtype, "bert_base L1")
+    for b in range(len(lens)):
+        assert not y[b, lens[b]:].any()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=3, S=9, lens=[9, 1, 0], H=64, heads=4, F=256),         # empty and single-token sequences
+    dict(B=1, S=200, lens=[200], H=256, heads=2, F=512),          # head_dim 128, one sequence
+    dict(B=5, S=70, lens=[70, 33, 64, 65, 2], H=128, heads=8, F=384),   # head_dim 16
+    dict(B=2, S=40, lens=[40, 17], H=96, heads=3, F=384),         # head_dim 32, H 96
+])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_edge_shapes(shape, dtype):
+    cfg = ti.custom_encoder_config(shape["B"], shape["S"], shape["lens"], shape["H"],
+                                   shape["heads"], shape["F"], dtype=dtype, seed=shape["S"], layers=2)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(2)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    assert_close(y, _oracle(cfg, lens, x, ws), dtype, f"edge {shape}")
+
+
+def test_bert_base_12_layers_sampled_sequences():
+    """The benchmarked call: 12 BERT-base layers on the full batch. The oracle computes a
+    sample of sequences (independent of one another) through the same 12 layers."""
+    cfg = ti.ENCODER_CONFIGS["bert_base"]
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i) for i in range(cfg["layers"])]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 31})
+    ref = _oracle(cfg, lens[pick], x[pick], ws)
+    got = y[pick]
+    ma, rel = errors(enc.remove_padding(got, lens[pick]), enc.remove_padding(ref, lens[pick]))
+    print(f"bert_base 12 layers, sequences {pick}: max_abs={ma:.3e} rel_frob={rel:.3e}")
+    assert_close(enc.remove_padding(got, lens[pick]), enc.remove_padding(ref, lens[pick]), "f16",
+                 "bert_base 12 layers")
+
+
+def test_bert_large_tput_one_layer_sampled():
+    """BERT-large throughput batch (B 64, S 384, lengths U{64..384}), one layer on the GPU for
+    the whole batch; the oracle checks a sample of sequences."""
+    cfg = ti.ENCODER_CONFIGS["bert_large_tput"]
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, 0, variant=True)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 40})
+    ref = _oracle(cfg, lens[pick], x[pick], ws)
+    assert_close(enc.remove_padding(y[pick], lens[pick]), enc.remove_padding(ref, lens[pick]),
+                 "f16", "bert_large_tput L1")
+
+
+def test_deterministic_repeat():
+    """Two runs give bitwise-identical outputs (no races in LDS staging)."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base"], batch=8)
+    lens, x = ti.encoder_input(cfg)
+    lens, x = lens[:8], x[:8]
+    ws = [ti.encoder_layer_weights(cfg, 0, variant=True)]
+    y1 = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    y2 = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    assert np.array_equal(y1, y2)

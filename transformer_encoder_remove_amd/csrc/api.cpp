@@ -1,0 +1,341 @@
+// C ABI of libtel.so (declared in include/tel.h): host-side argument validation,
+// packed-weight and workspace layouts, and the launch sequence of each entry point.
+// Nothing here allocates device memory; every buffer belongs to the caller.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "tel.h"
+
+using namespace tel;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+inline int status_of(hipError_t e) { return e == hipSuccess ? TEL_OK : TEL_EDEVICE; }
+inline bool float_type(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT_BF16; }
+
+#define TEL_TRY(expr)                         \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return TEL_EDEVICE; \
+  } while (0)
+
+// ------------------------------------------------------------------ packed layer layout
+// Storage-type weights first (GEMM operands, [N][K] as given), then float32 vectors.
+struct LayerLayout {
+  size_t w_qkv, w_o, w_1, w_2;
+  size_t b_qkv, b_o, ln1_g, ln1_b, b_1, b_2, ln2_g, ln2_b;
+  size_t total;
+};
+
+bool desc_ok(const tel_encoder_desc* d) {
+  if (!d) return false;
+  if (d->hidden <= 0 || d->heads <= 0 || d->ffn <= 0) return false;
+  if (d->hidden % d->heads) return false;
+  if (!(d->ln_eps >= 0.f)) return false;
+  return true;
+}
+
+int desc_supported(const tel_encoder_desc* d) {
+  if (!desc_ok(d)) return TEL_EINVAL;
+  if (!float_type(d->dtype)) return TEL_EUNSUPPORTED;
+  if (d->int8_gemm) return TEL_EUNSUPPORTED;
+  if (d->hidden % 8 || d->ffn % 8) return TEL_EUNSUPPORTED;
+  if (!attention_supported(d->dtype, d->hidden / d->heads)) return TEL_EUNSUPPORTED;
+  if (!layernorm_supported(d->dtype, d->hidden)) return TEL_EUNSUPPORTED;
+  return TEL_OK;
+}
+
+LayerLayout layer_layout(const tel_encoder_desc* d) {
+  const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
+  LayerLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  L.w_qkv = take(3 * H * H * es);
+  L.w_o = take(H * H * es);
+  L.w_1 = take(F * H * es);
+  L.w_2 = take(H * F * es);
+  L.b_qkv = take(3 * H * 4);
+  L.b_o = take(H * 4);
+  L.ln1_g = take(H * 4);
+  L.ln1_b = take(H * 4);
+  L.b_1 = take(F * 4);
+  L.b_2 = take(H * 4);
+  L.ln2_g = take(H * 4);
+  L.ln2_b = take(H * 4);
+  L.total = o;
+  return L;
+}
+
+// ------------------------------------------------------------------ layer workspace
+struct LayerWs {
+  size_t qkv, ctx, pre, h1, f, total;
+};
+
+LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
+  const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
+  LayerWs w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  w.qkv = take(3 * T * H * es);
+  w.ctx = take(T * H * es);
+  w.pre = take(T * H * es);
+  w.h1 = take(T * H * es);
+  w.f = take(T * F * es);
+  w.total = o;
+  return w;
+}
+
+struct StackWs {
+  size_t cu, po, xa, xb, layer, total;
+};
+
+StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
+  const size_t T = (size_t)batch * max_seq, H = d->hidden, es = dtype_size(d->dtype);
+  StackWs s;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  s.cu = take(((size_t)batch + 1) * 4);
+  s.po = take(T * 4);
+  s.xa = take(T * H * es);
+  s.xb = take(T * H * es);
+  s.layer = take(layer_ws(d, T).total);
+  s.total = o;
+  return s;
+}
+
+int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void* y,
+                  const int32_t* cu, int batch, int T, int max_len, char* ws, hipStream_t st) {
+  if (T == 0) return TEL_OK;
+  const LayerLayout L = layer_layout(d);
+  const LayerWs W = layer_ws(d, (size_t)T);
+  const int H = d->hidden, F = d->ffn, nh = d->heads, dt = d->dtype;
+  void* qkv = ws + W.qkv;
+  void* ctx = ws + W.ctx;
+  void* pre = ws + W.pre;
+  void* h1 = ws + W.h1;
+  void* f = ws + W.f;
+  auto F32 = [&](size_t off) { return (const float*)(P + off); };
+
+  GemmArgs g{};
+  // QKV projection + bias, written head-split for the attention kernel
+  g = GemmArgs{EPI_QKV_SPLIT, x, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
+  TEL_TRY(launch_gemm(dt, g, st));
+  TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
+  // output projection + bias + residual, then LayerNorm
+  g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
+  TEL_TRY(launch_gemm(dt, g, st));
+  TEL_TRY(launch_layernorm(dt, pre, h1, F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, st));
+  // FFN: bias + GELU, then bias + residual, then LayerNorm
+  g = GemmArgs{EPI_BIAS_GELU, h1, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
+  TEL_TRY(launch_gemm(dt, g, st));
+  g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
+  TEL_TRY(launch_gemm(dt, g, st));
+  TEL_TRY(launch_layernorm(dt, pre, y, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, st));
+  return TEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tel_status_str(int s) {
+  switch (s) {
+    case TEL_OK: return "TEL_OK";
+    case TEL_EINVAL: return "TEL_EINVAL: invalid argument";
+    case TEL_EUNSUPPORTED: return "TEL_EUNSUPPORTED: unsupported shape or type";
+    case TEL_EWORKSPACE: return "TEL_EWORKSPACE: buffer too small";
+    case TEL_EDEVICE: return "TEL_EDEVICE: HIP runtime error";
+  }
+  return "unknown tel_status";
+}
+
+const char* tel_version(void) { return "tel 0.1 (gfx950)"; }
+
+int tel_build_offsets(const int32_t* seq_lens, int batch, int max_seq, int32_t* cu_seqlens,
+                      int32_t* padding_offset, void* stream) {
+  if (!seq_lens || !cu_seqlens || !padding_offset) return TEL_EINVAL;
+  if (batch <= 0 || max_seq <= 0) return TEL_EINVAL;
+  if ((long long)batch * max_seq > INT32_MAX) return TEL_EUNSUPPORTED;
+  return status_of(launch_offsets(seq_lens, batch, max_seq, cu_seqlens, padding_offset,
+                                  as_stream(stream)));
+}
+
+int tel_remove_padding(const void* x_pad, void* x_packed, const int32_t* padding_offset,
+                       int total_tokens, int width, int dtype, void* stream) {
+  if (total_tokens < 0 || width <= 0) return TEL_EINVAL;
+  if (!float_type(dtype) && dtype != DT_I8) return TEL_EINVAL;
+  if (total_tokens == 0) return TEL_OK;
+  if (!x_pad || !x_packed || !padding_offset) return TEL_EINVAL;
+  if (!aligned16(x_pad) || !aligned16(x_packed)) return TEL_EINVAL;
+  const long long row_bytes = (long long)width * dtype_size(dtype);
+  if (row_bytes % 16) return TEL_EUNSUPPORTED;
+  return status_of(launch_remove_padding(x_pad, x_packed, padding_offset, total_tokens,
+                                         (int)row_bytes, as_stream(stream)));
+}
+
+int tel_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu_seqlens, int batch,
+                        int max_seq, int width, int dtype, void* stream) {
+  if (batch <= 0 || max_seq <= 0 || width <= 0) return TEL_EINVAL;
+  if (!float_type(dtype) && dtype != DT_I8) return TEL_EINVAL;
+  if (!x_packed || !x_pad || !cu_seqlens) return TEL_EINVAL;
+  if (!aligned16(x_pad) || !aligned16(x_packed)) return TEL_EINVAL;
+  const long long row_bytes = (long long)width * dtype_size(dtype);
+  if (row_bytes % 16) return TEL_EUNSUPPORTED;
+  return status_of(launch_rebuild_padding(x_packed, x_pad, cu_seqlens, batch, max_seq,
+                                          (int)row_bytes, as_stream(stream)));
+}
+
+size_t tel_encoder_packed_size(const tel_encoder_desc* d) {
+  if (desc_supported(d) != TEL_OK) return 0;
+  return layer_layout(d).total;
+}
+
+int tel_encoder_prepare(const tel_encoder_desc* d, const tel_encoder_weights* w, void* packed,
+                        size_t packed_bytes, void* stream) {
+  const int sup = desc_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (!w || !packed || !aligned256(packed)) return TEL_EINVAL;
+  const void* ptrs[] = {w->w_qkv, w->b_qkv, w->w_o, w->b_o, w->ln1_g, w->ln1_b,
+                        w->w_1, w->b_1, w->w_2, w->b_2, w->ln2_g, w->ln2_b};
+  for (const void* p : ptrs)
+    if (!p) return TEL_EINVAL;
+  const LayerLayout L = layer_layout(d);
+  if (packed_bytes < L.total) return TEL_EWORKSPACE;
+  const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
+  char* P = (char*)packed;
+  hipStream_t st = as_stream(stream);
+  TEL_TRY(hipMemcpyAsync(P + L.w_qkv, w->w_qkv, 3 * H * H * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_o, w->w_o, H * H * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_1, w->w_1, F * H * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_2, w->w_2, H * F * es, hipMemcpyDeviceToDevice, st));
+  const int dt = d->dtype;
+  TEL_TRY(launch_widen_f32(dt, w->b_qkv, (float*)(P + L.b_qkv), 3 * H, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_o, (float*)(P + L.b_o), H, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln1_g, (float*)(P + L.ln1_g), H, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln1_b, (float*)(P + L.ln1_b), H, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_1, (float*)(P + L.b_1), F, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_2, (float*)(P + L.b_2), H, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln2_g, (float*)(P + L.ln2_g), H, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln2_b, (float*)(P + L.ln2_b), H, st));
+  return TEL_OK;
+}
+
+size_t tel_encoder_workspace_size(const tel_encoder_desc* d, int max_tokens) {
+  if (desc_supported(d) != TEL_OK || max_tokens < 0) return 0;
+  return layer_ws(d, (size_t)max_tokens).total;
+}
+
+int tel_encoder_layer_forward(const tel_encoder_desc* d, const void* packed, const void* x,
+                              void* y, const int32_t* cu_seqlens, int batch, int total_tokens,
+                              int max_len, void* workspace, size_t ws_bytes, void* stream) {
+  const int sup = desc_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (batch <= 0 || total_tokens < 0 || max_len < 0) return TEL_EINVAL;
+  if (total_tokens == 0) return TEL_OK;
+  if (max_len == 0) return TEL_EINVAL;
+  if (!packed || !x || !y || !cu_seqlens || !workspace) return TEL_EINVAL;
+  if (!aligned256(packed) || !aligned256(workspace) || !aligned16(x) || !aligned16(y))
+    return TEL_EINVAL;
+  if (x == y) return TEL_EINVAL;
+  if (ws_bytes < layer_ws(d, (size_t)total_tokens).total) return TEL_EWORKSPACE;
+  return layer_forward(d, (const char*)packed, x, y, cu_seqlens, batch, total_tokens, max_len,
+                       (char*)workspace, as_stream(stream));
+}
+
+size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* d, int batch, int max_seq) {
+  if (desc_supported(d) != TEL_OK || batch <= 0 || max_seq <= 0) return 0;
+  return stack_ws(d, batch, max_seq).total;
+}
+
+int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_layers, int n_layers,
+                        const void* x_pad, void* y_pad, const int32_t* seq_lens, int batch,
+                        int max_seq, int total_tokens, int max_len, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  const int sup = desc_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (batch <= 0 || max_seq <= 0 || n_layers < 0 || total_tokens < 0 || max_len < 0)
+    return TEL_EINVAL;
+  if ((long long)batch * max_seq > INT32_MAX) return TEL_EUNSUPPORTED;
+  if (total_tokens > batch * max_seq || max_len > max_seq) return TEL_EINVAL;
+  if (total_tokens > 0 && max_len == 0) return TEL_EINVAL;
+  if (!x_pad || !y_pad || !seq_lens || !workspace || (n_layers > 0 && !packed_layers))
+    return TEL_EINVAL;
+  for (int i = 0; i < n_layers; ++i)
+    if (!packed_layers[i] || !aligned256(packed_layers[i])) return TEL_EINVAL;
+  if (!aligned256(workspace) || !aligned16(x_pad) || !aligned16(y_pad)) return TEL_EINVAL;
+  if (x_pad == y_pad) return TEL_EINVAL;
+  const StackWs S = stack_ws(d, batch, max_seq);
+  if (ws_bytes < S.total) return TEL_EWORKSPACE;
+  char* ws = (char*)workspace;
+  int32_t* cu = (int32_t*)(ws + S.cu);
+  int32_t* po = (int32_t*)(ws + S.po);
+  void* xa = ws + S.xa;
+  void* xb = ws + S.xb;
+  hipStream_t st = as_stream(stream);
+  const int row_bytes = d->hidden * dtype_size(d->dtype);
+  TEL_TRY(launch_offsets(seq_lens, batch, max_seq, cu, po, st));
+  TEL_TRY(launch_remove_padding(x_pad, xa, po, total_tokens, row_bytes, st));
+  for (int i = 0; i < n_layers; ++i) {
+    const int r = layer_forward(d, (const char*)packed_layers[i], xa, xb, cu, batch,
+                                total_tokens, max_len, ws + S.layer, st);
+    if (r != TEL_OK) return r;
+    void* t = xa;
+    xa = xb;
+    xb = t;
+  }
+  TEL_TRY(launch_rebuild_padding(xa, y_pad, cu, batch, max_seq, row_bytes, st));
+  return TEL_OK;
+}
+
+int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
+             const void* resid, void* C, int M, int N, int K, int heads, void* stream) {
+  if (!float_type(dtype)) return TEL_EUNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
+  if (epilogue < TEL_EPI_BIAS || epilogue > TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
+  if (M == 0) return TEL_OK;
+  if (!A || !W || !bias || !C) return TEL_EINVAL;
+  if (epilogue == TEL_EPI_BIAS_RESID && !resid) return TEL_EINVAL;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(bias) || !aligned16(C)) return TEL_EINVAL;
+  if (resid && !aligned16(resid)) return TEL_EINVAL;
+  if (K % 8 || N % 4) return TEL_EUNSUPPORTED;
+  if (epilogue == TEL_EPI_QKV_SPLIT) {
+    if (heads <= 0 || N % 3 || (N / 3) % heads || ((N / 3) / heads) % 4) return TEL_EUNSUPPORTED;
+  }
+  GemmArgs g{epilogue, A, W, bias, resid, C, M, N, K, heads};
+  return status_of(launch_gemm(dtype, g, as_stream(stream)));
+}
+
+int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,
+                         int total_tokens, int max_len, int heads, int head_dim, int dtype,
+                         void* stream) {
+  if (batch <= 0 || total_tokens < 0 || max_len < 0 || heads <= 0 || head_dim <= 0)
+    return TEL_EINVAL;
+  if (!attention_supported(dtype, head_dim)) return TEL_EUNSUPPORTED;
+  if (total_tokens == 0) return TEL_OK;
+  if (max_len == 0) return TEL_EINVAL;
+  if (!qkv_split || !ctx || !cu_seqlens) return TEL_EINVAL;
+  if (!aligned16(qkv_split) || !aligned16(ctx)) return TEL_EINVAL;
+  return status_of(launch_attention(dtype, qkv_split, ctx, cu_seqlens, batch, total_tokens,
+                                    max_len, heads, head_dim, as_stream(stream)));
+}
+
+int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,
+                  int width, float eps, int dtype, void* stream) {
+  if (rows < 0 || width <= 0 || !(eps >= 0.f)) return TEL_EINVAL;
+  if (!layernorm_supported(dtype, width)) return TEL_EUNSUPPORTED;
+  if (rows == 0) return TEL_OK;
+  if (!x || !y || !gamma || !beta) return TEL_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta)) return TEL_EINVAL;
+  return status_of(launch_layernorm(dtype, x, y, gamma, beta, rows, width, eps,
+                                    as_stream(stream)));
+}
+
+}  // extern "C"

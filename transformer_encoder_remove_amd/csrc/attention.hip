@@ -1,0 +1,218 @@
+// Variable-length multi-head self-attention over packed sequences, one fused kernel
+// (the fMHA of the Swin talk "大規模なビジュアル モデル…", section 3: batched GEMM, softmax
+// and batched GEMM in one kernel, with the head transposes folded into its loads and
+// stores). Padding never enters: a query of sequence b reads only the keys
+// cu[b] .. cu[b+1]-1 (Kuaishou "如何让Transformer在GPU上跑得更快", Fig. 10).
+//
+// Input: Q, K, V head-split as [3][heads][T][D] (the QKV GEMM's epilogue layout), so a
+// head's keys are one contiguous [len][D] block. Output: ctx [T][heads * D].
+//
+// Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid =
+// (ceil(max_len / 64), heads, batch), workgroups past a sequence's end exit at once.
+// Per 64-key block:
+//  * K [64][D] and V^T [D][64] are staged in LDS (16-byte global loads);
+//  * each wavefront computes S^T = K Q^T for its 16 queries with 16x16 MFMAs, so that
+//    every lane holds scores of ONE query (column l % 16) for 16 keys;
+//  * online softmax in base 2: the row max and row sum need only the lane's own 16
+//    values plus two cross-lane butterflies (xor 16, xor 32);
+//  * O^T += V^T P^T with P^T taken straight from the score registers (no LDS round
+//    trip): the MFMA k index is mapped to the keys each lane already holds, and the
+//    V^T fragment is read with the same mapping;
+//  * O^T keeps one query per lane as well, so the rescale by exp2(m_old - m_new) and
+//    the final 1/l are per-lane scalars.
+#include <math.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace tel {
+
+constexpr int ATT_QB = 64;   // queries per workgroup
+constexpr int ATT_KB = 64;   // keys per LDS block
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ qkv,
+                                                          T* __restrict__ ctx,
+                                                          const int32_t* __restrict__ cu,
+                                                          int total_tokens, int heads,
+                                                          float scale_log2) {
+  using MF = Mfma<T>;
+  typedef typename MF::frag frag;
+  constexpr int KPL = MF::KPL, KMF = 4 * KPL;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LDK = D + VEC;
+  constexpr int LDV = ATT_KB + (sizeof(T) == 4 ? 1 : 4);
+  constexpr int NKS = (D + KMF - 1) / KMF;
+  constexpr int NCB = D / 16;
+  constexpr int NJ = ATT_KB / 16;
+  constexpr int VPRK = D / VEC;
+  static_assert(D % 16 == 0 && D % VEC == 0, "head_dim");
+
+  __shared__ __attribute__((aligned(16))) T sK[ATT_KB * LDK];
+  __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int start = cu[b], L = cu[b + 1] - start;
+  const int q0 = blockIdx.x * ATT_QB;
+  if (q0 >= L) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const size_t hs = (size_t)total_tokens * D;
+  const T* Qh = qkv + (size_t)h * hs + (size_t)start * D;
+  const T* Kh = qkv + (size_t)(heads + h) * hs + (size_t)start * D;
+  const T* Vh = qkv + (size_t)(2 * heads + h) * hs + (size_t)start * D;
+
+  const int qi = q0 + wave * 16 + lr;
+  const int qc = min(qi, L - 1);
+  frag qf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int d0 = s * KMF + lg * KPL;
+    qf[s] = (d0 < D) ? *reinterpret_cast<const frag*>(Qh + (size_t)qc * D + d0) : frag{};
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb0 = 0; kb0 < L; kb0 += ATT_KB) {
+    for (int idx = tid; idx < ATT_KB * VPRK; idx += 256) {
+      const int r = idx / VPRK, v = idx - r * VPRK;
+      const int key = min(kb0 + r, L - 1);
+      const Vec16<T> kv = *reinterpret_cast<const Vec16<T>*>(Kh + (size_t)key * D + v * VEC);
+      *reinterpret_cast<Vec16<T>*>(&sK[r * LDK + v * VEC]) = kv;
+      const Vec16<T> vv = *reinterpret_cast<const Vec16<T>*>(Vh + (size_t)key * D + v * VEC);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sVt[(v * VEC + e) * LDV + r] = vv.v[e];
+    }
+    __syncthreads();
+
+    // scores S^T[key][query] for 4 sub-blocks of 16 keys
+    f32x4 sc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int d0 = s * KMF + lg * KPL;
+        const frag kf = (d0 < D) ? *reinterpret_cast<const frag*>(&sK[(j * 16 + lr) * LDK + d0])
+                                 : frag{};
+        sc[j] = MF::mma(kf, qf[s], sc[j]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb0 + j * 16 + lg * 4 + i;
+        const float s = key < L ? sc[j][i] * scale_log2 : -INFINITY;
+        sc[j][i] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);       // finite: key 0 of the sequence is valid
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sc[j][i] - m_new);
+        sc[j][i] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) o[c] *= alpha;
+
+    // O^T[c][q] += sum_key V^T[c][key] * P^T[key][q]; MFMA k element e of step t is the
+    // lane's score f = t*KPL + e, i.e. key 16*(f/4) + 4*lg + f%4.
+#pragma unroll
+    for (int t = 0; t < ATT_KB / KMF; ++t) {
+      T pv[KPL];
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const int f = t * KPL + e;
+        pv[e] = from_f32<T>(sc[f / 4][f % 4]);
+      }
+      frag pb;
+      __builtin_memcpy(&pb, pv, sizeof(frag));
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const T* vrow = &sVt[(c * 16 + lr) * LDV];
+        frag va;
+        if constexpr (KPL == 8) {
+          T tmp[8];
+          const int k0 = 16 * (2 * t) + 4 * lg, k1 = k0 + 16;
+          __builtin_memcpy(tmp, vrow + k0, 4 * sizeof(T));
+          __builtin_memcpy(tmp + 4, vrow + k1, 4 * sizeof(T));
+          __builtin_memcpy(&va, tmp, sizeof(frag));
+        } else {
+          const int f = t;
+          va = vrow[16 * (f / 4) + 4 * lg + (f % 4)];
+        }
+        o[c] = MF::mma(va, pb, o[c]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (qi < L) {
+    const float inv_l = 1.f / l_run;
+    T* out = ctx + (size_t)(start + qi) * (heads * D) + h * D;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      Vec4<T> w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w.v[i] = from_f32<T>(o[c][i] * inv_l);
+      *reinterpret_cast<Vec4<T>*>(out + c * 16 + 4 * lg) = w;
+    }
+  }
+}
+
+bool attention_supported(int dtype, int head_dim) {
+  if (dtype != DT_F16 && dtype != DT_BF16 && dtype != DT_F32) return false;
+  return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
+}
+
+template <typename T, int D>
+static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
+                           int max_len, int heads, hipStream_t stream) {
+  const dim3 grid((max_len + ATT_QB - 1) / ATT_QB, heads, batch);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  attn_varlen_kernel<T, D><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total, heads,
+                                                     scale_log2);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t run_attn_d(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
+                             int max_len, int heads, int d, hipStream_t stream) {
+  switch (d) {
+    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, stream);
+    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, stream);
+    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, stream);
+    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
+                            int total, int max_len, int heads, int head_dim, hipStream_t stream) {
+  if (total == 0 || max_len == 0) return hipSuccess;
+  switch (dtype) {
+    case DT_F16: return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
+    case DT_BF16: return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
+    case DT_F32: return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tel

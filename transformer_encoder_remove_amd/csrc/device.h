@@ -1,0 +1,91 @@
+// Device-side helpers shared by the library's HIP kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tel {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16 bytes of elements, the unit of every vector global load/store here.
+template <typename T> struct alignas(16) Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+  T v[N];
+};
+// 4 elements (8 bytes for 16-bit types, 16 for fp32): the epilogue store unit.
+template <typename T> struct alignas(4 * sizeof(T)) Vec4 { T v[4]; };
+
+// ------------------------------------------------------------------ MFMA 16x16 shapes
+// One wavefront computes D[16][16] += A[16][K] * B[K][16]. Lane l holds KPL consecutive
+// k of A row (l % 16) and of B column (l % 16), at k offset KPL * (l / 16) (the same
+// mapping for both operands, which is all a dot product needs); it receives
+// D[4 * (l / 16) + i][l % 16] for i = 0..3.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<f16> {
+  static constexpr int KPL = 8;                 // 16x16x32
+  typedef f16x8 frag;
+  typedef f32x4 acc;
+  __device__ __forceinline__ static acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;                 // 16x16x32
+  typedef bf16x8 frag;
+  typedef f32x4 acc;
+  __device__ __forceinline__ static acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;                 // 16x16x4
+  typedef float frag;
+  typedef f32x4 acc;
+  __device__ __forceinline__ static acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<int8_t> {
+  static constexpr int KPL = 16;                // 16x16x64, int32 accumulation
+  typedef i32x4 frag;
+  typedef i32x4 acc;
+  __device__ __forceinline__ static acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------ wavefront reductions
+template <int G> __device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <int G> __device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+}  // namespace tel

@@ -1,0 +1,50 @@
+// Host-side launchers of the library's kernels (internal; the public ABI is include/tel.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tel {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
+enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3 };
+
+inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
+
+// offsets.hip
+hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* cu,
+                          int32_t* padding_offset, hipStream_t stream);
+// padding.hip (row_bytes % 16 == 0)
+hipError_t launch_remove_padding(const void* x_pad, void* x_packed, const int32_t* padding_offset,
+                                 int total_tokens, int row_bytes, hipStream_t stream);
+hipError_t launch_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu, int batch,
+                                  int max_seq, int row_bytes, hipStream_t stream);
+
+// gemm.hip
+struct GemmArgs {
+  int epi;
+  const void* A;        // [M][K]
+  const void* W;        // [N][K]
+  const float* bias;    // [N] float32
+  const void* resid;    // [M][N] (EPI_BIAS_RESID)
+  void* C;
+  int M, N, K;
+  int heads;            // EPI_QKV_SPLIT
+};
+hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
+
+// attention.hip
+bool attention_supported(int dtype, int head_dim);
+hipError_t launch_attention(int dtype, const void* qkv_split, void* ctx, const int32_t* cu,
+                            int batch, int total_tokens, int max_len, int heads, int head_dim,
+                            hipStream_t stream);
+
+// layernorm.hip
+bool layernorm_supported(int dtype, int width);
+hipError_t launch_layernorm(int dtype, const void* x, void* y, const float* gamma,
+                            const float* beta, int rows, int width, float eps, hipStream_t stream);
+
+// prepare.hip
+hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);
+
+}  // namespace tel

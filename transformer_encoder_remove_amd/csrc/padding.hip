@@ -1,0 +1,67 @@
+// Padding removal and rebuild (Kuaishou "如何让Transformer在GPU上跑得更快", Figs. 9-10):
+// whole rows move between the padded [B*S][W] layout and the packed [T][W] layout.
+// Bandwidth-bound copies: every thread moves 16-byte vectors, consecutive threads cover
+// consecutive bytes of a row, so each wavefront reads and writes 1 KiB contiguous runs.
+#include "device.h"
+#include "launch.h"
+
+namespace tel {
+
+constexpr int PAD_THREADS = 256;
+
+__global__ __launch_bounds__(PAD_THREADS) void remove_padding_kernel(
+    const u32x4* __restrict__ x_pad, u32x4* __restrict__ x_packed,
+    const int32_t* __restrict__ po, int total_tokens, int vec_per_row) {
+  const size_t n = (size_t)total_tokens * vec_per_row;
+  for (size_t i = (size_t)blockIdx.x * PAD_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * PAD_THREADS) {
+    const int t = (int)(i / vec_per_row), v = (int)(i - (size_t)t * vec_per_row);
+    const size_t src_row = (size_t)t + po[t];
+    x_packed[i] = __builtin_nontemporal_load(&x_pad[src_row * vec_per_row + v]);
+  }
+}
+
+__global__ __launch_bounds__(PAD_THREADS) void rebuild_padding_kernel(
+    const u32x4* __restrict__ x_packed, u32x4* __restrict__ x_pad,
+    const int32_t* __restrict__ cu, int max_seq, int batch, int vec_per_row) {
+  const size_t n = (size_t)batch * max_seq * vec_per_row;
+  for (size_t i = (size_t)blockIdx.x * PAD_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * PAD_THREADS) {
+    const size_t r = i / vec_per_row;
+    const int v = (int)(i - r * vec_per_row);
+    const int b = (int)(r / max_seq), p = (int)(r - (size_t)b * max_seq);
+    const int32_t start = cu[b], len = cu[b + 1] - start;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (p < len) val = x_packed[(size_t)(start + p) * vec_per_row + v];
+    __builtin_nontemporal_store(val, &x_pad[i]);
+  }
+}
+
+static int grid_for(size_t n) {
+  size_t blocks = (n + PAD_THREADS - 1) / PAD_THREADS;
+  const size_t cap = 256 * 32;   // enough waves to fill 256 CUs; the loop covers the rest
+  if (blocks > cap) blocks = cap;
+  return (int)(blocks == 0 ? 1 : blocks);
+}
+
+hipError_t launch_remove_padding(const void* x_pad, void* x_packed, const int32_t* po,
+                                 int total_tokens, int row_bytes, hipStream_t stream) {
+  const int vpr = row_bytes / 16;
+  const size_t n = (size_t)total_tokens * vpr;
+  if (n == 0) return hipSuccess;
+  remove_padding_kernel<<<grid_for(n), PAD_THREADS, 0, stream>>>(
+      (const u32x4*)x_pad, (u32x4*)x_packed, po, total_tokens, vpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu, int batch,
+                                  int max_seq, int row_bytes, hipStream_t stream) {
+  const int vpr = row_bytes / 16;
+  const size_t n = (size_t)batch * max_seq * vpr;
+  if (n == 0) return hipSuccess;
+  rebuild_padding_kernel<<<grid_for(n), PAD_THREADS, 0, stream>>>(
+      (const u32x4*)x_packed, (u32x4*)x_pad, cu, max_seq, batch, vpr);
+  return hipGetLastError();
+}
+
+}  // namespace tel

@@ -1,0 +1,26 @@
+// One-time weight preprocessing kernels (the Swin talk "大規模なビジュアル モデル…",
+// section 3: work that needs doing only once is done ahead of inference and reused).
+#include "device.h"
+#include "launch.h"
+
+namespace tel {
+
+template <typename T>
+__global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ src, float* __restrict__ dst,
+                                                    int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) dst[i] = to_f32(src[i]);
+}
+
+hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int grid = min((n + 255) / 256, 1024);
+  switch (dtype) {
+    case DT_F16: widen_kernel<f16><<<grid, 256, 0, stream>>>((const f16*)src, dst, n); break;
+    case DT_BF16: widen_kernel<bf16><<<grid, 256, 0, stream>>>((const bf16*)src, dst, n); break;
+    case DT_F32: widen_kernel<float><<<grid, 256, 0, stream>>>((const float*)src, dst, n); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tel
