@@ -166,6 +166,17 @@ typedef enum {
 int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
              const void* resid, void* C, int M, int N, int K, int heads, void* stream);
 
+/* Number of entries in the GEMM tile table (tile_config 0 .. n-1 of tel_gemm_ex). */
+int tel_gemm_tile_configs(void);
+
+/* tel_gemm with an explicit tile configuration, for tuning and tests:
+ *   -2 = automatic (the choice tel_gemm makes), -1 = register-staged 64x64 kernel (any K with
+ *   K % 8 == 0), 0 .. n-1 = entries of the pipelined tile table (K * element size must be
+ *   a multiple of 128 bytes). Other arguments as tel_gemm. */
+int tel_gemm_ex(int epilogue, int dtype, int tile_config, const void* A, const void* W,
+                const float* bias, const void* resid, void* C, int M, int N, int K, int heads,
+                void* stream);
+
 /* Variable-length multi-head attention ([SW] section 3, fMHA: batched GEMM, softmax and
  * batched GEMM in one kernel). qkv_split [3][heads][total_tokens][head_dim] (the
  * TEL_EPI_QKV_SPLIT layout); ctx [total_tokens][heads*head_dim]; query i of sequence b

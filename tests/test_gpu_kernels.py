@@ -108,3 +108,17 @@ def test_layernorm(dtype, rows, width):
     torch.cuda.synchronize()
     assert_close(host(y), enc.layer_norm(x, g.astype(np.float32), b.astype(np.float32), EPS),
                  dtype, "layernorm")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(300, 400, 320), (2557, 768, 768), (17, 1028, 64)])
+def test_gemm_every_tile_config(dtype, M, N, K):
+    """Each entry of the tile table (and the register-staged kernel) on ragged M and N."""
+    a, w, b, r = _operands(M, N, K, dtype, seed=7 + M)
+    A, W, R, bias = dev(a, dtype), dev(w, dtype), dev(r, dtype), dev_f32(b)
+    ref = enc.linear(a, w, b) + r.astype(np.float64)
+    for cfg in range(-1, tel.tel_gemm_tile_configs()):
+        C = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+        tel.tel_gemm_ex(tel.TEL_EPI_BIAS_RESID, cfg, A, W, bias, C, resid=R)
+        torch.cuda.synchronize()
+        assert_close(host(C), ref, dtype, f"tile config {cfg} {dtype} {M}x{N}x{K}")

@@ -1,6 +1,8 @@
 """Build libtel.so for gfx950 with hipcc (in-tree: the library lands next to this file).
 
-    python -m transformer_encoder_remove_amd.build [-v]
+    python transformer_encoder_remove_amd/build.py [-v]
+
+(Run as a script, not with -m: importing the package loads the library it builds.)
 
 Every source under csrc/ is compiled to an object in <repo>/_build/ (parallel jobs),
 then linked into transformer_encoder_remove_amd/libtel.so.

@@ -75,19 +75,27 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
 }
 
 // ------------------------------------------------------------------ layer workspace
+// A bf16 layer keeps its pre-LayerNorm sums and its residual stream (h1) in float32:
+// bf16 keeps 8 significant bits, and rounding those two values to bf16 alone costs more
+// than the 2e-2 absolute error budget at |y| ~ 4; fp16 and fp32 layers keep them in
+// their storage type.
 struct LayerWs {
-  size_t qkv, ctx, pre, h1, f, total;
+  size_t qkv, ctx, pre, h1, h1f, f, total;
 };
+
+inline bool f32_stream(const tel_encoder_desc* d) { return d->dtype == DT_BF16; }
 
 LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
+  const size_t pes = f32_stream(d) ? 4 : es;
   LayerWs w;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   w.qkv = take(3 * T * H * es);
   w.ctx = take(T * H * es);
-  w.pre = take(T * H * es);
+  w.pre = take(T * H * pes);
   w.h1 = take(T * H * es);
+  w.h1f = f32_stream(d) ? take(T * H * 4) : 0;
   w.f = take(T * F * es);
   w.total = o;
   return w;
@@ -122,6 +130,9 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   void* pre = ws + W.pre;
   void* h1 = ws + W.h1;
   void* f = ws + W.f;
+  const bool f32s = f32_stream(d);
+  float* h1f = f32s ? (float*)(ws + W.h1f) : nullptr;
+  const int pre_dt = f32s ? (int)DT_F32 : dt;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
 
   GemmArgs g{};
@@ -130,15 +141,18 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   TEL_TRY(launch_gemm(dt, g, st));
   TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
   // output projection + bias + residual, then LayerNorm
-  g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
+  g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
   TEL_TRY(launch_gemm(dt, g, st));
-  TEL_TRY(launch_layernorm(dt, pre, h1, F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, st));
+  TEL_TRY(launch_layernorm(pre_dt, dt, pre, h1, h1f, F32(L.ln1_g), F32(L.ln1_b), T, H,
+                           d->ln_eps, st));
   // FFN: bias + GELU, then bias + residual, then LayerNorm
   g = GemmArgs{EPI_BIAS_GELU, h1, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
   TEL_TRY(launch_gemm(dt, g, st));
-  g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
+  g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), f32s ? (const void*)h1f : h1, pre,
+               T, H, F, nh, f32s, f32s};
   TEL_TRY(launch_gemm(dt, g, st));
-  TEL_TRY(launch_layernorm(dt, pre, y, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, st));
+  TEL_TRY(launch_layernorm(pre_dt, dt, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                           d->ln_eps, st));
   return TEL_OK;
 }
 
@@ -295,22 +309,34 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   return TEL_OK;
 }
 
-int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
-             const void* resid, void* C, int M, int N, int K, int heads, void* stream) {
+int tel_gemm_tile_configs(void) { return gemm_tile_configs(); }
+
+int tel_gemm_ex(int epilogue, int dtype, int tile_config, const void* A, const void* W,
+                const float* bias, const void* resid, void* C, int M, int N, int K, int heads,
+                void* stream) {
   if (!float_type(dtype)) return TEL_EUNSUPPORTED;
   if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
   if (epilogue < TEL_EPI_BIAS || epilogue > TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
+  if (tile_config < -2 || tile_config >= gemm_tile_configs()) return TEL_EINVAL;
   if (M == 0) return TEL_OK;
   if (!A || !W || !bias || !C) return TEL_EINVAL;
   if (epilogue == TEL_EPI_BIAS_RESID && !resid) return TEL_EINVAL;
   if (!aligned16(A) || !aligned16(W) || !aligned16(bias) || !aligned16(C)) return TEL_EINVAL;
   if (resid && !aligned16(resid)) return TEL_EINVAL;
   if (K % 8 || N % 4) return TEL_EUNSUPPORTED;
+  if (tile_config >= 0 && ((long long)K * dtype_size(dtype)) % 128) return TEL_EUNSUPPORTED;
   if (epilogue == TEL_EPI_QKV_SPLIT) {
     if (heads <= 0 || N % 3 || (N / 3) % heads || ((N / 3) / heads) % 4) return TEL_EUNSUPPORTED;
   }
   GemmArgs g{epilogue, A, W, bias, resid, C, M, N, K, heads};
-  return status_of(launch_gemm(dtype, g, as_stream(stream)));
+  const hipStream_t st = as_stream(stream);
+  return status_of(tile_config == -2 ? launch_gemm(dtype, g, st)
+                                     : launch_gemm_cfg(dtype, tile_config, g, st));
+}
+
+int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
+             const void* resid, void* C, int M, int N, int K, int heads, void* stream) {
+  return tel_gemm_ex(epilogue, dtype, -2, A, W, bias, resid, C, M, N, K, heads, stream);
 }
 
 int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,
@@ -334,7 +360,7 @@ int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta,
   if (rows == 0) return TEL_OK;
   if (!x || !y || !gamma || !beta) return TEL_EINVAL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta)) return TEL_EINVAL;
-  return status_of(launch_layernorm(dtype, x, y, gamma, beta, rows, width, eps,
+  return status_of(launch_layernorm(dtype, dtype, x, y, nullptr, gamma, beta, rows, width, eps,
                                     as_stream(stream)));
 }
 

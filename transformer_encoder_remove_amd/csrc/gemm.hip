@@ -23,30 +23,36 @@
 //    4 biases with one 16-byte load and stores 4 outputs with one 8-byte store;
 //  * ragged M and N: rows past the end are clamped on load (their results are never
 //    stored); K % (16 bytes) == 0 is required, slices past K are zero-filled.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
 namespace tel {
 
-template <typename T> struct EpiArgs {
+// Epilogue operands. The residual and the output of EPI_BIAS_RESID may be float32
+// (TR, TO) so that a bf16 layer can keep its pre-LayerNorm sums and residual stream in
+// float32; every other output has the operand type T.
+template <typename T, typename TR, typename TO> struct EpiArgs {
   const float* bias;
-  const T* resid;
-  T* C;
+  const TR* resid;
+  TO* C;
   int M, N, heads;
 };
 
-template <int EPI, typename T>
-__device__ __forceinline__ void epilogue_store(const EpiArgs<T>& e, int m, int n, f32x4 acc) {
+template <int EPI, typename T, typename TR, typename TO>
+__device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
+                                               f32x4 acc) {
   const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
   float v[4] = {acc[0] + b.x, acc[1] + b.y, acc[2] + b.z, acc[3] + b.w};
-  Vec4<T> out;
+  Vec4<TO> out;
   size_t idx;
   if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
   }
   if constexpr (EPI == EPI_BIAS_RESID) {
-    const Vec4<T> r = *reinterpret_cast<const Vec4<T>*>(e.resid + (size_t)m * e.N + n);
+    const Vec4<TR> r = *reinterpret_cast<const Vec4<TR>*>(e.resid + (size_t)m * e.N + n);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] += to_f32(r.v[i]);
   }
@@ -60,14 +66,14 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T>& e, int m, int n
     idx = (size_t)m * e.N + n;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out.v[i] = from_f32<T>(v[i]);
-  *reinterpret_cast<Vec4<T>*>(e.C + idx) = out;
+  for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(v[i]);
+  *reinterpret_cast<Vec4<TO>*>(e.C + idx) = out;
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int EPI>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int EPI, typename TR, typename TO>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ W, int K,
-                                                              EpiArgs<T> e) {
+                                                              EpiArgs<T, TR, TO> e) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int NT = WM * WN * 64;
@@ -160,33 +166,262 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int m = m0 + wm * TM + j * 16 + lr;
-      if (m < M && n < N) epilogue_store<EPI, T>(e, m, n, acc[i][j]);
+      if (m < M && n < N) epilogue_store<EPI, T, TR, TO>(e, m, n, acc[i][j]);
     }
   }
 #undef TEL_GEMM_FETCH
 #undef TEL_GEMM_STASH
 }
 
+// ------------------------------------------------------------------ pipelined variant
+// Same contract as gemm_nt_kernel, for K % (128 bytes) == 0. Warp-specialised:
+//  * WM x WN compute wavefronts read MFMA fragments from LDS and run the MFMAs;
+//  * 2 producer wavefronts copy k-slices from global memory straight into LDS with the
+//    gfx950 direct path (global_load_lds_dwordx4: lane i's 16 bytes land at LDS base +
+//    16 * i, no VGPR staging), keeping S - 1 slices in flight in an S-stage LDS ring.
+// One barrier per slice: a producer passes barrier kt once slice kt has landed (its own
+// vmcnt), a compute wave reaches it once its reads of slice kt - 1 are done; after it the
+// producers refill the stage of slice kt - 1. Keeping the copies out of the compute
+// wavefronts matters for the schedule: with copies in the same instruction stream the
+// compiler's wait-count analysis waits for every outstanding LDS read before each MFMA
+// block, serialising LDS reads and MFMAs. Compute wavefronts double-buffer fragments in
+// registers: the next k-step's reads (also across a slice boundary) are issued before
+// the current k-step's MFMAs. Two producers, because one wavefront can have at most 63
+// copies outstanding.
+//
+// LDS rows are 128 bytes (8 chunks of 16 bytes) with no padding; bank conflicts are avoided
+// by an XOR swizzle: chunk c of row r is stored in slot c ^ (r % 8). A copy instruction
+// fills a block of 8 rows (1 KiB); lane i fills slot i % 8 of row i / 8, so it fetches chunk
+// (i % 8) ^ (i / 8) of that row: 8 lanes still cover each 128-byte row segment.
+//
+// Workgroup -> tile order is XCD-aware: the dispatcher hands consecutive workgroup ids to
+// the 8 XCDs in turn, so ids are regrouped so that each XCD walks a contiguous run of
+// tiles (M-fastest), i.e. the tiles that share weight columns share that XCD's L2.
+
+constexpr int PIPE_PRODUCERS = 2;
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
+  constexpr int NX = 8;
+  const int per = ntiles / NX, extra = ntiles % NX;   // the first `extra` XCDs get one more
+  const int x = bid % NX, i = bid / NX;
+  if (i >= per + (x < extra ? 1 : 0)) return bid;     // unreachable when grid == ntiles
+  return x * per + min(x, extra) + i;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
+__global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
+    const T* __restrict__ A, const T* __restrict__ W, int K, EpiArgs<T, TR, TO> e) {
+  using MF = Mfma<T>;
+  typedef typename MF::frag frag;
+  constexpr int NW = WM * WN;                       // compute wavefronts
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int BK = 8 * VEC;                       // 128-byte rows
+  constexpr int KPL = MF::KPL, KMF = 4 * KPL;
+  constexpr int KS = BK / KMF;                      // k-steps per slice (even)
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int NB = (BM + BN) / 8;                 // 1 KiB blocks per slice
+  constexpr int LJ = NB / PIPE_PRODUCERS;           // copies per producer per slice
+  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int INFLIGHT = LJ * (S - 2) < 63 ? LJ * (S - 2) : 63;
+  static_assert(NB % PIPE_PRODUCERS == 0 && BM % 8 == 0 && BN % 8 == 0, "copy split");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+  static_assert(KS % 2 == 0, "k-steps per slice must be even");
+  static_assert(S >= 2, "stages");
+
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+  const int M = e.M, N = e.N;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nk = K / BK;
+
+  if (wave >= NW) {
+    // ---------------- producer: block b = p + PIPE_PRODUCERS * j of every slice
+    const int p = wave - NW;
+    const T* src[LJ];
+    const int chunk = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int j = 0; j < LJ; ++j) {
+      const int b = p + PIPE_PRODUCERS * j;
+      if (b < BM / 8) {
+        src[j] = A + (size_t)min(m0 + b * 8 + (lane >> 3), M - 1) * K + chunk * VEC;
+      } else {
+        src[j] = W + (size_t)min(n0 + (b - BM / 8) * 8 + (lane >> 3), N - 1) * K + chunk * VEC;
+      }
+    }
+    // copy k-slice `data` into the stage of slice number `slot`
+    auto issue = [&](int slot, int data) {
+      char* dst = smem + (slot % S) * STAGE + p * 1024;
+      const size_t koff = (size_t)data * BK;
+#pragma unroll
+      for (int j = 0; j < LJ; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src[j] + koff),
+            (void __attribute__((address_space(3)))*)(dst + j * PIPE_PRODUCERS * 1024), 16, 0, 0);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue(s, min(s, nk - 1));
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<INFLIGHT>();                   // slice kt has landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(kt + S - 1, min(kt + S - 1, nk - 1));   // into the stage of slice kt - 1
+    }
+    __builtin_amdgcn_s_barrier();   // matches the compute wavefronts' final barrier
+    wait_vmcnt<0>();   // no copy may still be writing LDS when the workgroup ends
+    return;
+  }
+
+  // ---------------- compute wavefronts
+  const int wm = wave % WM, wn = wave / WM;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int xr = lr & 7;
+  const int rowA = (wm * TM + lr) * 128, rowW = BM * 128 + (wn * TN + lr) * 128;
+  frag fa[2][FN], fb[2][FM];
+#define TEL_PIPE_FRAGS(buf, slice, kk)                                                      \
+  do {                                                                                      \
+    const char* st_ = smem + ((slice) % S) * STAGE;                                         \
+    const int k_ = (kk) * KMF + lg * KPL;                                                   \
+    const int off_ = (((k_ / VEC) ^ xr) * 16) + (k_ % VEC) * (int)sizeof(T);                \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[buf][i] =                            \
+        *reinterpret_cast<const frag*>(st_ + rowW + i * 16 * 128 + off_);                   \
+    _Pragma("unroll") for (int j = 0; j < FM; ++j) fb[buf][j] =                            \
+        *reinterpret_cast<const frag*>(st_ + rowA + j * 16 * 128 + off_);                   \
+  } while (0)
+
+  typename MF::acc acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = typename MF::acc{};
+
+  // Materialise the epilogue's kernel arguments before the loop: a scalar load still in
+  // flight there would make the compiler wait for every LDS read before each MFMA block.
+  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads));
+  __builtin_amdgcn_s_barrier();                     // slice 0 has landed
+  asm volatile("" ::: "memory");
+  TEL_PIPE_FRAGS(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KS) {
+        TEL_PIPE_FRAGS(cur ^ 1, kt, kk + 1);
+      } else {
+        // Branch-free on purpose (a conditional here makes the compiler wait for every
+        // outstanding LDS read before the MFMAs below). After the last slice this is one
+        // extra barrier, matched by the producers, and a read nobody uses.
+        wait_lgkmcnt0();                            // reads of slice kt are done
+        __builtin_amdgcn_s_barrier();               // slice kt + 1 has landed
+        asm volatile("" ::: "memory");
+        TEL_PIPE_FRAGS(cur ^ 1, min(kt + 1, nk - 1), 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::mma(fa[cur][i], fb[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef TEL_PIPE_FRAGS
+
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * TN + i * 16 + lg * 4;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * TM + j * 16 + lr;
+      if (m < M && n < N) epilogue_store<EPI, T, TR, TO>(e, m, n, acc[i][j]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
-template <typename T, int BM, int BN, int WM, int WN>
-static hipError_t run_cfg(const GemmArgs& a, hipStream_t stream) {
+// Tile configurations. The register-staged kernel (gemm_nt_kernel) serves K that is not a
+// multiple of 128 bytes; every other shape uses the pipelined kernel with one of these
+// tiles (the GEMM-configuration tuning of the Kuaishou article, Fig. 11).
+struct PipeCfg { int bm, bn, wm, wn, s; };
+constexpr PipeCfg PIPE_CFGS[] = {
+    {128, 256, 2, 4, 3},   // 0: 8 waves, wave tile 64x64, 144 KiB LDS
+    {128, 192, 2, 4, 3},   // 1: 8 waves, wave tile 64x48, 120 KiB
+    {128, 128, 2, 2, 4},   // 2: 4 waves, wave tile 64x64, 128 KiB
+    {64, 128, 2, 2, 4},    // 3: 4 waves, wave tile 32x64, 96 KiB
+    {64, 64, 2, 2, 4},     // 4: 4 waves, wave tile 32x32, 64 KiB
+    {128, 256, 2, 2, 3},   // 5: 4 waves, wave tile 64x128, 144 KiB
+    {256, 128, 2, 2, 3},   // 6: 4 waves, wave tile 128x64, 144 KiB
+    {128, 128, 2, 2, 2},   // 7: 4 waves, wave tile 64x64, 64 KiB (two workgroups per CU)
+    {64, 128, 1, 2, 3},    // 8: 2 waves, wave tile 64x64, 72 KiB
+};
+constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
+
+template <typename T, int BM, int BN, int WM, int WN, int EPI, typename TR, typename TO>
+static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
-  EpiArgs<T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads};
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads};
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const T* A = (const T*)a.A;
-  const T* W = (const T*)a.W;
+  gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI, TR, TO><<<grid, WM * WN * 64, 0, stream>>>(
+      (const T*)a.A, (const T*)a.W, a.K, e);
+}
+
+template <typename T, int C, int EPI, typename TR, typename TO>
+static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
+  constexpr PipeCfg c = PIPE_CFGS[C];
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads};
+  const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
+  gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
+      <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>((const T*)a.A, (const T*)a.W,
+                                                                 a.K, e);
+}
+
+// cfg < 0: register-staged 64x64 kernel; otherwise PIPE_CFGS[cfg].
+template <typename T, int EPI, typename TR, typename TO>
+static void launch_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
+  switch (cfg) {
+    case 0: launch_pipe<T, 0, EPI, TR, TO>(a, stream); break;
+    case 1: launch_pipe<T, 1, EPI, TR, TO>(a, stream); break;
+    case 2: launch_pipe<T, 2, EPI, TR, TO>(a, stream); break;
+    case 3: launch_pipe<T, 3, EPI, TR, TO>(a, stream); break;
+    case 4: launch_pipe<T, 4, EPI, TR, TO>(a, stream); break;
+    case 5: launch_pipe<T, 5, EPI, TR, TO>(a, stream); break;
+    case 6: launch_pipe<T, 6, EPI, TR, TO>(a, stream); break;
+    case 7: launch_pipe<T, 7, EPI, TR, TO>(a, stream); break;
+    case 8: launch_pipe<T, 8, EPI, TR, TO>(a, stream); break;
+    default: launch_one<T, 64, 64, 2, 2, EPI, TR, TO>(a, stream); break;
+  }
+}
+
+template <typename T>
+static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
   switch (a.epi) {
-    case EPI_BIAS:
-      gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI_BIAS><<<grid, WM * WN * 64, 0, stream>>>(A, W, a.K, e);
-      break;
-    case EPI_BIAS_GELU:
-      gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI_BIAS_GELU><<<grid, WM * WN * 64, 0, stream>>>(A, W, a.K, e);
-      break;
+    case EPI_BIAS: launch_cfg<T, EPI_BIAS, T, T>(cfg, a, stream); break;
+    case EPI_BIAS_GELU: launch_cfg<T, EPI_BIAS_GELU, T, T>(cfg, a, stream); break;
+    case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, T, T>(cfg, a, stream); break;
     case EPI_BIAS_RESID:
-      gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI_BIAS_RESID><<<grid, WM * WN * 64, 0, stream>>>(A, W, a.K, e);
-      break;
-    case EPI_QKV_SPLIT:
-      gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI_QKV_SPLIT><<<grid, WM * WN * 64, 0, stream>>>(A, W, a.K, e);
+      if constexpr (std::is_same<T, bf16>::value) {
+        if (a.resid_f32 && a.out_f32) {
+          launch_cfg<T, EPI_BIAS_RESID, float, float>(cfg, a, stream);
+          break;
+        }
+        if (a.out_f32 && !a.resid_f32) {
+          launch_cfg<T, EPI_BIAS_RESID, T, float>(cfg, a, stream);
+          break;
+        }
+      }
+      if (a.resid_f32 || a.out_f32) return hipErrorInvalidValue;
+      launch_cfg<T, EPI_BIAS_RESID, T, T>(cfg, a, stream);
       break;
     default:
       return hipErrorInvalidValue;
@@ -194,22 +429,39 @@ static hipError_t run_cfg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile choice per shape (the GEMM-configuration tuning of the Kuaishou article, Fig. 11):
-// the largest tile that still gives at least one workgroup per compute unit (256).
-template <typename T>
-static hipError_t run_typed(const GemmArgs& a, hipStream_t stream) {
-  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (tiles(128, 128) >= 256) return run_cfg<T, 128, 128, 2, 2>(a, stream);
-  if (tiles(128, 64) >= 256) return run_cfg<T, 128, 64, 2, 2>(a, stream);
-  return run_cfg<T, 64, 64, 2, 2>(a, stream);
+// The largest tile that still yields about one workgroup per compute unit.
+static int pick_cfg(const GemmArgs& a, int elem_bytes) {
+  if ((a.K * elem_bytes) % 128) return -1;
+  for (int c = 0; c < 5; ++c) {
+    const PipeCfg& p = PIPE_CFGS[c];
+    const long tiles = (long)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
+    if (tiles >= 200) return c;
+  }
+  return 4;
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   switch (dtype) {
-    case DT_F16: return run_typed<f16>(a, stream);
-    case DT_BF16: return run_typed<bf16>(a, stream);
-    case DT_F32: return run_typed<float>(a, stream);
+    case DT_F16: return run_epi<f16>(pick_cfg(a, 2), a, stream);
+    case DT_BF16: return run_epi<bf16>(pick_cfg(a, 2), a, stream);
+    case DT_F32: return run_epi<float>(pick_cfg(a, 4), a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int gemm_tile_configs() { return N_PIPE_CFGS; }
+
+// Explicit configuration (tuning and tests): cfg in [-1, N_PIPE_CFGS).
+hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream) {
+  if (a.M == 0) return hipSuccess;
+  if (cfg < -1 || cfg >= N_PIPE_CFGS) return hipErrorInvalidValue;
+  const int es = dtype == DT_F32 ? 4 : 2;
+  if (cfg >= 0 && (a.K * es) % 128) return hipErrorInvalidValue;
+  switch (dtype) {
+    case DT_F16: return run_epi<f16>(cfg, a, stream);
+    case DT_BF16: return run_epi<bf16>(cfg, a, stream);
+    case DT_F32: return run_epi<float>(cfg, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,8 +30,13 @@ struct GemmArgs {
   void* C;
   int M, N, K;
   int heads;            // EPI_QKV_SPLIT
+  int resid_f32 = 0;    // EPI_BIAS_RESID, bf16 operands only: residual is float32
+  int out_f32 = 0;      // EPI_BIAS_RESID, bf16 operands only: output is float32
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
+// Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
+hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
+int gemm_tile_configs();
 
 // attention.hip
 bool attention_supported(int dtype, int head_dim);
@@ -39,10 +44,12 @@ hipError_t launch_attention(int dtype, const void* qkv_split, void* ctx, const i
                             int batch, int total_tokens, int max_len, int heads, int head_dim,
                             hipStream_t stream);
 
-// layernorm.hip
+// layernorm.hip: y = LN(x) in type dtype_out from x in type dtype_in; when y_f32 is not
+// null the same result is also written there in float32.
 bool layernorm_supported(int dtype, int width);
-hipError_t launch_layernorm(int dtype, const void* x, void* y, const float* gamma,
-                            const float* beta, int rows, int width, float eps, hipStream_t stream);
+hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,
+                            const float* gamma, const float* beta, int rows, int width, float eps,
+                            hipStream_t stream);
 
 // prepare.hip
 hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);

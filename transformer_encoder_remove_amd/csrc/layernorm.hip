@@ -4,8 +4,11 @@
 // whose indices are compile-time after unrolling (the register-array technique of the
 // Swin talk "大規模なビジュアル モデル…", section 3), so the two statistics passes
 // (mean, then the variance of the centred values) re-read registers, not memory.
-// Element assignment is strided so that the G lanes of a row read G consecutive
-// 16-byte vectors per load (coalesced), and reductions are G-lane butterflies.
+// Each lane owns NV groups of 8 consecutive elements (one 16-byte load for 16-bit
+// types, two for float32); group k of lane s starts at element (k * G + s) * 8, so the
+// G lanes of a row read G consecutive groups per load (coalesced). Reductions are
+// G-lane butterflies. The input may be float32 (a bf16 layer's pre-LN sums) and the
+// result may also be written a second time in float32 (its residual stream).
 #include "device.h"
 #include "launch.h"
 
@@ -13,66 +16,87 @@ namespace tel {
 
 constexpr int LN_THREADS = 256;
 
-template <typename T, int G, int NV>
-__global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const T* __restrict__ x,
-                                                               T* __restrict__ y,
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const Vec16<T> t = *reinterpret_cast<const Vec16<T>*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = to_f32(t.v[e]);
+  }
+}
+
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    Vec16<T> t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t.v[e] = from_f32<T>(v[e]);
+    *reinterpret_cast<Vec16<T>*>(p) = t;
+  }
+}
+
+template <typename TI, typename TO, bool COPY, int G, int NV>
+__global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restrict__ x,
+                                                               TO* __restrict__ y,
+                                                               float* __restrict__ y32,
                                                                const float* __restrict__ gamma,
                                                                const float* __restrict__ beta,
                                                                int rows, float eps) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int H = G * NV * VEC;
+  constexpr int H = G * NV * 8;
   const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
   if (row >= rows) return;   // whole G-lane groups leave together
-  const T* xr = x + (size_t)row * H;
-  float v[NV][VEC];
+  const TI* xr = x + (size_t)row * H;
+  float v[NV][8];
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const Vec16<T> t = *reinterpret_cast<const Vec16<T>*>(xr + (k * G + sub) * VEC);
+    load8(xr + (k * G + sub) * 8, v[k]);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      v[k][e] = to_f32(t.v[e]);
-      s += v[k][e];
-    }
+    for (int e = 0; e < 8; ++e) s += v[k][e];
   }
   const float mean = group_sum<G>(s) * (1.f / H);
   float q = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
+    for (int e = 0; e < 8; ++e) {
       v[k][e] -= mean;
       q += v[k][e] * v[k][e];
     }
   const float rstd = rsqrtf(group_sum<G>(q) * (1.f / H) + eps);
-  T* yr = y + (size_t)row * H;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int c0 = (k * G + sub) * VEC;
-    Vec16<T> o;
+    const int c0 = (k * G + sub) * 8;
+    float o[8];
 #pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
+    for (int e = 0; e < 8; e += 4) {
       const float4 g = *reinterpret_cast<const float4*>(gamma + c0 + e);
       const float4 b = *reinterpret_cast<const float4*>(beta + c0 + e);
-      o.v[e + 0] = from_f32<T>(v[k][e + 0] * rstd * g.x + b.x);
-      o.v[e + 1] = from_f32<T>(v[k][e + 1] * rstd * g.y + b.y);
-      o.v[e + 2] = from_f32<T>(v[k][e + 2] * rstd * g.z + b.z);
-      o.v[e + 3] = from_f32<T>(v[k][e + 3] * rstd * g.w + b.w);
+      o[e + 0] = v[k][e + 0] * rstd * g.x + b.x;
+      o[e + 1] = v[k][e + 1] * rstd * g.y + b.y;
+      o[e + 2] = v[k][e + 2] * rstd * g.z + b.z;
+      o[e + 3] = v[k][e + 3] * rstd * g.w + b.w;
     }
-    *reinterpret_cast<Vec16<T>*>(yr + c0) = o;
+    store8(y + (size_t)row * H + c0, o);
+    if constexpr (COPY) store8(y32 + (size_t)row * H + c0, o);
   }
 }
 
-// Lanes per row G and vectors per lane NV with G * NV * (16 / sizeof(T)) == width.
-static bool pick_ln(int dtype, int width, int* g, int* nv) {
-  const int vec = 16 / dtype_size(dtype);
-  if (width <= 0 || width % vec) return false;
-  const int nvec = width / vec;
+// Lanes per row G and groups per lane NV with G * NV * 8 == width.
+static bool pick_ln(int width, int* g, int* nv) {
+  if (width <= 0 || width % 8) return false;
+  const int groups = width / 8;
   for (int G = 64; G >= 1; G >>= 1) {
-    if (nvec % G) continue;
-    const int n = nvec / G;
-    if (n == 1 || n == 2 || n == 3 || n == 4 || n == 6 || n == 8) {
+    if (groups % G) continue;
+    const int n = groups / G;
+    if (n >= 1 && n <= 4) {
       *g = G;
       *nv = n;
       return true;
@@ -84,57 +108,68 @@ static bool pick_ln(int dtype, int width, int* g, int* nv) {
 bool layernorm_supported(int dtype, int width) {
   int g, nv;
   if (dtype != DT_F16 && dtype != DT_BF16 && dtype != DT_F32) return false;
-  return pick_ln(dtype, width, &g, &nv);
+  return pick_ln(width, &g, &nv);
 }
 
-template <typename T, int G, int NV>
-static void run_ln(const void* x, void* y, const float* g, const float* b, int rows, float eps,
-                   hipStream_t stream) {
+struct LnArgs {
+  const void* x;
+  void* y;
+  float* y32;
+  const float* g;
+  const float* b;
+  int rows;
+  float eps;
+};
+
+template <typename TI, typename TO, bool COPY, int G, int NV>
+static void run_ln(const LnArgs& a, hipStream_t s) {
   constexpr int RPB = LN_THREADS / G;
-  layernorm_kernel<T, G, NV><<<(rows + RPB - 1) / RPB, LN_THREADS, 0, stream>>>(
-      (const T*)x, (T*)y, g, b, rows, eps);
+  layernorm_kernel<TI, TO, COPY, G, NV><<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>(
+      (const TI*)a.x, (TO*)a.y, a.y32, a.g, a.b, a.rows, a.eps);
 }
 
-template <typename T, int G>
-static bool run_ln_nv(int nv, const void* x, void* y, const float* g, const float* b, int rows,
-                      float eps, hipStream_t s) {
+template <typename TI, typename TO, bool COPY, int G>
+static bool run_ln_nv(int nv, const LnArgs& a, hipStream_t s) {
   switch (nv) {
-    case 1: run_ln<T, G, 1>(x, y, g, b, rows, eps, s); return true;
-    case 2: run_ln<T, G, 2>(x, y, g, b, rows, eps, s); return true;
-    case 3: run_ln<T, G, 3>(x, y, g, b, rows, eps, s); return true;
-    case 4: run_ln<T, G, 4>(x, y, g, b, rows, eps, s); return true;
-    case 6: run_ln<T, G, 6>(x, y, g, b, rows, eps, s); return true;
-    case 8: run_ln<T, G, 8>(x, y, g, b, rows, eps, s); return true;
+    case 1: run_ln<TI, TO, COPY, G, 1>(a, s); return true;
+    case 2: run_ln<TI, TO, COPY, G, 2>(a, s); return true;
+    case 3: run_ln<TI, TO, COPY, G, 3>(a, s); return true;
+    case 4: run_ln<TI, TO, COPY, G, 4>(a, s); return true;
   }
   return false;
 }
 
-template <typename T>
-static bool run_ln_g(int G, int nv, const void* x, void* y, const float* g, const float* b,
-                     int rows, float eps, hipStream_t s) {
+template <typename TI, typename TO, bool COPY>
+static bool run_ln_g(int G, int nv, const LnArgs& a, hipStream_t s) {
   switch (G) {
-    case 1: return run_ln_nv<T, 1>(nv, x, y, g, b, rows, eps, s);
-    case 2: return run_ln_nv<T, 2>(nv, x, y, g, b, rows, eps, s);
-    case 4: return run_ln_nv<T, 4>(nv, x, y, g, b, rows, eps, s);
-    case 8: return run_ln_nv<T, 8>(nv, x, y, g, b, rows, eps, s);
-    case 16: return run_ln_nv<T, 16>(nv, x, y, g, b, rows, eps, s);
-    case 32: return run_ln_nv<T, 32>(nv, x, y, g, b, rows, eps, s);
-    case 64: return run_ln_nv<T, 64>(nv, x, y, g, b, rows, eps, s);
+    case 1: return run_ln_nv<TI, TO, COPY, 1>(nv, a, s);
+    case 2: return run_ln_nv<TI, TO, COPY, 2>(nv, a, s);
+    case 4: return run_ln_nv<TI, TO, COPY, 4>(nv, a, s);
+    case 8: return run_ln_nv<TI, TO, COPY, 8>(nv, a, s);
+    case 16: return run_ln_nv<TI, TO, COPY, 16>(nv, a, s);
+    case 32: return run_ln_nv<TI, TO, COPY, 32>(nv, a, s);
+    case 64: return run_ln_nv<TI, TO, COPY, 64>(nv, a, s);
   }
   return false;
 }
 
-hipError_t launch_layernorm(int dtype, const void* x, void* y, const float* gamma,
-                            const float* beta, int rows, int width, float eps,
+hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y32,
+                            const float* gamma, const float* beta, int rows, int width, float eps,
                             hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   int G, nv;
-  if (!pick_ln(dtype, width, &G, &nv)) return hipErrorInvalidValue;
+  if (!pick_ln(width, &G, &nv)) return hipErrorInvalidValue;
+  const LnArgs a{x, y, y32, gamma, beta, rows, eps};
   bool ok = false;
-  switch (dtype) {
-    case DT_F16: ok = run_ln_g<f16>(G, nv, x, y, gamma, beta, rows, eps, stream); break;
-    case DT_BF16: ok = run_ln_g<bf16>(G, nv, x, y, gamma, beta, rows, eps, stream); break;
-    case DT_F32: ok = run_ln_g<float>(G, nv, x, y, gamma, beta, rows, eps, stream); break;
+  if (dtype_in == dtype_out && !y32) {
+    switch (dtype_in) {
+      case DT_F16: ok = run_ln_g<f16, f16, false>(G, nv, a, stream); break;
+      case DT_BF16: ok = run_ln_g<bf16, bf16, false>(G, nv, a, stream); break;
+      case DT_F32: ok = run_ln_g<float, float, false>(G, nv, a, stream); break;
+    }
+  } else if (dtype_in == DT_F32 && dtype_out == DT_BF16) {
+    ok = y32 ? run_ln_g<float, bf16, true>(G, nv, a, stream)
+             : run_ln_g<float, bf16, false>(G, nv, a, stream);
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
