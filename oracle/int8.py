@@ -13,10 +13,15 @@ LayerNorm stay in floating point. Readings where the page is silent:
     the page): a = max-abs of that GEMM's input on a calibration batch,
     s = a / 127, inv = 127 / a, both float32;
   * the GEMM output is INT32 (the INT8-output form is a later variant);
-  * QK^T and PV stay in floating point on the dequantised Q, K, V.
+  * QK^T and PV stay in floating point on the dequantised Q, K, V;
+  * the layer's activations are fp16: each dequantised GEMM result (with its bias,
+    and residual where there is one), the attention output and the LayerNorm output
+    is stored as fp16, as the workload defines the int8 GEMMs as dequantised to fp16
+    before softmax and LayerNorm (the page keeps bias, residual and LayerNorm in
+    FP16/FP32 after the dequantise node).
 Where a floating-point value decides a code, the decision is taken in float32
-exactly as stated here (the activation first rounded to the fp16 it is stored
-in), so that both implementations make the same decision.
+exactly as stated here (from the stored fp16 activation), so that both
+implementations make the same decision.
 """
 from __future__ import annotations
 
@@ -86,9 +91,14 @@ def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: floa
 
     ``w`` holds the floating-point weights; they are quantised here per
     quantize_weight. ``amax`` are the four calibration max-abs values.
-    ``storage`` is the type activations are stored in before quantisation.
+    ``storage`` is the type every activation is stored in (fp16): the dequantised
+    QKV, the attention output, the two pre-LayerNorm sums, h1 and the GELU output.
+    The returned output is not rounded.
     """
     scales = [act_scale(a) for a in amax]
+
+    def st(a):
+        return np.asarray(a, np.float64).astype(storage).astype(np.float64)
 
     def qlinear(a, wname, bname, g):
         wq, sw = quantize_weight(w[wname])
@@ -97,11 +107,11 @@ def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: floa
         return dequantize(int8_matmul(q, wq), s, sw, w[bname])
 
     x = np.asarray(x, np.float64)
-    qkv = qlinear(x, "w_qkv", "b_qkv", 0)
-    ctx = enc.attention(qkv, cu_seqlens, heads)
-    h1 = enc.layer_norm(qlinear(ctx, "w_o", "b_o", 1) + x, w["ln1_g"], w["ln1_b"], eps)
-    f = enc.gelu(qlinear(h1, "w_1", "b_1", 2))
-    return enc.layer_norm(qlinear(f, "w_2", "b_2", 3) + h1, w["ln2_g"], w["ln2_b"], eps)
+    qkv = st(qlinear(x, "w_qkv", "b_qkv", 0))
+    ctx = st(enc.attention(qkv, cu_seqlens, heads))
+    h1 = st(enc.layer_norm(st(qlinear(ctx, "w_o", "b_o", 1) + x), w["ln1_g"], w["ln1_b"], eps))
+    f = st(enc.gelu(qlinear(h1, "w_1", "b_1", 2)))
+    return enc.layer_norm(st(qlinear(f, "w_2", "b_2", 3) + h1), w["ln2_g"], w["ln2_b"], eps)
 
 
 def encoder_stack_int8(x, cu_seqlens, layers: list, amaxes: list, heads: int, eps: float,

@@ -88,8 +88,11 @@ def _q8(v32):
 def encoder_layer_int8_padded(x_pad, lens, w, heads, eps, amax):
     """Int8-GEMM layer, padded formulation, loops. Weights: per-row scale
     max|W|/127 (float32), codes rne(W/s) clamped; activations: fp16 storage, then
-    one float32 multiply by 127/amax, rne, clamp; int accumulate; y = acc*(s_a*s_w)+b."""
+    one float32 multiply by 127/amax, rne, clamp; int accumulate; y = acc*(s_a*s_w)+b.
+    Activations between the steps are fp16 values (the dequantised QKV, the attention
+    output, the pre-LN sums, h1 and the GELU output)."""
     f32 = np.float32
+    h = lambda v: float(np.float16(v))
     x_pad = np.asarray(x_pad, np.float64)
     B, S, H = x_pad.shape
     d = H // heads
@@ -126,20 +129,21 @@ def encoder_layer_int8_padded(x_pad, lens, w, heads, eps, amax):
     for b in range(B):
         L = int(lens[b])
         rows = [x_pad[b, i].tolist() for i in range(S)]
-        qkv = [qlin(r, "w_qkv", "b_qkv", 0) for r in rows]
+        qkv = [[h(v) for v in qlin(r, "w_qkv", "b_qkv", 0)] for r in rows]
         for i in range(L):
             ctx = [0.0] * H
-            for h in range(heads):
-                q = qkv[i][h * d:(h + 1) * d]
-                sc = [_dot(q, qkv[j][H + h * d:H + (h + 1) * d]) / math.sqrt(d) for j in range(S)]
+            for hh in range(heads):
+                q = qkv[i][hh * d:(hh + 1) * d]
+                sc = [_dot(q, qkv[j][H + hh * d:H + (hh + 1) * d]) / math.sqrt(d) for j in range(S)]
                 p = _softmax_masked(sc, [j < L for j in range(S)])
                 for c in range(d):
-                    ctx[h * d + c] = sum(p[j] * qkv[j][2 * H + h * d + c] for j in range(S))
+                    ctx[hh * d + c] = h(sum(p[j] * qkv[j][2 * H + hh * d + c] for j in range(S)))
             a = qlin(ctx, "w_o", "b_o", 1)
-            h1 = _ln([a[c] + rows[i][c] for c in range(H)], L64("ln1_g"), L64("ln1_b"), eps)
-            f = [_gelu(z) for z in qlin(h1, "w_1", "b_1", 2)]
+            h1 = [h(v) for v in _ln([h(a[c] + rows[i][c]) for c in range(H)], L64("ln1_g"),
+                                    L64("ln1_b"), eps)]
+            f = [h(_gelu(z)) for z in qlin(h1, "w_1", "b_1", 2)]
             o = qlin(f, "w_2", "b_2", 3)
-            out[b, i] = _ln([o[c] + h1[c] for c in range(H)], L64("ln2_g"), L64("ln2_b"), eps)
+            out[b, i] = _ln([h(o[c] + h1[c]) for c in range(H)], L64("ln2_g"), L64("ln2_b"), eps)
     return out
 
 
