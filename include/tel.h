@@ -97,7 +97,8 @@ typedef struct {
   int heads;       /* H % heads == 0; head_dim = H / heads in {16, 32, 64, 128} */
   int ffn;         /* F, multiple of 8                                         */
   int dtype;       /* storage type of activations and weights                 */
-  int int8_gemm;   /* 1: the four projection GEMMs run in int8 (dtype TEL_F16) */
+  int int8_gemm;   /* 1: the four projection GEMMs run in int8 (dtype TEL_F16; H and F
+                      multiples of 16); see the int8 section below                 */
   float ln_eps;
 } tel_encoder_desc;
 
@@ -184,6 +185,33 @@ int tel_gemm_ex(int epilogue, int dtype, int tile_config, const void* A, const v
 int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,
                          int total_tokens, int max_len, int heads, int head_dim, int dtype,
                          void* stream);
+
+/* ------------------------------------------------------------------ int8 GEMM variant
+ * [SW] section 3, INT8 quantisation: inputs and weights are quantised to INT8, the GEMM
+ * accumulates in INT32 and the result is dequantised; bias, residual and LayerNorm stay
+ * floating point. Here: symmetric codes in [-127, 127], round half to even; weights per
+ * output channel (s[n] = max_k |W[n][k]| / 127, 1 for a zero row), activations per tensor
+ * with static scales s_a = amax / 127 from calibration (tel_encoder_weights.act_amax).
+ * With desc->int8_gemm = 1 an encoder layer quantises the inputs of its QKV, O, FFN1 and
+ * FFN2 GEMMs, runs them on int8 MFMA with int32 accumulation and dequantises in the
+ * epilogue (acc * s_a * s[n] + bias); attention runs in fp16 on the dequantised Q, K, V.
+ * Every code is taken from the fp16-rounded value: code = clamp(rne(float(x) * 127/amax)). */
+
+/* q[i] = clamp(rne(float(x[i]) * inv_scale), -127, 127) for i < n; x of type dtype,
+ * 16-byte aligned; q 8-byte aligned; inv_scale [host] > 0 and finite. */
+int tel_quantize_i8(const void* x, int8_t* q, size_t n, float inv_scale, int dtype, void* stream);
+
+/* Per-output-channel weight quantisation of W [N][K] (type dtype): scales[n] =
+ * max_k |W[n][k]| / 127 (1 if the row is zero), q[n][k] = clamp(rne(W[n][k] / scales[n]),
+ * -127, 127), float32 arithmetic with correctly rounded division. */
+int tel_quantize_weight_i8(const void* w, int8_t* q, float* scales, int N, int K, int dtype,
+                           void* stream);
+
+/* C[m][n] = sum_k A[m][k] * B[n][k], exact int32 accumulation of int8 codes (the int8
+ * layer's GEMM without its epilogue). K % 16 == 0, N % 4 == 0, 16-byte aligned pointers.
+ * |C| <= K * 127^2 must fit in int32 (K <= 133,143). */
+int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, int K,
+                    void* stream);
 
 /* y[r][:] = LN(x[r][:]) * gamma + beta over rows of width `width` (float32 gamma/beta). */
 int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,

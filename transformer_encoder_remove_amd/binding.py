@@ -30,7 +30,8 @@ EXPORTS = (
     "tel_rebuild_padding", "tel_encoder_packed_size", "tel_encoder_prepare",
     "tel_encoder_workspace_size", "tel_encoder_layer_forward",
     "tel_encoder_forward_workspace_size", "tel_encoder_forward", "tel_gemm",
-    "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_layernorm",
+    "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_quantize_i8",
+    "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm",
 )
 
 
@@ -81,6 +82,9 @@ _SIG = {
     "tel_gemm_ex": (I, [I, I, I, P, P, P, P, P, I, I, I, I, P]),
     "tel_attention_varlen": (I, [P, P, P, I, I, I, I, I, I, P]),
     "tel_layernorm": (I, [P, P, P, P, I, I, F, I, P]),
+    "tel_quantize_i8": (I, [P, P, SZ, F, I, P]),
+    "tel_quantize_weight_i8": (I, [P, P, P, I, I, I, P]),
+    "tel_gemm_i8_i32": (I, [P, P, P, I, I, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -226,6 +230,24 @@ def tel_layernorm(x, y, gamma, beta, eps: float, stream=None):
     _check("tel_layernorm", lib.tel_layernorm(
         _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), rows, width, eps, dtype_code(x.dtype),
         _stream(stream)))
+
+
+def tel_quantize_i8(x, q, inv_scale: float, stream=None):
+    _check("tel_quantize_i8", lib.tel_quantize_i8(
+        _ptr(x), _ptr(q), x.numel(), inv_scale, dtype_code(x.dtype), _stream(stream)))
+
+
+def tel_quantize_weight_i8(w, q, scales, stream=None):
+    N, K = w.shape
+    _check("tel_quantize_weight_i8", lib.tel_quantize_weight_i8(
+        _ptr(w), _ptr(q), _ptr(scales), N, K, dtype_code(w.dtype), _stream(stream)))
+
+
+def tel_gemm_i8_i32(A, B, C, stream=None):
+    M, K = A.shape
+    N = B.shape[0]
+    _check("tel_gemm_i8_i32", lib.tel_gemm_i8_i32(_ptr(A), _ptr(B), _ptr(C), M, N, K,
+                                                  _stream(stream)))
 
 
 # ------------------------------------------------------------------ allocation helpers

@@ -29,9 +29,12 @@ inline bool float_type(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT
 
 // ------------------------------------------------------------------ packed layer layout
 // Storage-type weights first (GEMM operands, [N][K] as given), then float32 vectors.
+// An int8 layer stores int8 weight codes instead, followed by the per-row weight scales,
+// the per-column dequantisation scales and the activation scales s_a[4], inv_a[4].
 struct LayerLayout {
   size_t w_qkv, w_o, w_1, w_2;
   size_t b_qkv, b_o, ln1_g, ln1_b, b_1, b_2, ln2_g, ln2_b;
+  size_t sw_qkv, sw_o, sw_1, sw_2, dq_qkv, dq_o, dq_1, dq_2, act;
   size_t total;
 };
 
@@ -46,7 +49,7 @@ bool desc_ok(const tel_encoder_desc* d) {
 int desc_supported(const tel_encoder_desc* d) {
   if (!desc_ok(d)) return TEL_EINVAL;
   if (!float_type(d->dtype)) return TEL_EUNSUPPORTED;
-  if (d->int8_gemm) return TEL_EUNSUPPORTED;
+  if (d->int8_gemm && (d->dtype != DT_F16 || d->hidden % 16 || d->ffn % 16)) return TEL_EUNSUPPORTED;
   if (d->hidden % 8 || d->ffn % 8) return TEL_EUNSUPPORTED;
   if (!attention_supported(d->dtype, d->hidden / d->heads)) return TEL_EUNSUPPORTED;
   if (!layernorm_supported(d->dtype, d->hidden)) return TEL_EUNSUPPORTED;
@@ -54,8 +57,8 @@ int desc_supported(const tel_encoder_desc* d) {
 }
 
 LayerLayout layer_layout(const tel_encoder_desc* d) {
-  const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
-  LayerLayout L;
+  const size_t H = d->hidden, F = d->ffn, es = d->int8_gemm ? 1 : dtype_size(d->dtype);
+  LayerLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   L.w_qkv = take(3 * H * H * es);
@@ -70,6 +73,17 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
   L.b_2 = take(H * 4);
   L.ln2_g = take(H * 4);
   L.ln2_b = take(H * 4);
+  if (d->int8_gemm) {
+    L.sw_qkv = take(3 * H * 4);
+    L.sw_o = take(H * 4);
+    L.sw_1 = take(F * 4);
+    L.sw_2 = take(H * 4);
+    L.dq_qkv = take(3 * H * 4);
+    L.dq_o = take(H * 4);
+    L.dq_1 = take(F * 4);
+    L.dq_2 = take(H * 4);
+    L.act = take(8 * 4);
+  }
   L.total = o;
   return L;
 }
@@ -81,6 +95,7 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
 // their storage type.
 struct LayerWs {
   size_t qkv, ctx, pre, h1, h1f, f, total;
+  size_t xq, ctxq, h1q;   // int8 layer: codes of the inputs of the QKV, O and FFN1 GEMMs
 };
 
 inline bool f32_stream(const tel_encoder_desc* d) { return d->dtype == DT_BF16; }
@@ -88,7 +103,7 @@ inline bool f32_stream(const tel_encoder_desc* d) { return d->dtype == DT_BF16; 
 LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
   const size_t pes = f32_stream(d) ? 4 : es;
-  LayerWs w;
+  LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   w.qkv = take(3 * T * H * es);
@@ -96,7 +111,12 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   w.pre = take(T * H * pes);
   w.h1 = take(T * H * es);
   w.h1f = f32_stream(d) ? take(T * H * 4) : 0;
-  w.f = take(T * F * es);
+  w.f = take(T * F * (d->int8_gemm ? 1 : es));   // int8 layer: GELU output as codes
+  if (d->int8_gemm) {
+    w.xq = take(T * H);
+    w.ctxq = take(T * H);
+    w.h1q = take(T * H);
+  }
   w.total = o;
   return w;
 }
@@ -119,9 +139,55 @@ StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
   return s;
 }
 
+// Int8 layer ([SW] section 3, INT8: quantise -> INT8 GEMM -> INT32 -> dequantise; bias,
+// residual and LayerNorm stay floating point; attention runs in fp16 on the dequantised
+// Q, K, V). Codes are produced where the value is made: a quantise kernel for x and ctx,
+// the LayerNorm for h1, the FFN1 epilogue for the GELU output.
+int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, void* y,
+                       const int32_t* cu, int batch, int T, int max_len, char* ws,
+                       hipStream_t st) {
+  const LayerLayout L = layer_layout(d);
+  const LayerWs W = layer_ws(d, (size_t)T);
+  const int H = d->hidden, F = d->ffn, nh = d->heads;
+  auto F32 = [&](size_t off) { return (const float*)(P + off); };
+  const float* inv = F32(L.act) + 4;
+  int8_t* xq = (int8_t*)(ws + W.xq);
+  int8_t* ctxq = (int8_t*)(ws + W.ctxq);
+  int8_t* h1q = (int8_t*)(ws + W.h1q);
+  int8_t* fq = (int8_t*)(ws + W.f);
+  void* qkv = ws + W.qkv;
+  void* ctx = ws + W.ctx;
+  void* pre = ws + W.pre;
+  void* h1 = ws + W.h1;
+
+  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, inv + 0, 0.f, st));
+  GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
+  g.dq = F32(L.dq_qkv);
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
+  TEL_TRY(launch_quantize_act(DT_F16, ctx, ctxq, (size_t)T * H, inv + 1, 0.f, st));
+  g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
+  g.dq = F32(L.dq_o);
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(launch_layernorm_q8(pre, h1, h1q, inv + 2, F32(L.ln1_g), F32(L.ln1_b), T, H,
+                              d->ln_eps, st));
+  g = GemmArgs{EPI_BIAS_GELU, h1q, P + L.w_1, F32(L.b_1), nullptr, fq, T, F, H, nh};
+  g.dq = F32(L.dq_1);
+  g.qinv = inv + 3;
+  g.out_i8 = 1;
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
+  g.dq = F32(L.dq_2);
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                           d->ln_eps, st));
+  return TEL_OK;
+}
+
 int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void* y,
                   const int32_t* cu, int batch, int T, int max_len, char* ws, hipStream_t st) {
   if (T == 0) return TEL_OK;
+  if (d->int8_gemm) return layer_forward_int8(d, P, x, y, cu, batch, T, max_len, ws, st);
   const LayerLayout L = layer_layout(d);
   const LayerWs W = layer_ws(d, (size_t)T);
   const int H = d->hidden, F = d->ffn, nh = d->heads, dt = d->dtype;
@@ -226,11 +292,31 @@ int tel_encoder_prepare(const tel_encoder_desc* d, const tel_encoder_weights* w,
   const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
   char* P = (char*)packed;
   hipStream_t st = as_stream(stream);
-  TEL_TRY(hipMemcpyAsync(P + L.w_qkv, w->w_qkv, 3 * H * H * es, hipMemcpyDeviceToDevice, st));
-  TEL_TRY(hipMemcpyAsync(P + L.w_o, w->w_o, H * H * es, hipMemcpyDeviceToDevice, st));
-  TEL_TRY(hipMemcpyAsync(P + L.w_1, w->w_1, F * H * es, hipMemcpyDeviceToDevice, st));
-  TEL_TRY(hipMemcpyAsync(P + L.w_2, w->w_2, H * F * es, hipMemcpyDeviceToDevice, st));
   const int dt = d->dtype;
+  if (d->int8_gemm) {
+    float sa[4], inv[4];
+    for (int i = 0; i < 4; ++i) {
+      const float a = w->act_amax[i];
+      if (!(a > 0.f) || !(a < 3.0e38f)) return TEL_EINVAL;   // positive and finite
+      sa[i] = a / 127.0f;
+      inv[i] = 127.0f / a;
+    }
+    float act[8] = {sa[0], sa[1], sa[2], sa[3], inv[0], inv[1], inv[2], inv[3]};
+    TEL_TRY(launch_store_f32((float*)(P + L.act), act, 8, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_qkv, (int8_t*)(P + L.w_qkv), (float*)(P + L.sw_qkv),
+                                   (float*)(P + L.dq_qkv), sa[0], 3 * H, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_o, (int8_t*)(P + L.w_o), (float*)(P + L.sw_o),
+                                   (float*)(P + L.dq_o), sa[1], H, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_1, (int8_t*)(P + L.w_1), (float*)(P + L.sw_1),
+                                   (float*)(P + L.dq_1), sa[2], F, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_2, (int8_t*)(P + L.w_2), (float*)(P + L.sw_2),
+                                   (float*)(P + L.dq_2), sa[3], H, F, st));
+  } else {
+    TEL_TRY(hipMemcpyAsync(P + L.w_qkv, w->w_qkv, 3 * H * H * es, hipMemcpyDeviceToDevice, st));
+    TEL_TRY(hipMemcpyAsync(P + L.w_o, w->w_o, H * H * es, hipMemcpyDeviceToDevice, st));
+    TEL_TRY(hipMemcpyAsync(P + L.w_1, w->w_1, F * H * es, hipMemcpyDeviceToDevice, st));
+    TEL_TRY(hipMemcpyAsync(P + L.w_2, w->w_2, H * F * es, hipMemcpyDeviceToDevice, st));
+  }
   TEL_TRY(launch_widen_f32(dt, w->b_qkv, (float*)(P + L.b_qkv), 3 * H, st));
   TEL_TRY(launch_widen_f32(dt, w->b_o, (float*)(P + L.b_o), H, st));
   TEL_TRY(launch_widen_f32(dt, w->ln1_g, (float*)(P + L.ln1_g), H, st));
@@ -337,6 +423,35 @@ int tel_gemm_ex(int epilogue, int dtype, int tile_config, const void* A, const v
 int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float* bias,
              const void* resid, void* C, int M, int N, int K, int heads, void* stream) {
   return tel_gemm_ex(epilogue, dtype, -2, A, W, bias, resid, C, M, N, K, heads, stream);
+}
+
+int tel_quantize_i8(const void* x, int8_t* q, size_t n, float inv_scale, int dtype,
+                    void* stream) {
+  if (!float_type(dtype)) return TEL_EUNSUPPORTED;
+  if (!(inv_scale > 0.f) || !(inv_scale < 3.0e38f)) return TEL_EINVAL;
+  if (n == 0) return TEL_OK;
+  if (!x || !q || !aligned16(x) || ((uintptr_t)q & 7u)) return TEL_EINVAL;
+  return status_of(launch_quantize_act(dtype, x, q, n, nullptr, inv_scale, as_stream(stream)));
+}
+
+int tel_quantize_weight_i8(const void* w, int8_t* q, float* scales, int N, int K, int dtype,
+                           void* stream) {
+  if (!float_type(dtype)) return TEL_EUNSUPPORTED;
+  if (N < 0 || K <= 0) return TEL_EINVAL;
+  if (N == 0) return TEL_OK;
+  if (!w || !q || !scales) return TEL_EINVAL;
+  return status_of(launch_quantize_weight(dtype, w, q, scales, nullptr, 0.f, N, K,
+                                          as_stream(stream)));
+}
+
+int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, int K,
+                    void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
+  if (M == 0) return TEL_OK;
+  if (!A || !B || !C || !aligned16(A) || !aligned16(B) || !aligned16(C)) return TEL_EINVAL;
+  if (K % 16 || N % 4) return TEL_EUNSUPPORTED;
+  GemmArgs g{EPI_RAW_I32, A, B, nullptr, nullptr, C, M, N, K, 1};
+  return status_of(launch_gemm(DT_I8, g, as_stream(stream)));
 }
 
 int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,

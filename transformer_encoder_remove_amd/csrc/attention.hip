@@ -17,7 +17,7 @@
 //    values plus two cross-lane butterflies (xor 16, xor 32);
 //  * O^T += V^T P^T with P^T taken straight from the score registers (no LDS round
 //    trip): the MFMA k index is mapped to the keys each lane already holds, and the
-//    V^T fragment is read with the same mapping;
+//    V^T fragment is read with the same mapping; 16-bit P is split into hi + lo parts;
 //  * O^T keeps one query per lane as well, so the rescale by exp2(m_old - m_new) and
 //    the final 1/l are per-lane scalars.
 #include <math.h>
@@ -134,16 +134,22 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
 
     // O^T[c][q] += sum_key V^T[c][key] * P^T[key][q]; MFMA k element e of step t is the
     // lane's score f = t*KPL + e, i.e. key 16*(f/4) + 4*lg + f%4.
+    // For 16-bit types P is split into P_hi + P_lo (both representable), two MFMAs per
+    // step: P enters the product with ~2x the significant bits of one 16-bit value. The
+    // kernel is bound by memory latency, not by MFMA, so the extra MFMA costs nothing
+    // measurable, and downstream int8 codes flip far less often.
 #pragma unroll
     for (int t = 0; t < ATT_KB / KMF; ++t) {
-      T pv[KPL];
+      T pv[KPL], pl[KPL];
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         const int f = t * KPL + e;
         pv[e] = from_f32<T>(sc[f / 4][f % 4]);
+        pl[e] = from_f32<T>(sc[f / 4][f % 4] - to_f32(pv[e]));
       }
-      frag pb;
+      frag pb, pbl;
       __builtin_memcpy(&pb, pv, sizeof(frag));
+      __builtin_memcpy(&pbl, pl, sizeof(frag));
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         const T* vrow = &sVt[(c * 16 + lr) * LDV];
@@ -159,6 +165,7 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
           va = vrow[16 * (f / 4) + 4 * lg + (f % 4)];
         }
         o[c] = MF::mma(va, pb, o[c]);
+        if constexpr (KPL > 1) o[c] = MF::mma(va, pbl, o[c]);
       }
     }
     __syncthreads();

@@ -32,42 +32,76 @@ namespace tel {
 
 // Epilogue operands. The residual and the output of EPI_BIAS_RESID may be float32
 // (TR, TO) so that a bf16 layer can keep its pre-LayerNorm sums and residual stream in
-// float32; every other output has the operand type T.
+// float32. With int8 operands the int32 accumulator is dequantised by a per-column scale
+// (dq[n] = activation scale x weight scale); an int8 output (TO = int8_t) is quantised
+// again for the next int8 GEMM: the value is first rounded to fp16, the storage type it
+// would otherwise have, then q = clamp(rne(v * qinv), -127, 127).
 template <typename T, typename TR, typename TO> struct EpiArgs {
   const float* bias;
   const TR* resid;
   TO* C;
   int M, N, heads;
+  const float* dq;     // int8 operands: per-column dequantisation scale [N]
+  const float* qinv;   // int8 output: device scalar, 1 / activation scale of the consumer
 };
 
-template <int EPI, typename T, typename TR, typename TO>
+__device__ __forceinline__ int8_t quantize_code(float v, float inv) {
+  const float r = __builtin_rintf((float)(f16)v * inv);
+  return (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+}
+
+template <int EPI, typename T, typename TR, typename TO, typename ACC>
 __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
-                                               f32x4 acc) {
-  const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
-  float v[4] = {acc[0] + b.x, acc[1] + b.y, acc[2] + b.z, acc[3] + b.w};
-  Vec4<TO> out;
-  size_t idx;
-  if constexpr (EPI == EPI_BIAS_GELU) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
-  }
-  if constexpr (EPI == EPI_BIAS_RESID) {
-    const Vec4<TR> r = *reinterpret_cast<const Vec4<TR>*>(e.resid + (size_t)m * e.N + n);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] += to_f32(r.v[i]);
-  }
-  if constexpr (EPI == EPI_QKV_SPLIT) {
-    // [3][heads][M][d]: the attention kernel reads each head's Q, K and V as
-    // contiguous [tokens][d] blocks.
-    const int H = e.N / 3, d = H / e.heads;
-    const int which = n / H, rem = n - which * H, hh = rem / d, c = rem - hh * d;
-    idx = (((size_t)which * e.heads + hh) * e.M + m) * d + c;
+                                               ACC acc) {
+  if constexpr (EPI == EPI_RAW_I32) {
+    // int8 diagnostic: the exact int32 accumulators, no epilogue arithmetic
+    *reinterpret_cast<i32x4*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
+    return;
   } else {
-    idx = (size_t)m * e.N + n;
-  }
+    const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
+    float v[4];
+    if constexpr (std::is_same<T, int8_t>::value) {
+      const float4 d = *reinterpret_cast<const float4*>(e.dq + n);
+      v[0] = (float)acc[0] * d.x + b.x;
+      v[1] = (float)acc[1] * d.y + b.y;
+      v[2] = (float)acc[2] * d.z + b.z;
+      v[3] = (float)acc[3] * d.w + b.w;
+    } else {
+      v[0] = acc[0] + b.x;
+      v[1] = acc[1] + b.y;
+      v[2] = acc[2] + b.z;
+      v[3] = acc[3] + b.w;
+    }
+    Vec4<TO> out;
+    size_t idx;
+    if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(v[i]);
-  *reinterpret_cast<Vec4<TO>*>(e.C + idx) = out;
+      for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+    }
+    if constexpr (EPI == EPI_BIAS_RESID) {
+      const Vec4<TR> r = *reinterpret_cast<const Vec4<TR>*>(e.resid + (size_t)m * e.N + n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += to_f32(r.v[i]);
+    }
+    if constexpr (EPI == EPI_QKV_SPLIT) {
+      // [3][heads][M][d]: the attention kernel reads each head's Q, K and V as
+      // contiguous [tokens][d] blocks.
+      const int H = e.N / 3, d = H / e.heads;
+      const int which = n / H, rem = n - which * H, hh = rem / d, c = rem - hh * d;
+      idx = (((size_t)which * e.heads + hh) * e.M + m) * d + c;
+    } else {
+      idx = (size_t)m * e.N + n;
+    }
+    if constexpr (std::is_same<TO, int8_t>::value) {
+      const float inv = *e.qinv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out.v[i] = quantize_code(v[i], inv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(v[i]);
+    }
+    *reinterpret_cast<Vec4<TO>*>(e.C + idx) = out;
+  }
 }
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int EPI, typename TR, typename TO>
@@ -309,7 +343,8 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
 
   // Materialise the epilogue's kernel arguments before the loop: a scalar load still in
   // flight there would make the compiler wait for every LDS read before each MFMA block.
-  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads));
+  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads),
+               "s"(e.dq), "s"(e.qinv));
   __builtin_amdgcn_s_barrier();                     // slice 0 has landed
   asm volatile("" ::: "memory");
   TEL_PIPE_FRAGS(0, 0, 0);
@@ -370,7 +405,7 @@ constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 template <typename T, int BM, int BN, int WM, int WN, int EPI, typename TR, typename TO>
 static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
-  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads};
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv};
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI, TR, TO><<<grid, WM * WN * 64, 0, stream>>>(
       (const T*)a.A, (const T*)a.W, a.K, e);
@@ -379,7 +414,7 @@ static void launch_one(const GemmArgs& a, hipStream_t stream) {
 template <typename T, int C, int EPI, typename TR, typename TO>
 static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
-  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads};
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv};
   const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
       <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>((const T*)a.A, (const T*)a.W,
@@ -429,9 +464,28 @@ static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The largest tile that still yields about one workgroup per compute unit.
+// int8 operands: the epilogue output type follows the epilogue (fp16 activations,
+// int8 codes for the GELU output that feeds the next int8 GEMM, raw int32).
+static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
+  typedef int8_t T;
+  switch (a.epi) {
+    case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, f16, f16>(cfg, a, stream); break;
+    case EPI_BIAS_RESID: launch_cfg<T, EPI_BIAS_RESID, f16, f16>(cfg, a, stream); break;
+    case EPI_BIAS: launch_cfg<T, EPI_BIAS, f16, f16>(cfg, a, stream); break;
+    case EPI_BIAS_GELU:
+      if (a.out_i8) launch_cfg<T, EPI_BIAS_GELU, f16, int8_t>(cfg, a, stream);
+      else launch_cfg<T, EPI_BIAS_GELU, f16, f16>(cfg, a, stream);
+      break;
+    case EPI_RAW_I32: launch_cfg<T, EPI_RAW_I32, f16, int32_t>(cfg, a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The largest tile that still yields about one workgroup per compute unit (the order of
+// the table); shapes whose K is not a multiple of 128 bytes use the register-staged kernel.
 static int pick_cfg(const GemmArgs& a, int elem_bytes) {
-  if ((a.K * elem_bytes) % 128) return -1;
+  if (((long long)a.K * elem_bytes) % 128) return -1;
   for (int c = 0; c < 5; ++c) {
     const PipeCfg& p = PIPE_CFGS[c];
     const long tiles = (long)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
@@ -443,6 +497,7 @@ static int pick_cfg(const GemmArgs& a, int elem_bytes) {
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   switch (dtype) {
+    case DT_I8: return run_epi_i8(pick_cfg(a, 1), a, stream);
     case DT_F16: return run_epi<f16>(pick_cfg(a, 2), a, stream);
     case DT_BF16: return run_epi<bf16>(pick_cfg(a, 2), a, stream);
     case DT_F32: return run_epi<float>(pick_cfg(a, 4), a, stream);
@@ -456,9 +511,10 @@ int gemm_tile_configs() { return N_PIPE_CFGS; }
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   if (cfg < -1 || cfg >= N_PIPE_CFGS) return hipErrorInvalidValue;
-  const int es = dtype == DT_F32 ? 4 : 2;
+  const int es = dtype_size(dtype);
   if (cfg >= 0 && (a.K * es) % 128) return hipErrorInvalidValue;
   switch (dtype) {
+    case DT_I8: return run_epi_i8(cfg, a, stream);
     case DT_F16: return run_epi<f16>(cfg, a, stream);
     case DT_BF16: return run_epi<bf16>(cfg, a, stream);
     case DT_F32: return run_epi<float>(cfg, a, stream);

@@ -7,7 +7,7 @@
 namespace tel {
 
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
-enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3 };
+enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
 
@@ -32,6 +32,9 @@ struct GemmArgs {
   int heads;            // EPI_QKV_SPLIT
   int resid_f32 = 0;    // EPI_BIAS_RESID, bf16 operands only: residual is float32
   int out_f32 = 0;      // EPI_BIAS_RESID, bf16 operands only: output is float32
+  const float* dq = nullptr;    // int8 operands: per-column dequantisation scale [N]
+  const float* qinv = nullptr;  // int8 output (EPI_BIAS_GELU): device scalar 1 / scale
+  int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
@@ -50,8 +53,21 @@ bool layernorm_supported(int dtype, int width);
 hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,
                             const float* gamma, const float* beta, int rows, int width, float eps,
                             hipStream_t stream);
+// fp16 LayerNorm that also writes the int8 codes of its (fp16-rounded) output.
+hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* qinv,
+                               const float* gamma, const float* beta, int rows, int width,
+                               float eps, hipStream_t stream);
 
 // prepare.hip
 hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);
+hipError_t launch_store_f32(float* dst, const float* vals, int n, hipStream_t stream);
+// quant.hip: per-row weight quantisation W[N][K] -> codes [N][K], scales [N]; optional
+// per-column dequantisation scales dq[n] = act_scale * s_w[n] (dq may be null).
+hipError_t launch_quantize_weight(int dtype, const void* w, int8_t* q, float* s_w, float* dq,
+                                  float act_scale, int N, int K, hipStream_t stream);
+// q[i] = clamp(rne(float(x[i]) * inv), -127, 127); inv is a device scalar when inv_dev is
+// not null, else the host value inv_host.
+hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
+                               float inv_host, hipStream_t stream);
 
 }  // namespace tel

@@ -9,6 +9,8 @@
 // G lanes of a row read G consecutive groups per load (coalesced). Reductions are
 // G-lane butterflies. The input may be float32 (a bf16 layer's pre-LN sums) and the
 // result may also be written a second time in float32 (its residual stream).
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -41,13 +43,17 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
   }
 }
 
-template <typename TI, typename TO, bool COPY, int G, int NV>
+// Q8: also write the int8 codes of the output for an int8 GEMM that consumes it, taken
+// from the stored (TO-rounded) value: code = clamp(rne(float(y) * inv), -127, 127).
+template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restrict__ x,
                                                                TO* __restrict__ y,
                                                                float* __restrict__ y32,
                                                                const float* __restrict__ gamma,
                                                                const float* __restrict__ beta,
-                                                               int rows, float eps) {
+                                                               int rows, float eps,
+                                                               int8_t* __restrict__ yq = nullptr,
+                                                               const float* __restrict__ qinv = nullptr) {
   constexpr int H = G * NV * 8;
   const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
@@ -86,6 +92,18 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
     }
     store8(y + (size_t)row * H + c0, o);
     if constexpr (COPY) store8(y32 + (size_t)row * H + c0, o);
+    if constexpr (Q8) {
+      const float inv = *qinv;
+      int8_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = __builtin_rintf(to_f32(from_f32<TO>(o[e])) * inv);
+        c[e] = (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+      }
+      uint2 packed;
+      __builtin_memcpy(&packed, c, 8);
+      *reinterpret_cast<uint2*>(yq + (size_t)row * H + c0) = packed;
+    }
   }
 }
 
@@ -119,11 +137,20 @@ struct LnArgs {
   const float* b;
   int rows;
   float eps;
+  int8_t* yq = nullptr;
+  const float* qinv = nullptr;
 };
 
 template <typename TI, typename TO, bool COPY, int G, int NV>
 static void run_ln(const LnArgs& a, hipStream_t s) {
   constexpr int RPB = LN_THREADS / G;
+  if (a.yq) {
+    if constexpr (std::is_same<TI, f16>::value && std::is_same<TO, f16>::value && !COPY) {
+      layernorm_kernel<TI, TO, COPY, G, NV, true><<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>(
+          (const TI*)a.x, (TO*)a.y, a.y32, a.g, a.b, a.rows, a.eps, a.yq, a.qinv);
+    }
+    return;
+  }
   layernorm_kernel<TI, TO, COPY, G, NV><<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>(
       (const TI*)a.x, (TO*)a.y, a.y32, a.g, a.b, a.rows, a.eps);
 }
@@ -172,6 +199,19 @@ hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y,
              : run_ln_g<float, bf16, false>(G, nv, a, stream);
   }
   if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* qinv,
+                               const float* gamma, const float* beta, int rows, int width,
+                               float eps, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  int G, nv;
+  if (!pick_ln(width, &G, &nv)) return hipErrorInvalidValue;
+  LnArgs a{x, y, nullptr, gamma, beta, rows, eps};
+  a.yq = yq;
+  a.qinv = qinv;
+  if (!run_ln_g<f16, f16, false>(G, nv, a, stream)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
