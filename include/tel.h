@@ -149,6 +149,49 @@ int tel_encoder_forward(const tel_encoder_desc* desc, const void* const* packed_
                         int batch, int max_seq, int total_tokens, int max_len,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ shifted-window block
+ * Swin-style block ([SW] section 1: attention inside non-overlapping M x M windows, a
+ * cyclic window shift, a relative position bias; section 3: the bias lookup moved to
+ * preprocessing, a fused shift-window-partition kernel, fMHA), pre-LN:
+ *   Z  = LN1(X); Zs = roll(Z, -s) (both image axes); windows row-major, tokens row-major
+ *   A  = per window and head: softmax(q k^T / sqrt(d) + B_h + mask) v, heads concatenated,
+ *        then W_proj + b_proj; B_h[p][q] = table[(py_p - py_q + M - 1) * (2M - 1) +
+ *        (px_p - px_q + M - 1)][h]; mask excludes key q for query p unless both lie in
+ *        the same region of the shifted frame (per axis [0, L-M), [L-M, L-s), [L-s, L))
+ *   X1 = X + roll(window_reverse(A), +s);  Y = X1 + W_2 GELU(W_1 LN2(X1) + b_1) + b_2
+ * Tokens are in row-major image order: x, y [batch][height * width][channels].
+ * Supported: dtype TEL_F16 or TEL_F32; channels, mlp_hidden multiples of 8; head_dim in
+ * {16, 32, 64}; window * window <= 64; height, width multiples of window; 0 <= shift < window. */
+typedef struct {
+  int batch, height, width, channels, heads, window, shift, mlp_hidden;
+  int dtype;
+  float ln_eps;
+} tel_swin_desc;
+
+/* Device pointers, storage type desc->dtype: ln1/ln2 gamma, beta [C]; W_qkv [3C][C] (rows
+ * [Q heads | K heads | V heads]), b_qkv [3C]; rpb_table [(2M-1)^2][heads]; W_proj [C][C],
+ * b_proj [C]; W_1 [F][C], b_1 [F]; W_2 [C][F], b_2 [C]. */
+typedef struct {
+  const void *ln1_g, *ln1_b, *w_qkv, *b_qkv, *rpb_table, *w_proj, *b_proj;
+  const void *ln2_g, *ln2_b, *w_1, *b_1, *w_2, *b_2;
+} tel_swin_weights;
+
+/* tel_window_attention_forward flag: stop after X1 = X + attention branch (y := X1). */
+#define TEL_SWIN_ATTN_ONLY 1
+
+size_t tel_swin_packed_size(const tel_swin_desc* desc);
+/* One-time preprocessing: weights copied, vectors widened to float32, and the bias table
+ * expanded to [heads][M*M][64] float32 (times log2 e, -inf padding). packed: 256-byte
+ * aligned, >= tel_swin_packed_size bytes. */
+int tel_swin_prepare(const tel_swin_desc* desc, const tel_swin_weights* w, void* packed,
+                     size_t packed_bytes, void* stream);
+size_t tel_swin_workspace_size(const tel_swin_desc* desc);
+/* The block on x -> y (flags 0), or the attention half only (TEL_SWIN_ATTN_ONLY).
+ * Workspace: 256-byte aligned, >= tel_swin_workspace_size bytes. x and y must differ. */
+int tel_window_attention_forward(const tel_swin_desc* desc, const void* packed, const void* x,
+                                 void* y, int flags, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
 /* ------------------------------------------------------------------ kernel-level entry points
  * The same kernels the layer uses, exposed so that tests and per-kernel measurements can
  * localise a result to one kernel. */
@@ -212,6 +255,14 @@ int tel_quantize_weight_i8(const void* w, int8_t* q, float* scales, int N, int K
  * |C| <= K * 127^2 must fit in int32 (K <= 133,143). */
 int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, int K,
                     void* stream);
+
+/* Shifted-window partition with LayerNorm, one gather ([SW] section 3, the hand-written
+ * shift-window-partition kernel): y row r (window order: images, windows row-major,
+ * tokens row-major in a window) = LN(x image row ((wy*M + py + s) mod H, (wx*M + px + s)
+ * mod W)) * gamma + beta. x, y [batch * height * width][channels]. */
+int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, const float* beta,
+                                   int batch, int height, int width, int channels, int window,
+                                   int shift, float eps, int dtype, void* stream);
 
 /* y[r][:] = LN(x[r][:]) * gamma + beta over rows of width `width` (float32 gamma/beta). */
 int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,

@@ -31,8 +31,11 @@ EXPORTS = (
     "tel_encoder_workspace_size", "tel_encoder_layer_forward",
     "tel_encoder_forward_workspace_size", "tel_encoder_forward", "tel_gemm",
     "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_quantize_i8",
-    "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm",
+    "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
+    "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
+    "tel_window_partition_layernorm",
 )
+TEL_SWIN_ATTN_ONLY = 1
 
 
 class TelError(RuntimeError):
@@ -54,6 +57,19 @@ F = ctypes.c_float
 class tel_encoder_desc(ctypes.Structure):
     _fields_ = [("hidden", I), ("heads", I), ("ffn", I), ("dtype", I), ("int8_gemm", I),
                 ("ln_eps", F)]
+
+
+class tel_swin_desc(ctypes.Structure):
+    _fields_ = [(n, I) for n in ("batch", "height", "width", "channels", "heads", "window",
+                                 "shift", "mlp_hidden", "dtype")] + [("ln_eps", F)]
+
+
+_SWIN_WNAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "rpb_table", "w_proj", "b_proj", "ln2_g",
+                "ln2_b", "w_1", "b_1", "w_2", "b_2")
+
+
+class tel_swin_weights(ctypes.Structure):
+    _fields_ = [(n, P) for n in _SWIN_WNAMES]
 
 
 class tel_encoder_weights(ctypes.Structure):
@@ -85,6 +101,12 @@ _SIG = {
     "tel_quantize_i8": (I, [P, P, SZ, F, I, P]),
     "tel_quantize_weight_i8": (I, [P, P, P, I, I, I, P]),
     "tel_gemm_i8_i32": (I, [P, P, P, I, I, I, P]),
+    "tel_swin_packed_size": (SZ, [ctypes.POINTER(tel_swin_desc)]),
+    "tel_swin_prepare": (I, [ctypes.POINTER(tel_swin_desc), ctypes.POINTER(tel_swin_weights), P,
+                             SZ, P]),
+    "tel_swin_workspace_size": (SZ, [ctypes.POINTER(tel_swin_desc)]),
+    "tel_window_attention_forward": (I, [ctypes.POINTER(tel_swin_desc), P, P, P, I, P, SZ, P]),
+    "tel_window_partition_layernorm": (I, [P, P, P, P, I, I, I, I, I, I, F, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -248,6 +270,41 @@ def tel_gemm_i8_i32(A, B, C, stream=None):
     N = B.shape[0]
     _check("tel_gemm_i8_i32", lib.tel_gemm_i8_i32(_ptr(A), _ptr(B), _ptr(C), M, N, K,
                                                   _stream(stream)))
+
+
+def make_swin_desc(batch, height, width, channels, heads, window, shift, mlp_hidden,
+                   dtype: torch.dtype, eps=1e-5):
+    return tel_swin_desc(batch, height, width, channels, heads, window, shift, mlp_hidden,
+                         dtype_code(dtype), eps)
+
+
+def tel_swin_packed_size(desc) -> int:
+    return lib.tel_swin_packed_size(ctypes.byref(desc))
+
+
+def tel_swin_workspace_size(desc) -> int:
+    return lib.tel_swin_workspace_size(ctypes.byref(desc))
+
+
+def tel_swin_prepare(desc, weights: dict, packed, stream=None):
+    w = tel_swin_weights(*[_ptr(weights[n]) for n in _SWIN_WNAMES])
+    _check("tel_swin_prepare", lib.tel_swin_prepare(
+        ctypes.byref(desc), ctypes.byref(w), _ptr(packed), packed.numel() * packed.element_size(),
+        _stream(stream)))
+
+
+def tel_window_attention_forward(desc, packed, x, y, workspace, flags: int = 0, stream=None):
+    _check("tel_window_attention_forward", lib.tel_window_attention_forward(
+        ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tel_window_partition_layernorm(x, y, gamma, beta, batch, height, width, window, shift,
+                                   eps: float, stream=None):
+    C = x.shape[-1]
+    _check("tel_window_partition_layernorm", lib.tel_window_partition_layernorm(
+        _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), batch, height, width, C, window, shift, eps,
+        dtype_code(x.dtype), _stream(stream)))
 
 
 # ------------------------------------------------------------------ allocation helpers

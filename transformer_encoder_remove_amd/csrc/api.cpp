@@ -222,6 +222,85 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   return TEL_OK;
 }
 
+// ------------------------------------------------------------------ shifted-window block
+int swin_supported(const tel_swin_desc* d) {
+  if (!d) return TEL_EINVAL;
+  if (d->batch <= 0 || d->height <= 0 || d->width <= 0 || d->channels <= 0 || d->heads <= 0 ||
+      d->window <= 0 || d->mlp_hidden <= 0 || d->shift < 0 || !(d->ln_eps >= 0.f))
+    return TEL_EINVAL;
+  if (d->channels % d->heads || d->height % d->window || d->width % d->window ||
+      d->shift >= d->window)
+    return TEL_EINVAL;
+  if ((long long)d->batch * d->height * d->width > INT32_MAX / 4) return TEL_EUNSUPPORTED;
+  if (d->dtype != DT_F16 && d->dtype != DT_F32) return TEL_EUNSUPPORTED;
+  if (d->channels % 8 || d->mlp_hidden % 8) return TEL_EUNSUPPORTED;
+  if (!layernorm_supported(d->dtype, d->channels)) return TEL_EUNSUPPORTED;
+  if (!window_attention_supported(d->dtype, d->channels / d->heads, d->window * d->window))
+    return TEL_EUNSUPPORTED;
+  return TEL_OK;
+}
+
+SwinGeom swin_geom(const tel_swin_desc* d) {
+  SwinGeom g;
+  g.Hs = d->height;
+  g.Ws = d->width;
+  g.M = d->window;
+  g.s = d->shift;
+  g.nWx = d->width / d->window;
+  g.nW = (d->height / d->window) * g.nWx;
+  g.N = d->window * d->window;
+  return g;
+}
+
+struct SwinLayout {
+  size_t w_qkv, w_proj, w_1, w_2;
+  size_t ln1_g, ln1_b, b_qkv, b_proj, ln2_g, ln2_b, b_1, b_2, bias;
+  size_t total;
+};
+
+SwinLayout swin_layout(const tel_swin_desc* d) {
+  const size_t C = d->channels, F = d->mlp_hidden, es = dtype_size(d->dtype);
+  const size_t N = (size_t)d->window * d->window;
+  SwinLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  L.w_qkv = take(3 * C * C * es);
+  L.w_proj = take(C * C * es);
+  L.w_1 = take(F * C * es);
+  L.w_2 = take(C * F * es);
+  L.ln1_g = take(C * 4);
+  L.ln1_b = take(C * 4);
+  L.b_qkv = take(3 * C * 4);
+  L.b_proj = take(C * 4);
+  L.ln2_g = take(C * 4);
+  L.ln2_b = take(C * 4);
+  L.b_1 = take(F * 4);
+  L.b_2 = take(C * 4);
+  L.bias = take((size_t)d->heads * N * 64 * 4);
+  L.total = o;
+  return L;
+}
+
+struct SwinWs {
+  size_t zw, qkv, ctx, x1, h, f, total;
+};
+
+SwinWs swin_ws(const tel_swin_desc* d) {
+  const size_t T = (size_t)d->batch * d->height * d->width;
+  const size_t C = d->channels, F = d->mlp_hidden, es = dtype_size(d->dtype);
+  SwinWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  w.zw = take(T * C * es);
+  w.qkv = take(3 * T * C * es);
+  w.ctx = take(T * C * es);
+  w.x1 = take(T * C * es);
+  w.h = take(T * C * es);
+  w.f = take(T * F * es);
+  w.total = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -452,6 +531,113 @@ int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, 
   if (K % 16 || N % 4) return TEL_EUNSUPPORTED;
   GemmArgs g{EPI_RAW_I32, A, B, nullptr, nullptr, C, M, N, K, 1};
   return status_of(launch_gemm(DT_I8, g, as_stream(stream)));
+}
+
+size_t tel_swin_packed_size(const tel_swin_desc* d) {
+  if (swin_supported(d) != TEL_OK) return 0;
+  return swin_layout(d).total;
+}
+
+int tel_swin_prepare(const tel_swin_desc* d, const tel_swin_weights* w, void* packed,
+                     size_t packed_bytes, void* stream) {
+  const int sup = swin_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (!w || !packed || !aligned256(packed)) return TEL_EINVAL;
+  const void* ptrs[] = {w->ln1_g, w->ln1_b, w->w_qkv, w->b_qkv, w->rpb_table, w->w_proj,
+                        w->b_proj, w->ln2_g, w->ln2_b, w->w_1, w->b_1, w->w_2, w->b_2};
+  for (const void* p : ptrs)
+    if (!p) return TEL_EINVAL;
+  const SwinLayout L = swin_layout(d);
+  if (packed_bytes < L.total) return TEL_EWORKSPACE;
+  const size_t C = d->channels, F = d->mlp_hidden, es = dtype_size(d->dtype);
+  const int dt = d->dtype;
+  char* P = (char*)packed;
+  hipStream_t st = as_stream(stream);
+  TEL_TRY(hipMemcpyAsync(P + L.w_qkv, w->w_qkv, 3 * C * C * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_proj, w->w_proj, C * C * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_1, w->w_1, F * C * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(hipMemcpyAsync(P + L.w_2, w->w_2, C * F * es, hipMemcpyDeviceToDevice, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln1_g, (float*)(P + L.ln1_g), C, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln1_b, (float*)(P + L.ln1_b), C, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_qkv, (float*)(P + L.b_qkv), 3 * C, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_proj, (float*)(P + L.b_proj), C, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln2_g, (float*)(P + L.ln2_g), C, st));
+  TEL_TRY(launch_widen_f32(dt, w->ln2_b, (float*)(P + L.ln2_b), C, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_1, (float*)(P + L.b_1), F, st));
+  TEL_TRY(launch_widen_f32(dt, w->b_2, (float*)(P + L.b_2), C, st));
+  TEL_TRY(launch_expand_rel_bias(dt, w->rpb_table, (float*)(P + L.bias), d->window, d->heads, st));
+  return TEL_OK;
+}
+
+size_t tel_swin_workspace_size(const tel_swin_desc* d) {
+  if (swin_supported(d) != TEL_OK) return 0;
+  return swin_ws(d).total;
+}
+
+int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, const void* x,
+                                 void* y, int flags, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  const int sup = swin_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (flags & ~TEL_SWIN_ATTN_ONLY) return TEL_EINVAL;
+  if (!packed || !x || !y || !workspace) return TEL_EINVAL;
+  if (!aligned256(packed) || !aligned256(workspace) || !aligned16(x) || !aligned16(y))
+    return TEL_EINVAL;
+  if (x == y) return TEL_EINVAL;
+  const SwinWs W = swin_ws(d);
+  if (ws_bytes < W.total) return TEL_EWORKSPACE;
+  const SwinLayout L = swin_layout(d);
+  const SwinGeom g = swin_geom(d);
+  const int T = d->batch * d->height * d->width, C = d->channels, F = d->mlp_hidden;
+  const int nh = d->heads, dt = d->dtype;
+  const char* P = (const char*)packed;
+  char* ws = (char*)workspace;
+  auto F32 = [&](size_t off) { return (const float*)(P + off); };
+  hipStream_t st = as_stream(stream);
+  void* zw = ws + W.zw;
+  void* qkv = ws + W.qkv;
+  void* ctx = ws + W.ctx;
+  void* x1 = (flags & TEL_SWIN_ATTN_ONLY) ? y : (void*)(ws + W.x1);
+  void* hh = ws + W.h;
+  void* f = ws + W.f;
+  // LN1 + roll(-s) + window partition, one gather
+  TEL_TRY(launch_layernorm_gather(dt, x, zw, F32(L.ln1_g), F32(L.ln1_b), T, C, d->ln_eps, g, st));
+  GemmArgs a{EPI_QKV_SPLIT, zw, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * C, C, nh};
+  TEL_TRY(launch_gemm(dt, a, st));
+  TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh, st));
+  // proj + bias, window reverse + roll(+s) + residual in the epilogue
+  a = GemmArgs{EPI_SWIN_SCATTER, ctx, P + L.w_proj, F32(L.b_proj), x, x1, T, C, C, nh};
+  a.geom = g;
+  TEL_TRY(launch_gemm(dt, a, st));
+  if (flags & TEL_SWIN_ATTN_ONLY) return TEL_OK;
+  TEL_TRY(launch_layernorm(dt, dt, x1, hh, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, C, d->ln_eps,
+                           st));
+  a = GemmArgs{EPI_BIAS_GELU, hh, P + L.w_1, F32(L.b_1), nullptr, f, T, F, C, nh};
+  TEL_TRY(launch_gemm(dt, a, st));
+  a = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), x1, y, T, C, F, nh};
+  TEL_TRY(launch_gemm(dt, a, st));
+  return TEL_OK;
+}
+
+int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, const float* beta,
+                                   int batch, int height, int width, int channels, int window,
+                                   int shift, float eps, int dtype, void* stream) {
+  if (batch <= 0 || height <= 0 || width <= 0 || channels <= 0 || window <= 0 || shift < 0 ||
+      !(eps >= 0.f))
+    return TEL_EINVAL;
+  if (height % window || width % window || shift >= window) return TEL_EINVAL;
+  if (!layernorm_supported(dtype, channels)) return TEL_EUNSUPPORTED;
+  if ((long long)batch * height * width > INT32_MAX / 4) return TEL_EUNSUPPORTED;
+  if (!x || !y || !gamma || !beta) return TEL_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta)) return TEL_EINVAL;
+  if (x == y) return TEL_EINVAL;
+  tel_swin_desc d{};
+  d.height = height;
+  d.width = width;
+  d.window = window;
+  d.shift = shift;
+  return status_of(launch_layernorm_gather(dtype, x, y, gamma, beta, batch * height * width,
+                                           channels, eps, swin_geom(&d), as_stream(stream)));
 }
 
 int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,

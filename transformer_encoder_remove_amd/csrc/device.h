@@ -84,6 +84,42 @@ template <int G> __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// ------------------------------------------------------------------ shifted windows
+// Token order maps of the shifted-window block. Image order: row b * Hs * Ws + y * Ws + x.
+// Window order: windows row-major inside each image, images outermost, tokens row-major
+// inside a window (p = py * M + px). The block computes on the cyclically shifted image
+// (roll by -s on both axes), so window-order row r holds image row src(r) with
+// y = (wy * M + py + s) mod Hs, x = (wx * M + px + s) mod Ws. The same map serves the
+// gather before attention and the scatter (window reverse + roll by +s) after it.
+struct SwinGeom {
+  int Hs, Ws, M, s;   // image height/width, window size, shift
+  int nWx, nW, N;     // windows per image row, windows per image, tokens per window
+
+  __device__ __forceinline__ int src_row(int r) const {
+    const int per_img = nW * N;
+    const int b = r / per_img, rem = r - b * per_img;
+    const int w = rem / N, p = rem - w * N;
+    const int wy = w / nWx, wx = w - wy * nWx;
+    const int py = p / M, px = p - py * M;
+    int y = wy * M + py + s, x = wx * M + px + s;
+    if (y >= Hs) y -= Hs;
+    if (x >= Ws) x -= Ws;
+    return b * Hs * Ws + y * Ws + x;
+  }
+  // Shift-mask region of window-order token p of window w (image-local window index):
+  // per axis, [0, L-M) -> 0, [L-M, L-s) -> 1, [L-s, L) -> 2 in the shifted frame; no mask
+  // (one region) when s == 0.
+  __device__ __forceinline__ int region(int w, int p) const {
+    if (s == 0) return 0;
+    const int wy = w / nWx, wx = w - wy * nWx;
+    const int py = p / M, px = p - py * M;
+    const int Y = wy * M + py, X = wx * M + px;
+    const int ry = Y < Hs - M ? 0 : (Y < Hs - s ? 1 : 2);
+    const int rx = X < Ws - M ? 0 : (X < Ws - s ? 1 : 2);
+    return 3 * ry + rx;
+  }
+};
+
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }

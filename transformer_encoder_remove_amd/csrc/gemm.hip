@@ -43,6 +43,7 @@ template <typename T, typename TR, typename TO> struct EpiArgs {
   int M, N, heads;
   const float* dq;     // int8 operands: per-column dequantisation scale [N]
   const float* qinv;   // int8 output: device scalar, 1 / activation scale of the consumer
+  SwinGeom geom;       // EPI_SWIN_SCATTER: window order -> image order
 };
 
 __device__ __forceinline__ int8_t quantize_code(float v, float inv) {
@@ -78,8 +79,10 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
     }
-    if constexpr (EPI == EPI_BIAS_RESID) {
-      const Vec4<TR> r = *reinterpret_cast<const Vec4<TR>*>(e.resid + (size_t)m * e.N + n);
+    if constexpr (EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER) {
+      // the scatter epilogue reads the residual at the image-order row it writes
+      const size_t row = EPI == EPI_SWIN_SCATTER ? (size_t)e.geom.src_row(m) : (size_t)m;
+      const Vec4<TR> r = *reinterpret_cast<const Vec4<TR>*>(e.resid + row * e.N + n);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] += to_f32(r.v[i]);
     }
@@ -89,6 +92,8 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
       const int H = e.N / 3, d = H / e.heads;
       const int which = n / H, rem = n - which * H, hh = rem / d, c = rem - hh * d;
       idx = (((size_t)which * e.heads + hh) * e.M + m) * d + c;
+    } else if constexpr (EPI == EPI_SWIN_SCATTER) {
+      idx = (size_t)e.geom.src_row(m) * e.N + n;
     } else {
       idx = (size_t)m * e.N + n;
     }
@@ -345,6 +350,9 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   // flight there would make the compiler wait for every LDS read before each MFMA block.
   asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads),
                "s"(e.dq), "s"(e.qinv));
+  if constexpr (EPI == EPI_SWIN_SCATTER)
+    asm volatile("" ::"s"(e.geom.Hs), "s"(e.geom.Ws), "s"(e.geom.M), "s"(e.geom.s),
+                 "s"(e.geom.nWx), "s"(e.geom.nW), "s"(e.geom.N));
   __builtin_amdgcn_s_barrier();                     // slice 0 has landed
   asm volatile("" ::: "memory");
   TEL_PIPE_FRAGS(0, 0, 0);
@@ -405,7 +413,7 @@ constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 template <typename T, int BM, int BN, int WM, int WN, int EPI, typename TR, typename TO>
 static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
-  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv};
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI, TR, TO><<<grid, WM * WN * 64, 0, stream>>>(
       (const T*)a.A, (const T*)a.W, a.K, e);
@@ -414,7 +422,7 @@ static void launch_one(const GemmArgs& a, hipStream_t stream) {
 template <typename T, int C, int EPI, typename TR, typename TO>
 static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
-  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv};
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
   const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
       <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>((const T*)a.A, (const T*)a.W,
@@ -444,6 +452,7 @@ static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
     case EPI_BIAS: launch_cfg<T, EPI_BIAS, T, T>(cfg, a, stream); break;
     case EPI_BIAS_GELU: launch_cfg<T, EPI_BIAS_GELU, T, T>(cfg, a, stream); break;
     case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, T, T>(cfg, a, stream); break;
+    case EPI_SWIN_SCATTER: launch_cfg<T, EPI_SWIN_SCATTER, T, T>(cfg, a, stream); break;
     case EPI_BIAS_RESID:
       if constexpr (std::is_same<T, bf16>::value) {
         if (a.resid_f32 && a.out_f32) {

@@ -4,10 +4,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "device.h"
+
 namespace tel {
 
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
-enum Epi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4 };
+enum Epi {
+  EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4,
+  EPI_SWIN_SCATTER = 5   // bias + residual, row m written to image row geom.src_row(m)
+};
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
 
@@ -35,6 +40,7 @@ struct GemmArgs {
   const float* dq = nullptr;    // int8 operands: per-column dequantisation scale [N]
   const float* qinv = nullptr;  // int8 output (EPI_BIAS_GELU): device scalar 1 / scale
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
+  SwinGeom geom{};              // EPI_SWIN_SCATTER
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
@@ -53,10 +59,25 @@ bool layernorm_supported(int dtype, int width);
 hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,
                             const float* gamma, const float* beta, int rows, int width, float eps,
                             hipStream_t stream);
+// LayerNorm of the shifted-window gather: y[r] = LN(x[geom.src_row(r)]).
+hipError_t launch_layernorm_gather(int dtype, const void* x, void* y, const float* gamma,
+                                   const float* beta, int rows, int width, float eps,
+                                   const SwinGeom& geom, hipStream_t stream);
 // fp16 LayerNorm that also writes the int8 codes of its (fp16-rounded) output.
 hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* qinv,
                                const float* gamma, const float* beta, int rows, int width,
                                float eps, hipStream_t stream);
+
+// swin.hip: window attention with relative-position bias and shift mask over window-
+// order Q, K, V in the [3][heads][T][d] layout; bias_exp [heads][N][64] float32 (already
+// times log2 e, -inf in columns >= N). total_tokens = images * nW * N.
+bool window_attention_supported(int dtype, int head_dim, int N);
+hipError_t launch_window_attention(int dtype, const void* qkv_split, void* ctx,
+                                   const float* bias_exp, const SwinGeom& geom, int windows,
+                                   int heads, int head_dim, hipStream_t stream);
+// bias_exp[h][p][q] = table[idx(p, q)][h] * log2(e) for q < N = M * M, -inf for q >= N.
+hipError_t launch_expand_rel_bias(int dtype, const void* table, float* bias_exp, int M, int heads,
+                                  hipStream_t stream);
 
 // prepare.hip
 hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);

@@ -45,7 +45,9 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
 
 // Q8: also write the int8 codes of the output for an int8 GEMM that consumes it, taken
 // from the stored (TO-rounded) value: code = clamp(rne(float(y) * inv), -127, 127).
-template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false>
+// GATHER: output row r reads input row geom.src_row(r) (the shifted-window partition:
+// LayerNorm, cyclic shift and window partition in one pass).
+template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false, bool GATHER = false>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restrict__ x,
                                                                TO* __restrict__ y,
                                                                float* __restrict__ y32,
@@ -53,12 +55,13 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
                                                                const float* __restrict__ beta,
                                                                int rows, float eps,
                                                                int8_t* __restrict__ yq = nullptr,
-                                                               const float* __restrict__ qinv = nullptr) {
+                                                               const float* __restrict__ qinv = nullptr,
+                                                               SwinGeom geom = SwinGeom{}) {
   constexpr int H = G * NV * 8;
   const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
   if (row >= rows) return;   // whole G-lane groups leave together
-  const TI* xr = x + (size_t)row * H;
+  const TI* xr = x + (size_t)(GATHER ? geom.src_row(row) : row) * H;
   float v[NV][8];
   float s = 0.f;
 #pragma unroll
@@ -139,11 +142,20 @@ struct LnArgs {
   float eps;
   int8_t* yq = nullptr;
   const float* qinv = nullptr;
+  const SwinGeom* geom = nullptr;
 };
 
 template <typename TI, typename TO, bool COPY, int G, int NV>
 static void run_ln(const LnArgs& a, hipStream_t s) {
   constexpr int RPB = LN_THREADS / G;
+  if (a.geom) {
+    if constexpr (std::is_same<TI, TO>::value && !COPY) {
+      layernorm_kernel<TI, TO, COPY, G, NV, false, true>
+          <<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>((const TI*)a.x, (TO*)a.y, a.y32, a.g, a.b,
+                                                          a.rows, a.eps, nullptr, nullptr, *a.geom);
+    }
+    return;
+  }
   if (a.yq) {
     if constexpr (std::is_same<TI, f16>::value && std::is_same<TO, f16>::value && !COPY) {
       layernorm_kernel<TI, TO, COPY, G, NV, true><<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>(
@@ -197,6 +209,24 @@ hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y,
   } else if (dtype_in == DT_F32 && dtype_out == DT_BF16) {
     ok = y32 ? run_ln_g<float, bf16, true>(G, nv, a, stream)
              : run_ln_g<float, bf16, false>(G, nv, a, stream);
+  }
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_gather(int dtype, const void* x, void* y, const float* gamma,
+                                   const float* beta, int rows, int width, float eps,
+                                   const SwinGeom& geom, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  int G, nv;
+  if (!pick_ln(width, &G, &nv)) return hipErrorInvalidValue;
+  LnArgs a{x, y, nullptr, gamma, beta, rows, eps};
+  a.geom = &geom;
+  bool ok = false;
+  switch (dtype) {
+    case DT_F16: ok = run_ln_g<f16, f16, false>(G, nv, a, stream); break;
+    case DT_BF16: ok = run_ln_g<bf16, bf16, false>(G, nv, a, stream); break;
+    case DT_F32: ok = run_ln_g<float, float, false>(G, nv, a, stream); break;
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
