@@ -6,6 +6,11 @@ prepared weights are resident in HBM before the timed region. Prints ONE JSON li
 
     python bench.py [--steps K] [--warmup W] [--workload bert_base] [--no-cpu]
 
+Other workloads (same line format, measured the same way): bert_large_tput,
+bert_large_latency (24 fp16 layers), bert_base_int8 (int8 GEMMs; static activation
+scales from tel_encoder_calibrate on the same batch, i.e. post-training calibration,
+outside the timed region), swin_t_stage1 (one shifted-window block, tokens/s per block).
+
 Also measured here, each with HIP events on the stream its kernel is launched on:
 the average duration of every kernel of one layer (same shapes, launched through the
 kernel-level entry points) and the roofline fraction of the dominant one; and the CPU
@@ -59,9 +64,12 @@ def main():
     import tel_inputs as ti
     import transformer_encoder_remove_amd as tel
 
+    if args.workload in ti.SWIN_CONFIGS:
+        return bench_swin(args)
     cfg = dict(ti.ENCODER_CONFIGS[args.workload])
     if args.dtype:
         cfg["dtype"] = args.dtype
+    int8 = bool(cfg.get("int8"))
     dt = cfg["dtype"]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
     B, S, H, nh, F, NL = (cfg["batch"], cfg["max_seq"], cfg["hidden"], cfg["heads"], cfg["ffn"],
@@ -71,21 +79,47 @@ def main():
 
     lens, x_pad = ti.encoder_input(cfg)
     T, max_len = int(lens.sum()), int(lens.max())
-    log(f"[bench] workload {args.workload}: B={B} S={S} T={T} H={H} heads={nh} F={F} layers={NL} {dt}")
+    log(f"[bench] workload {args.workload}: B={B} S={S} T={T} H={H} heads={nh} F={F} layers={NL} "
+        f"{dt}{' int8 GEMMs' if int8 else ''}")
     desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS)
     psize = tel.tel_encoder_packed_size(desc)
-    packed, layer_w = [], []
+    packed, layer_w, dws = [], [], []
     for i in range(NL):
         w = ti.encoder_layer_weights(cfg, i)
         dw = {k: dev(v) for k, v in w.items()}
         p = tel.alloc_bytes(psize)
         tel.tel_encoder_prepare(desc, dw, p)
         packed.append(p)
+        dws.append(dw)
         if i == 0:
             layer_w = dw
     x = dev(x_pad)
     y = torch.empty_like(x)
     lens_d = torch.from_numpy(lens).cuda()
+    cu_d = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
+    if int8:
+        # post-training calibration on this batch (the float stack, layer by layer), then
+        # the int8 layers prepared with those static scales
+        from_pad = torch.empty((T, H), dtype=tdt, device="cuda")
+        po = torch.empty(B * S, dtype=torch.int32, device="cuda")
+        tel.tel_build_offsets(lens_d, S, cu_d, po)
+        tel.tel_remove_padding(x, from_pad, po, T)
+        amax = torch.zeros((NL, 4), dtype=torch.float32, device="cuda")
+        lws = tel.alloc_bytes(tel.tel_encoder_workspace_size(desc, T))
+        cur, nxt = from_pad, torch.empty_like(from_pad)
+        for i in range(NL):
+            tel.tel_encoder_calibrate(desc, packed[i], cur, nxt, cu_d, T, max_len, amax[i], lws)
+            cur, nxt = nxt, cur
+        amax_h = amax.cpu().numpy()
+        desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS, int8_gemm=True)
+        psize = tel.tel_encoder_packed_size(desc)
+        packed = []
+        for i in range(NL):
+            p = tel.alloc_bytes(psize)
+            tel.tel_encoder_prepare(desc, dws[i], p, act_amax=tuple(float(a) for a in amax_h[i]))
+            packed.append(p)
+        log(f"[bench] calibrated act_amax layer 0: {amax_h[0]}")
+    del dws
     ws = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
     torch.cuda.synchronize()
 
@@ -116,6 +150,9 @@ def main():
     # ---------------------------------------------------------------- per-kernel timing
     # Each kernel of one layer, same shapes and launch configuration as inside the stack,
     # timed with HIP events on the stream it is launched on.
+    if int8:   # the kernel-level entry points time float kernels; none for int8 here
+        cpu = None if args.no_cpu else cpu_baseline(cfg, lens, x_pad, args.cpu_seconds)
+        return emit(args, cfg, value, ms_per_step, T, max_len, None, {}, cpu)
     qkv = torch.randn(3 * T * H, device="cuda").to(tdt)
     hid = torch.randn(T, H, device="cuda").to(tdt)
     ctx = torch.empty(T, H, device="cuda", dtype=tdt)
@@ -181,20 +218,93 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, lens, x_pad, args.cpu_seconds)
 
+    return emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu,
+                layer_sum_us)
+
+
+def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, layer_sum_us=None):
+    NL = cfg["layers"]
+    int8 = bool(cfg.get("int8"))
     out = {
         "metric": "valid tokens/sec per encoder layer (BERT-base fp16) + % of MFMA/HBM roofline",
         "value": round(value, 1), "unit": "valid tokens/s per layer", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8" if int8 else cfg["dtype"],
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
-        "config": {"workload": f"{args.workload}: {NL}-layer post-LN encoder, offsets + padding "
-                               f"removal + layers + rebuild", "batch": B, "max_seq": S,
-                   "valid_tokens": T, "max_len": max_len, "hidden": H, "heads": nh, "ffn": F,
+        "config": {"workload": f"{args.workload}: {NL}-layer post-LN encoder"
+                               f"{' with int8 GEMMs' if int8 else ''}, offsets + padding removal "
+                               f"+ layers + rebuild", "batch": cfg["batch"],
+                   "max_seq": cfg["max_seq"], "valid_tokens": T, "max_len": max_len,
+                   "hidden": cfg["hidden"], "heads": cfg["heads"], "ffn": cfg["ffn"],
                    "layers": NL, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},
-        "layer_kernel_sum_us": round(layer_sum_us, 3),
+    }
+    if per_kernel:
+        out["kernels_us"] = {k: round(v["us"], 3) for k, v in per_kernel.items()}
+        out["layer_kernel_sum_us"] = round(layer_sum_us, 3)
+    print(json.dumps(out), flush=True)
+
+
+def bench_swin(args):
+    """One shifted-window block (Swin-T stage-1 shape) per step; tokens/s per block."""
+    import torch
+
+    import tel_inputs as ti
+    import transformer_encoder_remove_amd as tel
+    cfg = ti.SWIN_CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    tdt = torch.float16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).cuda().to(tdt)
+    x_np = ti.swin_input(cfg)
+    w = ti.swin_block_weights(cfg)
+    desc = tel.make_swin_desc(cfg["batch"], cfg["height"], cfg["width"], cfg["channels"],
+                              cfg["heads"], cfg["window"], cfg["shift"], cfg["mlp"], tdt, ti.LN_EPS)
+    packed = tel.alloc_bytes(tel.tel_swin_packed_size(desc))
+    tel.tel_swin_prepare(desc, {k: dev(v) for k, v in w.items()}, packed)
+    x = dev(x_np)
+    y = torch.empty_like(x)
+    ws = tel.alloc_bytes(tel.tel_swin_workspace_size(desc))
+    T = cfg["batch"] * cfg["height"] * cfg["width"]
+    log(f"[bench] workload {args.workload}: {cfg} tokens={T}")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        tel.tel_window_attention_forward(desc, packed, x, y, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        tel.tel_window_attention_forward(desc, packed, x, y, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = T / (ms / 1e3)
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {value / 1e9:.3f} G tokens/s per block")
+    cpu = None
+    if not args.no_cpu:
+        from oracle import swin
+        n_img, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and n_img < cfg["batch"]:
+            t0 = time.perf_counter()
+            swin.swin_block(x_np[n_img:n_img + 1], w, cfg["height"], cfg["width"], cfg["heads"],
+                            cfg["window"], cfg["shift"], ti.LN_EPS)
+            t_cpu += time.perf_counter() - t0
+            n_img += 1
+        tok = n_img * cfg["height"] * cfg["width"]
+        cpu = {"value": round(tok / t_cpu, 1), "unit": "tokens/s per block",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{n_img} image(s) of the same block, float64 NumPy, {t_cpu:.1f} s"}
+    out = {
+        "metric": "tokens/sec per shifted-window block (Swin-T stage-1 fp16)",
+        "value": round(value, 1), "unit": "tokens/s per block", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights and bias table)",
+        "config": {"workload": f"{args.workload}: shifted-window block, LN1 + shift + partition, "
+                               "QKV, window attention (bias + mask), proj + unshift + residual, "
+                               "LN2, MLP", **{k: v for k, v in cfg.items() if k != "dtype"}},
+        "roofline": None, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -214,11 +324,18 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     xp = enc.remove_padding(x_pad.astype(np.float64), lens)
     T = int(lens.sum())
     weights = [ti.encoder_layer_weights(cfg, i) for i in range(cfg["layers"])]
+    int8 = bool(cfg.get("int8"))
+    if int8:
+        from oracle import int8 as q8
     elapsed, done = 0.0, 0
     while elapsed < seconds:
         w = weights[done % len(weights)]
+        amax = q8.calibrate(xp, cu, w, cfg["heads"], ti.LN_EPS) if int8 else None
         t0 = time.perf_counter()
-        xp = enc.encoder_layer(xp, cu, w, cfg["heads"], ti.LN_EPS)
+        if int8:
+            xp = q8.encoder_layer_int8(xp, cu, w, cfg["heads"], ti.LN_EPS, amax)
+        else:
+            xp = enc.encoder_layer(xp, cu, w, cfg["heads"], ti.LN_EPS)
         elapsed += time.perf_counter() - t0
         done += 1
     cores = blas_threads or len(os.sched_getaffinity(0))

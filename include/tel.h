@@ -136,6 +136,17 @@ int tel_encoder_layer_forward(const tel_encoder_desc* desc, const void* packed,
                               int total_tokens, int max_len, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* Post-training calibration of the int8 variant's static activation scales: runs one
+ * floating-point layer (desc->int8_gemm == 0) exactly as tel_encoder_layer_forward and
+ * raises amax[0..3] (device float[4], caller-initialised, e.g. to 0) to the max-abs of
+ * the inputs of its QKV, O, FFN1 and FFN2 GEMMs (x, attention output, h1, GELU output).
+ * Calls accumulate, so a stack is calibrated layer by layer on one or more batches;
+ * the results become tel_encoder_weights.act_amax of the int8 layer. */
+int tel_encoder_calibrate(const tel_encoder_desc* desc, const void* packed, const void* x,
+                          void* y, const int32_t* cu_seqlens, int batch, int total_tokens,
+                          int max_len, float* amax, void* workspace, size_t ws_bytes,
+                          void* stream);
+
 /* Workspace bytes of tel_encoder_forward for a batch of `batch` x `max_seq`. */
 size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* desc, int batch, int max_seq);
 

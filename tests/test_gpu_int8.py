@@ -123,3 +123,28 @@ def test_int8_bert_base_12_layers_sampled():
     ma, rel = errors(got, ref)
     print(f"int8 12 layers vs Q-oracle (reported): max_abs={ma:.3e} rel_frob={rel:.3e}")
     assert rel < 0.1
+
+
+def test_calibrate_matches_oracle():
+    """tel_encoder_calibrate's max-abs of the four GEMM inputs vs the oracle's calibration
+    (fp16 intermediates on the GPU, float64 in the oracle: equal to ~fp16 precision)."""
+    cfg = ti.ENCODER_CONFIGS["bert_base"]
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], torch.float16, EPS)
+    packed = tel.alloc_bytes(tel.tel_encoder_packed_size(desc))
+    tel.tel_encoder_prepare(desc, {k: dev(v, "f16") for k, v in w.items()}, packed)
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    T = xp.shape[0]
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    xd = dev(xp, "f16")
+    yd = torch.empty_like(xd)
+    amax = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = tel.alloc_bytes(tel.tel_encoder_workspace_size(desc, T))
+    tel.tel_encoder_calibrate(desc, packed, xd, yd, torch.tensor(cu.astype(np.int32), device="cuda"),
+                              T, int(lens.max()), amax, ws)
+    torch.cuda.synchronize()
+    ref = np.array(q8.calibrate(xp, cu, w, cfg["heads"], EPS))
+    got = amax.cpu().numpy().astype(np.float64)
+    assert got[0] == ref[0]                               # the input itself: exact
+    assert np.all(np.abs(got - ref) <= 5e-3 * ref), (got, ref)

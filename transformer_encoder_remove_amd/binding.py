@@ -28,7 +28,7 @@ CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 EXPORTS = (
     "tel_status_str", "tel_version", "tel_build_offsets", "tel_remove_padding",
     "tel_rebuild_padding", "tel_encoder_packed_size", "tel_encoder_prepare",
-    "tel_encoder_workspace_size", "tel_encoder_layer_forward",
+    "tel_encoder_workspace_size", "tel_encoder_layer_forward", "tel_encoder_calibrate",
     "tel_encoder_forward_workspace_size", "tel_encoder_forward", "tel_gemm",
     "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_quantize_i8",
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
@@ -90,6 +90,8 @@ _SIG = {
     "tel_encoder_workspace_size": (SZ, [ctypes.POINTER(tel_encoder_desc), I]),
     "tel_encoder_layer_forward": (I, [ctypes.POINTER(tel_encoder_desc), P, P, P, P, I, I, I, P,
                                       SZ, P]),
+    "tel_encoder_calibrate": (I, [ctypes.POINTER(tel_encoder_desc), P, P, P, P, I, I, I, P, P, SZ,
+                                  P]),
     "tel_encoder_forward_workspace_size": (SZ, [ctypes.POINTER(tel_encoder_desc), I, I]),
     "tel_encoder_forward": (I, [ctypes.POINTER(tel_encoder_desc), ctypes.POINTER(P), I, P, P, P,
                                 I, I, I, I, P, SZ, P]),
@@ -206,6 +208,14 @@ def tel_encoder_layer_forward(desc, packed, x, y, cu_seqlens, total_tokens: int,
     _check("tel_encoder_layer_forward", lib.tel_encoder_layer_forward(
         ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
         cu_seqlens.numel() - 1, total_tokens, max_len, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tel_encoder_calibrate(desc, packed, x, y, cu_seqlens, total_tokens: int, max_len: int, amax,
+                          workspace, stream=None):
+    _check("tel_encoder_calibrate", lib.tel_encoder_calibrate(
+        ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, total_tokens, max_len, _ptr(amax), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

@@ -429,6 +429,27 @@ int tel_encoder_layer_forward(const tel_encoder_desc* d, const void* packed, con
                        (char*)workspace, as_stream(stream));
 }
 
+int tel_encoder_calibrate(const tel_encoder_desc* d, const void* packed, const void* x, void* y,
+                          const int32_t* cu_seqlens, int batch, int total_tokens, int max_len,
+                          float* amax, void* workspace, size_t ws_bytes, void* stream) {
+  if (d && d->int8_gemm) return TEL_EINVAL;
+  if (!amax) return TEL_EINVAL;
+  const int r = tel_encoder_layer_forward(d, packed, x, y, cu_seqlens, batch, total_tokens,
+                                          max_len, workspace, ws_bytes, stream);
+  if (r != TEL_OK || total_tokens == 0) return r;
+  const LayerWs W = layer_ws(d, (size_t)total_tokens);
+  const size_t T = total_tokens, H = d->hidden, F = d->ffn;
+  const char* ws = (const char*)workspace;
+  const int dt = d->dtype;
+  hipStream_t st = as_stream(stream);
+  // inputs of the QKV, O, FFN1 and FFN2 GEMMs: x, ctx, h1 and the GELU output
+  TEL_TRY(launch_absmax(dt, x, T * H, amax + 0, st));
+  TEL_TRY(launch_absmax(dt, ws + W.ctx, T * H, amax + 1, st));
+  TEL_TRY(launch_absmax(dt, ws + W.h1, T * H, amax + 2, st));
+  TEL_TRY(launch_absmax(dt, ws + W.f, T * F, amax + 3, st));
+  return TEL_OK;
+}
+
 size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* d, int batch, int max_seq) {
   if (desc_supported(d) != TEL_OK || batch <= 0 || max_seq <= 0) return 0;
   return stack_ws(d, batch, max_seq).total;

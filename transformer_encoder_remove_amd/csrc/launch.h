@@ -90,5 +90,7 @@ hipError_t launch_quantize_weight(int dtype, const void* w, int8_t* q, float* s_
 // not null, else the host value inv_host.
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
                                float inv_host, hipStream_t stream);
+// *out = max(*out, max |x[i]|) (calibration statistic; out is a device float >= 0)
+hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream);
 
 }  // namespace tel

@@ -110,4 +110,29 @@ hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, co
   return hipGetLastError();
 }
 
+// Calibration statistic: *out = max(*out, max_i |x[i]|). Non-negative floats order like
+// their bit patterns, so an unsigned atomic max is exact and order-independent.
+template <typename T>
+__global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, size_t n,
+                                                     float* __restrict__ out) {
+  float m = 0.f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(to_f32(x[i])));
+  m = group_max<64>(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  switch (dtype) {
+    case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out); break;
+    case DT_BF16: absmax_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, n, out); break;
+    case DT_F32: absmax_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, n, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace tel
