@@ -109,6 +109,60 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
   }
 }
 
+// The same epilogue on 8 consecutive columns n..n+7 of row m (n % 8 == 0), with the
+// column constants (bias bb, int8 dequantisation dd) and the residual r already in
+// registers: one 16-byte store for 16-bit outputs, 8 bytes for int8 codes, 2 x 16 bytes for
+// float32 and int32.
+template <typename T8> struct alignas(sizeof(T8) * 8) Vec8 { T8 v[8]; };
+
+template <int EPI, typename T, typename TR, typename TO>
+__device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int m, int n,
+                                                const float* acc, const float* bb,
+                                                const float* dd, const Vec8<TR>& r) {
+  if constexpr (EPI == EPI_RAW_I32) {
+    Vec8<int32_t> o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.v[i] = __float_as_int(acc[i]);   // staged as raw bits
+    *reinterpret_cast<Vec8<int32_t>*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = o;
+    return;
+  } else {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (std::is_same<T, int8_t>::value) v[i] = (float)__float_as_int(acc[i]) * dd[i] + bb[i];
+      else v[i] = acc[i] + bb[i];
+    }
+    if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = gelu_erf(v[i]);
+    }
+    size_t row = (size_t)m;
+    if constexpr (EPI == EPI_SWIN_SCATTER) row = (size_t)e.geom.src_row(m);
+    if constexpr (EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += to_f32(r.v[i]);
+    }
+    size_t idx;
+    if constexpr (EPI == EPI_QKV_SPLIT) {
+      const int H = e.N / 3, d = H / e.heads;
+      const int which = n / H, rem = n - which * H, hh = rem / d, c = rem - hh * d;
+      idx = (((size_t)which * e.heads + hh) * e.M + m) * d + c;
+    } else {
+      idx = row * e.N + n;
+    }
+    Vec8<TO> out;
+    if constexpr (std::is_same<TO, int8_t>::value) {
+      const float inv = *e.qinv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out.v[i] = quantize_code(v[i], inv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out.v[i] = from_f32<TO>(v[i]);
+    }
+    *reinterpret_cast<Vec8<TO>*>(e.C + idx) = out;
+  }
+}
+
 template <typename T, int BM, int BN, int BK, int WM, int WN, int EPI, typename TR, typename TO>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ W, int K,
@@ -276,7 +330,9 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   static_assert(KS % 2 == 0, "k-steps per slice must be even");
   static_assert(S >= 2, "stages");
 
-  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+  constexpr int LDC = TN + 4;                       // floats per staged epilogue row
+  constexpr int STAGED = TM * LDC * 4 * NW;         // epilogue staging bytes
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE > STAGED ? S * STAGE : STAGED];
 
   const int M = e.M, N = e.N;
   const int tiles_m = (M + BM - 1) / BM;
@@ -318,8 +374,8 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
       asm volatile("" ::: "memory");
       issue(kt + S - 1, min(kt + S - 1, nk - 1));   // into the stage of slice kt - 1
     }
+    wait_vmcnt<0>();   // every copy has landed before the LDS is reused for the epilogue
     __builtin_amdgcn_s_barrier();   // matches the compute wavefronts' final barrier
-    wait_vmcnt<0>();   // no copy may still be writing LDS when the workgroup ends
     return;
   }
 
@@ -381,13 +437,97 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   }
 #undef TEL_PIPE_FRAGS
 
+  // Epilogue through LDS. Every copy has landed and every real fragment read is done
+  // (the producers drained before the last barrier), so the ring is free: each wavefront
+  // parks its TM x TN accumulators there (row m, 4 consecutive n per lane), then reads
+  // them back as 8 consecutive columns per lane so that 8 lanes cover one 128-byte row
+  // segment of the output, and applies the epilogue per 8-column chunk.
+  float* stg = reinterpret_cast<float*>(smem) + wave * TM * LDC;
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int n = n0 + wn * TN + i * 16 + lg * 4;
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int m = m0 + wm * TM + j * 16 + lr;
-      if (m < M && n < N) epilogue_store<EPI, T, TR, TO>(e, m, n, acc[i][j]);
+      float4 v;
+      if constexpr (std::is_same<T, int8_t>::value) {
+        v = make_float4(__int_as_float(acc[i][j][0]), __int_as_float(acc[i][j][1]),
+                        __int_as_float(acc[i][j][2]), __int_as_float(acc[i][j][3]));
+      } else {
+        v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+      *reinterpret_cast<float4*>(stg + (j * 16 + lr) * LDC + i * 16 + lg * 4) = v;
+    }
+  // Lane -> (row rr of every pass, 8-column chunk c8): the chunk is fixed per lane, so
+  // the column constants are loaded once; RP rows per pass, lanes past RP * CPR idle.
+  constexpr int CPR = TN / 8;
+  constexpr int RP = 64 / CPR;
+  constexpr int NPASS = (TM + RP - 1) / RP;
+  constexpr int GP = NPASS < 8 ? NPASS : 8;   // passes whose residuals are loaded together
+  static_assert(TN % 8 == 0 && CPR <= 64 && NPASS % GP == 0, "epilogue chunking");
+  const int c8 = lane % CPR, rr = lane / CPR;
+  const int n = n0 + wn * TN + c8 * 8;
+  const bool lane_on = rr < RP && n < N;
+  const bool full8 = n + 8 <= N && (EPI != EPI_QKV_SPLIT || ((N / 3) / e.heads) % 8 == 0);
+  constexpr bool IS_I8 = std::is_same<T, int8_t>::value;
+  constexpr bool HAS_R = EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER;
+  float bb[8], dd[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bb[i] = dd[i] = 0.f;
+  if constexpr (EPI != EPI_RAW_I32) {
+    if (lane_on && full8) {
+      const float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
+      const float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
+      bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+      bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+      if constexpr (IS_I8) {
+        const float4 d0 = *reinterpret_cast<const float4*>(e.dq + n);
+        const float4 d1 = *reinterpret_cast<const float4*>(e.dq + n + 4);
+        dd[0] = d0.x; dd[1] = d0.y; dd[2] = d0.z; dd[3] = d0.w;
+        dd[4] = d1.x; dd[5] = d1.y; dd[6] = d1.z; dd[7] = d1.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NPASS / GP; ++g) {
+    // residual rows of GP passes first (loads issued back to back), then the stores
+    Vec8<TR> rv[GP];
+    if constexpr (HAS_R) {
+#pragma unroll
+      for (int q = 0; q < GP; ++q) {
+        const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
+        if (lane_on && full8 && r < TM && m < M) {
+          size_t row = (size_t)m;
+          if constexpr (EPI == EPI_SWIN_SCATTER) row = (size_t)e.geom.src_row(m);
+          rv[q] = *reinterpret_cast<const Vec8<TR>*>(e.resid + row * N + n);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GP; ++q) {
+      const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
+      if (!lane_on || r >= TM || m >= M) continue;
+      float v[8];
+      const float4 a0 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8);
+      const float4 a1 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8 + 4);
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+      if (full8) {
+        epilogue_apply8<EPI, T, TR, TO>(e, m, n, v, bb, dd, rv[q]);
+      } else {   // ragged N (N % 8 == 4) or head_dim % 8 == 4: two 4-column stores
+        typedef typename MF::acc ACC;
+        ACC lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (IS_I8) {
+            lo[i] = __float_as_int(v[i]);
+            hi[i] = __float_as_int(v[4 + i]);
+          } else {
+            lo[i] = v[i];
+            hi[i] = v[4 + i];
+          }
+        }
+        epilogue_store<EPI, T, TR, TO>(e, m, n, lo);
+        if (n + 4 < N) epilogue_store<EPI, T, TR, TO>(e, m, n + 4, hi);
+      }
     }
   }
 }
