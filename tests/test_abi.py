@@ -115,3 +115,75 @@ def test_kernel_entry_validation():
     assert L.tel_attention_varlen(FAKE, FAKE, FAKE, 2, 10, 0, 2, 64, f16, None) == tel.TEL_EINVAL
     assert L.tel_layernorm(FAKE, FAKE, FAKE, FAKE, 4, 20, 1e-5, f16, None) == tel.TEL_EUNSUPPORTED
     assert L.tel_layernorm(FAKE, FAKE, FAKE, FAKE, 4, 64, -1.0, f16, None) == tel.TEL_EINVAL
+
+
+def test_partial_plan_invariants():
+    """The k-split plan of the output projection / FFN2 GEMMs (host logic): splits only
+    when the unsplit tile grid is under 100 workgroups, a power of two up to 8, whole
+    128-byte slices with at least 8 per split, and never more than needed."""
+    cfgs = [(128, 256), (128, 192), (128, 128), (64, 128), (64, 64)]
+    for dt, es in ((tel.TEL_F16, 2), (tel.TEL_BF16, 2), (tel.TEL_F32, 4), (tel.TEL_I8, 1)):
+        for M in (1, 17, 128, 640, 2557, 14336, 24576):
+            for N, K in ((768, 768), (768, 3072), (1024, 1024), (1024, 4096), (64, 256)):
+                cfg, sp = tel.tel_gemm_partial_plan(dt, M, N, K)
+                nk = K * es // 128
+                assert 0 <= cfg < 5 and sp in (1, 2, 4, 8), (dt, M, N, K, cfg, sp)
+                bm, bn = cfgs[cfg]
+                tiles = -(-M // bm) * -(-N // bn)
+                if sp > 1:
+                    assert tiles < 100 and nk % sp == 0 and nk // sp >= 8
+                    assert tiles * sp // 2 < 100          # the smallest split that suffices
+                else:
+                    assert tiles >= 100 or nk % 2 or nk // 2 < 8
+    # a 128-token batch at BERT-large shape: output projection split in 2, FFN2 in 4
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (4, 2)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (4, 4)
+    # 2557 tokens at BERT-base shape: no split
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 768)[1] == 1
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 3072)[1] == 1
+    # K not a whole number of 128-byte slices: register-staged kernel, no split
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 100, 64, 72) == (-1, 1)
+
+
+def test_workspace_non_decreasing_in_tokens():
+    """A workspace sized for T tokens serves every smaller batch, although fewer tokens
+    can mean more k-splits (more partial-sum rows per token)."""
+    for kw in (dict(), dict(int8_gemm=1), dict(dtype=tel.TEL_BF16),
+               dict(hidden=1024, heads=16, ffn=4096)):
+        d = desc(**kw)
+        sizes = [tel.tel_encoder_workspace_size(d, t) for t in range(1, 3000, 37)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), kw
+
+
+def test_partial_gemm_and_reduce_validation():
+    f16, bf16, f32 = tel.TEL_F16, tel.TEL_BF16, tel.TEL_F32
+    P = L.tel_gemm_partial
+    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 0, 64, 64, None) == tel.TEL_OK          # empty
+    assert P(f16, 0, 0, FAKE, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL     # splits
+    assert P(f16, -2, 1, FAKE, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL    # no auto
+    assert P(f16, -1, 2, FAKE, FAKE, FAKE, 16, 64, 128, None) == tel.TEL_EUNSUPPORTED
+    assert P(f16, 0, 3, FAKE, FAKE, FAKE, 16, 64, 256, None) == tel.TEL_EUNSUPPORTED  # 4 slices
+    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 16, 64, 72, None) == tel.TEL_EUNSUPPORTED   # 144 B
+    assert P(tel.TEL_I8, -1, 1, FAKE, FAKE, FAKE, 16, 64, 24, None) == tel.TEL_EUNSUPPORTED
+    assert P(f16, 0, 1, FAKE_ODD, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL
+    R = L.tel_layernorm_reduce
+    ok = [FAKE, 1, None, FAKE, FAKE, f16, FAKE, f16, None, None, None, FAKE, FAKE, 4, 64,
+          1e-5, 0, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["part", "splits", "dq", "bias", "resid", "rdt", "y", "odt", "y32", "yq",
+                 "qinv", "g", "b", "rows", "width", "eps", "round", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return R(*a)
+    assert call(rows=0) == tel.TEL_OK
+    assert call(splits=0) == tel.TEL_EINVAL
+    assert call(splits=9) == tel.TEL_EINVAL
+    assert call(rdt=f16, odt=bf16) == tel.TEL_EUNSUPPORTED
+    assert call(rdt=bf16, odt=f32) == tel.TEL_EUNSUPPORTED
+    assert call(width=20) == tel.TEL_EUNSUPPORTED
+    assert call(bias=None) == tel.TEL_EINVAL
+    assert call(yq=FAKE) == tel.TEL_EINVAL                                     # no qinv
+    assert call(resid=FAKE_ODD) == tel.TEL_EINVAL
+    assert call(eps=float("nan")) == tel.TEL_EINVAL

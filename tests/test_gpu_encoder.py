@@ -86,6 +86,23 @@ def test_bert_large_tput_one_layer_sampled():
                  "f16", "bert_large_tput L1")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bert_large_latency_split_layers(dtype):
+    """BERT-large latency batch (one sequence of 128 tokens): the output projection and FFN2
+    run split over k (partial sums finished by the reduce-LayerNorm kernel). Two layers in
+    fp16; one in bf16, whose inter-layer storage rounding alone (8 significant bits at
+    |y| ~ 4.5) would take most of the 2e-2 budget in a second layer."""
+    nl = 2 if dtype == "f16" else 1
+    cfg = dict(ti.ENCODER_CONFIGS["bert_large_latency"], dtype=dtype, layers=nl)
+    dt = tel.TEL_F16 if dtype == "f16" else tel.TEL_BF16
+    assert tel.tel_gemm_partial_plan(dt, 128, 1024, 1024)[1] > 1
+    assert tel.tel_gemm_partial_plan(dt, 128, 1024, 4096)[1] > 1
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(nl)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    assert_close(y, _oracle(cfg, lens, x, ws), dtype, f"bert_large_latency {nl} layers")
+
+
 def test_deterministic_repeat():
     """Two runs give bitwise-identical outputs (no races in LDS staging)."""
     cfg = dict(ti.ENCODER_CONFIGS["bert_base"], batch=8)

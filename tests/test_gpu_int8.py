@@ -72,6 +72,8 @@ def _gpu_int8(cfg, lens, x, ws, amaxes):
 @pytest.mark.parametrize("shape", [
     dict(B=2, S=8, lens=[5, 8], H=64, heads=4, F=256),
     dict(B=3, S=40, lens=[40, 1, 17], H=128, heads=2, F=256),
+    # 128 tokens at BERT-base width: FFN2 runs split over k (int32 partial sums)
+    dict(B=2, S=96, lens=[96, 32], H=768, heads=12, F=3072),
 ])
 def test_int8_layer_small(shape):
     cfg = ti.custom_encoder_config(shape["B"], shape["S"], shape["lens"], shape["H"],

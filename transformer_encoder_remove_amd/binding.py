@@ -33,7 +33,8 @@ EXPORTS = (
     "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_quantize_i8",
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
-    "tel_window_partition_layernorm",
+    "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
+    "tel_layernorm_reduce",
 )
 TEL_SWIN_ATTN_ONLY = 1
 
@@ -109,6 +110,9 @@ _SIG = {
     "tel_swin_workspace_size": (SZ, [ctypes.POINTER(tel_swin_desc)]),
     "tel_window_attention_forward": (I, [ctypes.POINTER(tel_swin_desc), P, P, P, I, P, SZ, P]),
     "tel_window_partition_layernorm": (I, [P, P, P, P, I, I, I, I, I, I, F, I, P]),
+    "tel_gemm_partial": (I, [I, I, I, P, P, P, I, I, I, P]),
+    "tel_gemm_partial_plan": (I, [I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
+    "tel_layernorm_reduce": (I, [P, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -273,6 +277,32 @@ def tel_quantize_weight_i8(w, q, scales, stream=None):
     N, K = w.shape
     _check("tel_quantize_weight_i8", lib.tel_quantize_weight_i8(
         _ptr(w), _ptr(q), _ptr(scales), N, K, dtype_code(w.dtype), _stream(stream)))
+
+
+def tel_gemm_partial_plan(dtype: int, M: int, N: int, K: int) -> tuple[int, int]:
+    """(tile_config, splits) the encoder layer uses for a partial GEMM of this shape."""
+    cfg, sp = I(), I()
+    _check("tel_gemm_partial_plan", lib.tel_gemm_partial_plan(dtype, M, N, K, ctypes.byref(cfg),
+                                                               ctypes.byref(sp)))
+    return cfg.value, sp.value
+
+
+def tel_gemm_partial(tile_config: int, splits: int, A, W, partials, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _check("tel_gemm_partial", lib.tel_gemm_partial(
+        dtype_code(A.dtype), tile_config, splits, _ptr(A), _ptr(W), _ptr(partials), M, N, K,
+        _stream(stream)))
+
+
+def tel_layernorm_reduce(partials, splits: int, bias, resid, y, gamma, beta, eps: float,
+                         dq=None, y32=None, yq=None, qinv=None, round_pre: bool = False,
+                         stream=None):
+    rows, width = y.shape
+    _check("tel_layernorm_reduce", lib.tel_layernorm_reduce(
+        _ptr(partials), splits, _ptr(dq), _ptr(bias), _ptr(resid), dtype_code(resid.dtype),
+        _ptr(y), dtype_code(y.dtype), _ptr(y32), _ptr(yq), _ptr(qinv), _ptr(gamma), _ptr(beta),
+        rows, width, eps, int(round_pre), _stream(stream)))
 
 
 def tel_gemm_i8_i32(A, B, C, stream=None):

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "launch.h"
 #include "tel.h"
 
@@ -92,23 +94,44 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
 // A bf16 layer keeps its pre-LayerNorm sums and its residual stream (h1) in float32:
 // bf16 keeps 8 significant bits, and rounding those two values to bf16 alone costs more
 // than the 2e-2 absolute error budget at |y| ~ 4; fp16 and fp32 layers keep them in
-// their storage type.
+// their storage type. When few tokens leave most compute units idle, the output
+// projection and FFN2 run split over k instead: float32 (int32 for int8 operands)
+// partial sums that the reduce-LayerNorm kernel adds with bias and residual.
 struct LayerWs {
-  size_t qkv, ctx, pre, h1, h1f, f, total;
+  size_t qkv, ctx, pre, part, h1, h1f, f, total;
   size_t xq, ctxq, h1q;   // int8 layer: codes of the inputs of the QKV, O and FFN1 GEMMs
 };
 
 inline bool f32_stream(const tel_encoder_desc* d) { return d->dtype == DT_BF16; }
+inline int gemm_dtype(const tel_encoder_desc* d) { return d->int8_gemm ? (int)DT_I8 : d->dtype; }
+
+// Rows of partial sums the layer needs for T tokens: the k-split plans of the output
+// projection and FFN2 at every token count up to T (fewer tokens may mean more splits),
+// so a workspace sized for T also serves any smaller batch.
+size_t partial_rows(const tel_encoder_desc* d, size_t T) {
+  const int dt = gemm_dtype(d), H = d->hidden, F = d->ffn;
+  auto need = [&](size_t t) {
+    int cfg;
+    const int sp = std::max(gemm_partial_plan(dt, (int)t, H, H, &cfg),
+                            gemm_partial_plan(dt, (int)t, H, F, &cfg));
+    return sp > 1 ? (size_t)sp * t : 0;
+  };
+  // tile counts, hence plans, change only at multiples of 64 rows: the largest need
+  // inside each run of equal plans is at its top
+  size_t rows = need(T);
+  for (size_t t = 64; t < T; t += 64) rows = std::max(rows, need(t));
+  return rows;
+}
 
 LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   const size_t H = d->hidden, F = d->ffn, es = dtype_size(d->dtype);
-  const size_t pes = f32_stream(d) ? 4 : es;
   LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   w.qkv = take(3 * T * H * es);
   w.ctx = take(T * H * es);
-  w.pre = take(T * H * pes);
+  w.pre = take(T * H * (f32_stream(d) ? 4 : es));
+  w.part = take(partial_rows(d, T) * H * 4);
   w.h1 = take(T * H * es);
   w.h1f = f32_stream(d) ? take(T * H * 4) : 0;
   w.f = take(T * F * (d->int8_gemm ? 1 : es));   // int8 layer: GELU output as codes
@@ -158,7 +181,11 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   void* qkv = ws + W.qkv;
   void* ctx = ws + W.ctx;
   void* pre = ws + W.pre;
+  void* part = ws + W.part;
   void* h1 = ws + W.h1;
+  int cfg_o, cfg_2;
+  const int sp_o = gemm_partial_plan(DT_I8, T, H, H, &cfg_o);
+  const int sp_2 = gemm_partial_plan(DT_I8, T, H, F, &cfg_2);
 
   TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, inv + 0, 0.f, st));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
@@ -166,21 +193,42 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   TEL_TRY(launch_gemm(DT_I8, g, st));
   TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
   TEL_TRY(launch_quantize_act(DT_F16, ctx, ctxq, (size_t)T * H, inv + 1, 0.f, st));
-  g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
-  g.dq = F32(L.dq_o);
-  TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_layernorm_q8(pre, h1, h1q, inv + 2, F32(L.ln1_g), F32(L.ln1_b), T, H,
-                              d->ln_eps, st));
+  // output projection + dequantise + bias + residual (stored fp16), LayerNorm and the
+  // int8 codes of h1; split over k (int32 partials, all of that in the reduce kernel)
+  // when few tokens leave the GPU idle
+  if (sp_o > 1) {
+    g = GemmArgs{EPI_PARTIAL, ctxq, P + L.w_o, nullptr, nullptr, part, T, H, H, nh};
+    g.splits = sp_o;
+    TEL_TRY(launch_gemm_cfg(DT_I8, cfg_o, g, st));
+    const LnReduceArgs r{part, sp_o, F32(L.dq_o), F32(L.b_o), x, DT_F16, h1, DT_F16, nullptr,
+                         h1q, inv + 2, F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, 1};
+    TEL_TRY(launch_layernorm_reduce(r, st));
+  } else {
+    g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
+    g.dq = F32(L.dq_o);
+    TEL_TRY(launch_gemm(DT_I8, g, st));
+    TEL_TRY(launch_layernorm_q8(pre, h1, h1q, inv + 2, F32(L.ln1_g), F32(L.ln1_b), T, H,
+                                d->ln_eps, st));
+  }
   g = GemmArgs{EPI_BIAS_GELU, h1q, P + L.w_1, F32(L.b_1), nullptr, fq, T, F, H, nh};
   g.dq = F32(L.dq_1);
   g.qinv = inv + 3;
   g.out_i8 = 1;
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
-  g.dq = F32(L.dq_2);
-  TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
-                           d->ln_eps, st));
+  if (sp_2 > 1) {
+    g = GemmArgs{EPI_PARTIAL, fq, P + L.w_2, nullptr, nullptr, part, T, H, F, nh};
+    g.splits = sp_2;
+    TEL_TRY(launch_gemm_cfg(DT_I8, cfg_2, g, st));
+    const LnReduceArgs r{part, sp_2, F32(L.dq_2), F32(L.b_2), h1, DT_F16, y, DT_F16, nullptr,
+                         nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, 1};
+    TEL_TRY(launch_layernorm_reduce(r, st));
+  } else {
+    g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
+    g.dq = F32(L.dq_2);
+    TEL_TRY(launch_gemm(DT_I8, g, st));
+    TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                             d->ln_eps, st));
+  }
   return TEL_OK;
 }
 
@@ -194,31 +242,56 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   void* qkv = ws + W.qkv;
   void* ctx = ws + W.ctx;
   void* pre = ws + W.pre;
+  void* part = ws + W.part;
   void* h1 = ws + W.h1;
   void* f = ws + W.f;
   const bool f32s = f32_stream(d);
   float* h1f = f32s ? (float*)(ws + W.h1f) : nullptr;
-  const int pre_dt = f32s ? (int)DT_F32 : dt;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
+  int cfg_o, cfg_2;
+  const int sp_o = gemm_partial_plan(dt, T, H, H, &cfg_o);
+  const int sp_2 = gemm_partial_plan(dt, T, H, F, &cfg_2);
 
   GemmArgs g{};
   // QKV projection + bias, written head-split for the attention kernel
   g = GemmArgs{EPI_QKV_SPLIT, x, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   TEL_TRY(launch_gemm(dt, g, st));
   TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
-  // output projection + bias + residual, then LayerNorm
-  g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
-  TEL_TRY(launch_gemm(dt, g, st));
-  TEL_TRY(launch_layernorm(pre_dt, dt, pre, h1, h1f, F32(L.ln1_g), F32(L.ln1_b), T, H,
-                           d->ln_eps, st));
-  // FFN: bias + GELU, then bias + residual, then LayerNorm
+  const int pre_dt = f32s ? (int)DT_F32 : dt;
+  // output projection + bias + residual, then LayerNorm; split over k (float32
+  // partials, bias + residual + LayerNorm in the reduce kernel) when few tokens leave
+  // the GPU idle
+  if (sp_o > 1) {
+    g = GemmArgs{EPI_PARTIAL, ctx, P + L.w_o, nullptr, nullptr, part, T, H, H, nh};
+    g.splits = sp_o;
+    TEL_TRY(launch_gemm_cfg(dt, cfg_o, g, st));
+    const LnReduceArgs r{part, sp_o, nullptr, F32(L.b_o), x, dt, h1, dt, h1f, nullptr, nullptr,
+                         F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, 0};
+    TEL_TRY(launch_layernorm_reduce(r, st));
+  } else {
+    g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
+    TEL_TRY(launch_gemm(dt, g, st));
+    TEL_TRY(launch_layernorm(pre_dt, dt, pre, h1, h1f, F32(L.ln1_g), F32(L.ln1_b), T, H,
+                             d->ln_eps, st));
+  }
+  // FFN: bias + GELU, then bias + residual, then LayerNorm (FFN2 split as above)
   g = GemmArgs{EPI_BIAS_GELU, h1, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
   TEL_TRY(launch_gemm(dt, g, st));
-  g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), f32s ? (const void*)h1f : h1, pre,
-               T, H, F, nh, f32s, f32s};
-  TEL_TRY(launch_gemm(dt, g, st));
-  TEL_TRY(launch_layernorm(pre_dt, dt, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
-                           d->ln_eps, st));
+  const void* res2 = f32s ? (const void*)h1f : h1;
+  if (sp_2 > 1) {
+    g = GemmArgs{EPI_PARTIAL, f, P + L.w_2, nullptr, nullptr, part, T, H, F, nh};
+    g.splits = sp_2;
+    TEL_TRY(launch_gemm_cfg(dt, cfg_2, g, st));
+    const LnReduceArgs r{part, sp_2, nullptr, F32(L.b_2), res2, f32s ? (int)DT_F32 : dt, y, dt,
+                         nullptr, nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps,
+                         0};
+    TEL_TRY(launch_layernorm_reduce(r, st));
+  } else {
+    g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), res2, pre, T, H, F, nh, f32s, f32s};
+    TEL_TRY(launch_gemm(dt, g, st));
+    TEL_TRY(launch_layernorm(pre_dt, dt, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                             d->ln_eps, st));
+  }
   return TEL_OK;
 }
 
@@ -673,6 +746,52 @@ int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seq
   if (!aligned16(qkv_split) || !aligned16(ctx)) return TEL_EINVAL;
   return status_of(launch_attention(dtype, qkv_split, ctx, cu_seqlens, batch, total_tokens,
                                     max_len, heads, head_dim, as_stream(stream)));
+}
+
+int tel_gemm_partial(int dtype, int tile_config, int splits, const void* A, const void* W,
+                     void* partials, int M, int N, int K, void* stream) {
+  if (!float_type(dtype) && dtype != DT_I8) return TEL_EUNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0 || splits < 1) return TEL_EINVAL;
+  if (tile_config < -1 || tile_config >= gemm_tile_configs()) return TEL_EINVAL;
+  if (M == 0) return TEL_OK;
+  if (!A || !W || !partials) return TEL_EINVAL;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(partials)) return TEL_EINVAL;
+  const long long kb = (long long)K * dtype_size(dtype);
+  if (K % (dtype == DT_I8 ? 16 : 8) || N % 4) return TEL_EUNSUPPORTED;
+  if (tile_config >= 0 && kb % 128) return TEL_EUNSUPPORTED;
+  if (splits > 1 && (tile_config < 0 || (kb / 128) % splits)) return TEL_EUNSUPPORTED;
+  GemmArgs g{EPI_PARTIAL, A, W, nullptr, nullptr, partials, M, N, K, 1};
+  g.splits = splits;
+  return status_of(launch_gemm_cfg(dtype, tile_config, g, as_stream(stream)));
+}
+
+int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits) {
+  if (!tile_config || !splits) return TEL_EINVAL;
+  if (!float_type(dtype) && dtype != DT_I8) return TEL_EUNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
+  *splits = gemm_partial_plan(dtype, M, N, K, tile_config);
+  return TEL_OK;
+}
+
+int tel_layernorm_reduce(const void* partials, int splits, const float* dq, const float* bias,
+                         const void* resid, int resid_dtype, void* y, int out_dtype, float* y32,
+                         int8_t* yq, const float* qinv, const float* gamma, const float* beta,
+                         int rows, int width, float eps, int round_pre, void* stream) {
+  if (rows < 0 || width <= 0 || splits < 1 || splits > 8 || !(eps >= 0.f)) return TEL_EINVAL;
+  const bool combo = (resid_dtype == DT_F16 && out_dtype == DT_F16) ||
+                     (resid_dtype == DT_BF16 && out_dtype == DT_BF16) ||
+                     (resid_dtype == DT_F32 && (out_dtype == DT_BF16 || out_dtype == DT_F32));
+  if (!combo || !layernorm_supported(out_dtype, width)) return TEL_EUNSUPPORTED;
+  if (rows == 0) return TEL_OK;
+  if (!partials || !bias || !resid || !y || !gamma || !beta || (yq && !qinv)) return TEL_EINVAL;
+  for (const void* q : {partials, (const void*)bias, resid, (const void*)y, (const void*)gamma,
+                        (const void*)beta})
+    if (!aligned16(q)) return TEL_EINVAL;
+  if ((dq && !aligned16(dq)) || (y32 && !aligned16(y32)) || (yq && ((uintptr_t)yq % 8)))
+    return TEL_EINVAL;
+  const LnReduceArgs a{partials, splits, dq, bias, resid, resid_dtype, y, out_dtype, y32, yq,
+                       qinv, gamma, beta, rows, width, eps, round_pre ? 1 : 0};
+  return status_of(launch_layernorm_reduce(a, as_stream(stream)));
 }
 
 int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,

@@ -9,8 +9,10 @@
 //
 // Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid =
 // (ceil(max_len / 64), heads, batch), workgroups past a sequence's end exit at once.
-// Per 64-key block:
-//  * K [64][D] and V^T [D][64] are staged in LDS (16-byte global loads);
+// K and V blocks travel through a two-block register ring: Q and the first two key
+// blocks are requested together at the start, and each later block two blocks ahead of
+// its use, so the memory latency is paid about once per workgroup. Per 64-key block:
+//  * K [64][D] and V^T [D][64] are staged in LDS from those registers;
 //  * each wavefront computes S^T = K Q^T for its 16 queries with 16x16 MFMAs, so that
 //    every lane holds scores of ONE query (column l % 16) for 16 keys;
 //  * online softmax in base 2: the row max and row sum need only the lane's own 16
@@ -30,6 +32,137 @@ namespace tel {
 constexpr int ATT_QB = 64;   // queries per workgroup
 constexpr int ATT_KB = 64;   // keys per LDS block
 
+// Scores, online-softmax update and O update for one 64-key block staged in LDS.
+template <typename T, int D, int LDK, int LDV>
+__device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
+                                           const typename Mfma<T>::frag* qf, f32x4* o,
+                                           float& m_run, float& l_run, int kb0, int L,
+                                           float scale_log2, int lr, int lg) {
+  using MF = Mfma<T>;
+  typedef typename MF::frag frag;
+  constexpr int KPL = MF::KPL, KMF = 4 * KPL;
+  constexpr int NKS = (D + KMF - 1) / KMF;
+  constexpr int NCB = D / 16;
+  constexpr int NJ = ATT_KB / 16;
+
+  // scores S^T[key][query] for 4 sub-blocks of 16 keys
+  f32x4 sc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int d0 = s * KMF + lg * KPL;
+      const frag kf = (d0 < D) ? *reinterpret_cast<const frag*>(&sK[(j * 16 + lr) * LDK + d0])
+                               : frag{};
+      sc[j] = MF::mma(kf, qf[s], sc[j]);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb0 + j * 16 + lg * 4 + i;
+      const float s = key < L ? sc[j][i] * scale_log2 : -INFINITY;
+      sc[j][i] = s;
+      mx = fmaxf(mx, s);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m_run, mx);       // finite: key 0 of the sequence is valid
+  const float alpha = exp2f(m_run - m_new);
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = exp2f(sc[j][i] - m_new);
+      sc[j][i] = p;
+      psum += p;
+    }
+  psum += __shfl_xor(psum, 16, 64);
+  psum += __shfl_xor(psum, 32, 64);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) o[c] *= alpha;
+
+  // O^T[c][q] += sum_key V^T[c][key] * P^T[key][q]; MFMA k element e of step t is the
+  // lane's score f = t*KPL + e, i.e. key 16*(f/4) + 4*lg + f%4.
+  // For 16-bit types P is split into P_hi + P_lo (both representable), two MFMAs per
+  // step: P enters the product with ~2x the significant bits of one 16-bit value. The
+  // kernel is bound by memory latency, not by MFMA, so the extra MFMA costs nothing
+  // measurable, and downstream int8 codes flip far less often.
+#pragma unroll
+  for (int t = 0; t < ATT_KB / KMF; ++t) {
+    T pv[KPL], pl[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      const int f = t * KPL + e;
+      pv[e] = from_f32<T>(sc[f / 4][f % 4]);
+      pl[e] = from_f32<T>(sc[f / 4][f % 4] - to_f32(pv[e]));
+    }
+    frag pb, pbl;
+    __builtin_memcpy(&pb, pv, sizeof(frag));
+    __builtin_memcpy(&pbl, pl, sizeof(frag));
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const T* vrow = &sVt[(c * 16 + lr) * LDV];
+      frag va;
+      if constexpr (KPL == 8) {
+        T tmp[8];
+        const int k0 = 16 * (2 * t) + 4 * lg, k1 = k0 + 16;
+        __builtin_memcpy(tmp, vrow + k0, 4 * sizeof(T));
+        __builtin_memcpy(tmp + 4, vrow + k1, 4 * sizeof(T));
+        __builtin_memcpy(&va, tmp, sizeof(frag));
+      } else {
+        const int f = t;
+        va = vrow[16 * (f / 4) + 4 * lg + (f % 4)];
+      }
+      o[c] = MF::mma(va, pb, o[c]);
+      if constexpr (KPL > 1) o[c] = MF::mma(va, pbl, o[c]);
+    }
+  }
+}
+
+// 16-byte K and V vectors of one 64-key block held in registers: thread tid owns vectors
+// tid + 256 p (key row idx / VPRK, column chunk idx % VPRK); rows past the sequence end are
+// clamped to its last key (their scores are masked).
+template <typename T, int D> struct KvRegs {
+  static constexpr int VEC = 16 / sizeof(T), VPRK = D / VEC, NVEC = ATT_KB * VPRK;
+  static constexpr int PER = (NVEC + 255) / 256;
+  typedef T vec __attribute__((ext_vector_type(VEC)));
+  vec k[PER], v[PER];
+
+  __device__ __forceinline__ void load(const T* Kh, const T* Vh, int kb0, int L, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPRK, c = idx - r * VPRK;
+        const size_t off = (size_t)min(kb0 + r, L - 1) * D + c * VEC;
+        k[p] = *reinterpret_cast<const vec*>(Kh + off);
+        v[p] = *reinterpret_cast<const vec*>(Vh + off);
+      }
+    }
+  }
+  // K row-major [key][d] (stride LDK), V transposed [d][key] (stride LDV)
+  template <int LDK, int LDV>
+  __device__ __forceinline__ void store(T* sK, T* sVt, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPRK, c = idx - r * VPRK;
+        *reinterpret_cast<vec*>(&sK[r * LDK + c * VEC]) = k[p];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sVt[(c * VEC + e) * LDV + r] = v[p][e];
+      }
+    }
+  }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ qkv,
                                                           T* __restrict__ ctx,
@@ -45,7 +178,6 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
   constexpr int NKS = (D + KMF - 1) / KMF;
   constexpr int NCB = D / 16;
   constexpr int NJ = ATT_KB / 16;
-  constexpr int VPRK = D / VEC;
   static_assert(D % 16 == 0 && D % VEC == 0, "head_dim");
 
   __shared__ __attribute__((aligned(16))) T sK[ATT_KB * LDK];
@@ -63,6 +195,13 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
   const T* Kh = qkv + (size_t)(heads + h) * hs + (size_t)start * D;
   const T* Vh = qkv + (size_t)(2 * heads + h) * hs + (size_t)start * D;
 
+  // Every global load that does not depend on a result is issued here, so the
+  // workgroup pays one memory latency for Q and the first two key blocks together;
+  // later blocks are fetched two blocks ahead of their use.
+  KvRegs<T, D> kv0, kv1;
+  kv0.load(Kh, Vh, 0, L, tid);
+  if (ATT_KB < L) kv1.load(Kh, Vh, ATT_KB, L, tid);
+
   const int qi = q0 + wave * 16 + lr;
   const int qc = min(qi, L - 1);
   frag qf[NKS];
@@ -77,99 +216,22 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
 #pragma unroll
   for (int c = 0; c < NCB; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb0 = 0; kb0 < L; kb0 += ATT_KB) {
-    for (int idx = tid; idx < ATT_KB * VPRK; idx += 256) {
-      const int r = idx / VPRK, v = idx - r * VPRK;
-      const int key = min(kb0 + r, L - 1);
-      const Vec16<T> kv = *reinterpret_cast<const Vec16<T>*>(Kh + (size_t)key * D + v * VEC);
-      *reinterpret_cast<Vec16<T>*>(&sK[r * LDK + v * VEC]) = kv;
-      const Vec16<T> vv = *reinterpret_cast<const Vec16<T>*>(Vh + (size_t)key * D + v * VEC);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sVt[(v * VEC + e) * LDV + r] = vv.v[e];
-    }
-    __syncthreads();
+  // one 64-key block: stage the registers in LDS, refill them with the block two ahead,
+  // then scores, online softmax and O update
+#define TEL_ATT_BLOCK(KV, kb0)                                                              \
+  do {                                                                                      \
+    __syncthreads();                        /* the previous block's LDS reads are done */   \
+    KV.template store<LDK, LDV>(sK, sVt, tid);                                              \
+    if ((kb0) + 2 * ATT_KB < L) KV.load(Kh, Vh, (kb0) + 2 * ATT_KB, L, tid);                \
+    __syncthreads();                                                                        \
+    attn_block<T, D, LDK, LDV>(sK, sVt, qf, o, m_run, l_run, (kb0), L, scale_log2, lr, lg);  \
+  } while (0)
 
-    // scores S^T[key][query] for 4 sub-blocks of 16 keys
-    f32x4 sc[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int d0 = s * KMF + lg * KPL;
-        const frag kf = (d0 < D) ? *reinterpret_cast<const frag*>(&sK[(j * 16 + lr) * LDK + d0])
-                                 : frag{};
-        sc[j] = MF::mma(kf, qf[s], sc[j]);
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb0 + j * 16 + lg * 4 + i;
-        const float s = key < L ? sc[j][i] * scale_log2 : -INFINITY;
-        sc[j][i] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);       // finite: key 0 of the sequence is valid
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sc[j][i] - m_new);
-        sc[j][i] = p;
-        psum += p;
-      }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) o[c] *= alpha;
-
-    // O^T[c][q] += sum_key V^T[c][key] * P^T[key][q]; MFMA k element e of step t is the
-    // lane's score f = t*KPL + e, i.e. key 16*(f/4) + 4*lg + f%4.
-    // For 16-bit types P is split into P_hi + P_lo (both representable), two MFMAs per
-    // step: P enters the product with ~2x the significant bits of one 16-bit value. The
-    // kernel is bound by memory latency, not by MFMA, so the extra MFMA costs nothing
-    // measurable, and downstream int8 codes flip far less often.
-#pragma unroll
-    for (int t = 0; t < ATT_KB / KMF; ++t) {
-      T pv[KPL], pl[KPL];
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int f = t * KPL + e;
-        pv[e] = from_f32<T>(sc[f / 4][f % 4]);
-        pl[e] = from_f32<T>(sc[f / 4][f % 4] - to_f32(pv[e]));
-      }
-      frag pb, pbl;
-      __builtin_memcpy(&pb, pv, sizeof(frag));
-      __builtin_memcpy(&pbl, pl, sizeof(frag));
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const T* vrow = &sVt[(c * 16 + lr) * LDV];
-        frag va;
-        if constexpr (KPL == 8) {
-          T tmp[8];
-          const int k0 = 16 * (2 * t) + 4 * lg, k1 = k0 + 16;
-          __builtin_memcpy(tmp, vrow + k0, 4 * sizeof(T));
-          __builtin_memcpy(tmp + 4, vrow + k1, 4 * sizeof(T));
-          __builtin_memcpy(&va, tmp, sizeof(frag));
-        } else {
-          const int f = t;
-          va = vrow[16 * (f / 4) + 4 * lg + (f % 4)];
-        }
-        o[c] = MF::mma(va, pb, o[c]);
-        if constexpr (KPL > 1) o[c] = MF::mma(va, pbl, o[c]);
-      }
-    }
-    __syncthreads();
+  for (int kb0 = 0; kb0 < L; kb0 += 2 * ATT_KB) {
+    TEL_ATT_BLOCK(kv0, kb0);
+    if (kb0 + ATT_KB < L) TEL_ATT_BLOCK(kv1, kb0 + ATT_KB);
   }
+#undef TEL_ATT_BLOCK
 
   if (qi < L) {
     const float inv_l = 1.f / l_run;

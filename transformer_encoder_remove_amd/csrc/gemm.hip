@@ -54,9 +54,9 @@ __device__ __forceinline__ int8_t quantize_code(float v, float inv) {
 template <int EPI, typename T, typename TR, typename TO, typename ACC>
 __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
                                                ACC acc) {
-  if constexpr (EPI == EPI_RAW_I32) {
-    // int8 diagnostic: the exact int32 accumulators, no epilogue arithmetic
-    *reinterpret_cast<i32x4*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
+  if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
+    // the raw 32-bit accumulators (int32 for int8 operands), no epilogue arithmetic
+    *reinterpret_cast<ACC*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
     return;
   } else {
     const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
@@ -119,7 +119,7 @@ template <int EPI, typename T, typename TR, typename TO>
 __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int m, int n,
                                                 const float* acc, const float* bb,
                                                 const float* dd, const Vec8<TR>& r) {
-  if constexpr (EPI == EPI_RAW_I32) {
+  if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
     Vec8<int32_t> o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.v[i] = __float_as_int(acc[i]);   // staged as raw bits
@@ -311,7 +311,7 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 
 template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
 __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
-    const T* __restrict__ A, const T* __restrict__ W, int K, EpiArgs<T, TR, TO> e) {
+    const T* __restrict__ A, const T* __restrict__ W, int K, int splits, EpiArgs<T, TR, TO> e) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int NW = WM * WN;                       // compute wavefronts
@@ -336,11 +336,17 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
 
   const int M = e.M, N = e.N;
   const int tiles_m = (M + BM - 1) / BM;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  // blockIdx -> (output tile, k-split): the k-splits of a tile are neighbours, so they
+  // land on the same XCD and share the tile's L2 working set
+  const int ts = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = ts / splits, split = ts - tile * splits;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nk = K / BK;
+  const int nk = K / BK / splits;                   // k-slices of this split
+  A += (size_t)split * nk * BK;
+  W += (size_t)split * nk * BK;
+  if constexpr (EPI == EPI_PARTIAL) e.C += (size_t)split * M * N;
 
   if (wave >= NW) {
     // ---------------- producer: block b = p + PIPE_PRODUCERS * j of every slice
@@ -472,7 +478,7 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   float bb[8], dd[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) bb[i] = dd[i] = 0.f;
-  if constexpr (EPI != EPI_RAW_I32) {
+  if constexpr (EPI != EPI_RAW_I32 && EPI != EPI_PARTIAL) {
     if (lane_on && full8) {
       const float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
       const float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
@@ -563,10 +569,10 @@ template <typename T, int C, int EPI, typename TR, typename TO>
 static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
-  const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
+  const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn) * a.splits;
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
       <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>((const T*)a.A, (const T*)a.W,
-                                                                 a.K, e);
+                                                                 a.K, a.splits, e);
 }
 
 // cfg < 0: register-staged 64x64 kernel; otherwise PIPE_CFGS[cfg].
@@ -593,6 +599,7 @@ static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
     case EPI_BIAS_GELU: launch_cfg<T, EPI_BIAS_GELU, T, T>(cfg, a, stream); break;
     case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, T, T>(cfg, a, stream); break;
     case EPI_SWIN_SCATTER: launch_cfg<T, EPI_SWIN_SCATTER, T, T>(cfg, a, stream); break;
+    case EPI_PARTIAL: launch_cfg<T, EPI_PARTIAL, T, float>(cfg, a, stream); break;
     case EPI_BIAS_RESID:
       if constexpr (std::is_same<T, bf16>::value) {
         if (a.resid_f32 && a.out_f32) {
@@ -626,6 +633,7 @@ static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
       else launch_cfg<T, EPI_BIAS_GELU, f16, f16>(cfg, a, stream);
       break;
     case EPI_RAW_I32: launch_cfg<T, EPI_RAW_I32, f16, int32_t>(cfg, a, stream); break;
+    case EPI_PARTIAL: launch_cfg<T, EPI_PARTIAL, f16, int32_t>(cfg, a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -643,8 +651,32 @@ static int pick_cfg(const GemmArgs& a, int elem_bytes) {
   return 4;
 }
 
+// Partial-sum GEMMs: a shape whose tile grid leaves most compute units idle (few tokens,
+// e.g. one 128-token sequence) is split over k. The tile is the one the unsplit kernel
+// would take; the split count is the smallest power of two that reaches about 100
+// workgroups while every split keeps at least 8 k-slices (fewer make the prologue and the
+// partial-sum traffic dominate). Returns 1 when splitting does not pay.
+constexpr int SPLIT_MIN_TILES = 100, SPLIT_MIN_SLICES = 8, SPLIT_MAX = 8;
+
+int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
+  const int es = dtype_size(dtype);
+  GemmArgs a{};
+  a.M = M; a.N = N; a.K = K;
+  *cfg = (M > 0 && N > 0 && K > 0) ? pick_cfg(a, es) : -1;
+  if (*cfg < 0) return 1;
+  const PipeCfg& p = PIPE_CFGS[*cfg];
+  const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  const int nk = (int)((long long)K * es / 128);
+  int sp = 1;
+  while (sp < SPLIT_MAX && tiles * sp < SPLIT_MIN_TILES && nk % (2 * sp) == 0 &&
+         nk / (2 * sp) >= SPLIT_MIN_SLICES)
+    sp *= 2;
+  return sp;
+}
+
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
+  if (a.splits != 1) return hipErrorInvalidValue;   // splits need an explicit configuration
   switch (dtype) {
     case DT_I8: return run_epi_i8(pick_cfg(a, 1), a, stream);
     case DT_F16: return run_epi<f16>(pick_cfg(a, 2), a, stream);
@@ -662,6 +694,9 @@ hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t st
   if (cfg < -1 || cfg >= N_PIPE_CFGS) return hipErrorInvalidValue;
   const int es = dtype_size(dtype);
   if (cfg >= 0 && (a.K * es) % 128) return hipErrorInvalidValue;
+  if (a.splits < 1 || (a.splits > 1 && (cfg < 0 || ((long long)a.K * es / 128) % a.splits)))
+    return hipErrorInvalidValue;
+  if (a.splits > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_I8: return run_epi_i8(cfg, a, stream);
     case DT_F16: return run_epi<f16>(cfg, a, stream);

@@ -11,7 +11,9 @@ namespace tel {
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
 enum Epi {
   EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4,
-  EPI_SWIN_SCATTER = 5   // bias + residual, row m written to image row geom.src_row(m)
+  EPI_SWIN_SCATTER = 5,  // bias + residual, row m written to image row geom.src_row(m)
+  EPI_PARTIAL = 6        // raw 32-bit accumulators (float32, or int32 for int8 operands) of
+                         // k-split s at C + s * M * N; a reduce kernel finishes the sum
 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
@@ -41,11 +43,15 @@ struct GemmArgs {
   const float* qinv = nullptr;  // int8 output (EPI_BIAS_GELU): device scalar 1 / scale
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
   SwinGeom geom{};              // EPI_SWIN_SCATTER
+  int splits = 1;               // pipelined kernel only: K split over this many workgroups
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
 int gemm_tile_configs();
+// Tile configuration and number of k-splits for a partial-sum GEMM (EPI_PARTIAL) of this
+// shape; returns the splits (>= 1) and sets *cfg.
+int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg);
 
 // attention.hip
 bool attention_supported(int dtype, int head_dim);
@@ -56,6 +62,17 @@ hipError_t launch_attention(int dtype, const void* qkv_split, void* ctx, const i
 // layernorm.hip: y = LN(x) in type dtype_out from x in type dtype_in; when y_f32 is not
 // null the same result is also written there in float32.
 bool layernorm_supported(int dtype, int width);
+// LayerNorm of a sum finished here: x = sum_s part[s] (float32; int32 times dq[n] when dq is
+// set) + bias[n] + resid[row][n], optionally rounded to the output type first (the int8
+// layer's stored pre-LayerNorm values); writes y (dtype_out), optionally y32 (float32 copy)
+// and yq (int8 codes of the stored y, scale device scalar *qinv).
+struct LnReduceArgs {
+  const void* part; int nsplit; const float* dq; const float* bias;
+  const void* resid; int resid_dt;
+  void* y; int out_dt; float* y32; int8_t* yq; const float* qinv;
+  const float* gamma; const float* beta; int rows, width; float eps; int round_pre;
+};
+hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream);
 hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,
                             const float* gamma, const float* beta, int rows, int width, float eps,
                             hipStream_t stream);

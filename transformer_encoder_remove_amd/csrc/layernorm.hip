@@ -110,6 +110,121 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
   }
 }
 
+// LayerNorm of a sum that a split GEMM left unfinished: the row is assembled from the
+// k-split partial sums (float32, or int32 dequantised by dq[n]), the bias and the residual,
+// then normalised as above. This is where the output projection's and FFN2's bias +
+// residual + LayerNorm epilogue ([SW] section 3, the fused add-bias-residual-LayerNorm)
+// happens once the GEMM's k-splits are summed.
+constexpr int LNR_MAX_SPLITS = 8;
+
+struct LnRedParams {
+  const void* part; int nsplit; const float* dq; const float* bias; const void* resid;
+  void* y; float* y32; int8_t* yq; const float* qinv;
+  const float* gamma; const float* beta; int rows; float eps; int round_pre;
+};
+
+template <typename TR, typename TO, int G, int NV>
+__global__ __launch_bounds__(LN_THREADS) void layernorm_reduce_kernel(LnRedParams p) {
+  constexpr int H = G * NV * 8;
+  const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
+  const int sub = threadIdx.x % G;
+  if (row >= p.rows) return;
+  const size_t split_stride = (size_t)p.rows * H;
+  const TR* rr = (const TR*)p.resid + (size_t)row * H;
+  float v[NV][8];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c0 = (k * G + sub) * 8;
+    const size_t off = (size_t)row * H + c0;
+    float a[8];
+    if (p.dq) {   // int32 partial sums: the integer sum is exact, then dequantise
+      int32_t acc[8];
+      {
+        const int4 x0 = *reinterpret_cast<const int4*>((const int32_t*)p.part + off);
+        const int4 x1 = *reinterpret_cast<const int4*>((const int32_t*)p.part + off + 4);
+        acc[0] = x0.x; acc[1] = x0.y; acc[2] = x0.z; acc[3] = x0.w;
+        acc[4] = x1.x; acc[5] = x1.y; acc[6] = x1.z; acc[7] = x1.w;
+      }
+#pragma unroll
+      for (int sp = 1; sp < LNR_MAX_SPLITS; ++sp) {   // unrolled: the loads overlap
+        if (sp >= p.nsplit) break;
+        const int32_t* q = (const int32_t*)p.part + sp * split_stride + off;
+        const int4 x0 = *reinterpret_cast<const int4*>(q);
+        const int4 x1 = *reinterpret_cast<const int4*>(q + 4);
+        acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
+        acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+      }
+      float dq[8], b[8];
+      load8(p.dq + c0, dq);
+      load8(p.bias + c0, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = (float)acc[e] * dq[e] + b[e];
+    } else {
+      load8((const float*)p.part + off, a);
+#pragma unroll
+      for (int sp = 1; sp < LNR_MAX_SPLITS; ++sp) {   // unrolled: the loads overlap
+        if (sp >= p.nsplit) break;
+        float t[8];
+        load8((const float*)p.part + sp * split_stride + off, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += t[e];
+      }
+      float b[8];
+      load8(p.bias + c0, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += b[e];
+    }
+    float r[8];
+    load8(rr + c0, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] += r[e];
+      if (p.round_pre) a[e] = to_f32(from_f32<TO>(a[e]));
+      v[k][e] = a[e];
+      s += a[e];
+    }
+  }
+  const float mean = group_sum<G>(s) * (1.f / H);
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[k][e] -= mean;
+      q += v[k][e] * v[k][e];
+    }
+  const float rstd = rsqrtf(group_sum<G>(q) * (1.f / H) + p.eps);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c0 = (k * G + sub) * 8;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      const float4 g = *reinterpret_cast<const float4*>(p.gamma + c0 + e);
+      const float4 b = *reinterpret_cast<const float4*>(p.beta + c0 + e);
+      o[e + 0] = v[k][e + 0] * rstd * g.x + b.x;
+      o[e + 1] = v[k][e + 1] * rstd * g.y + b.y;
+      o[e + 2] = v[k][e + 2] * rstd * g.z + b.z;
+      o[e + 3] = v[k][e + 3] * rstd * g.w + b.w;
+    }
+    store8((TO*)p.y + (size_t)row * H + c0, o);
+    if (p.y32) store8(p.y32 + (size_t)row * H + c0, o);
+    if (p.yq) {
+      const float inv = *p.qinv;
+      int8_t c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = __builtin_rintf(to_f32(from_f32<TO>(o[e])) * inv);
+        c[e] = (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+      }
+      uint2 packed;
+      __builtin_memcpy(&packed, c, 8);
+      *reinterpret_cast<uint2*>(p.yq + (size_t)row * H + c0) = packed;
+    }
+  }
+}
+
 // Lanes per row G and groups per lane NV with G * NV * 8 == width.
 static bool pick_ln(int width, int* g, int* nv) {
   if (width <= 0 || width % 8) return false;
@@ -242,6 +357,52 @@ hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* 
   a.yq = yq;
   a.qinv = qinv;
   if (!run_ln_g<f16, f16, false>(G, nv, a, stream)) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace tel
+
+namespace tel {
+
+template <typename TR, typename TO, int G>
+static bool run_lnr_nv(int nv, const LnRedParams& p, hipStream_t s) {
+  const int blocks = (p.rows + LN_THREADS / G - 1) / (LN_THREADS / G);
+  switch (nv) {
+    case 1: layernorm_reduce_kernel<TR, TO, G, 1><<<blocks, LN_THREADS, 0, s>>>(p); return true;
+    case 2: layernorm_reduce_kernel<TR, TO, G, 2><<<blocks, LN_THREADS, 0, s>>>(p); return true;
+    case 3: layernorm_reduce_kernel<TR, TO, G, 3><<<blocks, LN_THREADS, 0, s>>>(p); return true;
+    case 4: layernorm_reduce_kernel<TR, TO, G, 4><<<blocks, LN_THREADS, 0, s>>>(p); return true;
+  }
+  return false;
+}
+
+template <typename TR, typename TO>
+static bool run_lnr(int G, int nv, const LnRedParams& p, hipStream_t s) {
+  switch (G) {
+    case 1: return run_lnr_nv<TR, TO, 1>(nv, p, s);
+    case 2: return run_lnr_nv<TR, TO, 2>(nv, p, s);
+    case 4: return run_lnr_nv<TR, TO, 4>(nv, p, s);
+    case 8: return run_lnr_nv<TR, TO, 8>(nv, p, s);
+    case 16: return run_lnr_nv<TR, TO, 16>(nv, p, s);
+    case 32: return run_lnr_nv<TR, TO, 32>(nv, p, s);
+    case 64: return run_lnr_nv<TR, TO, 64>(nv, p, s);
+  }
+  return false;
+}
+
+hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream) {
+  if (a.rows == 0) return hipSuccess;
+  int G, nv;
+  if (!pick_ln(a.width, &G, &nv) || a.nsplit < 1 || a.nsplit > LNR_MAX_SPLITS)
+    return hipErrorInvalidValue;
+  const LnRedParams p{a.part, a.nsplit, a.dq, a.bias, a.resid, a.y, a.y32, a.yq, a.qinv,
+                      a.gamma, a.beta, a.rows, a.eps, a.round_pre};
+  bool ok = false;
+  if (a.resid_dt == DT_F16 && a.out_dt == DT_F16) ok = run_lnr<f16, f16>(G, nv, p, stream);
+  else if (a.resid_dt == DT_BF16 && a.out_dt == DT_BF16) ok = run_lnr<bf16, bf16>(G, nv, p, stream);
+  else if (a.resid_dt == DT_F32 && a.out_dt == DT_BF16) ok = run_lnr<float, bf16>(G, nv, p, stream);
+  else if (a.resid_dt == DT_F32 && a.out_dt == DT_F32) ok = run_lnr<float, float>(G, nv, p, stream);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
