@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (the scale of HBM counters)")
     return ap.parse_args()
 
 
@@ -165,6 +167,17 @@ def main():
     g32 = torch.ones(H, device="cuda", dtype=torch.float32)
     cu = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
     Lbar = float((lens.astype(np.float64) ** 2).sum() / lens.sum())
+
+    def resid_gemm(a, w, K, N):
+        """The output projection / FFN2 GEMM as the layer launches it: bias + residual in
+        the epilogue, or split over k (partial sums) when the layer's plan splits it."""
+        cfg_, sp_ = tel.tel_gemm_partial_plan(tel.DTYPE_CODE[tdt], T, N, K)
+        if sp_ > 1:
+            part = torch.empty((sp_, T, N), device="cuda", dtype=torch.float32)
+            return lambda: tel.tel_gemm_partial(cfg_, sp_, a, w, part, stream=stream)
+        return lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, a, w, b32(N), pre, resid=hid,
+                                    stream=stream)
+
     kernels = {
         "gemm_qkv": (lambda: tel.tel_gemm(tel.TEL_EPI_QKV_SPLIT, hid, layer_w["w_qkv"], b32(3 * H),
                                           qkv_o, heads=nh, stream=stream),
@@ -172,33 +185,32 @@ def main():
         "attention": (lambda: tel.tel_attention_varlen(qkv, ctx, cu, T, max_len, nh, H // nh,
                                                        stream=stream),
                       4.0 * T * H * Lbar, 2.0 * 4 * T * H),
-        "gemm_o_resid": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, ctx, layer_w["w_o"], b32(H),
-                                              pre, resid=hid, stream=stream),
+        "gemm_o_resid": (resid_gemm(ctx, layer_w["w_o"], H, H),
                          2.0 * T * H * H, 2.0 * (3 * T * H + H * H)),
         "layernorm": (lambda: tel.tel_layernorm(pre, hid, g32, b32(H), ti.LN_EPS, stream=stream),
                       0.0, 2.0 * 2 * T * H),
         "gemm_ffn1_gelu": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_GELU, hid, layer_w["w_1"], b32(F),
                                                 ffo, stream=stream),
                            2.0 * T * H * F, 2.0 * (T * H + F * H + T * F)),
-        "gemm_ffn2_resid": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, ffn, layer_w["w_2"],
-                                                 b32(H), pre, resid=hid, stream=stream),
+        "gemm_ffn2_resid": (resid_gemm(ffn, layer_w["w_2"], F, H),
                             2.0 * T * H * F, 2.0 * (T * F + F * H + 2 * T * H)),
     }
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():
         fn()
         torch.cuda.synchronize()
-        # A spin kernel holds the GPU while the host enqueues every (event, kernel, event)
-        # triple, so each pair of events brackets one kernel and no host launch latency.
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
+        # A spin kernel holds the GPU while the host enqueues kernel_reps launches between
+        # one pair of HIP events on the launch stream: the average is the kernel's share of
+        # a back-to-back stream (what rocprofv3's kernel-trace durations add up to inside
+        # the stack), free of host launch latency.
+        e_s, e_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(50_000_000)
-        for i in range(args.kernel_reps):
-            starts[i].record(stream)
+        e_s.record(stream)
+        for _ in range(args.kernel_reps):
             fn()
-            ends[i].record(stream)
+        e_e.record(stream)
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])) * 1e3
+        us = e_s.elapsed_time(e_e) * 1e3 / args.kernel_reps
         per_kernel[name] = dict(us=us, tflops=flops / us / 1e6, gbs=nbytes / us / 1e3,
                                 flops=flops, bytes=nbytes)
         log(f"[bench] kernel {name:16s} {us:9.2f} us  {flops / us / 1e6:8.1f} TFLOP/s"
@@ -208,8 +220,11 @@ def main():
     d = per_kernel[dom]
     peak = PEAK_FP32_TFLOPS if dt == "f32" else PEAK_FP16_TFLOPS
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4),
+                "traffic": measured_traffic(args.workload, dom),
                 "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
+    if args.calib_copy:
+        calibration_copy(stream)
     # one layer launches every kernel above once, and the LayerNorm twice
     layer_sum_us = sum(v["us"] for v in per_kernel.values()) + per_kernel["layernorm"]["us"]
 
@@ -220,6 +235,51 @@ def main():
 
     return emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu,
                 layer_sum_us)
+
+
+KERNEL_SOURCES = ("transformer_encoder_remove_amd/csrc/gemm.hip",
+                  "transformer_encoder_remove_amd/csrc/device.h",
+                  "transformer_encoder_remove_amd/csrc/launch.h")
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes summarised in profiles/hbm_traffic.json, scaled by what the same
+    counters read for a plain device copy of known size; null when the counters were taken
+    on other kernel sources than the ones built now, or for another kernel/workload."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("kernels", []):
+        if r.get("workload") == workload and r.get("kernel") == kernel and \
+                r.get("sources_sha256") == kernel_sources_digest():
+            return r.get("bytes_per_launch")
+    return None
+
+
+def calibration_copy(stream, mib: int = 256, reps: int = 3):
+    """A plain device-to-device copy of known size, the scale for rocprofv3's FETCH_SIZE /
+    WRITE_SIZE counters (each copy reads and writes exactly mib MiB)."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {reps} x {mib} MiB device-to-device")
 
 
 def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, layer_sum_us=None):

@@ -108,7 +108,7 @@ inline int gemm_dtype(const tel_encoder_desc* d) { return d->int8_gemm ? (int)DT
 // Rows of partial sums the layer needs for T tokens: the k-split plans of the output
 // projection and FFN2 at every token count up to T (fewer tokens may mean more splits),
 // so a workspace sized for T also serves any smaller batch.
-size_t partial_rows(const tel_encoder_desc* d, size_t T) {
+size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
   const int dt = gemm_dtype(d), H = d->hidden, F = d->ffn;
   auto need = [&](size_t t) {
     int cfg;
@@ -120,6 +120,18 @@ size_t partial_rows(const tel_encoder_desc* d, size_t T) {
   // inside each run of equal plans is at its top
   size_t rows = need(T);
   for (size_t t = 64; t < T; t += 64) rows = std::max(rows, need(t));
+  return rows;
+}
+
+// The workspace layout is computed on every layer call; remember the last answer per
+// thread so a stack of layers at one token count pays for the plan scan once.
+size_t partial_rows(const tel_encoder_desc* d, size_t T) {
+  struct Key { int dt, H, F; size_t T; size_t rows; };
+  thread_local Key last{-1, 0, 0, 0, 0};
+  const int dt = gemm_dtype(d);
+  if (last.dt == dt && last.H == d->hidden && last.F == d->ffn && last.T == T) return last.rows;
+  const size_t rows = partial_rows_uncached(d, T);
+  last = Key{dt, d->hidden, d->ffn, T, rows};
   return rows;
 }
 

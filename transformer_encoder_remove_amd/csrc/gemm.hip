@@ -25,6 +25,8 @@
 //    stored); K % (16 bytes) == 0 is required, slices past K are zero-filled.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -311,7 +313,8 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 
 template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
 __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
-    const T* __restrict__ A, const T* __restrict__ W, int K, int splits, EpiArgs<T, TR, TO> e) {
+    const T* __restrict__ A, const T* __restrict__ W, int K, int splits, int gn,
+    EpiArgs<T, TR, TO> e) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int NW = WM * WN;                       // compute wavefronts
@@ -335,12 +338,16 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE > STAGED ? S * STAGE : STAGED];
 
   const int M = e.M, N = e.N;
-  const int tiles_m = (M + BM - 1) / BM;
-  // blockIdx -> (output tile, k-split): the k-splits of a tile are neighbours, so they
-  // land on the same XCD and share the tile's L2 working set
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  // blockIdx -> (output tile, k-split). Each XCD (own L2) takes a contiguous run of the
+  // tile order, and the order walks groups of gn tile columns row by row, so one XCD's
+  // tiles form a compact block of rows x columns that share their A rows and W columns
+  // in its L2. The k-splits of a tile are neighbours in the run.
   const int ts = xcd_tile(blockIdx.x, gridDim.x);
   const int tile = ts / splits, split = ts - tile * splits;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int g = tile / (tiles_m * gn), r = tile - g * (tiles_m * gn);
+  const int gw = min(gn, tiles_n - g * gn);
+  const int tm = r / gw, tn = g * gn + (r - (r / gw) * gw);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nk = K / BK / splits;                   // k-slices of this split
@@ -547,12 +554,12 @@ constexpr PipeCfg PIPE_CFGS[] = {
     {128, 256, 2, 4, 3},   // 0: 8 waves, wave tile 64x64, 144 KiB LDS
     {128, 192, 2, 4, 3},   // 1: 8 waves, wave tile 64x48, 120 KiB
     {128, 128, 2, 2, 4},   // 2: 4 waves, wave tile 64x64, 128 KiB
-    {64, 128, 2, 2, 4},    // 3: 4 waves, wave tile 32x64, 96 KiB
+    {64, 128, 2, 4, 4},    // 3: 8 waves, wave tile 32x32, 96 KiB
     {64, 64, 2, 2, 4},     // 4: 4 waves, wave tile 32x32, 64 KiB
     {128, 256, 2, 2, 3},   // 5: 4 waves, wave tile 64x128, 144 KiB
     {256, 128, 2, 2, 3},   // 6: 4 waves, wave tile 128x64, 144 KiB
     {128, 128, 2, 2, 2},   // 7: 4 waves, wave tile 64x64, 64 KiB (two workgroups per CU)
-    {64, 128, 1, 2, 3},    // 8: 2 waves, wave tile 64x64, 72 KiB
+    {64, 128, 2, 2, 4},    // 8: 4 waves, wave tile 32x64, 96 KiB
 };
 constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 
@@ -565,14 +572,36 @@ static void launch_one(const GemmArgs& a, hipStream_t stream) {
       (const T*)a.A, (const T*)a.W, a.K, e);
 }
 
+// Width (in tile columns) of the column groups of the tile order: one XCD's run of
+// about tiles / 8 consecutive tiles then covers rows x cols = ceil(per / gn) x gn tiles,
+// and streams (rows * BM + cols * BN) k-long operand rows through its L2; take the width
+// that minimises that, a width that does not divide the column count paying for its
+// ragged last group (ties: the wider group).
+static int xcd_group_width(int tiles_m, int tiles_n, int bm, int bn) {
+  const long per = ((long)tiles_m * tiles_n + 7) / 8;
+  int best = tiles_n;
+  long best_cost = -1;
+  for (int gn = 1; gn <= tiles_n; ++gn) {
+    const long rows = std::min<long>((per + gn - 1) / gn, tiles_m);
+    const long cols = std::min<long>(gn, per);
+    const long cost = rows * bm + cols * bn + (tiles_n % gn ? bn / 2 : 0);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = gn;
+    }
+  }
+  return best;
+}
+
 template <typename T, int C, int EPI, typename TR, typename TO>
 static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
-  const int grid = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn) * a.splits;
+  const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
+  const int grid = tm * tn * a.splits;
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
-      <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>((const T*)a.A, (const T*)a.W,
-                                                                 a.K, a.splits, e);
+      <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>(
+          (const T*)a.A, (const T*)a.W, a.K, a.splits, xcd_group_width(tm, tn, c.bm, c.bn), e);
 }
 
 // cfg < 0: register-staged 64x64 kernel; otherwise PIPE_CFGS[cfg].
