@@ -2,6 +2,8 @@
 and invariants. CPU only."""
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,31 @@ def test_offsets_tiny_closed_form():
     cu, po = enc.offsets([5, 8], 8)
     assert cu.tolist() == [0, 5, 13]
     assert po.tolist() == [0] * 5 + [3] * 8
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_rows(name):
+    """Whitespace-separated rows of a fixture under tests/golden, comments dropped."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]
+
+
+def test_offsets_golden():
+    """Hand-worked offset masks (tests/golden/offsets.txt, after [KS] Fig. 9)."""
+    cases, cur = [], None
+    for tok in golden_rows("offsets.txt"):
+        if tok[0] == "case":
+            cur = {}
+            cases.append(cur)
+        else:
+            cur[tok[0]] = [int(v) for v in tok[1:]]
+    assert len(cases) == 3
+    for c in cases:
+        cu, po = enc.offsets(c["lens"], c["S"][0])
+        assert cu.tolist() == c["cu_seqlens"], c
+        assert po.tolist() == c["padding_offset"], c
 
 
 def test_offsets_brute_force_random():
@@ -70,6 +97,15 @@ def test_gelu_closed_forms():
     # GELU(1) = Phi(1), the standard normal CDF at 1 (textbook table value)
     assert abs(enc.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
     assert abs(enc.gelu(np.array([-1.0]))[0] + 0.15865525393145707) < 1e-15
+
+
+def test_gelu_normal_cdf_golden():
+    """GELU(x) = x * Phi(x) at the table values of tests/golden/normal_cdf.txt."""
+    rows = golden_rows("normal_cdf.txt")
+    assert len(rows) == 4
+    for x, phi in rows:
+        x, phi = float(x), float(phi)
+        assert abs(enc.gelu(np.array([x]))[0] - x * phi) < 1e-15, x
 
 
 def test_layernorm_invariants():

@@ -9,6 +9,7 @@ import torch
 import tel_inputs as ti
 from oracle import encoder as enc
 from oracle import swin
+from tests.test_oracle_encoder import golden_rows
 from tests import brute
 
 EPS = ti.LN_EPS
@@ -41,6 +42,19 @@ def test_relative_position_index():
     assert idx.shape == (49, 49) and idx.min() == 0 and idx.max() == 168
     assert (np.diag(idx) == 6 * 13 + 6).all()                     # zero offset -> table centre
     assert idx[0, 48] == 0 and idx[48, 0] == 168
+
+
+def test_relative_position_index_golden():
+    """The 2x2-window index table worked by hand (tests/golden/relative_position_index_window2.txt)."""
+    want = np.array(golden_rows("relative_position_index_window2.txt"), dtype=np.int64)
+    assert np.array_equal(swin.relative_position_index(2), want)
+
+
+def test_shift_mask_golden():
+    """Masked windows of the Swin-T stage-1 grid (tests/golden/swin_shift_mask_56_7_3.txt)."""
+    grid = np.array(golden_rows("swin_shift_mask_56_7_3.txt"), dtype=np.int64).astype(bool)
+    m = swin.window_mask(56, 56, 7, 3)
+    assert np.array_equal(np.isinf(m).any(axis=(1, 2)).reshape(8, 8), grid)
 
 
 def test_mask_layout_56_7_3():
