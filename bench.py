@@ -221,7 +221,7 @@ def main():
     peak = PEAK_FP32_TFLOPS if dt == "f32" else PEAK_FP16_TFLOPS
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4),
-                "traffic": measured_traffic(args.workload, dom),
+                "traffic": measured_traffic(args.workload, dt, dom),
                 "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
     if args.calib_copy:
         calibration_copy(stream)
@@ -251,7 +251,7 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, dtype: str, kernel: str):
     """HBM bytes per launch of the dominant kernel from the rocprofv3 FETCH_SIZE and
     WRITE_SIZE passes summarised in profiles/hbm_traffic.json, scaled by what the same
     counters read for a plain device copy of known size; null when the counters were taken
@@ -263,8 +263,8 @@ def measured_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     for r in rec.get("kernels", []):
-        if r.get("workload") == workload and r.get("kernel") == kernel and \
-                r.get("sources_sha256") == kernel_sources_digest():
+        if r.get("workload") == workload and r.get("dtype") == dtype and \
+                r.get("kernel") == kernel and r.get("sources_sha256") == kernel_sources_digest():
             return r.get("bytes_per_launch")
     return None
 

@@ -8,7 +8,7 @@ import torch
 import tel_inputs as ti
 from oracle import encoder as enc
 from oracle import int8 as q8
-from tests.gpu_helpers import assert_close, dev, errors, gpu_encoder_forward
+from tests.gpu_helpers import assert_close, dev, errors, gpu_encoder_forward, host, prepare_layers
 
 pytestmark = pytest.mark.gpu
 
@@ -150,3 +150,43 @@ def test_calibrate_matches_oracle():
     got = amax.cpu().numpy().astype(np.float64)
     assert got[0] == ref[0]                               # the input itself: exact
     assert np.all(np.abs(got - ref) <= 5e-3 * ref), (got, ref)
+
+
+def test_int8_small_stack_vs_q_oracle():
+    """Three int8 layers through tel_encoder_forward, where each LN2 hands the next layer its
+    input codes, against the Q-oracle stack."""
+    cfg = ti.custom_encoder_config(3, 40, [40, 1, 17], 128, 2, 256, dtype="f16", seed=23,
+                                   layers=3)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(3)]
+    amaxes = _calibrated(cfg, lens, x, ws)
+    y = _gpu_int8(cfg, lens, x, ws, amaxes)
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    ref = q8.encoder_stack_int8(enc.remove_padding(x.astype(np.float64), lens), cu, ws, amaxes,
+                                cfg["heads"], EPS)
+    assert_close(enc.remove_padding(y, lens), ref, "f16", "int8 3-layer stack")
+
+
+def test_int8_stack_codes_equal_layer_by_layer():
+    """The stack's chained codes (LN2 quantising for the next layer) are exactly the codes the
+    per-layer entry point makes with its own quantise kernel: both runs agree bitwise."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base_int8"], layers=3)
+    lens, x = ti.encoder_input(cfg)
+    lens, x = lens[:8], x[:8]
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(3)]
+    amaxes = [[3.0, 2.5, 4.0, 1.5], [3.5, 2.0, 4.5, 1.0], [2.5, 3.0, 3.5, 2.0]]
+    y_stack = _gpu_int8(dict(cfg, batch=8), lens, x, ws, amaxes)
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], torch.float16,
+                                 ti.LN_EPS, int8_gemm=True)
+    packed = prepare_layers(tel, desc, ws, "f16", amaxes)
+    cu_h, _ = enc.offsets(lens, cfg["max_seq"])
+    T, max_len = int(np.sum(lens)), int(np.max(lens))
+    cur = dev(enc.remove_padding(x.astype(np.float64), lens), "f16")
+    cu = torch.from_numpy(np.asarray(cu_h, np.int32)).cuda()
+    lws = tel.alloc_bytes(tel.tel_encoder_workspace_size(desc, T))
+    for p in packed:
+        nxt = torch.empty_like(cur)
+        tel.tel_encoder_layer_forward(desc, p, cur, nxt, cu, T, max_len, lws)
+        cur = nxt
+    torch.cuda.synchronize()
+    assert np.array_equal(enc.remove_padding(y_stack, lens), host(cur))

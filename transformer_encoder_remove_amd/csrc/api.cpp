@@ -157,7 +157,7 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
 }
 
 struct StackWs {
-  size_t cu, po, xa, xb, layer, total;
+  size_t cu, po, xa, xb, qa, qb, layer, total;   // qa, qb: int8 stack, codes of xa / xb
 };
 
 StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
@@ -169,24 +169,36 @@ StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
   s.po = take(T * 4);
   s.xa = take(T * H * es);
   s.xb = take(T * H * es);
+  s.qa = d->int8_gemm ? take(T * H) : 0;
+  s.qb = d->int8_gemm ? take(T * H) : 0;
   s.layer = take(layer_ws(d, T).total);
   s.total = o;
   return s;
 }
 
+// Codes shared between consecutive int8 layers of a stack: xq_in holds this layer's input
+// codes (made by the previous layer's LN2), xq_out receives the output's codes at the next
+// layer's input scale *next_qinv. All null: quantise the input here, no codes out.
+struct Int8Link {
+  const int8_t* xq_in = nullptr;
+  int8_t* xq_out = nullptr;
+  const float* next_qinv = nullptr;
+};
+
 // Int8 layer ([SW] section 3, INT8: quantise -> INT8 GEMM -> INT32 -> dequantise; bias,
 // residual and LayerNorm stay floating point; attention runs in fp16 on the dequantised
-// Q, K, V). Codes are produced where the value is made: a quantise kernel for x and ctx,
-// the LayerNorm for h1, the FFN1 epilogue for the GELU output.
+// Q, K, V). Codes are produced where the value is made: the attention kernel for ctx, the
+// LayerNorm for h1 (and, in a stack, LN2 for the next layer's input), the FFN1 epilogue for
+// the GELU output; only a stack's first input goes through the quantise kernel.
 int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, void* y,
                        const int32_t* cu, int batch, int T, int max_len, char* ws,
-                       hipStream_t st) {
+                       hipStream_t st, const Int8Link& link = Int8Link{}) {
   const LayerLayout L = layer_layout(d);
   const LayerWs W = layer_ws(d, (size_t)T);
   const int H = d->hidden, F = d->ffn, nh = d->heads;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
   const float* inv = F32(L.act) + 4;
-  int8_t* xq = (int8_t*)(ws + W.xq);
+  const int8_t* xq = link.xq_in ? link.xq_in : (const int8_t*)(ws + W.xq);
   int8_t* ctxq = (int8_t*)(ws + W.ctxq);
   int8_t* h1q = (int8_t*)(ws + W.h1q);
   int8_t* fq = (int8_t*)(ws + W.f);
@@ -199,12 +211,14 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   const int sp_o = gemm_partial_plan(DT_I8, T, H, H, &cfg_o);
   const int sp_2 = gemm_partial_plan(DT_I8, T, H, F, &cfg_2);
 
-  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, inv + 0, 0.f, st));
+  if (!link.xq_in)
+    TEL_TRY(launch_quantize_act(DT_F16, x, (int8_t*)(ws + W.xq), (size_t)T * H, inv + 0, 0.f, st));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.dq = F32(L.dq_qkv);
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
-  TEL_TRY(launch_quantize_act(DT_F16, ctx, ctxq, (size_t)T * H, inv + 1, 0.f, st));
+  // attention writes the int8 codes of its fp16 output directly (the O projection's input)
+  TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, ctxq,
+                           inv + 1));
   // output projection + dequantise + bias + residual (stored fp16), LayerNorm and the
   // int8 codes of h1; split over k (int32 partials, all of that in the reduce kernel)
   // when few tokens leave the GPU idle
@@ -232,14 +246,19 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
     g.splits = sp_2;
     TEL_TRY(launch_gemm_cfg(DT_I8, cfg_2, g, st));
     const LnReduceArgs r{part, sp_2, F32(L.dq_2), F32(L.b_2), h1, DT_F16, y, DT_F16, nullptr,
-                         nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, 1};
+                         link.xq_out, link.next_qinv, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                         d->ln_eps, 1};
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
     g.dq = F32(L.dq_2);
     TEL_TRY(launch_gemm(DT_I8, g, st));
-    TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
-                             d->ln_eps, st));
+    if (link.xq_out)
+      TEL_TRY(launch_layernorm_q8(pre, y, link.xq_out, link.next_qinv, F32(L.ln2_g),
+                                  F32(L.ln2_b), T, H, d->ln_eps, st));
+    else
+      TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T,
+                               H, d->ln_eps, st));
   }
   return TEL_OK;
 }
@@ -568,9 +587,28 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   const int row_bytes = d->hidden * dtype_size(d->dtype);
   TEL_TRY(launch_offsets(seq_lens, batch, max_seq, cu, po, st));
   TEL_TRY(launch_remove_padding(x_pad, xa, po, total_tokens, row_bytes, st));
+  int8_t* qa = (int8_t*)(ws + S.qa);
+  int8_t* qb = (int8_t*)(ws + S.qb);
+  const size_t act_off = d->int8_gemm ? layer_layout(d).act : 0;
   for (int i = 0; i < n_layers; ++i) {
-    const int r = layer_forward(d, (const char*)packed_layers[i], xa, xb, cu, batch,
-                                total_tokens, max_len, ws + S.layer, st);
+    int r;
+    if (d->int8_gemm && total_tokens > 0) {
+      // each LN2 writes the codes of its output at the next layer's input scale
+      Int8Link link;
+      link.xq_in = i > 0 ? qa : nullptr;
+      if (i + 1 < n_layers) {
+        link.xq_out = qb;
+        link.next_qinv = (const float*)((const char*)packed_layers[i + 1] + act_off) + 4;
+      }
+      r = layer_forward_int8(d, (const char*)packed_layers[i], xa, xb, cu, batch, total_tokens,
+                             max_len, ws + S.layer, st, link);
+      int8_t* tq = qa;
+      qa = qb;
+      qb = tq;
+    } else {
+      r = layer_forward(d, (const char*)packed_layers[i], xa, xb, cu, batch, total_tokens,
+                        max_len, ws + S.layer, st);
+    }
     if (r != TEL_OK) return r;
     void* t = xa;
     xa = xb;

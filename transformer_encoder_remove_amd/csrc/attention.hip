@@ -168,7 +168,9 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
                                                           T* __restrict__ ctx,
                                                           const int32_t* __restrict__ cu,
                                                           int total_tokens, int heads,
-                                                          float scale_log2) {
+                                                          float scale_log2,
+                                                          int8_t* __restrict__ ctxq,
+                                                          const float* __restrict__ qinv) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int KPL = MF::KPL, KMF = 4 * KPL;
@@ -235,13 +237,31 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
 
   if (qi < L) {
     const float inv_l = 1.f / l_run;
-    T* out = ctx + (size_t)(start + qi) * (heads * D) + h * D;
+    const size_t base = (size_t)(start + qi) * (heads * D) + h * D;
+    if (ctxq) {
+      // int8 layer: only the int8 codes of the stored-type context feed the next GEMM,
+      // code = clamp(rne(float(T(ctx)) * inv), -127, 127), as the quantise kernel computes
+      const float inv = *qinv;
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      Vec4<T> w;
+      for (int c = 0; c < NCB; ++c) {
+        int8_t q[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w.v[i] = from_f32<T>(o[c][i] * inv_l);
-      *reinterpret_cast<Vec4<T>*>(out + c * 16 + 4 * lg) = w;
+        for (int i = 0; i < 4; ++i) {
+          const float r = __builtin_rintf(to_f32(from_f32<T>(o[c][i] * inv_l)) * inv);
+          q[i] = (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+        }
+        uint32_t packed;
+        __builtin_memcpy(&packed, q, 4);
+        *reinterpret_cast<uint32_t*>(ctxq + base + c * 16 + 4 * lg) = packed;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        Vec4<T> w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.v[i] = from_f32<T>(o[c][i] * inv_l);
+        *reinterpret_cast<Vec4<T>*>(ctx + base + c * 16 + 4 * lg) = w;
+      }
     }
   }
 }
@@ -253,33 +273,40 @@ bool attention_supported(int dtype, int head_dim) {
 
 template <typename T, int D>
 static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
-                           int max_len, int heads, hipStream_t stream) {
+                           int max_len, int heads, int8_t* ctxq, const float* qinv,
+                           hipStream_t stream) {
   const dim3 grid((max_len + ATT_QB - 1) / ATT_QB, heads, batch);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   attn_varlen_kernel<T, D><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total, heads,
-                                                     scale_log2);
+                                                     scale_log2, ctxq, qinv);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t run_attn_d(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
-                             int max_len, int heads, int d, hipStream_t stream) {
+                             int max_len, int heads, int d, int8_t* ctxq, const float* qinv,
+                             hipStream_t stream) {
   switch (d) {
-    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, stream);
-    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, stream);
-    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, stream);
-    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, stream);
+    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
+    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
+    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
+    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
-                            int total, int max_len, int heads, int head_dim, hipStream_t stream) {
+                            int total, int max_len, int heads, int head_dim, hipStream_t stream,
+                            int8_t* ctxq, const float* qinv) {
   if (total == 0 || max_len == 0) return hipSuccess;
+  if (ctxq && !qinv) return hipErrorInvalidValue;
   switch (dtype) {
-    case DT_F16: return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
-    case DT_BF16: return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
-    case DT_F32: return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, stream);
+    case DT_F16:
+      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
+    case DT_BF16:
+      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
+    case DT_F32:
+      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include <algorithm>
+#include <cmath>
 
 #include "device.h"
 #include "launch.h"
@@ -668,16 +669,32 @@ static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The largest tile that still yields about one workgroup per compute unit (the order of
-// the table); shapes whose K is not a multiple of 128 bytes use the register-staged kernel.
+// Tile choice by a small cost model. All workgroups of these tiles fit one per compute
+// unit, so a launch runs in rounds of 256 tiles, and each round costs the tile's MFMA loop
+// plus a fixed ~3.5 us (first slice in flight, epilogue, stores). The loop rate per compute
+// unit is the one measured for the 128x256 tile (3.19e6 MACs/us for 16-bit operands, 1.9x
+// that for int8 codes), scaled by each smaller tile's measured efficiency. A grid just
+// past a multiple of 256 pays a whole extra round (wave quantisation), which the model
+// sees and the plain "enough tiles" rule did not. Shapes whose K is not a multiple of 128
+// bytes use the register-staged kernel.
 static int pick_cfg(const GemmArgs& a, int elem_bytes) {
   if (((long long)a.K * elem_bytes) % 128) return -1;
+  constexpr double EFF[5] = {1.0, 0.9, 0.8, 0.62, 0.5};
+  constexpr double FIXED_US = 3.5, CUS = 256;
+  const double rate = elem_bytes == 1 ? 6.06e6 : elem_bytes == 2 ? 3.19e6 : 0.2e6;
+  int best = 0;
+  double best_us = -1;
   for (int c = 0; c < 5; ++c) {
     const PipeCfg& p = PIPE_CFGS[c];
-    const long tiles = (long)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
-    if (tiles >= 200) return c;
+    const double tiles = (double)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
+    const double rounds = std::ceil(tiles / CUS);
+    const double us = rounds * ((double)p.bm * p.bn * a.K / (rate * EFF[c]) + FIXED_US);
+    if (best_us < 0 || us < best_us) {
+      best_us = us;
+      best = c;
+    }
   }
-  return 4;
+  return best;
 }
 
 // Partial-sum GEMMs: a shape whose tile grid leaves most compute units idle (few tokens,

@@ -55,9 +55,10 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg);
 
 // attention.hip
 bool attention_supported(int dtype, int head_dim);
-hipError_t launch_attention(int dtype, const void* qkv_split, void* ctx, const int32_t* cu,
-                            int batch, int total_tokens, int max_len, int heads, int head_dim,
-                            hipStream_t stream);
+// ctxq != nullptr: write only the int8 codes of the stored-type output (scale *qinv)
+hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
+                            int total, int max_len, int heads, int head_dim, hipStream_t stream,
+                            int8_t* ctxq = nullptr, const float* qinv = nullptr);
 
 // layernorm.hip: y = LN(x) in type dtype_out from x in type dtype_in; when y_f32 is not
 // null the same result is also written there in float32.
