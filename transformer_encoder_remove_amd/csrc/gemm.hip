@@ -162,7 +162,19 @@ __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int
 #pragma unroll
       for (int i = 0; i < 8; ++i) out.v[i] = from_f32<TO>(v[i]);
     }
-    *reinterpret_cast<Vec8<TO>*>(e.C + idx) = out;
+    // non-temporal: the output is read by the next kernel, on other XCDs; leaving it
+    // dirty in this XCD's L2 only lengthens the write-back at the end of the kernel
+    if constexpr (sizeof(Vec8<TO>) == 16) {
+      u32x4 bits;
+      __builtin_memcpy(&bits, &out, 16);
+      __builtin_nontemporal_store(bits, reinterpret_cast<u32x4*>(e.C + idx));
+    } else if constexpr (sizeof(Vec8<TO>) == 8) {
+      u32x2 bits;
+      __builtin_memcpy(&bits, &out, 8);
+      __builtin_nontemporal_store(bits, reinterpret_cast<u32x2*>(e.C + idx));
+    } else {
+      *reinterpret_cast<Vec8<TO>*>(e.C + idx) = out;
+    }
   }
 }
 
@@ -546,6 +558,129 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   }
 }
 
+// ------------------------------------------------------------------ skinny GEMMs
+// Narrow, HBM-bound GEMMs of the shifted-window block (channels 96: QKV 96 -> 288, proj
+// 96 -> 96, fc1 96 -> 384, fc2 384 -> 96, over ~2e5 tokens). A tile narrower than N
+// would re-read the token matrix once per tile column; here each workgroup keeps the
+// whole weight matrix (N x K <= 384 x 96 or 96 x 384) in LDS and owns full output rows, so
+// every token row is read exactly once. Persistent: a workgroup walks row blocks of 64
+// tokens (16 per wavefront) with a stride of the grid, holding the token fragments of its
+// next two blocks in registers while it computes the current one. The weight tile is the
+// MFMA A operand, so each lane ends with 4 consecutive columns of one token and the
+// 4-column epilogue above (bias, GELU, QKV split, window scatter, residual) applies as is.
+constexpr int ROWS_WG = 64;
+
+template <typename T, int KS>
+__device__ __forceinline__ void rows_load(typename Mfma<T>::frag (&buf)[KS], const T* A, int M,
+                                          int row0, int lr, int lg) {
+  constexpr int K = KS * 32;
+  const T* src = A + (size_t)min(row0 + lr, M - 1) * K + lg * 8;
+#pragma unroll
+  for (int t = 0; t < KS; ++t) buf[t] = *reinterpret_cast<const typename Mfma<T>::frag*>(src + t * 32);
+}
+
+// Output fragments in groups of 6 and k in chunks of 3 steps, with scheduling barriers
+// between them: the live weight fragments stay at 6 x 3 (72 VGPRs) instead of the whole
+// weight slice, which keeps two or three wavefronts per SIMD resident.
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO>
+__device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS], const T* sW,
+                                           const EpiArgs<T, TR, TO>& e, int row0, int lr,
+                                           int lg) {
+  using MF = Mfma<T>;
+  constexpr int LDW = KS * 32 + 8, G = 6, KC = 3;
+  static_assert(NF % G == 0 && KS % KC == 0, "fragment groups");
+  const int m = row0 + lr;
+#pragma unroll
+  for (int g = 0; g < NF / G; ++g) {
+    typename MF::acc acc[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) acc[i] = typename MF::acc{};
+#pragma unroll
+    for (int t0 = 0; t0 < KS; t0 += KC) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = t0; t < t0 + KC; ++t)
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const typename MF::frag w = *reinterpret_cast<const typename MF::frag*>(
+              sW + ((g * G + i) * 16 + lr) * LDW + t * 32 + lg * 8);
+          acc[i] = MF::mma(w, a[t], acc[i]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (m < e.M) {
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        epilogue_store<EPI, T, TR, TO>(e, m, (g * G + i) * 16 + lg * 4, acc[i]);
+    }
+  }
+}
+
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
+                                                        const T* __restrict__ W,
+                                                        EpiArgs<T, TR, TO> e) {
+  using MF = Mfma<T>;
+  static_assert(MF::KPL == 8, "16-bit operands");
+  constexpr int N = NF * 16, K = KS * 32, LDW = K + 8;
+  __shared__ __attribute__((aligned(16))) T sW[N * LDW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int idx = tid; idx < N * (K / 8); idx += 256) {
+    const int r = idx / (K / 8), c = idx - r * (K / 8);
+    *reinterpret_cast<u32x4*>(sW + r * LDW + c * 8) =
+        *reinterpret_cast<const u32x4*>(W + (size_t)r * K + c * 8);
+  }
+  __syncthreads();
+  const int M = e.M, stride = gridDim.x * ROWS_WG;
+  typename MF::frag a0[KS], a1[KS];
+  int rb = blockIdx.x * ROWS_WG + wave * 16;   // this wavefront's 16 rows of the block
+  if (rb < M) rows_load<T, KS>(a0, A, M, rb, lr, lg);
+  if (rb + stride < M) rows_load<T, KS>(a1, A, M, rb + stride, lr, lg);
+  for (; rb < M; rb += 2 * stride) {
+    rows_block<T, NF, KS, EPI, TR, TO>(a0, sW, e, rb, lr, lg);
+    if (rb + 2 * stride < M) rows_load<T, KS>(a0, A, M, rb + 2 * stride, lr, lg);
+    if (rb + stride >= M) break;
+    rows_block<T, NF, KS, EPI, TR, TO>(a1, sW, e, rb + stride, lr, lg);
+    if (rb + 3 * stride < M) rows_load<T, KS>(a1, A, M, rb + 3 * stride, lr, lg);
+  }
+}
+
+template <typename T, int NF, int KS>
+static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
+  const int blocks = (a.M + ROWS_WG - 1) / ROWS_WG;
+  const int grid = std::min(blocks, 512);   // two workgroups per CU (<= 80 KiB of LDS each)
+#define TEL_ROWS(EPI)                                                                        \
+  do {                                                                                       \
+    EpiArgs<T, T, T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, \
+                       a.geom};                                                              \
+    gemm_rows_kernel<T, NF, KS, EPI, T, T><<<grid, 256, 0, stream>>>((const T*)a.A,         \
+                                                                    (const T*)a.W, e);       \
+  } while (0)
+  switch (a.epi) {
+    case EPI_BIAS: TEL_ROWS(EPI_BIAS); break;
+    case EPI_BIAS_GELU: TEL_ROWS(EPI_BIAS_GELU); break;
+    case EPI_BIAS_RESID: TEL_ROWS(EPI_BIAS_RESID); break;
+    case EPI_QKV_SPLIT: TEL_ROWS(EPI_QKV_SPLIT); break;
+    case EPI_SWIN_SCATTER: TEL_ROWS(EPI_SWIN_SCATTER); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef TEL_ROWS
+  return hipGetLastError();
+}
+
+// The (N, K) shapes the skinny kernel is built for; false: use the tiled kernels.
+template <typename T>
+static bool launch_rows(const GemmArgs& a, hipStream_t stream, hipError_t* err) {
+  if (a.resid_f32 || a.out_f32) return false;
+  if (a.N == 288 && a.K == 96) *err = launch_rows_nk<T, 18, 3>(a, stream);
+  else if (a.N == 96 && a.K == 96) *err = launch_rows_nk<T, 6, 3>(a, stream);
+  else if (a.N == 384 && a.K == 96) *err = launch_rows_nk<T, 24, 3>(a, stream);
+  else if (a.N == 96 && a.K == 384) *err = launch_rows_nk<T, 6, 12>(a, stream);
+  else return false;
+  return true;
+}
+
 // ------------------------------------------------------------------ dispatch
 // Tile configurations. The register-staged kernel (gemm_nt_kernel) serves K that is not a
 // multiple of 128 bytes; every other shape uses the pipelined kernel with one of these
@@ -725,8 +860,16 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.splits != 1) return hipErrorInvalidValue;   // splits need an explicit configuration
   switch (dtype) {
     case DT_I8: return run_epi_i8(pick_cfg(a, 1), a, stream);
-    case DT_F16: return run_epi<f16>(pick_cfg(a, 2), a, stream);
-    case DT_BF16: return run_epi<bf16>(pick_cfg(a, 2), a, stream);
+    case DT_F16: {
+      hipError_t err;
+      if (launch_rows<f16>(a, stream, &err)) return err;
+      return run_epi<f16>(pick_cfg(a, 2), a, stream);
+    }
+    case DT_BF16: {
+      hipError_t err;
+      if (launch_rows<bf16>(a, stream, &err)) return err;
+      return run_epi<bf16>(pick_cfg(a, 2), a, stream);
+    }
     case DT_F32: return run_epi<float>(pick_cfg(a, 4), a, stream);
     default: return hipErrorInvalidValue;
   }

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
 
   __shared__ __attribute__((aligned(16))) T sK[WIN_TOK * LDK];
   __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+  __shared__ int sReg[WIN_TOK];                      // shift-mask region of every key
 
   const int win = blockIdx.x, h = blockIdx.y;
   const int N = g.N;
@@ -69,9 +70,16 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
     const int d0 = s * KMF + lg * KPL;
     qf[s] = (d0 < D) ? *reinterpret_cast<const frag*>(Qh + (size_t)qc * D + d0) : frag{};
   }
-  const int qreg = g.region(wimg, qc);
+  // Only windows in the last window row or column straddle a region border (the shifted
+  // image splits each axis at L - M and L - s, and only the last window spans them), so
+  // the mask test is skipped everywhere else; where it applies, the 64 key regions are
+  // computed once into LDS.
+  const int wy = wimg / g.nWx, wx = wimg - wy * g.nWx;
+  const bool masked = g.s > 0 && (wy == g.nW / g.nWx - 1 || wx == g.nWx - 1);
+  if (masked && tid < WIN_TOK) sReg[tid] = g.region(wimg, min(tid, N - 1));
   const float* brow = bias_exp + ((size_t)h * N + qc) * WIN_TOK;
   __syncthreads();
+  const int qreg = masked ? sReg[qc] : 0;
 
   f32x4 sc[NJ];
 #pragma unroll
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
     for (int i = 0; i < 4; ++i) {
       const int key = j * 16 + lg * 4 + i;
       float s = sc[j][i] * scale_log2 + bb[i];            // -inf for padded keys
-      if (key < N && g.region(wimg, key) != qreg) s = -INFINITY;
+      if (masked && key < N && sReg[key] != qreg) s = -INFINITY;
       sc[j][i] = s;
       mx = fmaxf(mx, s);
     }
