@@ -279,6 +279,17 @@ int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, c
 int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,
                   int width, float eps, int dtype, void* stream);
 
+/* Graph cache of tel_encoder_forward, for callers whose host is slow to enqueue (off by
+ * default; the environment variable TEL_GRAPHS=1 turns it on at load). With it on, the
+ * first call with a given set of arguments (device,
+ * descriptor, layer pointers, buffers, sizes) records the forward's kernels as one HIP graph
+ * on an internal stream, and every call replays that graph on the caller's stream: one
+ * launch instead of ~10 per layer. Buffer contents (inputs, lengths, weights) are read when
+ * the graph runs, so refilling buffers between calls is safe; at most 8 graphs are kept (the
+ * eviction of the oldest waits for the device to drain). enable: 1 on, 0 off, -1 query only;
+ * returns the previous setting. Thread-safe. */
+int tel_graph_cache(int enable);
+
 /* Split-k GEMM without epilogue: the first half of a layer's output projection and FFN2,
  * whose add-bias + residual + LayerNorm epilogue ([SW] section 3, the fused
  * add-bias-residual-LayerNorm) tel_layernorm_reduce finishes.

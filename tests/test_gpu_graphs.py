@@ -1,0 +1,84 @@
+"""tel_encoder_forward's graph cache: replays of the recorded forward equal the eager
+forward bitwise, across several replays with unrelated eager GPU work and synchronisations
+in between, and read buffer contents (inputs, lengths) at replay time."""
+import numpy as np
+import pytest
+import torch
+
+import tel_inputs as ti
+from tests.gpu_helpers import TORCH_DT, dev, prepare_layers
+
+pytestmark = pytest.mark.gpu
+
+tel = pytest.importorskip("transformer_encoder_remove_amd")
+
+
+@pytest.fixture
+def cache_state():
+    prev = tel.tel_graph_cache(-1)
+    yield
+    tel.tel_graph_cache(prev)
+
+
+def _setup(name, dtype, layers, int8=False):
+    cfg = dict(ti.ENCODER_CONFIGS[name], dtype=dtype, layers=layers)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(layers)]
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT[dtype],
+                                 ti.LN_EPS, int8_gemm=int8)
+    amax = [[3.0, 2.5, 4.0, 1.5]] * layers if int8 else None
+    packed = prepare_layers(tel, desc, ws, dtype, amax)
+    B, S, _ = x.shape
+    xd = dev(x, dtype)
+    yd = torch.empty_like(xd)
+    lens_d = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    wsb = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
+    T, max_len = int(np.sum(lens)), int(np.max(lens))
+    run = lambda: tel.tel_encoder_forward(desc, packed, xd, yd, lens_d, T, max_len, wsb)
+    return cfg, lens, x, xd, yd, lens_d, run
+
+
+@pytest.mark.parametrize("name,dtype,layers,int8", [("bert_base", "f16", 2, False),
+                                                      ("bert_large_latency", "f16", 2, False),
+                                                      ("bert_base_int8", "f16", 3, True)])
+def test_graph_replays_equal_eager(cache_state, name, dtype, layers, int8):
+    cfg, lens, x, xd, yd, lens_d, run = _setup(name, dtype, layers, int8)
+    tel.tel_graph_cache(0)
+    yd.fill_(float("nan"))
+    run()
+    torch.cuda.synchronize()
+    ref = yd.clone()
+    tel.tel_graph_cache(1)
+    for i in range(4):
+        yd.fill_(float("nan"))
+        run()
+        # unrelated eager work between replays
+        junk = torch.randn(1 << 20, device="cuda")
+        _ = (junk * 2).sum().item()
+        torch.cuda.synchronize()
+        assert torch.equal(yd, ref), f"replay {i}"
+
+
+def test_graph_reads_buffers_at_replay(cache_state):
+    """Same buffers and sizes (same graph), new contents: new inputs, and the lengths
+    permuted (same total and maximum), give the eager results of the new contents."""
+    cfg, lens, x, xd, yd, lens_d, run = _setup("bert_base", "f16", 2)
+    tel.tel_graph_cache(1)
+    run()                                       # records the graph
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    x2 = ti.to_storage(rng.standard_normal(x.shape), "f16")
+    perm = np.asarray(lens)[::-1].copy()
+    for new_x, new_lens in ((x2, lens), (x2, perm)):
+        xd.copy_(dev(new_x, "f16"))
+        lens_d.copy_(torch.from_numpy(np.asarray(new_lens, np.int32)))
+        tel.tel_graph_cache(0)
+        yd.fill_(float("nan"))
+        run()
+        torch.cuda.synchronize()
+        ref = yd.clone()
+        tel.tel_graph_cache(1)
+        yd.fill_(float("nan"))
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(yd, ref)

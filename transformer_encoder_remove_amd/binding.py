@@ -34,7 +34,7 @@ EXPORTS = (
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
-    "tel_layernorm_reduce",
+    "tel_layernorm_reduce", "tel_graph_cache",
 )
 TEL_SWIN_ATTN_ONLY = 1
 
@@ -113,6 +113,7 @@ _SIG = {
     "tel_gemm_partial": (I, [I, I, I, P, P, P, I, I, I, P]),
     "tel_gemm_partial_plan": (I, [I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
     "tel_layernorm_reduce": (I, [P, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
+    "tel_graph_cache": (I, [I]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -277,6 +278,12 @@ def tel_quantize_weight_i8(w, q, scales, stream=None):
     N, K = w.shape
     _check("tel_quantize_weight_i8", lib.tel_quantize_weight_i8(
         _ptr(w), _ptr(q), _ptr(scales), N, K, dtype_code(w.dtype), _stream(stream)))
+
+
+def tel_graph_cache(enable: int = -1) -> int:
+    """Turn tel_encoder_forward's graph cache on (1) or off (0); -1 queries. Returns the
+    previous setting."""
+    return lib.tel_graph_cache(enable)
 
 
 def tel_gemm_partial_plan(dtype: int, M: int, N: int, K: int) -> tuple[int, int]:

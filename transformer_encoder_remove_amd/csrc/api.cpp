@@ -7,6 +7,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "launch.h"
 #include "tel.h"
@@ -559,31 +562,18 @@ size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* d, int batch, 
   return stack_ws(d, batch, max_seq).total;
 }
 
-int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_layers, int n_layers,
-                        const void* x_pad, void* y_pad, const int32_t* seq_lens, int batch,
-                        int max_seq, int total_tokens, int max_len, void* workspace,
-                        size_t ws_bytes, void* stream) {
-  const int sup = desc_supported(d);
-  if (sup != TEL_OK) return sup;
-  if (batch <= 0 || max_seq <= 0 || n_layers < 0 || total_tokens < 0 || max_len < 0)
-    return TEL_EINVAL;
-  if ((long long)batch * max_seq > INT32_MAX) return TEL_EUNSUPPORTED;
-  if (total_tokens > batch * max_seq || max_len > max_seq) return TEL_EINVAL;
-  if (total_tokens > 0 && max_len == 0) return TEL_EINVAL;
-  if (!x_pad || !y_pad || !seq_lens || !workspace || (n_layers > 0 && !packed_layers))
-    return TEL_EINVAL;
-  for (int i = 0; i < n_layers; ++i)
-    if (!packed_layers[i] || !aligned256(packed_layers[i])) return TEL_EINVAL;
-  if (!aligned256(workspace) || !aligned16(x_pad) || !aligned16(y_pad)) return TEL_EINVAL;
-  if (x_pad == y_pad) return TEL_EINVAL;
+// The whole forward (offsets, remove padding, layers, rebuild) enqueued on stream st;
+// arguments already validated.
+static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_layers,
+                           int n_layers, const void* x_pad, void* y_pad,
+                           const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
+                           int max_len, void* workspace, hipStream_t st) {
   const StackWs S = stack_ws(d, batch, max_seq);
-  if (ws_bytes < S.total) return TEL_EWORKSPACE;
   char* ws = (char*)workspace;
   int32_t* cu = (int32_t*)(ws + S.cu);
   int32_t* po = (int32_t*)(ws + S.po);
   void* xa = ws + S.xa;
   void* xb = ws + S.xb;
-  hipStream_t st = as_stream(stream);
   const int row_bytes = d->hidden * dtype_size(d->dtype);
   TEL_TRY(launch_offsets(seq_lens, batch, max_seq, cu, po, st));
   TEL_TRY(launch_remove_padding(x_pad, xa, po, total_tokens, row_bytes, st));
@@ -616,6 +606,117 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   }
   TEL_TRY(launch_rebuild_padding(xa, y_pad, cu, batch, max_seq, row_bytes, st));
   return TEL_OK;
+}
+
+// ------------------------------------------------------------------ forward graph cache
+// A forward is ~7 launches per layer; replaying them as one HIP graph removes the host's
+// per-launch cost, which matters when the caller's host is slow to enqueue. Measured on the
+// encoder workloads here the host keeps ahead of the GPU (graph and eager steps within 1 %),
+// so the cache is off unless asked for. Graphs are captured on an internal stream
+// (capture is not allowed on the legacy default stream) the first time a given set of
+// arguments is seen, and launched on the caller's stream afterwards. The key holds every
+// argument the launches depend on (pointers, sizes, device); buffer contents and weights
+// are read when the graph runs, so reusing buffers is safe. The forward records no memset
+// or host work, only kernels.
+namespace {
+struct GraphEntry {
+  std::vector<uintptr_t> key;
+  hipGraphExec_t exec;
+};
+std::mutex g_graph_mu;
+std::vector<GraphEntry> g_graphs;                 // most recently used last
+std::vector<hipStream_t> g_capture_streams;       // per device, created on first use
+int g_graphs_on = -1;                              // -1: read TEL_GRAPHS once
+constexpr size_t GRAPH_CACHE_MAX = 8;
+
+bool graphs_on_locked() {
+  if (g_graphs_on < 0) {
+    const char* e = getenv("TEL_GRAPHS");
+    g_graphs_on = (e && e[0] == '1') ? 1 : 0;
+  }
+  return g_graphs_on == 1;
+}
+}  // namespace
+
+int tel_graph_cache(int enable) {
+  std::lock_guard<std::mutex> lk(g_graph_mu);
+  const int prev = graphs_on_locked() ? 1 : 0;
+  if (enable >= 0) g_graphs_on = enable ? 1 : 0;
+  return prev;
+}
+
+int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_layers, int n_layers,
+                        const void* x_pad, void* y_pad, const int32_t* seq_lens, int batch,
+                        int max_seq, int total_tokens, int max_len, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  const int sup = desc_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (batch <= 0 || max_seq <= 0 || n_layers < 0 || total_tokens < 0 || max_len < 0)
+    return TEL_EINVAL;
+  if ((long long)batch * max_seq > INT32_MAX) return TEL_EUNSUPPORTED;
+  if (total_tokens > batch * max_seq || max_len > max_seq) return TEL_EINVAL;
+  if (total_tokens > 0 && max_len == 0) return TEL_EINVAL;
+  if (!x_pad || !y_pad || !seq_lens || !workspace || (n_layers > 0 && !packed_layers))
+    return TEL_EINVAL;
+  for (int i = 0; i < n_layers; ++i)
+    if (!packed_layers[i] || !aligned256(packed_layers[i])) return TEL_EINVAL;
+  if (!aligned256(workspace) || !aligned16(x_pad) || !aligned16(y_pad)) return TEL_EINVAL;
+  if (x_pad == y_pad) return TEL_EINVAL;
+  const StackWs S = stack_ws(d, batch, max_seq);
+  if (ws_bytes < S.total) return TEL_EWORKSPACE;
+  hipStream_t st = as_stream(stream);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TEL_EDEVICE;
+  std::unique_lock<std::mutex> lk(g_graph_mu);
+  if (!graphs_on_locked()) {
+    lk.unlock();
+    return forward_enqueue(d, packed_layers, n_layers, x_pad, y_pad, seq_lens, batch, max_seq,
+                           total_tokens, max_len, workspace, st);
+  }
+  std::vector<uintptr_t> key = {(uintptr_t)dev, (uintptr_t)d->hidden, (uintptr_t)d->heads,
+                                (uintptr_t)d->ffn, (uintptr_t)d->dtype, (uintptr_t)d->int8_gemm,
+                                (uintptr_t)n_layers, (uintptr_t)x_pad, (uintptr_t)y_pad,
+                                (uintptr_t)seq_lens, (uintptr_t)batch, (uintptr_t)max_seq,
+                                (uintptr_t)total_tokens, (uintptr_t)max_len,
+                                (uintptr_t)workspace};
+  uint32_t eps_bits;
+  memcpy(&eps_bits, &d->ln_eps, 4);
+  key.push_back(eps_bits);
+  for (int i = 0; i < n_layers; ++i) key.push_back((uintptr_t)packed_layers[i]);
+  for (size_t i = 0; i < g_graphs.size(); ++i) {
+    if (g_graphs[i].key == key) {
+      GraphEntry e = g_graphs[i];
+      g_graphs.erase(g_graphs.begin() + i);
+      g_graphs.push_back(e);
+      return status_of(hipGraphLaunch(e.exec, st));
+    }
+  }
+  if ((int)g_capture_streams.size() <= dev) g_capture_streams.resize(dev + 1, nullptr);
+  if (!g_capture_streams[dev] &&
+      hipStreamCreateWithFlags(&g_capture_streams[dev], hipStreamNonBlocking) != hipSuccess)
+    return TEL_EDEVICE;
+  hipStream_t cs = g_capture_streams[dev];
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return TEL_EDEVICE;
+  const int r = forward_enqueue(d, packed_layers, n_layers, x_pad, y_pad, seq_lens, batch,
+                                max_seq, total_tokens, max_len, workspace, cs);
+  hipGraph_t graph = nullptr;
+  const hipError_t ce = hipStreamEndCapture(cs, &graph);
+  if (r != TEL_OK || ce != hipSuccess || !graph) {
+    if (graph) hipGraphDestroy(graph);
+    return r != TEL_OK ? r : TEL_EDEVICE;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  hipGraphDestroy(graph);
+  if (ie != hipSuccess || !exec) return TEL_EDEVICE;
+  if (g_graphs.size() >= GRAPH_CACHE_MAX) {
+    // the evicted graph may still be running on some stream: let the device drain first
+    if (hipDeviceSynchronize() != hipSuccess) return TEL_EDEVICE;
+    hipGraphExecDestroy(g_graphs.front().exec);
+    g_graphs.erase(g_graphs.begin());
+  }
+  g_graphs.push_back(GraphEntry{key, exec});
+  return status_of(hipGraphLaunch(exec, st));
 }
 
 int tel_gemm_tile_configs(void) { return gemm_tile_configs(); }
