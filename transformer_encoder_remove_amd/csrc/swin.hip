@@ -3,8 +3,9 @@
 // module that takes the mask and the bias as tensors; section 3, the bias-table lookup
 // moved to preprocessing and the fMHA kernel for inference).
 //
-// One workgroup per (window, head): 4 wavefronts x 16 queries cover a window of up to 64
-// tokens (7 x 7 = 49 here; the 15 padded queries are computed and dropped). K [64][d] and
+// One workgroup per (head, run of WIN_PER_WG windows): 4 wavefronts x 16 queries cover a
+// window of up to 64 tokens (7 x 7 = 49 here; the 15 padded queries are computed and
+// dropped). K [64][d] and
 // V^T [d][64] of the window are staged in LDS; S^T = K Q^T and O^T += V^T P^T on 16x16
 // MFMAs with one query per lane, exactly as in the variable-length kernel. The
 // relative-position bias comes pre-expanded, pre-scaled and padded ([heads][N][64],
@@ -18,69 +19,72 @@
 namespace tel {
 
 constexpr int WIN_TOK = 64;   // tokens per window, padded
+constexpr int WIN_PER_WG = 4; // windows one workgroup walks through, one head
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void window_attention_kernel(const T* __restrict__ qkv,
-                                                               T* __restrict__ ctx,
-                                                               const float* __restrict__ bias_exp,
-                                                               SwinGeom g, int total_tokens,
-                                                               int heads, float scale_log2) {
+// Q fragments and the 16-byte K / V vectors of one window, held in registers: the next
+// window's are requested while the current one is computed.
+template <typename T, int D> struct WinRegs {
+  using MF = Mfma<T>;
+  static constexpr int KPL = MF::KPL, KMF = 4 * KPL, NKS = (D + KMF - 1) / KMF;
+  static constexpr int VEC = 16 / sizeof(T), VPRK = D / VEC, NVEC = WIN_TOK * VPRK;
+  static constexpr int PER = (NVEC + 255) / 256;
+  typedef T vec __attribute__((ext_vector_type(VEC)));
+  typename MF::frag q[NKS];
+  vec k[PER], v[PER];
+
+  __device__ __forceinline__ void load(const T* qkv, size_t hs, int heads, int h, int start,
+                                       int N, int D_, int tid, int qc, int lg) {
+    const T* Qh = qkv + (size_t)h * hs + (size_t)start * D;
+    const T* Kh = qkv + (size_t)(heads + h) * hs + (size_t)start * D;
+    const T* Vh = qkv + (size_t)(2 * heads + h) * hs + (size_t)start * D;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPRK, c = idx - r * VPRK;
+        const size_t off = (size_t)min(r, N - 1) * D + c * VEC;
+        k[p] = *reinterpret_cast<const vec*>(Kh + off);
+        v[p] = *reinterpret_cast<const vec*>(Vh + off);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int d0 = s * KMF + lg * KPL;
+      q[s] = (d0 < D) ? *reinterpret_cast<const typename MF::frag*>(Qh + (size_t)qc * D + d0)
+                      : typename MF::frag{};
+    }
+    (void)D_;
+  }
+  template <int LDK, int LDV>
+  __device__ __forceinline__ void stage(T* sK, T* sVt, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPRK, c = idx - r * VPRK;
+        *reinterpret_cast<vec*>(&sK[r * LDK + c * VEC]) = k[p];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sVt[(c * VEC + e) * LDV + r] = v[p][e];
+      }
+    }
+  }
+};
+
+// One window of one head, K and V^T staged in LDS: scores with the lane's bias values and
+// the shift mask, softmax, O^T += V^T P^T, output of the lane's query.
+template <typename T, int D, int LDK, int LDV>
+__device__ __forceinline__ void window_block(const T* sK, const T* sVt, const int* sReg,
+                                             const typename Mfma<T>::frag* qf,
+                                             const float (&bias)[WIN_TOK / 16][4], bool masked,
+                                             int N, int qi, int qc, float scale_log2, int lr,
+                                             int lg, T* out) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int KPL = MF::KPL, KMF = 4 * KPL;
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int LDK = D + VEC;
-  constexpr int LDV = WIN_TOK + (sizeof(T) == 4 ? 1 : 4);
   constexpr int NKS = (D + KMF - 1) / KMF;
   constexpr int NCB = D / 16;
   constexpr int NJ = WIN_TOK / 16;
-  constexpr int VPRK = D / VEC;
-  static_assert(D % 16 == 0 && D % VEC == 0, "head_dim");
-
-  __shared__ __attribute__((aligned(16))) T sK[WIN_TOK * LDK];
-  __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
-  __shared__ int sReg[WIN_TOK];                      // shift-mask region of every key
-
-  const int win = blockIdx.x, h = blockIdx.y;
-  const int N = g.N;
-  const int start = win * N;
-  const int wimg = win % g.nW;                       // window index inside its image
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const size_t hs = (size_t)total_tokens * D;
-  const T* Qh = qkv + (size_t)h * hs + (size_t)start * D;
-  const T* Kh = qkv + (size_t)(heads + h) * hs + (size_t)start * D;
-  const T* Vh = qkv + (size_t)(2 * heads + h) * hs + (size_t)start * D;
-
-  for (int idx = tid; idx < WIN_TOK * VPRK; idx += 256) {
-    const int r = idx / VPRK, v = idx - r * VPRK;
-    const int key = min(r, N - 1);
-    const Vec16<T> kv = *reinterpret_cast<const Vec16<T>*>(Kh + (size_t)key * D + v * VEC);
-    *reinterpret_cast<Vec16<T>*>(&sK[r * LDK + v * VEC]) = kv;
-    const Vec16<T> vv = *reinterpret_cast<const Vec16<T>*>(Vh + (size_t)key * D + v * VEC);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) sVt[(v * VEC + e) * LDV + r] = vv.v[e];
-  }
-
-  const int qi = wave * 16 + lr;
-  const int qc = min(qi, N - 1);
-  frag qf[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const int d0 = s * KMF + lg * KPL;
-    qf[s] = (d0 < D) ? *reinterpret_cast<const frag*>(Qh + (size_t)qc * D + d0) : frag{};
-  }
-  // Only windows in the last window row or column straddle a region border (the shifted
-  // image splits each axis at L - M and L - s, and only the last window spans them), so
-  // the mask test is skipped everywhere else; where it applies, the 64 key regions are
-  // computed once into LDS.
-  const int wy = wimg / g.nWx, wx = wimg - wy * g.nWx;
-  const bool masked = g.s > 0 && (wy == g.nW / g.nWx - 1 || wx == g.nWx - 1);
-  if (masked && tid < WIN_TOK) sReg[tid] = g.region(wimg, min(tid, N - 1));
-  const float* brow = bias_exp + ((size_t)h * N + qc) * WIN_TOK;
-  __syncthreads();
   const int qreg = masked ? sReg[qc] : 0;
-
   f32x4 sc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -95,18 +99,15 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const float4 b = *reinterpret_cast<const float4*>(brow + j * 16 + lg * 4);
-    const float bb[4] = {b.x, b.y, b.z, b.w};
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = j * 16 + lg * 4 + i;
-      float s = sc[j][i] * scale_log2 + bb[i];            // -inf for padded keys
+      float s = sc[j][i] * scale_log2 + bias[j][i];       // -inf for padded keys
       if (masked && key < N && sReg[key] != qreg) s = -INFINITY;
       sc[j][i] = s;
       mx = fmaxf(mx, s);
     }
-  }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));   // finite: a token always sees itself
   float psum = 0.f;
@@ -155,10 +156,8 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
       if constexpr (KPL > 1) o[c] = MF::mma(va, pbl, o[c]);
     }
   }
-
   if (qi < N) {
     const float inv_l = 1.f / psum;
-    T* out = ctx + (size_t)(start + qi) * (heads * D) + h * D;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
       Vec4<T> w;
@@ -166,6 +165,71 @@ __global__ __launch_bounds__(256) void window_attention_kernel(const T* __restri
       for (int i = 0; i < 4; ++i) w.v[i] = from_f32<T>(o[c][i] * inv_l);
       *reinterpret_cast<Vec4<T>*>(out + c * 16 + 4 * lg) = w;
     }
+  }
+}
+
+// Grid (ceil(windows / WIN_PER_WG), heads); 4 wavefronts x 16 queries cover a window of up
+// to 64 tokens (49 here; the padded queries are computed and dropped). The lane's bias
+// values (its query row against the 64 key slots) are the same in every window of the
+// head, so they are loaded once; each window's K and V^T are staged in LDS from the
+// register ring while the next window's Q, K, V are in flight.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void window_attention_kernel(const T* __restrict__ qkv,
+                                                               T* __restrict__ ctx,
+                                                               const float* __restrict__ bias_exp,
+                                                               SwinGeom g, int total_tokens,
+                                                               int heads, float scale_log2,
+                                                               int windows) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LDK = D + VEC;
+  constexpr int LDV = WIN_TOK + (sizeof(T) == 4 ? 1 : 4);
+  constexpr int NJ = WIN_TOK / 16;
+  static_assert(D % 16 == 0 && D % VEC == 0, "head_dim");
+
+  __shared__ __attribute__((aligned(16))) T sK[WIN_TOK * LDK];
+  __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+  __shared__ int sReg[WIN_TOK];                      // shift-mask region of every key
+
+  const int h = blockIdx.y, w0 = blockIdx.x * WIN_PER_WG;
+  const int N = g.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int qi = wave * 16 + lr, qc = min(qi, N - 1);
+  const size_t hs = (size_t)total_tokens * D;
+  const int nWy = g.nW / g.nWx;
+
+  float bias[NJ][4];
+  {
+    const float* brow = bias_exp + ((size_t)h * N + qc) * WIN_TOK;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float4 b = *reinterpret_cast<const float4*>(brow + j * 16 + lg * 4);
+      bias[j][0] = b.x; bias[j][1] = b.y; bias[j][2] = b.z; bias[j][3] = b.w;
+    }
+  }
+  WinRegs<T, D> r0, r1;
+  r0.load(qkv, hs, heads, h, w0 * N, N, D, tid, qc, lg);
+#pragma unroll
+  for (int i = 0; i < WIN_PER_WG; ++i) {
+    const int win = w0 + i;
+    if (win >= windows) break;                       // uniform across the workgroup
+    WinRegs<T, D>& cur = (i % 2 == 0) ? r0 : r1;
+    WinRegs<T, D>& nxt = (i % 2 == 0) ? r1 : r0;
+    // Only windows in the last window row or column straddle a region border (the
+    // shifted image splits each axis at L - M and L - s, and only the last window spans
+    // them), so the mask test is skipped everywhere else; where it applies, the 64 key
+    // regions are computed once into LDS.
+    const int wimg = win % g.nW, wy = wimg / g.nWx, wx = wimg - wy * g.nWx;
+    const bool masked = g.s > 0 && (wy == nWy - 1 || wx == g.nWx - 1);
+    __syncthreads();                                 // the previous window's reads are done
+    cur.template stage<LDK, LDV>(sK, sVt, tid);
+    if (masked && tid < WIN_TOK) sReg[tid] = g.region(wimg, min(tid, N - 1));
+    if (i + 1 < WIN_PER_WG && win + 1 < windows)
+      nxt.load(qkv, hs, heads, h, (win + 1) * N, N, D, tid, qc, lg);
+    __syncthreads();
+    T* out = ctx + (size_t)(win * N + qi) * (heads * D) + h * D;
+    window_block<T, D, LDK, LDV>(sK, sVt, sReg, cur.q, bias, masked, N, qi, qc, scale_log2, lr,
+                                 lg, out);
   }
 }
 
@@ -179,8 +243,9 @@ template <typename T, int D>
 static void run_win(const void* qkv, void* ctx, const float* bias, const SwinGeom& g, int windows,
                     int heads, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  window_attention_kernel<T, D><<<dim3(windows, heads), 256, 0, stream>>>(
-      (const T*)qkv, (T*)ctx, bias, g, windows * g.N, heads, scale_log2);
+  window_attention_kernel<T, D><<<dim3((windows + WIN_PER_WG - 1) / WIN_PER_WG, heads), 256, 0,
+                                  stream>>>((const T*)qkv, (T*)ctx, bias, g, windows * g.N,
+                                            heads, scale_log2, windows);
 }
 
 template <typename T>
