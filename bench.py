@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
+PEAK_INT8_TOPS = 5000.0         # dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -152,9 +153,6 @@ def main():
     # ---------------------------------------------------------------- per-kernel timing
     # Each kernel of one layer, same shapes and launch configuration as inside the stack,
     # timed with HIP events on the stream it is launched on.
-    if int8:   # the kernel-level entry points time float kernels; none for int8 here
-        cpu = None if args.no_cpu else cpu_baseline(cfg, lens, x_pad, args.cpu_seconds)
-        return emit(args, cfg, value, ms_per_step, T, max_len, None, {}, cpu)
     qkv = torch.randn(3 * T * H, device="cuda").to(tdt)
     hid = torch.randn(T, H, device="cuda").to(tdt)
     ctx = torch.empty(T, H, device="cuda", dtype=tdt)
@@ -195,6 +193,30 @@ def main():
         "gemm_ffn2_resid": (resid_gemm(ffn, layer_w["w_2"], F, H),
                             2.0 * T * H * F, 2.0 * (T * F + F * H + 2 * T * H)),
     }
+    if int8:
+        # the int8 layer's GEMMs one by one (int8 codes in, epilogues as in the layer: head
+        # split, dequantise + residual, GELU written as int8 codes); random codes and scales
+        rnd = lambda *shape: torch.randint(-127, 128, shape, device="cuda", dtype=torch.int8)
+        xq, cq, hq, fq = rnd(T, H), rnd(T, H), rnd(T, H), rnd(T, F)
+        wq = {"qkv": rnd(3 * H, H), "o": rnd(H, H), "1": rnd(F, H), "2": rnd(H, F)}
+        dqs = {n: torch.full((n,), 1e-4, device="cuda") for n in (H, 3 * H, F)}
+        qinv = torch.full((1,), 10.0, device="cuda")
+        f_codes = torch.empty(T, F, dtype=torch.int8, device="cuda")
+        kernels.update({
+            "gemm_qkv": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_QKV_SPLIT, xq, wq["qkv"], dqs[3 * H],
+                                                 b32(3 * H), qkv_o, heads=nh, stream=stream),
+                         2.0 * T * H * 3 * H, T * H + 3 * H * H + 2.0 * 3 * T * H),
+            "gemm_o_resid": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_BIAS_RESID, cq, wq["o"], dqs[H],
+                                                     b32(H), pre, resid=hid, stream=stream),
+                             2.0 * T * H * H, T * H + H * H + 2.0 * 2 * T * H),
+            "gemm_ffn1_gelu": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_BIAS_GELU, hq, wq["1"], dqs[F],
+                                                       b32(F), f_codes, qinv=qinv, out_int8=True,
+                                                       stream=stream),
+                               2.0 * T * H * F, T * H + F * H + 1.0 * T * F),
+            "gemm_ffn2_resid": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_BIAS_RESID, fq, wq["2"], dqs[H],
+                                                        b32(H), pre, resid=hid, stream=stream),
+                                2.0 * T * H * F, T * F + F * H + 2.0 * 2 * T * H),
+        })
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():
         fn()
@@ -218,10 +240,10 @@ def main():
     gemms = {k: v for k, v in per_kernel.items() if k.startswith("gemm")}
     dom = max(gemms, key=lambda k: gemms[k]["us"])
     d = per_kernel[dom]
-    peak = PEAK_FP32_TFLOPS if dt == "f32" else PEAK_FP16_TFLOPS
+    peak = PEAK_INT8_TOPS if int8 else PEAK_FP32_TFLOPS if dt == "f32" else PEAK_FP16_TFLOPS
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4),
-                "traffic": measured_traffic(args.workload, dt, dom),
+                "unit": "TOP/s" if int8 else "TFLOP/s", "frac": round(d["tflops"] / peak, 4),
+                "traffic": measured_traffic(args.workload, "i8" if int8 else dt, dom),
                 "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
     if args.calib_copy:
         calibration_copy(stream)

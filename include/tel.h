@@ -267,6 +267,18 @@ int tel_quantize_weight_i8(const void* w, int8_t* q, float* scales, int N, int K
 int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, int K,
                     void* stream);
 
+/* One GEMM of the int8 layer with its epilogue ([SW] section 3, INT8: INT8 GEMM, INT32
+ * accumulation, dequantised outputs): acc[m][n] = sum_k A[m][k] * W[n][k] over int8 codes,
+ * exact in int32, then v = acc * dq[n] + bias[n] (float32 arithmetic; dq[n] = activation
+ * scale * weight scale of column n) and the epilogue of tel_gemm: TEL_EPI_BIAS, _BIAS_GELU,
+ * _BIAS_RESID (resid fp16 [M][N]) or _QKV_SPLIT. C is fp16 ([M][N], or the head-split
+ * layout), except out_int8 != 0 (TEL_EPI_BIAS_GELU only): C receives int8 codes
+ * clamp(rne(float(fp16(v)) * *qinv), -127, 127), qinv a device scalar. A [M][K], W [N][K];
+ * K % 16 == 0, N % 4 == 0, 16-byte aligned pointers. */
+int tel_gemm_i8(int epilogue, const int8_t* A, const int8_t* W, const float* dq,
+                const float* bias, const void* resid, void* C, const float* qinv, int out_int8,
+                int M, int N, int K, int heads, void* stream);
+
 /* Shifted-window partition with LayerNorm, one gather ([SW] section 3, the hand-written
  * shift-window-partition kernel): y row r (window order: images, windows row-major,
  * tokens row-major in a window) = LN(x image row ((wy*M + py + s) mod H, (wx*M + px + s)

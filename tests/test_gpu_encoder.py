@@ -103,6 +103,19 @@ def test_bert_large_latency_split_layers(dtype):
     assert_close(y, _oracle(cfg, lens, x, ws), dtype, f"bert_large_latency {nl} layers")
 
 
+@pytest.mark.parametrize("int8", [False, True])
+def test_all_sequences_empty(int8):
+    """Every length 0 (T = 0): the stack runs no layer work and the padded output is all
+    zeros."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base"], layers=2)
+    lens = np.zeros(4, np.int64)
+    x = np.ones((4, 16, cfg["hidden"]), np.float32)
+    ws = [ti.encoder_layer_weights(cfg, i) for i in range(2)]
+    y = gpu_encoder_forward(tel, dict(cfg, batch=4, max_seq=16), lens, x, ws, int8=int8,
+                            act_amax=[[1.0] * 4] * 2)
+    assert y.shape == x.shape and not y.any()
+
+
 def test_deterministic_repeat():
     """Two runs give bitwise-identical outputs (no races in LDS staging)."""
     cfg = dict(ti.ENCODER_CONFIGS["bert_base"], batch=8)

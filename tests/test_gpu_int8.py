@@ -190,3 +190,52 @@ def test_int8_stack_codes_equal_layer_by_layer():
         cur = nxt
     torch.cuda.synchronize()
     assert np.array_equal(enc.remove_padding(y_stack, lens), host(cur))
+
+
+@pytest.mark.parametrize("epi", ["bias", "gelu", "resid", "qkv", "gelu_codes"])
+@pytest.mark.parametrize("M,N,K", [(300, 768, 768), (77, 2304, 768), (2900, 3072, 768)])
+def test_gemm_i8_epilogues(epi, M, N, K):
+    """One int8-layer GEMM with each epilogue: exact int32 products, dequantise with the
+    column scales, bias (+ GELU, + residual, head split) against the Q-oracle's steps."""
+    if epi == "qkv" and N != 2304:
+        pytest.skip("head split needs N = 3 * heads * head_dim")
+    rng = np.random.default_rng(M + N)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s_w = (np.abs(rng.standard_normal(N)) * 2e-4 + 1e-5).astype(np.float32)
+    s_a, _ = q8.act_scale(3.0)
+    dq = (np.float32(s_a) * s_w).astype(np.float32)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    r = ti.to_storage(rng.standard_normal((M, N)), "f16")
+    v = q8.dequantize(q8.int8_matmul(qa, qw), s_a, s_w, b)
+    A, W = torch.from_numpy(qa).cuda(), torch.from_numpy(qw).cuda()
+    dq_d, b_d = torch.from_numpy(dq).cuda(), torch.from_numpy(b).cuda()
+    heads = 12
+    code = {"bias": tel.TEL_EPI_BIAS, "gelu": tel.TEL_EPI_BIAS_GELU, "resid": tel.TEL_EPI_BIAS_RESID,
+            "qkv": tel.TEL_EPI_QKV_SPLIT, "gelu_codes": tel.TEL_EPI_BIAS_GELU}[epi]
+    if epi == "gelu_codes":
+        _, inv = q8.act_scale(4.0)
+        qinv = torch.tensor([inv], dtype=torch.float32, device="cuda")
+        C = torch.zeros((M, N), dtype=torch.int8, device="cuda")
+        tel.tel_gemm_i8(code, A, W, dq_d, b_d, C, qinv=qinv, out_int8=True)
+        torch.cuda.synchronize()
+        ref = q8.quantize_act(ti.to_storage(enc.gelu(v), "f16"), inv)
+        d = np.abs(C.cpu().numpy().astype(np.int32) - ref.astype(np.int32))
+        assert d.max() <= 1 and (d > 0).mean() < 5e-3, (d.max(), (d > 0).mean())
+        return
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    tel.tel_gemm_i8(code, A, W, dq_d, b_d, C, resid=dev(r, "f16") if epi == "resid" else None,
+                    heads=heads)
+    torch.cuda.synchronize()
+    got = host(C)
+    if epi == "bias":
+        ref = v
+    elif epi == "gelu":
+        ref = enc.gelu(v)
+    elif epi == "resid":
+        ref = v + r.astype(np.float64)
+    else:
+        d_h = N // 3 // heads
+        ref = v.reshape(M, 3, heads, d_h).transpose(1, 2, 0, 3)
+        got = got.reshape(-1)[: 3 * heads * M * d_h].reshape(3, heads, M, d_h)
+    assert_close(got, ref, "f16", f"int8 GEMM {epi} {M}x{N}x{K}")

@@ -75,7 +75,7 @@ def test_attention_head_dims(dtype, d):
 
 
 @pytest.mark.parametrize("lens", [[128] * 32, list(np.random.default_rng(1).integers(32, 129, 32)),
-                                  [0, 5, 0, 1], [384, 64, 200]])
+                                  [0, 5, 0, 1], [384, 64, 200], [1000, 3]])
 def test_attention_lengths(lens):
     out, ref = _attention_case(lens, 12, 64, "f16", seed=len(lens))
     assert_close(out, ref, "f16", f"attention lens={lens[:4]}")

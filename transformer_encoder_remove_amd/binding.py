@@ -34,7 +34,7 @@ EXPORTS = (
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
-    "tel_layernorm_reduce", "tel_graph_cache",
+    "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8",
 )
 TEL_SWIN_ATTN_ONLY = 1
 
@@ -114,6 +114,7 @@ _SIG = {
     "tel_gemm_partial_plan": (I, [I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
     "tel_layernorm_reduce": (I, [P, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
     "tel_graph_cache": (I, [I]),
+    "tel_gemm_i8": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -310,6 +311,16 @@ def tel_layernorm_reduce(partials, splits: int, bias, resid, y, gamma, beta, eps
         _ptr(partials), splits, _ptr(dq), _ptr(bias), _ptr(resid), dtype_code(resid.dtype),
         _ptr(y), dtype_code(y.dtype), _ptr(y32), _ptr(yq), _ptr(qinv), _ptr(gamma), _ptr(beta),
         rows, width, eps, int(round_pre), _stream(stream)))
+
+
+def tel_gemm_i8(epilogue: int, A, W, dq, bias, C, resid=None, qinv=None, out_int8=False,
+                heads: int = 1, stream=None):
+    """One int8-layer GEMM with its epilogue (A, W int8 codes; C fp16, or int8 codes)."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check("tel_gemm_i8", lib.tel_gemm_i8(
+        epilogue, _ptr(A), _ptr(W), _ptr(dq), _ptr(bias), _ptr(resid), _ptr(C), _ptr(qinv),
+        int(out_int8), M, N, K, heads, _stream(stream)))
 
 
 def tel_gemm_i8_i32(A, B, C, stream=None):

@@ -778,6 +778,29 @@ int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, 
   return status_of(launch_gemm(DT_I8, g, as_stream(stream)));
 }
 
+int tel_gemm_i8(int epilogue, const int8_t* A, const int8_t* W, const float* dq,
+                const float* bias, const void* resid, void* C, const float* qinv, int out_int8,
+                int M, int N, int K, int heads, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
+  if (epilogue < TEL_EPI_BIAS || epilogue > TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
+  if (out_int8 && epilogue != TEL_EPI_BIAS_GELU) return TEL_EINVAL;
+  if (M == 0) return TEL_OK;
+  if (!A || !W || !dq || !bias || !C || (out_int8 && !qinv)) return TEL_EINVAL;
+  if (epilogue == TEL_EPI_BIAS_RESID && !resid) return TEL_EINVAL;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(dq) || !aligned16(bias) || !aligned16(C))
+    return TEL_EINVAL;
+  if (resid && !aligned16(resid)) return TEL_EINVAL;
+  if (K % 16 || N % 4) return TEL_EUNSUPPORTED;
+  if (epilogue == TEL_EPI_QKV_SPLIT &&
+      (heads <= 0 || N % 3 || (N / 3) % heads || ((N / 3) / heads) % 4))
+    return TEL_EUNSUPPORTED;
+  GemmArgs g{epilogue, A, W, bias, resid, C, M, N, K, heads};
+  g.dq = dq;
+  g.qinv = qinv;
+  g.out_i8 = out_int8 ? 1 : 0;
+  return status_of(launch_gemm(DT_I8, g, as_stream(stream)));
+}
+
 size_t tel_swin_packed_size(const tel_swin_desc* d) {
   if (swin_supported(d) != TEL_OK) return 0;
   return swin_layout(d).total;
