@@ -868,9 +868,21 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
   void* x1 = (flags & TEL_SWIN_ATTN_ONLY) ? y : (void*)(ws + W.x1);
   void* hh = ws + W.h;
   void* f = ws + W.f;
-  // LN1 + roll(-s) + window partition, one gather
-  TEL_TRY(launch_layernorm_gather(dt, x, zw, F32(L.ln1_g), F32(L.ln1_b), T, C, d->ln_eps, g, st));
+  // LN1 + roll(-s) + window partition, one gather: on the QKV GEMM's input rows when the
+  // skinny kernel serves these shapes (no LN1 tensor at all), else a gather LayerNorm
+  const bool fuse_ln = gemm_rows_supported(dt, 3 * C, C) && gemm_rows_supported(dt, F, C);
   GemmArgs a{EPI_QKV_SPLIT, zw, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * C, C, nh};
+  if (fuse_ln) {
+    a.A = x;
+    a.ln_g = F32(L.ln1_g);
+    a.ln_b = F32(L.ln1_b);
+    a.ln_eps = d->ln_eps;
+    a.ln_gather = 1;
+    a.geom = g;
+  } else {
+    TEL_TRY(launch_layernorm_gather(dt, x, zw, F32(L.ln1_g), F32(L.ln1_b), T, C, d->ln_eps, g,
+                                    st));
+  }
   TEL_TRY(launch_gemm(dt, a, st));
   TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh, st));
   // proj + bias, window reverse + roll(+s) + residual in the epilogue
@@ -878,9 +890,17 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
   a.geom = g;
   TEL_TRY(launch_gemm(dt, a, st));
   if (flags & TEL_SWIN_ATTN_ONLY) return TEL_OK;
-  TEL_TRY(launch_layernorm(dt, dt, x1, hh, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, C, d->ln_eps,
-                           st));
+  // LN2 on fc1's input rows (or a LayerNorm kernel), fc1 + bias + GELU
   a = GemmArgs{EPI_BIAS_GELU, hh, P + L.w_1, F32(L.b_1), nullptr, f, T, F, C, nh};
+  if (fuse_ln) {
+    a.A = x1;
+    a.ln_g = F32(L.ln2_g);
+    a.ln_b = F32(L.ln2_b);
+    a.ln_eps = d->ln_eps;
+  } else {
+    TEL_TRY(launch_layernorm(dt, dt, x1, hh, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, C,
+                             d->ln_eps, st));
+  }
   TEL_TRY(launch_gemm(dt, a, st));
   a = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), x1, y, T, C, F, nh};
   TEL_TRY(launch_gemm(dt, a, st));

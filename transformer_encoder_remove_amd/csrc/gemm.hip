@@ -570,13 +570,53 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
 // 4-column epilogue above (bias, GELU, QKV split, window scatter, residual) applies as is.
 constexpr int ROWS_WG = 64;
 
-template <typename T, int KS>
+template <typename T, int KS, bool GATHER>
 __device__ __forceinline__ void rows_load(typename Mfma<T>::frag (&buf)[KS], const T* A, int M,
-                                          int row0, int lr, int lg) {
+                                          int row0, int lr, int lg, const SwinGeom& geom) {
   constexpr int K = KS * 32;
-  const T* src = A + (size_t)min(row0 + lr, M - 1) * K + lg * 8;
+  int row = min(row0 + lr, M - 1);
+  if constexpr (GATHER) row = geom.src_row(row);
+  const T* src = A + (size_t)row * K + lg * 8;
 #pragma unroll
   for (int t = 0; t < KS; ++t) buf[t] = *reinterpret_cast<const typename Mfma<T>::frag*>(src + t * 32);
+}
+
+// LayerNorm of the rows held in fragments: the 4 lanes lg = 0..3 of a row hold its K values
+// (8 per k-step each), so the two-pass statistics are the lane's own sums plus butterflies
+// over xor 16 and xor 32; the normalised values replace the fragments (rounded to T, as a
+// stored LayerNorm output would be). g, b: the lane's gamma/beta for its K/4 positions.
+template <typename T, int KS>
+__device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS],
+                                               const float (&g)[KS][8], const float (&b)[KS][8],
+                                               float eps) {
+  constexpr int K = KS * 32;
+  float v[KS][8];
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[t][e] = to_f32(buf[t][e]);
+      s += v[t][e];
+    }
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  const float mean = s * (1.f / K);
+  float q = 0.f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[t][e] -= mean;
+      q += v[t][e] * v[t][e];
+    }
+  q += __shfl_xor(q, 16, 64);
+  q += __shfl_xor(q, 32, 64);
+  const float rstd = rsqrtf(q * (1.f / K) + eps);
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) buf[t][e] = from_f32<T>(v[t][e] * rstd * g[t][e] + b[t][e]);
 }
 
 // Output fragments in groups of 6 and k in chunks of 3 steps, with scheduling barriers
@@ -616,10 +656,13 @@ __device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS]
   }
 }
 
-template <typename T, int NF, int KS, int EPI, typename TR, typename TO>
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
                                                         const T* __restrict__ W,
-                                                        EpiArgs<T, TR, TO> e) {
+                                                        EpiArgs<T, TR, TO> e,
+                                                        const float* __restrict__ ln_g,
+                                                        const float* __restrict__ ln_b,
+                                                        float ln_eps) {
   using MF = Mfma<T>;
   static_assert(MF::KPL == 8, "16-bit operands");
   constexpr int N = NF * 16, K = KS * 32, LDW = K + 8;
@@ -633,16 +676,31 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
   }
   __syncthreads();
   const int M = e.M, stride = gridDim.x * ROWS_WG;
+  // the lane's gamma / beta of the A-operand LayerNorm: k = t * 32 + lg * 8 + j
+  float lg_g[KS][8], lg_b[KS][8];
+  if constexpr (LNA) {
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const float4 gv = *reinterpret_cast<const float4*>(ln_g + t * 32 + lg * 8 + j);
+        const float4 bv = *reinterpret_cast<const float4*>(ln_b + t * 32 + lg * 8 + j);
+        lg_g[t][j] = gv.x; lg_g[t][j + 1] = gv.y; lg_g[t][j + 2] = gv.z; lg_g[t][j + 3] = gv.w;
+        lg_b[t][j] = bv.x; lg_b[t][j + 1] = bv.y; lg_b[t][j + 2] = bv.z; lg_b[t][j + 3] = bv.w;
+      }
+  }
   typename MF::frag a0[KS], a1[KS];
   int rb = blockIdx.x * ROWS_WG + wave * 16;   // this wavefront's 16 rows of the block
-  if (rb < M) rows_load<T, KS>(a0, A, M, rb, lr, lg);
-  if (rb + stride < M) rows_load<T, KS>(a1, A, M, rb + stride, lr, lg);
+  if (rb < M) rows_load<T, KS, GATHER>(a0, A, M, rb, lr, lg, e.geom);
+  if (rb + stride < M) rows_load<T, KS, GATHER>(a1, A, M, rb + stride, lr, lg, e.geom);
   for (; rb < M; rb += 2 * stride) {
+    if constexpr (LNA) rows_layernorm<T, KS>(a0, lg_g, lg_b, ln_eps);
     rows_block<T, NF, KS, EPI, TR, TO>(a0, sW, e, rb, lr, lg);
-    if (rb + 2 * stride < M) rows_load<T, KS>(a0, A, M, rb + 2 * stride, lr, lg);
+    if (rb + 2 * stride < M) rows_load<T, KS, GATHER>(a0, A, M, rb + 2 * stride, lr, lg, e.geom);
     if (rb + stride >= M) break;
+    if constexpr (LNA) rows_layernorm<T, KS>(a1, lg_g, lg_b, ln_eps);
     rows_block<T, NF, KS, EPI, TR, TO>(a1, sW, e, rb + stride, lr, lg);
-    if (rb + 3 * stride < M) rows_load<T, KS>(a1, A, M, rb + 3 * stride, lr, lg);
+    if (rb + 3 * stride < M) rows_load<T, KS, GATHER>(a1, A, M, rb + 3 * stride, lr, lg, e.geom);
   }
 }
 
@@ -650,13 +708,22 @@ template <typename T, int NF, int KS>
 static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
   const int blocks = (a.M + ROWS_WG - 1) / ROWS_WG;
   const int grid = std::min(blocks, 512);   // two workgroups per CU (<= 80 KiB of LDS each)
-#define TEL_ROWS(EPI)                                                                        \
+#define TEL_ROWS_LN(EPI, LNA, GATHER)                                                        \
   do {                                                                                       \
     EpiArgs<T, T, T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, \
                        a.geom};                                                              \
-    gemm_rows_kernel<T, NF, KS, EPI, T, T><<<grid, 256, 0, stream>>>((const T*)a.A,         \
-                                                                    (const T*)a.W, e);       \
+    gemm_rows_kernel<T, NF, KS, EPI, T, T, LNA, GATHER><<<grid, 256, 0, stream>>>(          \
+        (const T*)a.A, (const T*)a.W, e, a.ln_g, a.ln_b, a.ln_eps);                         \
   } while (0)
+#define TEL_ROWS(EPI) TEL_ROWS_LN(EPI, false, false)
+  if (a.ln_g) {   // A-operand LayerNorm: the shifted-window block's LN1 (+ partition) and LN2
+    if (!a.ln_b) return hipErrorInvalidValue;
+    if (a.epi == EPI_QKV_SPLIT && a.ln_gather) TEL_ROWS_LN(EPI_QKV_SPLIT, true, true);
+    else if (a.epi == EPI_QKV_SPLIT) TEL_ROWS_LN(EPI_QKV_SPLIT, true, false);
+    else if (a.epi == EPI_BIAS_GELU && !a.ln_gather) TEL_ROWS_LN(EPI_BIAS_GELU, true, false);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   switch (a.epi) {
     case EPI_BIAS: TEL_ROWS(EPI_BIAS); break;
     case EPI_BIAS_GELU: TEL_ROWS(EPI_BIAS_GELU); break;
@@ -666,7 +733,14 @@ static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 #undef TEL_ROWS
+#undef TEL_ROWS_LN
   return hipGetLastError();
+}
+
+bool gemm_rows_supported(int dtype, int N, int K) {
+  if (dtype != DT_F16 && dtype != DT_BF16) return false;
+  return (N == 288 && K == 96) || (N == 96 && K == 96) || (N == 384 && K == 96) ||
+         (N == 96 && K == 384);
 }
 
 // The (N, K) shapes the skinny kernel is built for; false: use the tiled kernels.
@@ -858,16 +932,19 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   if (a.splits != 1) return hipErrorInvalidValue;   // splits need an explicit configuration
+  if (a.ln_g && (dtype == DT_I8 || dtype == DT_F32)) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_I8: return run_epi_i8(pick_cfg(a, 1), a, stream);
     case DT_F16: {
       hipError_t err;
       if (launch_rows<f16>(a, stream, &err)) return err;
+      if (a.ln_g) return hipErrorInvalidValue;
       return run_epi<f16>(pick_cfg(a, 2), a, stream);
     }
     case DT_BF16: {
       hipError_t err;
       if (launch_rows<bf16>(a, stream, &err)) return err;
+      if (a.ln_g) return hipErrorInvalidValue;
       return run_epi<bf16>(pick_cfg(a, 2), a, stream);
     }
     case DT_F32: return run_epi<float>(pick_cfg(a, 4), a, stream);

@@ -44,7 +44,16 @@ struct GemmArgs {
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
   SwinGeom geom{};              // EPI_SWIN_SCATTER
   int splits = 1;               // pipelined kernel only: K split over this many workgroups
+  // LayerNorm applied to each row of A before the product (skinny kernel only, see
+  // gemm_rows_supported): A row r is LN(A[r]) * ln_g + ln_b, read from row geom.src_row(r)
+  // when ln_gather is set (the shifted-window partition)
+  const float* ln_g = nullptr;
+  const float* ln_b = nullptr;
+  float ln_eps = 0.f;
+  int ln_gather = 0;
 };
+// The (dtype, N, K) the skinny row kernel serves (the shifted-window block's projections).
+bool gemm_rows_supported(int dtype, int N, int K);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
