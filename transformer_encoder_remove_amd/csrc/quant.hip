@@ -111,21 +111,29 @@ hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, co
 }
 
 // Calibration statistic: *out = max(*out, max_i |x[i]|). Non-negative floats order like
-// their bit patterns, so an unsigned atomic max is exact and order-independent.
+// their bit patterns, so an unsigned atomic max is exact and order-independent. The
+// workgroup reduces through LDS first: one atomic per workgroup, not per wavefront (atomics
+// on one address serialise).
 template <typename T>
 __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, size_t n,
                                                      float* __restrict__ out) {
+  __shared__ float wave_max[4];
   float m = 0.f;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
     m = fmaxf(m, fabsf(to_f32(x[i])));
   m = group_max<64>(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  }
 }
 
 hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 1024) blocks = 1024;
   switch (dtype) {
     case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out); break;
     case DT_BF16: absmax_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, n, out); break;
