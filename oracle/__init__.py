@@ -21,9 +21,10 @@ Modules:
   encoder  offsets, padding removal/rebuild, the post-LN encoder layer and stack
   int8     int8-GEMM variant of the layer (quantise, int32 accumulate, dequantise)
   swin     shifted-window attention block with relative-position bias
+  sparse   2:4 structured-sparse projection weights (magnitude pruning, compressed form)
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against brute
 force, a textbook library routine, closed forms or invariants; none is "parity
 unpinned".
 """
-from . import encoder, int8, swin  # noqa: F401
+from . import encoder, int8, sparse, swin  # noqa: F401
