@@ -240,6 +240,31 @@ int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seq
                          int total_tokens, int max_len, int heads, int head_dim, int dtype,
                          void* stream);
 
+/* ------------------------------------------------------------------ 2:4 sparse weights
+ * [TRT], the paragraphs on sparsity of the Ampere architecture: weak connections are
+ * pruned, removing about half of the weights, and the matrix hardware skips their work.
+ * Here: fine-grained 2:4 structured sparsity along the input dimension k, by magnitude,
+ * executed on gfx950's sparse MFMA (v_smfmac_f32_16x16x64_{f16,bf16}). */
+
+/* Prune W [N][K] (type dtype: TEL_F16 or TEL_BF16) 2:4 and write it compressed: in every
+ * group of four consecutive k of a row the two weights of largest |w| are kept (ties to the
+ * lower k); values [N][K/2] receive them in increasing k; index [N][K/16] receives one
+ * 16-bit word per 16 k with group g's two positions (0..3) in bits 4g..4g+3, the first in
+ * the low two bits. K % 16 == 0; w and values 16-byte aligned, index 2-byte aligned. */
+int tel_prune_2of4(const void* w, void* values, uint16_t* index, int N, int K, int dtype,
+                   void* stream);
+
+/* Number of entries in the 2:4-sparse GEMM's tile table (tile_config of tel_gemm_2of4). */
+int tel_gemm_2of4_tile_configs(void);
+
+/* C = epilogue(A W^T) with W given in the compressed 2:4 form of tel_prune_2of4 (values,
+ * index), i.e. the product with the pruned matrix; epilogues, bias, resid, heads and the
+ * storage type as tel_gemm (TEL_F16 or TEL_BF16). K % 128 == 0, N % 4 == 0, 16-byte aligned
+ * pointers. tile_config: -2 automatic, else 0 .. tel_gemm_2of4_tile_configs() - 1. */
+int tel_gemm_2of4(int epilogue, int dtype, int tile_config, const void* A, const void* values,
+                  const uint16_t* index, const float* bias, const void* resid, void* C, int M,
+                  int N, int K, int heads, void* stream);
+
 /* ------------------------------------------------------------------ int8 GEMM variant
  * [SW] section 3, INT8 quantisation: inputs and weights are quantised to INT8, the GEMM
  * accumulates in INT32 and the result is dequantised; bias, residual and LayerNorm stay

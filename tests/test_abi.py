@@ -187,3 +187,31 @@ def test_partial_gemm_and_reduce_validation():
     assert call(yq=FAKE) == tel.TEL_EINVAL                                     # no qinv
     assert call(resid=FAKE_ODD) == tel.TEL_EINVAL
     assert call(eps=float("nan")) == tel.TEL_EINVAL
+
+
+def test_sparse_2of4_validation():
+    f16 = tel.TEL_F16
+    Pr = L.tel_prune_2of4
+    assert Pr(FAKE, FAKE, FAKE, 0, 64, f16, None) == tel.TEL_OK                 # empty
+    assert Pr(FAKE, FAKE, FAKE, 4, 24, f16, None) == tel.TEL_EUNSUPPORTED       # K % 16
+    assert Pr(FAKE, FAKE, FAKE, 4, 64, tel.TEL_F32, None) == tel.TEL_EUNSUPPORTED
+    assert Pr(FAKE_ODD, FAKE, FAKE, 4, 64, f16, None) == tel.TEL_EINVAL
+    assert Pr(FAKE, FAKE, ctypes.c_void_p((1 << 20) + 1), 4, 64, f16, None) == tel.TEL_EINVAL
+    assert Pr(None, FAKE, FAKE, 4, 64, f16, None) == tel.TEL_EINVAL
+    G = L.tel_gemm_2of4
+    n = tel.tel_gemm_2of4_tile_configs()
+    assert n >= 1
+    args = [tel.TEL_EPI_BIAS, f16, -2, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 64, 128, 1, None]
+    assert G(*args) == tel.TEL_OK                                              # empty
+    bad = list(args); bad[11] = 64                                             # K % 128
+    assert G(*bad) == tel.TEL_EUNSUPPORTED
+    bad = list(args); bad[2] = n                                               # tile config
+    assert G(*bad) == tel.TEL_EINVAL
+    bad = list(args); bad[2] = -1                                              # no staged kernel
+    assert G(*bad) == tel.TEL_EINVAL
+    bad = list(args); bad[1] = tel.TEL_I8
+    assert G(*bad) == tel.TEL_EUNSUPPORTED
+    bad = list(args); bad[0] = tel.TEL_EPI_BIAS_RESID; bad[9] = 4              # no residual
+    assert G(*bad) == tel.TEL_EINVAL
+    bad = list(args); bad[9] = 4; bad[3] = FAKE_ODD
+    assert G(*bad) == tel.TEL_EINVAL

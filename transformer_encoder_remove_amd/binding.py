@@ -34,7 +34,8 @@ EXPORTS = (
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
-    "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8",
+    "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
+    "tel_gemm_2of4_tile_configs", "tel_gemm_2of4",
 )
 TEL_SWIN_ATTN_ONLY = 1
 
@@ -115,6 +116,9 @@ _SIG = {
     "tel_layernorm_reduce": (I, [P, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
     "tel_graph_cache": (I, [I]),
     "tel_gemm_i8": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, P]),
+    "tel_prune_2of4": (I, [P, P, P, I, I, I, P]),
+    "tel_gemm_2of4_tile_configs": (I, []),
+    "tel_gemm_2of4": (I, [I, I, I, P, P, P, P, P, P, I, I, I, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -241,6 +245,26 @@ def tel_gemm(epilogue: int, A, W, bias, C, resid=None, heads: int = 1, stream=No
     _check("tel_gemm", lib.tel_gemm(
         epilogue, dtype_code(A.dtype), _ptr(A), _ptr(W), _ptr(bias), _ptr(resid), _ptr(C),
         M, N, K, heads, _stream(stream)))
+
+
+def tel_prune_2of4(w, values, index, stream=None):
+    """values [N][K/2] (w's dtype), index [N][K/16] (int16 tensor holding the 16-bit words)."""
+    N, K = w.shape
+    _check("tel_prune_2of4", lib.tel_prune_2of4(
+        _ptr(w), _ptr(values), _ptr(index), N, K, dtype_code(w.dtype), _stream(stream)))
+
+
+def tel_gemm_2of4_tile_configs() -> int:
+    return lib.tel_gemm_2of4_tile_configs()
+
+
+def tel_gemm_2of4(epilogue: int, A, values, index, bias, C, resid=None, heads: int = 1,
+                  tile_config: int = -2, stream=None):
+    M, K = A.shape
+    N = values.shape[0]
+    _check("tel_gemm_2of4", lib.tel_gemm_2of4(
+        epilogue, dtype_code(A.dtype), tile_config, _ptr(A), _ptr(values), _ptr(index),
+        _ptr(bias), _ptr(resid), _ptr(C), M, N, K, heads, _stream(stream)))
 
 
 def tel_gemm_tile_configs() -> int:

@@ -749,6 +749,44 @@ int tel_gemm(int epilogue, int dtype, const void* A, const void* W, const float*
   return tel_gemm_ex(epilogue, dtype, -2, A, W, bias, resid, C, M, N, K, heads, stream);
 }
 
+int tel_prune_2of4(const void* w, void* values, uint16_t* index, int N, int K, int dtype,
+                   void* stream) {
+  if (dtype != DT_F16 && dtype != DT_BF16) return TEL_EUNSUPPORTED;
+  if (N < 0 || K <= 0) return TEL_EINVAL;
+  if (K % 16) return TEL_EUNSUPPORTED;
+  if (N == 0) return TEL_OK;
+  if (!w || !values || !index || !aligned16(w) || !aligned16(values) || ((uintptr_t)index & 1u))
+    return TEL_EINVAL;
+  return status_of(launch_prune_2of4(dtype, w, values, index, N, K, as_stream(stream)));
+}
+
+int tel_gemm_2of4_tile_configs(void) { return gemm_sparse_tile_configs(); }
+
+int tel_gemm_2of4(int epilogue, int dtype, int tile_config, const void* A, const void* values,
+                  const uint16_t* index, const float* bias, const void* resid, void* C, int M,
+                  int N, int K, int heads, void* stream) {
+  if (dtype != DT_F16 && dtype != DT_BF16) return TEL_EUNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
+  if (epilogue < TEL_EPI_BIAS || epilogue > TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
+  if (tile_config < -2 || tile_config == -1 || tile_config >= gemm_sparse_tile_configs())
+    return TEL_EINVAL;
+  if (K % 128 || N % 4) return TEL_EUNSUPPORTED;
+  if (epilogue == TEL_EPI_QKV_SPLIT &&
+      (heads <= 0 || N % 3 || (N / 3) % heads || ((N / 3) / heads) % 4))
+    return TEL_EUNSUPPORTED;
+  if (M == 0) return TEL_OK;
+  if (!A || !values || !index || !bias || !C) return TEL_EINVAL;
+  if (epilogue == TEL_EPI_BIAS_RESID && !resid) return TEL_EINVAL;
+  if (!aligned16(A) || !aligned16(values) || !aligned16(index) || !aligned16(bias) ||
+      !aligned16(C) || (resid && !aligned16(resid)))
+    return TEL_EINVAL;
+  GemmArgs g{epilogue, A, values, bias, resid, C, M, N, K, heads};
+  g.w_idx = index;
+  const hipStream_t st = as_stream(stream);
+  return status_of(tile_config == -2 ? launch_gemm(dtype, g, st)
+                                     : launch_gemm_cfg(dtype, tile_config, g, st));
+}
+
 int tel_quantize_i8(const void* x, int8_t* q, size_t n, float inv_scale, int dtype,
                     void* stream) {
   if (!float_type(dtype)) return TEL_EUNSUPPORTED;

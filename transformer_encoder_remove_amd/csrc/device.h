@@ -10,6 +10,8 @@ typedef __bf16 bf16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -69,6 +71,32 @@ template <> struct Mfma<int8_t> {
   typedef i32x4 acc;
   __device__ __forceinline__ static acc mma(frag a, frag b, acc c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------ sparse MFMA 16x16x64
+// D[16][16] += A[16][64] * B[64][16] with A 2:4-sparse along k (two non-zeros in every
+// group of four), gfx950 v_smfmac_f32_16x16x64_{f16,bf16}. Lane l (row l % 16, lane group
+// a = l / 16) holds the 8 kept values of A row l % 16 at dense k [16a, 16a + 16), two per
+// group of four in increasing k, and in bits 4g .. 4g+3 of its index word the positions
+// (0..3) of the two values of group g (first in the low two bits). B: lane l holds column
+// l % 16 at k [8a, 8a + 8) in elements 0..7 and k [32 + 8a, 32 + 8a + 8) in elements 8..15.
+// D as for the dense shapes. (Layout established by probing the instruction.)
+template <typename T> struct Smfma;
+template <> struct Smfma<f16> {
+  typedef f16x8 afrag;
+  typedef f16x16 bfrag;
+  typedef f32x4 acc;
+  __device__ __forceinline__ static acc mma(afrag a, bfrag b, acc c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, idx, 0, 0);
+  }
+};
+template <> struct Smfma<bf16> {
+  typedef bf16x8 afrag;
+  typedef bf16x16 bfrag;
+  typedef f32x4 acc;
+  __device__ __forceinline__ static acc mma(afrag a, bfrag b, acc c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
   }
 };
 

@@ -324,6 +324,110 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return x * per + min(x, extra) + i;
 }
 
+// Epilogue of the pipelined kernels, for one compute wavefront's TM x TN accumulators
+// (lane: 4 consecutive columns n of one row m per 16x16 block, the MFMA output layout).
+template <int EPI, typename T, typename TR, typename TO, int TM, int TN, typename ACC, int FN,
+          int FM>
+__device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* smem,
+                                              const EpiArgs<T, TR, TO>& e, int m0, int n0,
+                                              int wm, int wn, int wave, int lane) {
+  const int M = e.M, N = e.N;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int LDC = TN + 4;                       // floats per staged epilogue row
+  // Epilogue through LDS. Every copy has landed and every real fragment read is done
+  // (the producers drained before the last barrier), so the ring is free: each wavefront
+  // parks its TM x TN accumulators there (row m, 4 consecutive n per lane), then reads
+  // them back as 8 consecutive columns per lane so that 8 lanes cover one 128-byte row
+  // segment of the output, and applies the epilogue per 8-column chunk.
+  float* stg = reinterpret_cast<float*>(smem) + wave * TM * LDC;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      float4 v;
+      if constexpr (std::is_same<T, int8_t>::value) {
+        v = make_float4(__int_as_float(acc[i][j][0]), __int_as_float(acc[i][j][1]),
+                        __int_as_float(acc[i][j][2]), __int_as_float(acc[i][j][3]));
+      } else {
+        v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+      *reinterpret_cast<float4*>(stg + (j * 16 + lr) * LDC + i * 16 + lg * 4) = v;
+    }
+  // Lane -> (row rr of every pass, 8-column chunk c8): the chunk is fixed per lane, so
+  // the column constants are loaded once; RP rows per pass, lanes past RP * CPR idle.
+  constexpr int CPR = TN / 8;
+  constexpr int RP = 64 / CPR;
+  constexpr int NPASS = (TM + RP - 1) / RP;
+  constexpr int GP = NPASS < 8 ? NPASS : 8;   // passes whose residuals are loaded together
+  static_assert(TN % 8 == 0 && CPR <= 64 && NPASS % GP == 0, "epilogue chunking");
+  const int c8 = lane % CPR, rr = lane / CPR;
+  const int n = n0 + wn * TN + c8 * 8;
+  const bool lane_on = rr < RP && n < N;
+  const bool full8 = n + 8 <= N && (EPI != EPI_QKV_SPLIT || ((N / 3) / e.heads) % 8 == 0);
+  constexpr bool IS_I8 = std::is_same<T, int8_t>::value;
+  constexpr bool HAS_R = EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER;
+  float bb[8], dd[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bb[i] = dd[i] = 0.f;
+  if constexpr (EPI != EPI_RAW_I32 && EPI != EPI_PARTIAL) {
+    if (lane_on && full8) {
+      const float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
+      const float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
+      bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+      bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+      if constexpr (IS_I8) {
+        const float4 d0 = *reinterpret_cast<const float4*>(e.dq + n);
+        const float4 d1 = *reinterpret_cast<const float4*>(e.dq + n + 4);
+        dd[0] = d0.x; dd[1] = d0.y; dd[2] = d0.z; dd[3] = d0.w;
+        dd[4] = d1.x; dd[5] = d1.y; dd[6] = d1.z; dd[7] = d1.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NPASS / GP; ++g) {
+    // residual rows of GP passes first (loads issued back to back), then the stores
+    Vec8<TR> rv[GP];
+    if constexpr (HAS_R) {
+#pragma unroll
+      for (int q = 0; q < GP; ++q) {
+        const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
+        if (lane_on && full8 && r < TM && m < M) {
+          size_t row = (size_t)m;
+          if constexpr (EPI == EPI_SWIN_SCATTER) row = (size_t)e.geom.src_row(m);
+          rv[q] = *reinterpret_cast<const Vec8<TR>*>(e.resid + row * N + n);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GP; ++q) {
+      const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
+      if (!lane_on || r >= TM || m >= M) continue;
+      float v[8];
+      const float4 a0 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8);
+      const float4 a1 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8 + 4);
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+      if (full8) {
+        epilogue_apply8<EPI, T, TR, TO>(e, m, n, v, bb, dd, rv[q]);
+      } else {   // ragged N (N % 8 == 4) or head_dim % 8 == 4: two 4-column stores
+        ACC lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (IS_I8) {
+            lo[i] = __float_as_int(v[i]);
+            hi[i] = __float_as_int(v[4 + i]);
+          } else {
+            lo[i] = v[i];
+            hi[i] = v[4 + i];
+          }
+        }
+        epilogue_store<EPI, T, TR, TO>(e, m, n, lo);
+        if (n + 4 < N) epilogue_store<EPI, T, TR, TO>(e, m, n + 4, hi);
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
 __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
     const T* __restrict__ A, const T* __restrict__ W, int K, int splits, int gn,
@@ -463,99 +567,160 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   }
 #undef TEL_PIPE_FRAGS
 
-  // Epilogue through LDS. Every copy has landed and every real fragment read is done
-  // (the producers drained before the last barrier), so the ring is free: each wavefront
-  // parks its TM x TN accumulators there (row m, 4 consecutive n per lane), then reads
-  // them back as 8 consecutive columns per lane so that 8 lanes cover one 128-byte row
-  // segment of the output, and applies the epilogue per 8-column chunk.
-  float* stg = reinterpret_cast<float*>(smem) + wave * TM * LDC;
+  pipe_epilogue<EPI, T, TR, TO, TM, TN>(acc, smem, e, m0, n0, wm, wn, wave, lane);
+}
+
+// ------------------------------------------------------------------ 2:4 sparse weights
+// C = epilogue(A W^T) with W pruned 2:4 along k and stored compressed: Wv [N][K/2] (the two
+// kept weights of every group of four, increasing k) and Wi [N][K/16] (one 16-bit word per
+// 16 k; group g's two positions in bits 4g..4g+3), which is the operand form of the sparse
+// MFMA (Smfma). The weight tile is the sparse A operand, so the epilogue is the dense
+// kernel's. Same pipeline as gemm_nt_pipe_kernel, with 128 dense k per slice: a stage holds
+// the activation rows (256 bytes: two 128-byte halves, chunk c of row r in slot c ^ (r % 8)
+// like the dense rows), the compressed weight rows (128 bytes, same swizzle) and the index
+// rows (16 bytes), each part a whole number of 1 KiB copy blocks; one sparse MFMA covers
+// 64 dense k, two per slice. Half the weight bytes cross HBM and LDS, and each MFMA does
+// the work of two dense ones.
+template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
+__global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_kernel(
+    const T* __restrict__ A, const T* __restrict__ Wv, const uint16_t* __restrict__ Wi, int K,
+    int gn, EpiArgs<T, TR, TO> e) {
+  using SM = Smfma<T>;
+  typedef typename SM::afrag afrag;
+  typedef typename SM::bfrag bfrag;
+  constexpr int NW = WM * WN;
+  constexpr int BK = 128;                           // dense k per slice
+  constexpr int NB_A = BM / 4, NB_W = BN / 8, NB_I = BN / 64;   // 1 KiB copy blocks
+  constexpr int NB = NB_A + NB_W + NB_I;
+  constexpr int LJ = NB / PIPE_PRODUCERS;
+  constexpr int STAGE = NB * 1024;
+  constexpr int W_OFF = NB_A * 1024, I_OFF = (NB_A + NB_W) * 1024;
+  constexpr int INFLIGHT = LJ * (S - 2) < 63 ? LJ * (S - 2) : 63;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  static_assert(BN % 64 == 0 && BM % 8 == 0 && NB % PIPE_PRODUCERS == 0, "copy split");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && S >= 2, "wave tile, stages");
+  constexpr int LDC = TN + 4;
+  constexpr int STAGED = TM * LDC * 4 * NW;
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE > STAGED ? S * STAGE : STAGED];
+
+  const int M = e.M, N = e.N;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int g = tile / (tiles_m * gn), r = tile - g * (tiles_m * gn);
+  const int gw = min(gn, tiles_n - g * gn);
+  const int tm = r / gw, tn = g * gn + (r - (r / gw) * gw);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nk = K / BK;
+
+  if (wave >= NW) {
+    // ---------------- producer: block b = p + PIPE_PRODUCERS * j of every slice; lane i of
+    // a block fills bytes 16 i .. 16 i + 15 of it
+    const int p = wave - NW;
+    const char* src[LJ];
+    int step[LJ];                                   // bytes of the block's rows per slice
+    const int sub = lane >> 3, slot = lane & 7;
+#pragma unroll
+    for (int j = 0; j < LJ; ++j) {
+      const int b = p + PIPE_PRODUCERS * j;
+      if (b < NB_A) {                               // activation: half rows 8b .. 8b + 7
+        const int hr = 8 * b + sub, row = hr >> 1, half = hr & 1;
+        const int chunk = slot ^ (row & 7);
+        src[j] = reinterpret_cast<const char*>(A + (size_t)min(m0 + row, M - 1) * K +
+                                               half * 64 + chunk * 8);
+        step[j] = BK * 2;
+      } else if (b < NB_A + NB_W) {                 // compressed weights: rows 8 b' ..
+        const int row = 8 * (b - NB_A) + sub, chunk = slot ^ (row & 7);
+        src[j] = reinterpret_cast<const char*>(Wv + (size_t)min(n0 + row, N - 1) * (K / 2) +
+                                               chunk * 8);
+        step[j] = BK;
+      } else {                                      // index words: rows 64 b'' + lane
+        const int row = 64 * (b - NB_A - NB_W) + lane;
+        src[j] = reinterpret_cast<const char*>(Wi + (size_t)min(n0 + row, N - 1) * (K / 16));
+        step[j] = BK / 8;
+      }
+    }
+    auto issue = [&](int slot_no, int data) {
+      char* dst = smem + (slot_no % S) * STAGE + p * 1024;
+#pragma unroll
+      for (int j = 0; j < LJ; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src[j] + (size_t)data * step[j]),
+            (void __attribute__((address_space(3)))*)(dst + j * PIPE_PRODUCERS * 1024), 16, 0, 0);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue(s, min(s, nk - 1));
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<INFLIGHT>();                   // slice kt has landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(kt + S - 1, min(kt + S - 1, nk - 1));   // into the stage of slice kt - 1
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // matches the compute wavefronts' final barrier
+    return;
+  }
+
+  // ---------------- compute wavefronts
+  const int wm = wave % WM, wn = wave / WM;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int xr = lr & 7;
+  const int rowA = (wm * TM + lr) * 256;
+  const int rowW = W_OFF + (wn * TN + lr) * 128, rowI = I_OFF + (wn * TN + lr) * 16;
+  afrag fa[2][FN];
+  int fi[2][FN];
+  bfrag fb[2][FM];
+#define TEL_SP_FRAGS(buf, slice, kk)                                                        \
+  do {                                                                                      \
+    const char* st_ = smem + ((slice) % S) * STAGE;                                         \
+    const int wc_ = ((((kk) * 4 + lg) ^ xr) * 16);                                          \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                        \
+      fa[buf][i] = *reinterpret_cast<const afrag*>(st_ + rowW + i * 16 * 128 + wc_);        \
+      fi[buf][i] = *reinterpret_cast<const uint16_t*>(st_ + rowI + i * 16 * 16 +            \
+                                                      ((kk) * 4 + lg) * 2);                 \
+    }                                                                                       \
+    _Pragma("unroll") for (int j = 0; j < FM; ++j) {                                        \
+      const char* a_ = st_ + rowA + j * 16 * 256 + (kk) * 128;                              \
+      const afrag lo_ = *reinterpret_cast<const afrag*>(a_ + ((lg ^ xr) * 16));             \
+      const afrag hi_ = *reinterpret_cast<const afrag*>(a_ + (((lg + 4) ^ xr) * 16));       \
+      fb[buf][j] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,  \
+                                           12, 13, 14, 15);                                 \
+    }                                                                                       \
+  } while (0)
+
+  typename SM::acc acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      float4 v;
-      if constexpr (std::is_same<T, int8_t>::value) {
-        v = make_float4(__int_as_float(acc[i][j][0]), __int_as_float(acc[i][j][1]),
-                        __int_as_float(acc[i][j][2]), __int_as_float(acc[i][j][3]));
+    for (int j = 0; j < FM; ++j) acc[i][j] = typename SM::acc{};
+
+  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads));
+  __builtin_amdgcn_s_barrier();                     // slice 0 has landed
+  asm volatile("" ::: "memory");
+  TEL_SP_FRAGS(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int cur = kk & 1;
+      if (kk == 0) {
+        TEL_SP_FRAGS(1, kt, 1);
       } else {
-        v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        wait_lgkmcnt0();                            // reads of slice kt are done
+        __builtin_amdgcn_s_barrier();               // slice kt + 1 has landed
+        asm volatile("" ::: "memory");
+        TEL_SP_FRAGS(0, min(kt + 1, nk - 1), 0);
       }
-      *reinterpret_cast<float4*>(stg + (j * 16 + lr) * LDC + i * 16 + lg * 4) = v;
-    }
-  // Lane -> (row rr of every pass, 8-column chunk c8): the chunk is fixed per lane, so
-  // the column constants are loaded once; RP rows per pass, lanes past RP * CPR idle.
-  constexpr int CPR = TN / 8;
-  constexpr int RP = 64 / CPR;
-  constexpr int NPASS = (TM + RP - 1) / RP;
-  constexpr int GP = NPASS < 8 ? NPASS : 8;   // passes whose residuals are loaded together
-  static_assert(TN % 8 == 0 && CPR <= 64 && NPASS % GP == 0, "epilogue chunking");
-  const int c8 = lane % CPR, rr = lane / CPR;
-  const int n = n0 + wn * TN + c8 * 8;
-  const bool lane_on = rr < RP && n < N;
-  const bool full8 = n + 8 <= N && (EPI != EPI_QKV_SPLIT || ((N / 3) / e.heads) % 8 == 0);
-  constexpr bool IS_I8 = std::is_same<T, int8_t>::value;
-  constexpr bool HAS_R = EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER;
-  float bb[8], dd[8];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bb[i] = dd[i] = 0.f;
-  if constexpr (EPI != EPI_RAW_I32 && EPI != EPI_PARTIAL) {
-    if (lane_on && full8) {
-      const float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
-      const float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
-      bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
-      bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-      if constexpr (IS_I8) {
-        const float4 d0 = *reinterpret_cast<const float4*>(e.dq + n);
-        const float4 d1 = *reinterpret_cast<const float4*>(e.dq + n + 4);
-        dd[0] = d0.x; dd[1] = d0.y; dd[2] = d0.z; dd[3] = d0.w;
-        dd[4] = d1.x; dd[5] = d1.y; dd[6] = d1.z; dd[7] = d1.w;
-      }
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = SM::mma(fa[cur][i], fb[cur][j], acc[i][j], fi[cur][i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-#pragma unroll
-  for (int g = 0; g < NPASS / GP; ++g) {
-    // residual rows of GP passes first (loads issued back to back), then the stores
-    Vec8<TR> rv[GP];
-    if constexpr (HAS_R) {
-#pragma unroll
-      for (int q = 0; q < GP; ++q) {
-        const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
-        if (lane_on && full8 && r < TM && m < M) {
-          size_t row = (size_t)m;
-          if constexpr (EPI == EPI_SWIN_SCATTER) row = (size_t)e.geom.src_row(m);
-          rv[q] = *reinterpret_cast<const Vec8<TR>*>(e.resid + row * N + n);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < GP; ++q) {
-      const int r = rr + RP * (g * GP + q), m = m0 + wm * TM + r;
-      if (!lane_on || r >= TM || m >= M) continue;
-      float v[8];
-      const float4 a0 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8);
-      const float4 a1 = *reinterpret_cast<const float4*>(stg + r * LDC + c8 * 8 + 4);
-      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
-      if (full8) {
-        epilogue_apply8<EPI, T, TR, TO>(e, m, n, v, bb, dd, rv[q]);
-      } else {   // ragged N (N % 8 == 4) or head_dim % 8 == 4: two 4-column stores
-        typedef typename MF::acc ACC;
-        ACC lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (IS_I8) {
-            lo[i] = __float_as_int(v[i]);
-            hi[i] = __float_as_int(v[4 + i]);
-          } else {
-            lo[i] = v[i];
-            hi[i] = v[4 + i];
-          }
-        }
-        epilogue_store<EPI, T, TR, TO>(e, m, n, lo);
-        if (n + 4 < N) epilogue_store<EPI, T, TR, TO>(e, m, n + 4, hi);
-      }
-    }
-  }
+#undef TEL_SP_FRAGS
+  pipe_epilogue<EPI, T, TR, TO, TM, TN>(acc, smem, e, m0, n0, wm, wn, wave, lane);
 }
 
 // ------------------------------------------------------------------ skinny GEMMs
@@ -773,6 +938,14 @@ constexpr PipeCfg PIPE_CFGS[] = {
 };
 constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 
+// Tiles of the 2:4-sparse kernel (stage = BM/4 + BN/8 + BN/64 KiB; an even block count).
+constexpr PipeCfg SP_CFGS[] = {
+    {64, 128, 2, 4, 4},    // 0: 8 waves, wave tile 32x32, 136 KiB
+    {128, 128, 2, 2, 3},   // 1: 4 waves, wave tile 64x64, 150 KiB
+    {64, 256, 2, 4, 2},    // 2: 8 waves, wave tile 32x64, 104 KiB
+};
+constexpr int N_SP_CFGS = sizeof(SP_CFGS) / sizeof(SP_CFGS[0]);
+
 template <typename T, int BM, int BN, int WM, int WN, int EPI, typename TR, typename TO>
 static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
@@ -812,6 +985,51 @@ static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
       <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>(
           (const T*)a.A, (const T*)a.W, a.K, a.splits, xcd_group_width(tm, tn, c.bm, c.bn), e);
+}
+
+template <typename T, int C, int EPI, typename TR, typename TO>
+static void launch_sp(const GemmArgs& a, hipStream_t stream) {
+  constexpr PipeCfg c = SP_CFGS[C];
+  EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
+  const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
+  gemm_sp_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
+      <<<tm * tn, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>(
+          (const T*)a.A, (const T*)a.W, a.w_idx, a.K, xcd_group_width(tm, tn, c.bm, c.bn), e);
+}
+
+template <typename T, int EPI, typename TR, typename TO>
+static void launch_sp_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
+  switch (cfg) {
+    case 0: launch_sp<T, 0, EPI, TR, TO>(a, stream); break;
+    case 1: launch_sp<T, 1, EPI, TR, TO>(a, stream); break;
+    default: launch_sp<T, 2, EPI, TR, TO>(a, stream); break;
+  }
+}
+
+template <typename T>
+static hipError_t run_epi_sp(int cfg, const GemmArgs& a, hipStream_t stream) {
+  switch (a.epi) {
+    case EPI_BIAS: launch_sp_cfg<T, EPI_BIAS, T, T>(cfg, a, stream); break;
+    case EPI_BIAS_GELU: launch_sp_cfg<T, EPI_BIAS_GELU, T, T>(cfg, a, stream); break;
+    case EPI_QKV_SPLIT: launch_sp_cfg<T, EPI_QKV_SPLIT, T, T>(cfg, a, stream); break;
+    case EPI_BIAS_RESID:
+      if constexpr (std::is_same<T, bf16>::value) {
+        if (a.resid_f32 && a.out_f32) {
+          launch_sp_cfg<T, EPI_BIAS_RESID, float, float>(cfg, a, stream);
+          break;
+        }
+        if (a.out_f32 && !a.resid_f32) {
+          launch_sp_cfg<T, EPI_BIAS_RESID, T, float>(cfg, a, stream);
+          break;
+        }
+      }
+      if (a.resid_f32 || a.out_f32) return hipErrorInvalidValue;
+      launch_sp_cfg<T, EPI_BIAS_RESID, T, T>(cfg, a, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // cfg < 0: register-staged 64x64 kernel; otherwise PIPE_CFGS[cfg].
@@ -929,9 +1147,42 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
   return sp;
 }
 
+// Sparse tile choice: the dense cost model's rounds of 256 tiles, with the loop rate of a
+// sparse MFMA step (twice the dense k per instruction) and each tile's efficiency.
+static int pick_sp_cfg(const GemmArgs& a) {
+  constexpr double EFF[N_SP_CFGS] = {0.62, 0.8, 0.75};
+  constexpr double FIXED_US = 3.5, CUS = 256, RATE = 2 * 3.19e6;
+  int best = 0;
+  double best_us = -1;
+  for (int c = 0; c < N_SP_CFGS; ++c) {
+    const PipeCfg& p = SP_CFGS[c];
+    const double tiles = (double)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
+    const double us = std::ceil(tiles / CUS) * ((double)p.bm * p.bn * a.K / (RATE * EFF[c]) + FIXED_US);
+    if (best_us < 0 || us < best_us) {
+      best_us = us;
+      best = c;
+    }
+  }
+  return best;
+}
+
+static bool sparse_ok(int dtype, const GemmArgs& a) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && a.K % 128 == 0 && a.splits == 1 && !a.ln_g &&
+         (a.epi == EPI_BIAS || a.epi == EPI_BIAS_GELU || a.epi == EPI_BIAS_RESID ||
+          a.epi == EPI_QKV_SPLIT);
+}
+
+int gemm_sparse_tile_configs() { return N_SP_CFGS; }
+
+static hipError_t launch_gemm_sparse(int dtype, int cfg, const GemmArgs& a, hipStream_t stream) {
+  if (!sparse_ok(dtype, a) || cfg < 0 || cfg >= N_SP_CFGS) return hipErrorInvalidValue;
+  return dtype == DT_F16 ? run_epi_sp<f16>(cfg, a, stream) : run_epi_sp<bf16>(cfg, a, stream);
+}
+
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   if (a.splits != 1) return hipErrorInvalidValue;   // splits need an explicit configuration
+  if (a.w_idx) return launch_gemm_sparse(dtype, pick_sp_cfg(a), a, stream);
   if (a.ln_g && (dtype == DT_I8 || dtype == DT_F32)) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_I8: return run_epi_i8(pick_cfg(a, 1), a, stream);
@@ -957,6 +1208,7 @@ int gemm_tile_configs() { return N_PIPE_CFGS; }
 // Explicit configuration (tuning and tests): cfg in [-1, N_PIPE_CFGS).
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
+  if (a.w_idx) return launch_gemm_sparse(dtype, cfg, a, stream);   // cfg: SP_CFGS entry
   if (cfg < -1 || cfg >= N_PIPE_CFGS) return hipErrorInvalidValue;
   const int es = dtype_size(dtype);
   if (cfg >= 0 && (a.K * es) % 128) return hipErrorInvalidValue;

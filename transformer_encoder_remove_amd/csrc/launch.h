@@ -51,6 +51,9 @@ struct GemmArgs {
   const float* ln_b = nullptr;
   float ln_eps = 0.f;
   int ln_gather = 0;
+  // 2:4-sparse weights (f16/bf16, K % 128 == 0): W holds the kept values [N][K/2] and
+  // w_idx the 16-bit index words [N][K/16] (the form launch_prune_2of4 writes)
+  const uint16_t* w_idx = nullptr;
 };
 // The (dtype, N, K) the skinny row kernel serves (the shifted-window block's projections).
 bool gemm_rows_supported(int dtype, int N, int K);
@@ -58,6 +61,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
 int gemm_tile_configs();
+int gemm_sparse_tile_configs();   // tile table of the 2:4-sparse kernel
 // Tile configuration and number of k-splits for a partial-sum GEMM (EPI_PARTIAL) of this
 // shape; returns the splits (>= 1) and sets *cfg.
 int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg);
@@ -105,6 +109,12 @@ hipError_t launch_window_attention(int dtype, const void* qkv_split, void* ctx,
 // bias_exp[h][p][q] = table[idx(p, q)][h] * log2(e) for q < N = M * M, -inf for q >= N.
 hipError_t launch_expand_rel_bias(int dtype, const void* table, float* bias_exp, int M, int heads,
                                   hipStream_t stream);
+
+// sparse.hip: 2:4 magnitude pruning of W [N][K] (K % 16 == 0) into kept values [N][K/2]
+// and 16-bit index words [N][K/16] (two largest |w| of every group of four along k, ties to
+// the lower k; group g of a word in bits 4g..4g+3, first position in the low two bits).
+hipError_t launch_prune_2of4(int dtype, const void* w, void* values, uint16_t* index, int N,
+                             int K, hipStream_t stream);
 
 // prepare.hip
 hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);
