@@ -9,7 +9,9 @@ prepared weights are resident in HBM before the timed region. Prints ONE JSON li
 Other workloads (same line format, measured the same way): bert_large_tput,
 bert_large_latency (24 fp16 layers), bert_base_int8 (int8 GEMMs; static activation
 scales from tel_encoder_calibrate on the same batch, i.e. post-training calibration,
-outside the timed region), swin_t_stage1 (one shifted-window block, tokens/s per block).
+outside the timed region), bert_base_sparse (the bert_base layers with their projection
+matrices pruned 2:4 when prepared, on the sparse MFMA), swin_t_stage1 (one shifted-window
+block, tokens/s per block).
 
 Also measured here, each with HIP events on the stream its kernel is launched on:
 the average duration of every kernel of one layer (same shapes, launched through the
@@ -73,6 +75,7 @@ def main():
     if args.dtype:
         cfg["dtype"] = args.dtype
     int8 = bool(cfg.get("int8"))
+    sparse = bool(cfg.get("sparse"))
     dt = cfg["dtype"]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
     B, S, H, nh, F, NL = (cfg["batch"], cfg["max_seq"], cfg["hidden"], cfg["heads"], cfg["ffn"],
@@ -83,8 +86,8 @@ def main():
     lens, x_pad = ti.encoder_input(cfg)
     T, max_len = int(lens.sum()), int(lens.max())
     log(f"[bench] workload {args.workload}: B={B} S={S} T={T} H={H} heads={nh} F={F} layers={NL} "
-        f"{dt}{' int8 GEMMs' if int8 else ''}")
-    desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS)
+        f"{dt}{' int8 GEMMs' if int8 else ''}{' 2:4-sparse weights' if sparse else ''}")
+    desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS, sparse_2of4=sparse)
     psize = tel.tel_encoder_packed_size(desc)
     packed, layer_w, dws = [], [], []
     for i in range(NL):
@@ -217,6 +220,32 @@ def main():
                                                         b32(H), pre, resid=hid, stream=stream),
                                 2.0 * T * H * F, T * F + F * H + 2.0 * 2 * T * H),
         })
+    if sparse:
+        # the 2:4 layer's GEMMs (compressed weights of layer 0's matrices, as prepared);
+        # flops count the kept weights only (half the dense product), bytes the compressed
+        # weights (values + 16-bit index words: 9/16 of the dense weight bytes)
+        comp = {}
+        for k, (n_, k_) in {"w_qkv": (3 * H, H), "w_o": (H, H), "w_1": (F, H),
+                            "w_2": (H, F)}.items():
+            v_ = torch.empty((n_, k_ // 2), dtype=tdt, device="cuda")
+            i_ = torch.empty((n_, k_ // 16), dtype=torch.int16, device="cuda")
+            tel.tel_prune_2of4(layer_w[k], v_, i_)
+            comp[k] = (v_, i_)
+        wb = lambda n_, k_: 2.0 * n_ * k_ * 9 / 16
+        kernels.update({
+            "gemm_qkv": (lambda: tel.tel_gemm_2of4(tel.TEL_EPI_QKV_SPLIT, hid, *comp["w_qkv"],
+                                                   b32(3 * H), qkv_o, heads=nh, stream=stream),
+                         T * H * 3 * H, 2.0 * (T * H + 3 * T * H) + wb(3 * H, H)),
+            "gemm_o_resid": (lambda: tel.tel_gemm_2of4(tel.TEL_EPI_BIAS_RESID, ctx, *comp["w_o"],
+                                                       b32(H), pre, resid=hid, stream=stream),
+                             T * H * H, 2.0 * 3 * T * H + wb(H, H)),
+            "gemm_ffn1_gelu": (lambda: tel.tel_gemm_2of4(tel.TEL_EPI_BIAS_GELU, hid, *comp["w_1"],
+                                                         b32(F), ffo, stream=stream),
+                               T * H * F, 2.0 * (T * H + T * F) + wb(F, H)),
+            "gemm_ffn2_resid": (lambda: tel.tel_gemm_2of4(tel.TEL_EPI_BIAS_RESID, ffn, *comp["w_2"],
+                                                          b32(H), pre, resid=hid, stream=stream),
+                                T * H * F, 2.0 * (T * F + 2 * T * H) + wb(H, F)),
+        })
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():
         fn()
@@ -315,7 +344,9 @@ def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, l
         "dtype": "i8" if int8 else cfg["dtype"],
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
         "config": {"workload": f"{args.workload}: {NL}-layer post-LN encoder"
-                               f"{' with int8 GEMMs' if int8 else ''}, offsets + padding removal "
+                               f"{' with int8 GEMMs' if int8 else ''}"
+                               f"{' with 2:4-sparse projection weights' if cfg.get('sparse') else ''}"
+                               f", offsets + padding removal "
                                f"+ layers + rebuild", "batch": cfg["batch"],
                    "max_seq": cfg["max_seq"], "valid_tokens": T, "max_len": max_len,
                    "hidden": cfg["hidden"], "heads": cfg["heads"], "ffn": cfg["ffn"],
@@ -406,6 +437,9 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     xp = enc.remove_padding(x_pad.astype(np.float64), lens)
     T = int(lens.sum())
     weights = [ti.encoder_layer_weights(cfg, i) for i in range(cfg["layers"])]
+    if cfg.get("sparse"):
+        from oracle import sparse as sp
+        weights = [sp.prune_layer_weights(w) for w in weights]
     int8 = bool(cfg.get("int8"))
     if int8:
         from oracle import int8 as q8

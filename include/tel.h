@@ -100,6 +100,9 @@ typedef struct {
   int int8_gemm;   /* 1: the four projection GEMMs run in int8 (dtype TEL_F16; H and F
                       multiples of 16); see the int8 section below                 */
   float ln_eps;
+  int sparse_2of4; /* 1: the four projection matrices are pruned 2:4 when prepared and run
+                      on the sparse MFMA (dtype TEL_F16 or TEL_BF16, not int8_gemm; H and F
+                      multiples of 128); see the 2:4 section below                   */
 } tel_encoder_desc;
 
 /* Canonical weights of one layer, storage type desc->dtype, device pointers:

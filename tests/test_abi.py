@@ -215,3 +215,15 @@ def test_sparse_2of4_validation():
     assert G(*bad) == tel.TEL_EINVAL
     bad = list(args); bad[9] = 4; bad[3] = FAKE_ODD
     assert G(*bad) == tel.TEL_EINVAL
+
+
+def test_sparse_encoder_desc():
+    dense = tel.tel_encoder_packed_size(desc())
+    sparse = tel.tel_encoder_packed_size(desc(sparse_2of4=1))
+    # weights: half the values plus one 16-bit word per 16 weights (9/16 of the dense bytes)
+    w = 12 * 768 * 768 * 2
+    assert sparse < dense and abs((dense - sparse) - (w - w * 9 // 16)) < 64 * 1024
+    assert tel.tel_encoder_packed_size(desc(sparse_2of4=1, dtype=tel.TEL_BF16)) == sparse
+    for bad in (dict(int8_gemm=1), dict(dtype=tel.TEL_F32), dict(hidden=640, heads=10),
+                dict(ffn=3000)):
+        assert tel.tel_encoder_packed_size(desc(sparse_2of4=1, **bad)) == 0, bad

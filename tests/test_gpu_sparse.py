@@ -98,3 +98,44 @@ def test_sparse_gemm_shapes_auto(M, N, K):
     tel.tel_gemm_2of4(tel.TEL_EPI_BIAS, dev(a, "f16"), values, index, dev_f32(b), C)
     torch.cuda.synchronize()
     assert_close(host(C), enc.linear(a, sp.prune_2of4(w), b), "f16", f"{M}x{N}x{K}")
+
+
+def _sparse_stack(cfg, layers, lens=None, x=None):
+    from tests.gpu_helpers import prepare_layers
+    dt = cfg["dtype"]
+    if lens is None:
+        lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(layers)]
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT[dt], ti.LN_EPS,
+                                 sparse_2of4=True)
+    packed = prepare_layers(tel, desc, ws, dt)
+    B, S, H = x.shape
+    X = dev(x, dt)
+    Y = torch.full_like(X, float("nan"))
+    lens_d = torch.from_numpy(np.asarray(lens, np.int32)).to("cuda")
+    wsb = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
+    tel.tel_encoder_forward(desc, packed, X, Y, lens_d, int(np.sum(lens)), int(np.max(lens)), wsb)
+    torch.cuda.synchronize()
+    pruned = [sp.prune_layer_weights(w) for w in ws]
+    return lens, x, host(Y), pruned
+
+
+@pytest.mark.parametrize("dtype,layers", [("f16", 2), ("bf16", 1)])
+def test_sparse_encoder_stack(dtype, layers):
+    """The whole path with 2:4 layers against the oracle's encoder on pruned weights; ragged
+    lengths, an empty sequence and one single-token sequence."""
+    cfg = ti.custom_encoder_config(4, 70, [70, 1, 0, 45], 256, 4, 1024, dtype=dtype, seed=11,
+                                   layers=layers)
+    lens, x, y, pruned = _sparse_stack(cfg, layers)
+    ref = enc.encoder_forward(x, lens, pruned, cfg["heads"], ti.LN_EPS)
+    assert_close(y, ref, dtype, f"sparse stack {dtype}")
+
+
+def test_sparse_bert_base_one_layer_full_batch():
+    """One BERT-base layer with 2:4 weights on the full seeded batch (what the benchmark's
+    sparse line runs, one layer of it)."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base"])
+    lens, x, y, pruned = _sparse_stack(cfg, 1)
+    ref = enc.encoder_forward(x, lens, pruned, cfg["heads"], ti.LN_EPS)
+    assert_close(enc.remove_padding(y, lens), enc.remove_padding(ref, lens), "f16",
+                 "sparse bert_base layer")

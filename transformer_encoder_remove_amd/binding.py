@@ -58,7 +58,7 @@ F = ctypes.c_float
 
 class tel_encoder_desc(ctypes.Structure):
     _fields_ = [("hidden", I), ("heads", I), ("ffn", I), ("dtype", I), ("int8_gemm", I),
-                ("ln_eps", F)]
+                ("ln_eps", F), ("sparse_2of4", I)]
 
 
 class tel_swin_desc(ctypes.Structure):
@@ -185,8 +185,10 @@ def tel_rebuild_padding(x_packed, x_pad, cu_seqlens, stream=None):
         _stream(stream)))
 
 
-def make_encoder_desc(hidden, heads, ffn, dtype: torch.dtype, eps=1e-5, int8_gemm=False):
-    return tel_encoder_desc(hidden, heads, ffn, dtype_code(dtype), int(int8_gemm), eps)
+def make_encoder_desc(hidden, heads, ffn, dtype: torch.dtype, eps=1e-5, int8_gemm=False,
+                      sparse_2of4=False):
+    return tel_encoder_desc(hidden, heads, ffn, dtype_code(dtype), int(int8_gemm), eps,
+                            int(sparse_2of4))
 
 
 def tel_encoder_packed_size(desc) -> int:

@@ -38,6 +38,7 @@ inline bool float_type(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT
 // the per-column dequantisation scales and the activation scales s_a[4], inv_a[4].
 struct LayerLayout {
   size_t w_qkv, w_o, w_1, w_2;
+  size_t wi_qkv, wi_o, wi_1, wi_2;   // 2:4 layers: index words of the compressed weights
   size_t b_qkv, b_o, ln1_g, ln1_b, b_1, b_2, ln2_g, ln2_b;
   size_t sw_qkv, sw_o, sw_1, sw_2, dq_qkv, dq_o, dq_1, dq_2, act;
   size_t total;
@@ -55,6 +56,9 @@ int desc_supported(const tel_encoder_desc* d) {
   if (!desc_ok(d)) return TEL_EINVAL;
   if (!float_type(d->dtype)) return TEL_EUNSUPPORTED;
   if (d->int8_gemm && (d->dtype != DT_F16 || d->hidden % 16 || d->ffn % 16)) return TEL_EUNSUPPORTED;
+  if (d->sparse_2of4 && (d->int8_gemm || (d->dtype != DT_F16 && d->dtype != DT_BF16) ||
+                         d->hidden % 128 || d->ffn % 128))
+    return TEL_EUNSUPPORTED;
   if (d->hidden % 8 || d->ffn % 8) return TEL_EUNSUPPORTED;
   if (!attention_supported(d->dtype, d->hidden / d->heads)) return TEL_EUNSUPPORTED;
   if (!layernorm_supported(d->dtype, d->hidden)) return TEL_EUNSUPPORTED;
@@ -66,10 +70,21 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
   LayerLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
-  L.w_qkv = take(3 * H * H * es);
-  L.w_o = take(H * H * es);
-  L.w_1 = take(F * H * es);
-  L.w_2 = take(H * F * es);
+  if (d->sparse_2of4) {   // kept values [N][K/2] and index words [N][K/16]
+    L.w_qkv = take(3 * H * H / 2 * es);
+    L.w_o = take(H * H / 2 * es);
+    L.w_1 = take(F * H / 2 * es);
+    L.w_2 = take(H * F / 2 * es);
+    L.wi_qkv = take(3 * H * H / 16 * 2);
+    L.wi_o = take(H * H / 16 * 2);
+    L.wi_1 = take(F * H / 16 * 2);
+    L.wi_2 = take(H * F / 16 * 2);
+  } else {
+    L.w_qkv = take(3 * H * H * es);
+    L.w_o = take(H * H * es);
+    L.w_1 = take(F * H * es);
+    L.w_2 = take(H * F * es);
+  }
   L.b_qkv = take(3 * H * 4);
   L.b_o = take(H * 4);
   L.ln1_g = take(H * 4);
@@ -282,13 +297,17 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   const bool f32s = f32_stream(d);
   float* h1f = f32s ? (float*)(ws + W.h1f) : nullptr;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
+  // 2:4 layers: compressed weights on the sparse MFMA, never split over k
+  const bool sparse = d->sparse_2of4 != 0;
+  auto IDX = [&](size_t off) { return sparse ? (const uint16_t*)(P + off) : nullptr; };
   int cfg_o, cfg_2;
-  const int sp_o = gemm_partial_plan(dt, T, H, H, &cfg_o);
-  const int sp_2 = gemm_partial_plan(dt, T, H, F, &cfg_2);
+  const int sp_o = sparse ? 1 : gemm_partial_plan(dt, T, H, H, &cfg_o);
+  const int sp_2 = sparse ? 1 : gemm_partial_plan(dt, T, H, F, &cfg_2);
 
   GemmArgs g{};
   // QKV projection + bias, written head-split for the attention kernel
   g = GemmArgs{EPI_QKV_SPLIT, x, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
+  g.w_idx = IDX(L.wi_qkv);
   TEL_TRY(launch_gemm(dt, g, st));
   TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
   const int pre_dt = f32s ? (int)DT_F32 : dt;
@@ -304,12 +323,14 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
+    g.w_idx = IDX(L.wi_o);
     TEL_TRY(launch_gemm(dt, g, st));
     TEL_TRY(launch_layernorm(pre_dt, dt, pre, h1, h1f, F32(L.ln1_g), F32(L.ln1_b), T, H,
                              d->ln_eps, st));
   }
   // FFN: bias + GELU, then bias + residual, then LayerNorm (FFN2 split as above)
   g = GemmArgs{EPI_BIAS_GELU, h1, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
+  g.w_idx = IDX(L.wi_1);
   TEL_TRY(launch_gemm(dt, g, st));
   const void* res2 = f32s ? (const void*)h1f : h1;
   if (sp_2 > 1) {
@@ -322,6 +343,7 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), res2, pre, T, H, F, nh, f32s, f32s};
+    g.w_idx = IDX(L.wi_2);
     TEL_TRY(launch_gemm(dt, g, st));
     TEL_TRY(launch_layernorm(pre_dt, dt, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
                              d->ln_eps, st));
@@ -497,6 +519,11 @@ int tel_encoder_prepare(const tel_encoder_desc* d, const tel_encoder_weights* w,
                                    (float*)(P + L.dq_1), sa[2], F, H, st));
     TEL_TRY(launch_quantize_weight(dt, w->w_2, (int8_t*)(P + L.w_2), (float*)(P + L.sw_2),
                                    (float*)(P + L.dq_2), sa[3], H, F, st));
+  } else if (d->sparse_2of4) {   // prune 2:4 and compress into the sparse MFMA operand form
+    TEL_TRY(launch_prune_2of4(dt, w->w_qkv, P + L.w_qkv, (uint16_t*)(P + L.wi_qkv), 3 * H, H, st));
+    TEL_TRY(launch_prune_2of4(dt, w->w_o, P + L.w_o, (uint16_t*)(P + L.wi_o), H, H, st));
+    TEL_TRY(launch_prune_2of4(dt, w->w_1, P + L.w_1, (uint16_t*)(P + L.wi_1), F, H, st));
+    TEL_TRY(launch_prune_2of4(dt, w->w_2, P + L.w_2, (uint16_t*)(P + L.wi_2), H, F, st));
   } else {
     TEL_TRY(hipMemcpyAsync(P + L.w_qkv, w->w_qkv, 3 * H * H * es, hipMemcpyDeviceToDevice, st));
     TEL_TRY(hipMemcpyAsync(P + L.w_o, w->w_o, H * H * es, hipMemcpyDeviceToDevice, st));
@@ -675,6 +702,7 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   }
   std::vector<uintptr_t> key = {(uintptr_t)dev, (uintptr_t)d->hidden, (uintptr_t)d->heads,
                                 (uintptr_t)d->ffn, (uintptr_t)d->dtype, (uintptr_t)d->int8_gemm,
+                                (uintptr_t)d->sparse_2of4,
                                 (uintptr_t)n_layers, (uintptr_t)x_pad, (uintptr_t)y_pad,
                                 (uintptr_t)seq_lens, (uintptr_t)batch, (uintptr_t)max_seq,
                                 (uintptr_t)total_tokens, (uintptr_t)max_len,

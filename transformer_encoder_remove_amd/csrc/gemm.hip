@@ -1147,10 +1147,11 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
   return sp;
 }
 
-// Sparse tile choice: the dense cost model's rounds of 256 tiles, with the loop rate of a
-// sparse MFMA step (twice the dense k per instruction) and each tile's efficiency.
+// Sparse tile choice: the dense cost model's rounds of 256 tiles (one workgroup per CU),
+// with per-tile loop rates measured at BERT shapes (in dense-equivalent multiply-adds: the
+// loop is bound by LDS traffic, mostly the dense activation fragments, not by the MFMAs).
 static int pick_sp_cfg(const GemmArgs& a) {
-  constexpr double EFF[N_SP_CFGS] = {0.62, 0.8, 0.75};
+  constexpr double EFF[N_SP_CFGS] = {0.26, 0.25, 0.27};
   constexpr double FIXED_US = 3.5, CUS = 256, RATE = 2 * 3.19e6;
   int best = 0;
   double best_us = -1;
