@@ -668,6 +668,81 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
   const int xr = lr & 7;
   const int rowA = (wm * TM + lr) * 256;
   const int rowW = W_OFF + (wn * TN + lr) * 128, rowI = I_OFF + (wn * TN + lr) * 16;
+  typename SM::acc acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = typename SM::acc{};
+  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads));
+
+  if constexpr (FN >= 8) {
+    // Wide wave tile (TN >= 128 weight rows): too many registers to double-buffer both
+    // operands, so the activation fragments (8 registers each) go through a two-slot ring
+    // one column block ahead, while the weight fragments of the next k-step are loaded two
+    // per column block during the current one. The slice barrier sits in the last column
+    // block of the second k-step, after the last read of the old slice.
+    afrag wa[2][FN];
+    int wi[2][FN];
+    bfrag br[2];
+#define TEL_SPW_W(buf, slice, kk, i)                                                        \
+  do {                                                                                      \
+    const char* st_ = smem + ((slice) % S) * STAGE;                                         \
+    wa[buf][i] = *reinterpret_cast<const afrag*>(st_ + rowW + (i) * 16 * 128 +              \
+                                                 ((((kk) * 4 + lg) ^ xr) * 16));            \
+    wi[buf][i] = *reinterpret_cast<const uint16_t*>(st_ + rowI + (i) * 16 * 16 +            \
+                                                    ((kk) * 4 + lg) * 2);                   \
+  } while (0)
+#define TEL_SPW_B(r, slice, kk, j)                                                          \
+  do {                                                                                      \
+    const char* a_ = smem + ((slice) % S) * STAGE + rowA + (j) * 16 * 256 + (kk) * 128;     \
+    const afrag lo_ = *reinterpret_cast<const afrag*>(a_ + ((lg ^ xr) * 16));               \
+    const afrag hi_ = *reinterpret_cast<const afrag*>(a_ + (((lg + 4) ^ xr) * 16));         \
+    br[r] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,  \
+                                    14, 15);                                                \
+  } while (0)
+    __builtin_amdgcn_s_barrier();                   // slice 0 has landed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < FN; ++i) TEL_SPW_W(0, 0, 0, i);
+    TEL_SPW_B(0, 0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {               // k-step 0 of slice kt
+        if (j + 1 < FM) TEL_SPW_B((j + 1) & 1, kt, 0, j + 1);
+        else TEL_SPW_B(FM & 1, kt, 1, 0);
+#pragma unroll
+        for (int i = j * FN / FM; i < (j + 1) * FN / FM; ++i) TEL_SPW_W(1, kt, 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][j] = SM::mma(wa[0][i], br[j & 1], acc[i][j], wi[0][i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {               // k-step 1 of slice kt
+        const int r = (FM + j) & 1;                 // ring slot holding column block j
+        if (j + 1 < FM) {
+          TEL_SPW_B(r ^ 1, kt, 1, j + 1);
+        } else {
+          wait_lgkmcnt0();                          // reads of slice kt are done
+          __builtin_amdgcn_s_barrier();             // slice kt + 1 has landed
+          asm volatile("" ::: "memory");
+          const int nx = min(kt + 1, nk - 1);
+          TEL_SPW_B(r ^ 1, nx, 0, 0);
+#pragma unroll
+          for (int i = 0; i < FN; ++i) TEL_SPW_W(0, nx, 0, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][j] = SM::mma(wa[1][i], br[r], acc[i][j], wi[1][i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#undef TEL_SPW_W
+#undef TEL_SPW_B
+    pipe_epilogue<EPI, T, TR, TO, TM, TN>(acc, smem, e, m0, n0, wm, wn, wave, lane);
+    return;
+  }
+
   afrag fa[2][FN];
   int fi[2][FN];
   bfrag fb[2][FM];
@@ -689,13 +764,6 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
     }                                                                                       \
   } while (0)
 
-  typename SM::acc acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = typename SM::acc{};
-
-  asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads));
   __builtin_amdgcn_s_barrier();                     // slice 0 has landed
   asm volatile("" ::: "memory");
   TEL_SP_FRAGS(0, 0, 0);
@@ -943,6 +1011,7 @@ constexpr PipeCfg SP_CFGS[] = {
     {64, 128, 2, 4, 4},    // 0: 8 waves, wave tile 32x32, 136 KiB
     {128, 128, 2, 2, 3},   // 1: 4 waves, wave tile 64x64, 150 KiB
     {64, 256, 2, 4, 2},    // 2: 8 waves, wave tile 32x64, 104 KiB
+    {128, 256, 2, 2, 2},   // 3: 4 waves, wave tile 64x128 (activation ring), 136 KiB
 };
 constexpr int N_SP_CFGS = sizeof(SP_CFGS) / sizeof(SP_CFGS[0]);
 
@@ -1002,7 +1071,8 @@ static void launch_sp_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
   switch (cfg) {
     case 0: launch_sp<T, 0, EPI, TR, TO>(a, stream); break;
     case 1: launch_sp<T, 1, EPI, TR, TO>(a, stream); break;
-    default: launch_sp<T, 2, EPI, TR, TO>(a, stream); break;
+    case 2: launch_sp<T, 2, EPI, TR, TO>(a, stream); break;
+    default: launch_sp<T, 3, EPI, TR, TO>(a, stream); break;
   }
 }
 
@@ -1151,7 +1221,7 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
 // with per-tile loop rates measured at BERT shapes (in dense-equivalent multiply-adds: the
 // loop is bound by LDS traffic, mostly the dense activation fragments, not by the MFMAs).
 static int pick_sp_cfg(const GemmArgs& a) {
-  constexpr double EFF[N_SP_CFGS] = {0.26, 0.25, 0.27};
+  constexpr double EFF[N_SP_CFGS] = {0.26, 0.25, 0.27, 0.5};
   constexpr double FIXED_US = 3.5, CUS = 256, RATE = 2 * 3.19e6;
   int best = 0;
   double best_us = -1;
