@@ -324,6 +324,13 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
   return x * per + min(x, extra) + i;
 }
 
+// The largest divisor of n that is at most 8 (epilogue passes grouped for their loads).
+constexpr int group_passes(int n) {
+  for (int g = 8; g > 1; --g)
+    if (n % g == 0) return g;
+  return 1;
+}
+
 // Epilogue of the pipelined kernels, for one compute wavefront's TM x TN accumulators
 // (lane: 4 consecutive columns n of one row m per 16x16 block, the MFMA output layout).
 template <int EPI, typename T, typename TR, typename TO, int TM, int TN, typename ACC, int FN,
@@ -358,7 +365,7 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
   constexpr int CPR = TN / 8;
   constexpr int RP = 64 / CPR;
   constexpr int NPASS = (TM + RP - 1) / RP;
-  constexpr int GP = NPASS < 8 ? NPASS : 8;   // passes whose residuals are loaded together
+  constexpr int GP = group_passes(NPASS);     // passes whose residuals are loaded together
   static_assert(TN % 8 == 0 && CPR <= 64 && NPASS % GP == 0, "epilogue chunking");
   const int c8 = lane % CPR, rr = lane / CPR;
   const int n = n0 + wn * TN + c8 * 8;
@@ -592,13 +599,13 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
   constexpr int BK = 128;                           // dense k per slice
   constexpr int NB_A = BM / 4, NB_W = BN / 8, NB_I = BN / 64;   // 1 KiB copy blocks
   constexpr int NB = NB_A + NB_W + NB_I;
-  constexpr int LJ = NB / PIPE_PRODUCERS;
+  // copies per producer per slice: producer 0 takes the odd block out when NB is odd
+  constexpr int LJ0 = (NB + 1) / PIPE_PRODUCERS, LJ1 = NB / PIPE_PRODUCERS;
   constexpr int STAGE = NB * 1024;
   constexpr int W_OFF = NB_A * 1024, I_OFF = (NB_A + NB_W) * 1024;
-  constexpr int INFLIGHT = LJ * (S - 2) < 63 ? LJ * (S - 2) : 63;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  static_assert(BN % 64 == 0 && BM % 8 == 0 && NB % PIPE_PRODUCERS == 0, "copy split");
+  static_assert(BN % 64 == 0 && BM % 8 == 0 && PIPE_PRODUCERS == 2, "copy split");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && S >= 2, "wave tile, stages");
   constexpr int LDC = TN + 4;
   constexpr int STAGED = TM * LDC * 4 * NW;
@@ -618,6 +625,9 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
     // ---------------- producer: block b = p + PIPE_PRODUCERS * j of every slice; lane i of
     // a block fills bytes 16 i .. 16 i + 15 of it
     const int p = wave - NW;
+    auto produce = [&](auto lj_c) {
+    constexpr int LJ = decltype(lj_c)::value;
+    constexpr int INFLIGHT = LJ * (S - 2) < 63 ? LJ * (S - 2) : 63;
     const char* src[LJ];
     int step[LJ];                                   // bytes of the block's rows per slice
     const int sub = lane >> 3, slot = lane & 7;
@@ -658,6 +668,9 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
       issue(kt + S - 1, min(kt + S - 1, nk - 1));   // into the stage of slice kt - 1
     }
     wait_vmcnt<0>();
+    };
+    if (p == 0) produce(std::integral_constant<int, LJ0>{});
+    else produce(std::integral_constant<int, LJ1>{});
     __builtin_amdgcn_s_barrier();   // matches the compute wavefronts' final barrier
     return;
   }
@@ -1006,12 +1019,13 @@ constexpr PipeCfg PIPE_CFGS[] = {
 };
 constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 
-// Tiles of the 2:4-sparse kernel (stage = BM/4 + BN/8 + BN/64 KiB; an even block count).
+// Tiles of the 2:4-sparse kernel (stage = BM/4 + BN/8 + BN/64 KiB of copy blocks).
 constexpr PipeCfg SP_CFGS[] = {
     {64, 128, 2, 4, 4},    // 0: 8 waves, wave tile 32x32, 136 KiB
     {128, 128, 2, 2, 3},   // 1: 4 waves, wave tile 64x64, 150 KiB
     {64, 256, 2, 4, 2},    // 2: 8 waves, wave tile 32x64, 104 KiB
     {128, 256, 2, 2, 2},   // 3: 4 waves, wave tile 64x128 (activation ring), 136 KiB
+    {128, 192, 2, 2, 2},   // 4: 4 waves, wave tile 64x96, 118 KiB (59 blocks: 30 + 29)
 };
 constexpr int N_SP_CFGS = sizeof(SP_CFGS) / sizeof(SP_CFGS[0]);
 
@@ -1072,7 +1086,8 @@ static void launch_sp_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
     case 0: launch_sp<T, 0, EPI, TR, TO>(a, stream); break;
     case 1: launch_sp<T, 1, EPI, TR, TO>(a, stream); break;
     case 2: launch_sp<T, 2, EPI, TR, TO>(a, stream); break;
-    default: launch_sp<T, 3, EPI, TR, TO>(a, stream); break;
+    case 3: launch_sp<T, 3, EPI, TR, TO>(a, stream); break;
+    default: launch_sp<T, 4, EPI, TR, TO>(a, stream); break;
   }
 }
 
@@ -1221,7 +1236,7 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
 // with per-tile loop rates measured at BERT shapes (in dense-equivalent multiply-adds: the
 // loop is bound by LDS traffic, mostly the dense activation fragments, not by the MFMAs).
 static int pick_sp_cfg(const GemmArgs& a) {
-  constexpr double EFF[N_SP_CFGS] = {0.26, 0.25, 0.27, 0.5};
+  constexpr double EFF[N_SP_CFGS] = {0.26, 0.25, 0.27, 0.5, 0.45};
   constexpr double FIXED_US = 3.5, CUS = 256, RATE = 2 * 3.19e6;
   int best = 0;
   double best_us = -1;
