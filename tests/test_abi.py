@@ -121,13 +121,17 @@ def test_partial_plan_invariants():
     """The k-split plan of the output projection / FFN2 GEMMs (host logic): splits only
     when the unsplit tile grid is under 100 workgroups, a power of two up to 8, whole
     128-byte slices with at least 8 per split, and never more than needed."""
-    cfgs = [(128, 256), (128, 192), (128, 128), (64, 128), (64, 64)]
+    # (BM, BN) of the pipelined tile table, in its order (gemm.hip PIPE_CFGS)
+    cfgs = [(128, 256), (128, 192), (128, 128), (64, 128), (64, 64), (128, 256), (256, 128),
+            (128, 128), (64, 128), (192, 192), (96, 128)]
+    assert len(cfgs) == tel.tel_gemm_tile_configs()
     for dt, es in ((tel.TEL_F16, 2), (tel.TEL_BF16, 2), (tel.TEL_F32, 4), (tel.TEL_I8, 1)):
         for M in (1, 17, 128, 640, 2557, 14336, 24576):
             for N, K in ((768, 768), (768, 3072), (1024, 1024), (1024, 4096), (64, 256)):
                 cfg, sp = tel.tel_gemm_partial_plan(dt, M, N, K)
                 nk = K * es // 128
-                assert 0 <= cfg < 5 and sp in (1, 2, 4, 8), (dt, M, N, K, cfg, sp)
+                assert 0 <= cfg < tel.tel_gemm_tile_configs() and sp in (1, 2, 4, 8), \
+                    (dt, M, N, K, cfg, sp)
                 bm, bn = cfgs[cfg]
                 tiles = -(-M // bm) * -(-N // bn)
                 if sp > 1:

@@ -1016,6 +1016,8 @@ constexpr PipeCfg PIPE_CFGS[] = {
     {256, 128, 2, 2, 3},   // 6: 4 waves, wave tile 128x64, 144 KiB
     {128, 128, 2, 2, 2},   // 7: 4 waves, wave tile 64x64, 64 KiB (two workgroups per CU)
     {64, 128, 2, 2, 4},    // 8: 4 waves, wave tile 32x64, 96 KiB
+    {192, 192, 2, 4, 3},   // 9: 8 waves, wave tile 96x48, 144 KiB
+    {96, 128, 2, 4, 4},    // 10: 8 waves, wave tile 48x32, 112 KiB
 };
 constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 
@@ -1130,6 +1132,8 @@ static void launch_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
     case 6: launch_pipe<T, 6, EPI, TR, TO>(a, stream); break;
     case 7: launch_pipe<T, 7, EPI, TR, TO>(a, stream); break;
     case 8: launch_pipe<T, 8, EPI, TR, TO>(a, stream); break;
+    case 9: launch_pipe<T, 9, EPI, TR, TO>(a, stream); break;
+    case 10: launch_pipe<T, 10, EPI, TR, TO>(a, stream); break;
     default: launch_one<T, 64, 64, 2, 2, EPI, TR, TO>(a, stream); break;
   }
 }
@@ -1191,19 +1195,23 @@ static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
 // bytes use the register-staged kernel.
 static int pick_cfg(const GemmArgs& a, int elem_bytes) {
   if (((long long)a.K * elem_bytes) % 128) return -1;
-  constexpr double EFF[5] = {1.0, 0.9, 0.8, 0.62, 0.5};
+  // (tile, loop efficiency relative to the 128x256 tile); 192x192 and 96x128 fill one
+  // round of 256 tiles at token counts where 128x256 or 64x128 would spill into a second
+  struct Cand { int cfg; double eff; };
+  constexpr Cand CANDS[] = {{0, 1.0}, {1, 0.9}, {2, 0.65}, {3, 0.62}, {4, 0.5}, {9, 0.95},
+                            {10, 0.55}};
   constexpr double FIXED_US = 3.5, CUS = 256;
   const double rate = elem_bytes == 1 ? 6.06e6 : elem_bytes == 2 ? 3.19e6 : 0.2e6;
   int best = 0;
   double best_us = -1;
-  for (int c = 0; c < 5; ++c) {
-    const PipeCfg& p = PIPE_CFGS[c];
+  for (const Cand& c : CANDS) {
+    const PipeCfg& p = PIPE_CFGS[c.cfg];
     const double tiles = (double)((a.M + p.bm - 1) / p.bm) * ((a.N + p.bn - 1) / p.bn);
     const double rounds = std::ceil(tiles / CUS);
-    const double us = rounds * ((double)p.bm * p.bn * a.K / (rate * EFF[c]) + FIXED_US);
+    const double us = rounds * ((double)p.bm * p.bn * a.K / (rate * c.eff) + FIXED_US);
     if (best_us < 0 || us < best_us) {
       best_us = us;
-      best = c;
+      best = c.cfg;
     }
   }
   return best;
