@@ -24,6 +24,8 @@
 //    the final 1/l are per-lane scalars.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -33,7 +35,7 @@ constexpr int ATT_QB = 64;   // queries per workgroup
 constexpr int ATT_KB = 64;   // keys per LDS block
 
 // Scores, online-softmax update and O update for one 64-key block staged in LDS.
-template <typename T, int D, int LDK, int LDV>
+template <typename T, int D, int LDK, int LDV, bool PSPLIT>
 __device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
                                            const typename Mfma<T>::frag* qf, f32x4* o,
                                            float& m_run, float& l_run, int kb0, int L,
@@ -90,10 +92,10 @@ __device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
 
   // O^T[c][q] += sum_key V^T[c][key] * P^T[key][q]; MFMA k element e of step t is the
   // lane's score f = t*KPL + e, i.e. key 16*(f/4) + 4*lg + f%4.
-  // For 16-bit types P is split into P_hi + P_lo (both representable), two MFMAs per
-  // step: P enters the product with ~2x the significant bits of one 16-bit value. The
-  // kernel is bound by memory latency, not by MFMA, so the extra MFMA costs nothing
-  // measurable, and downstream int8 codes flip far less often.
+  // PSPLIT (bf16, and fp16 when the int8 codes of the output are written): P is split
+  // into P_hi + P_lo (both representable), two MFMAs per step, so P enters the product
+  // with ~2x the significant bits of one 16-bit value: bf16 keeps only 8 of them, and
+  // downstream int8 codes flip far less often. Plain fp16 rounds P once (11 bits).
 #pragma unroll
   for (int t = 0; t < ATT_KB / KMF; ++t) {
     T pv[KPL], pl[KPL];
@@ -101,7 +103,7 @@ __device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
     for (int e = 0; e < KPL; ++e) {
       const int f = t * KPL + e;
       pv[e] = from_f32<T>(sc[f / 4][f % 4]);
-      pl[e] = from_f32<T>(sc[f / 4][f % 4] - to_f32(pv[e]));
+      pl[e] = PSPLIT ? from_f32<T>(sc[f / 4][f % 4] - to_f32(pv[e])) : pv[e];
     }
     frag pb, pbl;
     __builtin_memcpy(&pb, pv, sizeof(frag));
@@ -121,7 +123,7 @@ __device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
         va = vrow[16 * (f / 4) + 4 * lg + (f % 4)];
       }
       o[c] = MF::mma(va, pb, o[c]);
-      if constexpr (KPL > 1) o[c] = MF::mma(va, pbl, o[c]);
+      if constexpr (KPL > 1 && PSPLIT) o[c] = MF::mma(va, pbl, o[c]);
     }
   }
 }
@@ -163,7 +165,7 @@ template <typename T, int D> struct KvRegs {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool PSPLIT>
 __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ qkv,
                                                           T* __restrict__ ctx,
                                                           const int32_t* __restrict__ cu,
@@ -226,7 +228,8 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
     KV.template store<LDK, LDV>(sK, sVt, tid);                                              \
     if ((kb0) + 2 * ATT_KB < L) KV.load(Kh, Vh, (kb0) + 2 * ATT_KB, L, tid);                \
     __syncthreads();                                                                        \
-    attn_block<T, D, LDK, LDV>(sK, sVt, qf, o, m_run, l_run, (kb0), L, scale_log2, lr, lg);  \
+    attn_block<T, D, LDK, LDV, PSPLIT>(sK, sVt, qf, o, m_run, l_run, (kb0), L, scale_log2, lr, \
+                                       lg);                                                 \
   } while (0)
 
   for (int kb0 = 0; kb0 < L; kb0 += 2 * ATT_KB) {
@@ -277,8 +280,12 @@ static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int ba
                            hipStream_t stream) {
   const dim3 grid((max_len + ATT_QB - 1) / ATT_QB, heads, batch);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  attn_varlen_kernel<T, D><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total, heads,
-                                                     scale_log2, ctxq, qinv);
+  if (ctxq || !std::is_same<T, f16>::value)   // P split (see attn_block)
+    attn_varlen_kernel<T, D, true><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total,
+                                                             heads, scale_log2, ctxq, qinv);
+  else
+    attn_varlen_kernel<T, D, false><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total,
+                                                              heads, scale_log2, ctxq, qinv);
   return hipGetLastError();
 }
 
