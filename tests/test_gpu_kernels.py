@@ -122,3 +122,35 @@ def test_gemm_every_tile_config(dtype, M, N, K):
         tel.tel_gemm_ex(tel.TEL_EPI_BIAS_RESID, cfg, A, W, bias, C, resid=R)
         torch.cuda.synchronize()
         assert_close(host(C), ref, dtype, f"tile config {cfg} {dtype} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N,K", [(288, 96), (96, 96), (384, 96), (96, 384)])
+def test_skinny_gemm_shapes(dtype, N, K):
+    """The narrow projections of the shifted-window block (weights held in LDS, 8-column
+    stores after a lane exchange), every plain epilogue, a ragged token count."""
+    M = 1000
+    a, w, b, r = _operands(M, N, K, dtype, seed=N + K)
+    A, W, R = dev(a, dtype), dev(w, dtype), dev(r, dtype)
+    bias = dev_f32(b)
+    lin = enc.linear(a, w, b)
+    for epi, ref in ((tel.TEL_EPI_BIAS, lin), (tel.TEL_EPI_BIAS_GELU, enc.gelu(lin)),
+                     (tel.TEL_EPI_BIAS_RESID, lin + r.astype(np.float64))):
+        C = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+        tel.tel_gemm(epi, A, W, bias, C, resid=R if epi == tel.TEL_EPI_BIAS_RESID else None)
+        torch.cuda.synchronize()
+        assert_close(host(C), ref, dtype, f"skinny epi {epi} {dtype} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("heads", [3, 24])
+def test_skinny_qkv_split(heads):
+    """QKV head split at the shifted-window block's width (N 288, K 96): head_dim 32 runs on
+    the skinny kernel, head_dim 4 (fewer than 8 columns per head) on the tiled one."""
+    M, H = 777, 96
+    a, w, b, _ = _operands(M, 3 * H, H, "f16", seed=heads)
+    C = torch.full((3 * M * H,), float("nan"), dtype=torch.float16, device="cuda")
+    tel.tel_gemm(tel.TEL_EPI_QKV_SPLIT, dev(a, "f16"), dev(w, "f16"), dev_f32(b), C, heads=heads)
+    torch.cuda.synchronize()
+    d = H // heads
+    ref = enc.linear(a, w, b).reshape(M, 3, heads, d).transpose(1, 2, 0, 3)
+    assert_close(host(C).reshape(3, heads, M, d), ref, "f16", f"qkv split heads {heads}")
