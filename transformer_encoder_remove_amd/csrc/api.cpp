@@ -602,8 +602,13 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
   void* xa = ws + S.xa;
   void* xb = ws + S.xb;
   const int row_bytes = d->hidden * dtype_size(d->dtype);
-  TEL_TRY(launch_offsets(seq_lens, batch, max_seq, cu, po, st));
-  TEL_TRY(launch_remove_padding(x_pad, xa, po, total_tokens, row_bytes, st));
+  if (batch <= 1024) {   // one launch for both (padding_offset not needed afterwards)
+    TEL_TRY(launch_offsets_remove_padding(seq_lens, batch, max_seq, cu, x_pad, xa,
+                                          total_tokens, row_bytes, st));
+  } else {
+    TEL_TRY(launch_offsets(seq_lens, batch, max_seq, cu, po, st));
+    TEL_TRY(launch_remove_padding(x_pad, xa, po, total_tokens, row_bytes, st));
+  }
   int8_t* qa = (int8_t*)(ws + S.qa);
   int8_t* qb = (int8_t*)(ws + S.qb);
   const size_t act_off = d->int8_gemm ? layer_layout(d).act : 0;

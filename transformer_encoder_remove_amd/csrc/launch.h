@@ -26,6 +26,11 @@ hipError_t launch_remove_padding(const void* x_pad, void* x_packed, const int32_
                                  int total_tokens, int row_bytes, hipStream_t stream);
 hipError_t launch_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu, int batch,
                                   int max_seq, int row_bytes, hipStream_t stream);
+// Offsets (cu only) and padding removal in one launch; batch <= 1024, else
+// hipErrorInvalidValue (use launch_offsets + launch_remove_padding).
+hipError_t launch_offsets_remove_padding(const int32_t* lens, int batch, int max_seq,
+                                        int32_t* cu, const void* x_pad, void* x_packed,
+                                        int total_tokens, int row_bytes, hipStream_t stream);
 
 // gemm.hip
 struct GemmArgs {
