@@ -128,21 +128,37 @@ __device__ __forceinline__ void attn_block(const T* sK, const T* sVt,
   }
 }
 
-// 16-byte K and V vectors of one 64-key block held in registers: thread tid owns vectors
-// tid + 256 p (key row idx / VPRK, column chunk idx % VPRK); rows past the sequence end are
-// clamped to its last key (their scores are masked).
+// 16-byte K and V vectors of one 64-key block held in registers. 16-bit types with an even
+// number of vectors per thread (head_dim 64, 128): thread tid owns, in chunk c = tid % VPRK,
+// the key rows 2 rp and 2 rp + 1 of row pair rp = tid / VPRK + (256 / VPRK) * pp, so that the
+// transposed V can be stored as 4-byte pairs of consecutive keys (half the LDS stores of
+// one element at a time); otherwise thread tid owns vectors tid + 256 p (key row idx / VPRK,
+// chunk idx % VPRK). Rows past the sequence end are clamped to its last key (their scores
+// are masked).
 template <typename T, int D> struct KvRegs {
   static constexpr int VEC = 16 / sizeof(T), VPRK = D / VEC, NVEC = ATT_KB * VPRK;
   static constexpr int PER = (NVEC + 255) / 256;
+  static constexpr bool PAIRS = sizeof(T) == 2 && PER % 2 == 0 && NVEC % 256 == 0;
   typedef T vec __attribute__((ext_vector_type(VEC)));
   vec k[PER], v[PER];
+
+  __device__ __forceinline__ static void slot(int tid, int p, int& r, int& c) {
+    if constexpr (PAIRS) {
+      c = tid % VPRK;
+      r = 2 * (tid / VPRK + (256 / VPRK) * (p >> 1)) + (p & 1);
+    } else {
+      const int idx = tid + 256 * p;
+      r = idx / VPRK;
+      c = idx - r * VPRK;
+    }
+  }
 
   __device__ __forceinline__ void load(const T* Kh, const T* Vh, int kb0, int L, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p;
-      if (NVEC % 256 == 0 || idx < NVEC) {
-        const int r = idx / VPRK, c = idx - r * VPRK;
+      if (NVEC % 256 == 0 || tid + 256 * p < NVEC) {
+        int r, c;
+        slot(tid, p, r, c);
         const size_t off = (size_t)min(kb0 + r, L - 1) * D + c * VEC;
         k[p] = *reinterpret_cast<const vec*>(Kh + off);
         v[p] = *reinterpret_cast<const vec*>(Vh + off);
@@ -154,12 +170,25 @@ template <typename T, int D> struct KvRegs {
   __device__ __forceinline__ void store(T* sK, T* sVt, int tid) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p;
-      if (NVEC % 256 == 0 || idx < NVEC) {
-        const int r = idx / VPRK, c = idx - r * VPRK;
+      if (NVEC % 256 == 0 || tid + 256 * p < NVEC) {
+        int r, c;
+        slot(tid, p, r, c);
         *reinterpret_cast<vec*>(&sK[r * LDK + c * VEC]) = k[p];
+        if constexpr (PAIRS) {
+          if (p & 1) {   // rows r - 1, r: one 4-byte store per transposed element pair
+            static_assert(LDV % 2 == 0, "4-byte aligned key pairs");
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sVt[(c * VEC + e) * LDV + r] = v[p][e];
+            for (int e = 0; e < VEC; ++e) {
+              T two[2] = {v[p - 1][e], v[p][e]};
+              uint32_t w;
+              __builtin_memcpy(&w, two, 4);
+              *reinterpret_cast<uint32_t*>(&sVt[(c * VEC + e) * LDV + r - 1]) = w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sVt[(c * VEC + e) * LDV + r] = v[p][e];
+        }
       }
     }
   }
