@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-hbm", action="store_true",
+                    help="skip the memory-bound kernels' flushed-cache timings")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the scale of HBM counters)")
     return ap.parse_args()
@@ -138,17 +140,20 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event before every step and one after the last: the K steps run back to back,
+    # the first-to-last span gives ms_per_step, the gaps give per-step statistics
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i].record(stream)
         step()
-    e1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
+    step_ms = step_stats([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     value = T * NL / (ms_per_step / 1e3)
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}),"
         f" {value / 1e6:.2f} M valid tokens/s per layer")
@@ -248,20 +253,7 @@ def main():
         })
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():
-        fn()
-        torch.cuda.synchronize()
-        # A spin kernel holds the GPU while the host enqueues kernel_reps launches between
-        # one pair of HIP events on the launch stream: the average is the kernel's share of
-        # a back-to-back stream (what rocprofv3's kernel-trace durations add up to inside
-        # the stack), free of host launch latency.
-        e_s, e_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(50_000_000)
-        e_s.record(stream)
-        for _ in range(args.kernel_reps):
-            fn()
-        e_e.record(stream)
-        torch.cuda.synchronize()
-        us = e_s.elapsed_time(e_e) * 1e3 / args.kernel_reps
+        us = back_to_back_us(fn, stream, args.kernel_reps)
         per_kernel[name] = dict(us=us, tflops=flops / us / 1e6, gbs=nbytes / us / 1e3,
                                 flops=flops, bytes=nbytes)
         log(f"[bench] kernel {name:16s} {us:9.2f} us  {flops / us / 1e6:8.1f} TFLOP/s"
@@ -279,13 +271,55 @@ def main():
     # one layer launches every kernel above once, and the LayerNorm twice
     layer_sum_us = sum(v["us"] for v in per_kernel.values()) + per_kernel["layernorm"]["us"]
 
+    # ---------------------------------------------------------------- HBM-bound kernels
+    # achieved bytes/s of the memory-bound kernels against 8 TB/s: back to back (operands
+    # may sit in the 256 MB last-level cache) and with that cache flushed before every
+    # launch (a 1 GiB buffer written in between)
+    hbm = {}
+    if not args.no_hbm:
+        pad_o = torch.empty(B * S, dtype=torch.int32, device="cuda")
+        tel.tel_build_offsets(lens_d, S, cu_d, pad_o)
+        xp_o = torch.empty((T, H), dtype=tdt, device="cuda")
+        xr_o = torch.empty_like(x)
+        el = x.element_size()
+        stress = ti.offsets_stress_lengths()
+        Bs, Ss = ti.OFFSETS_STRESS["batch"], ti.OFFSETS_STRESS["max_seq"]
+        Ts = int(stress.sum())
+        lens_s = torch.from_numpy(stress).cuda()
+        cu_s = torch.empty(Bs + 1, dtype=torch.int32, device="cuda")
+        po_s = torch.empty(Bs * Ss, dtype=torch.int32, device="cuda")
+        hbm_kernels = {
+            "attention": (kernels["attention"][0], per_kernel["attention"]["bytes"]),
+            "layernorm": (kernels["layernorm"][0], per_kernel["layernorm"]["bytes"]),
+            "remove_padding": (lambda: tel.tel_remove_padding(x, xp_o, pad_o, T, stream=stream),
+                               2.0 * T * H * el),
+            "rebuild_padding": (lambda: tel.tel_rebuild_padding(xp_o, xr_o, cu_d, stream=stream),
+                                (T + B * S) * H * el),
+            # lengths read, cu_seqlens and T padding offsets written (4-byte integers)
+            f"offsets_stress_B{Bs}_T{Ts}": (
+                lambda: tel.tel_build_offsets(lens_s, Ss, cu_s, po_s, stream=stream),
+                4.0 * (Bs + (Bs + 1) + Ts)),
+        }
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        for name, (fn, nbytes) in hbm_kernels.items():
+            b2b = per_kernel[name]["us"] if name in per_kernel else back_to_back_us(
+                fn, stream, args.kernel_reps)
+            fl = flushed_us(fn, stream, flush)
+            hbm[name] = {"bytes": nbytes, "us": round(b2b, 3), "us_flushed": round(fl, 3),
+                         "gbs": round(nbytes / b2b / 1e3, 1),
+                         "gbs_flushed": round(nbytes / fl / 1e3, 1),
+                         "frac_flushed": round(nbytes / fl / 1e3 / PEAK_HBM_GBS, 4)}
+            log(f"[bench] hbm {name:28s} {b2b:8.2f} us ({nbytes / b2b / 1e3:7.1f} GB/s) "
+                f"flushed {fl:8.2f} us ({nbytes / fl / 1e3:7.1f} GB/s)")
+        del flush
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, lens, x_pad, args.cpu_seconds)
 
     return emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu,
-                layer_sum_us)
+                layer_sum_us, step_ms=step_ms, hbm=hbm)
 
 
 KERNEL_SOURCES = ("transformer_encoder_remove_amd/csrc/gemm.hip",
@@ -333,7 +367,50 @@ def calibration_copy(stream, mib: int = 256, reps: int = 3):
     log(f"[bench] calibration copy: {reps} x {mib} MiB device-to-device")
 
 
-def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, layer_sum_us=None):
+def back_to_back_us(fn, stream, reps: int) -> float:
+    """Average duration of one launch in a back-to-back stream: a spin kernel holds the GPU
+    while the host enqueues `reps` launches between one pair of HIP events on the launch
+    stream (what rocprofv3's kernel-trace durations add up to inside the stack), free of
+    host launch latency."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e_s, e_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(50_000_000)
+    e_s.record(stream)
+    for _ in range(reps):
+        fn()
+    e_e.record(stream)
+    torch.cuda.synchronize()
+    return e_s.elapsed_time(e_e) * 1e3 / reps
+
+
+def flushed_us(fn, stream, flush, reps: int = 10) -> float:
+    """Median duration of one launch right after a 1 GiB buffer has been written (larger
+    than the 256 MB last-level cache, so the kernel's operands come from HBM): one HIP event
+    pair around each launch, on the launch stream, which the flush keeps busy while the
+    host enqueues."""
+    import torch
+    times = []
+    for r in range(reps):
+        e_s, e_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush.fill_(float(r))
+        e_s.record(stream)
+        fn()
+        e_e.record(stream)
+        torch.cuda.synchronize()
+        times.append(e_s.elapsed_time(e_e) * 1e3)
+    return float(np.median(times))
+
+
+def step_stats(ms: list) -> dict:
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "min": round(float(a.min()), 5), "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, layer_sum_us=None,
+         step_ms=None, hbm=None):
     NL = cfg["layers"]
     int8 = bool(cfg.get("int8"))
     out = {
@@ -353,7 +430,10 @@ def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, l
                    "layers": NL, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "step_ms": step_ms,
     }
+    if hbm:
+        out["hbm_kernels"] = hbm
     if per_kernel:
         out["kernels_us"] = {k: round(v["us"], 3) for k, v in per_kernel.items()}
         out["layer_kernel_sum_us"] = round(layer_sum_us, 3)
@@ -394,6 +474,33 @@ def bench_swin(args):
     ms = e0.elapsed_time(e1) / args.steps
     value = T / (ms / 1e3)
     log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {value / 1e9:.3f} G tokens/s per block")
+
+    # each kernel of the block as launched inside it (TEL_SWIN_ONE_STAGE on the workspace
+    # the block leaves behind); algorithmic bytes: inputs read once, outputs written once
+    C, F, el = cfg["channels"], cfg["mlp"], 2
+    stages = {   # name: (stage, bytes per token, flops per token)
+        "ln1_shift_partition_qkv": (0, el * (C + 3 * C), 2 * C * 3 * C),
+        "window_attention": (1, el * (3 * C + C), 4 * cfg["window"] ** 2 * C),
+        "proj_reverse_unshift_resid": (2, el * (C + C + C), 2 * C * C),
+        "ln2_fc1_gelu": (3, el * (C + F), 2 * C * F),
+        "fc2_resid": (4, el * (F + C + C), 2 * F * C),
+    }
+    per_kernel = {}
+    for name, (k, bpt, fpt) in stages.items():
+        fn = lambda k=k: tel.tel_window_attention_forward(desc, packed, x, y, ws,
+                                                          flags=tel.TEL_SWIN_ONE_STAGE(k),
+                                                          stream=stream)
+        us = back_to_back_us(fn, stream, args.kernel_reps)
+        per_kernel[name] = dict(us=us, bytes=bpt * T, flops=fpt * T)
+        log(f"[bench] kernel {name:28s} {us:9.2f} us  {bpt * T / us / 1e3:8.1f} GB/s"
+            f"  {fpt * T / us / 1e6:7.1f} TFLOP/s")
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
+    d = per_kernel[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(d["bytes"] / d["us"] / 1e3, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(d["bytes"] / d["us"] / 1e3 / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(args.workload, "f16", dom),
+                "avg_us": round(d["us"], 3), "bytes_per_launch": d["bytes"]}
     cpu = None
     if not args.no_cpu:
         from oracle import swin
@@ -417,7 +524,9 @@ def bench_swin(args):
         "config": {"workload": f"{args.workload}: shifted-window block, LN1 + shift + partition, "
                                "QKV, window attention (bias + mask), proj + unshift + residual, "
                                "LN2, MLP", **{k: v for k, v in cfg.items() if k != "dtype"}},
-        "roofline": None, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu,
+        "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},
+        "block_kernel_sum_us": round(sum(v["us"] for v in per_kernel.values()), 3),
     }
     print(json.dumps(out), flush=True)
 
@@ -456,10 +565,34 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
         done += 1
     cores = blas_threads or len(os.sched_getaffinity(0))
     log(f"[bench] cpu oracle: {done} layers x {T} tokens in {elapsed:.1f} s on {cores} threads")
-    return {"value": round(T * done / elapsed, 1), "unit": "valid tokens/s per layer",
-            "cores": cores, "kind": "oracle",
-            "sample": f"{done} layer(s) of the same workload on the full batch ({T} valid "
-                      f"tokens), float64 NumPy, {elapsed:.1f} s"}
+    out = {"value": round(T * done / elapsed, 1), "unit": "valid tokens/s per layer",
+           "cores": cores, "kind": "oracle",
+           "sample": f"{done} layer(s) of the same workload on the full batch ({T} valid "
+                     f"tokens), float64 NumPy, {elapsed:.1f} s"}
+    # the same oracle on one thread: layer 0 on the leading sequences up to ~768 tokens
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        return out
+    nb = max(1, int(np.searchsorted(np.cumsum(lens), 768, side="right")))
+    sub_lens = lens[:nb]
+    cu1, _ = enc.offsets(sub_lens, S)
+    x1 = enc.remove_padding(x_pad[:nb].astype(np.float64), sub_lens)
+    w = weights[0]
+    with threadpool_limits(limits=1):
+        amax = q8.calibrate(x1, cu1, w, cfg["heads"], ti.LN_EPS) if int8 else None
+        t0 = time.perf_counter()
+        if int8:
+            q8.encoder_layer_int8(x1, cu1, w, cfg["heads"], ti.LN_EPS, amax)
+        else:
+            enc.encoder_layer(x1, cu1, w, cfg["heads"], ti.LN_EPS)
+        t1 = time.perf_counter() - t0
+    t_sub = int(sub_lens.sum())
+    out["value_1thread"] = round(t_sub / t1, 1)
+    out["sample_1thread"] = (f"layer 0 on the first {nb} sequences ({t_sub} valid tokens), one "
+                             f"BLAS thread, {t1:.2f} s")
+    log(f"[bench] cpu oracle, 1 thread: {t_sub} tokens in {t1:.2f} s")
+    return out
 
 
 if __name__ == "__main__":

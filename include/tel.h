@@ -192,6 +192,14 @@ typedef struct {
 
 /* tel_window_attention_forward flag: stop after X1 = X + attention branch (y := X1). */
 #define TEL_SWIN_ATTN_ONLY 1
+/* tel_window_attention_forward flag for per-kernel measurement: run stage k alone, reading and
+ * writing the workspace buffers exactly as the whole block does (k = 0: LN1 + shift + window
+ * partition + QKV; 1: window attention; 2: proj + window reverse + unshift + residual; 3: LN2 +
+ * fc1 + GELU; 4: fc2 + residual, which writes y). Stage k reads what stages < k wrote into the
+ * same workspace, so a whole-block call on that workspace must come first; running the five
+ * stages in order equals one whole-block call. Not combinable with TEL_SWIN_ATTN_ONLY
+ * (TEL_EINVAL). */
+#define TEL_SWIN_ONE_STAGE(k) (((k) + 1) << 8)
 
 size_t tel_swin_packed_size(const tel_swin_desc* desc);
 /* One-time preprocessing: weights copied, vectors widened to float32, and the bias table

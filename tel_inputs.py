@@ -84,6 +84,16 @@ def encoder_lengths(cfg: dict, seed: int | None = None) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=cfg["batch"]).astype(np.int32)
 
 
+# Stress shape for the offsets kernel alone: many sequences, T near 2^24 valid tokens.
+OFFSETS_STRESS = dict(batch=65536, max_seq=512, seed=123)
+
+
+def offsets_stress_lengths(cfg: dict = OFFSETS_STRESS) -> np.ndarray:
+    """lens ~ U{0..max_seq} for the offsets stress shape (int32)."""
+    rng = np.random.default_rng(cfg["seed"])
+    return rng.integers(0, cfg["max_seq"] + 1, size=cfg["batch"]).astype(np.int32)
+
+
 def encoder_input(cfg: dict, seed: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     """(lens[B] int32, x_pad[B, S, H]) with x ~ N(0, 1) everywhere, pads included."""
     s = cfg["seed"] if seed is None else seed

@@ -231,3 +231,22 @@ def test_sparse_encoder_desc():
     for bad in (dict(int8_gemm=1), dict(dtype=tel.TEL_F32), dict(hidden=640, heads=10),
                 dict(ffn=3000)):
         assert tel.tel_encoder_packed_size(desc(sparse_2of4=1, **bad)) == 0, bad
+
+
+def test_swin_flag_validation():
+    import torch
+    d = tel.make_swin_desc(2, 56, 56, 96, 3, 7, 3, 384, torch.float16)
+    wsb = tel.tel_swin_workspace_size(d)
+    assert wsb > 0
+    y = ctypes.c_void_p(2 << 20)
+
+    def call(flags):
+        return L.tel_window_attention_forward(ctypes.byref(d), FAKE, FAKE, y, flags, FAKE, wsb,
+                                              None)
+    assert call(2) == tel.TEL_EINVAL                                           # unknown bit
+    assert call(tel.TEL_SWIN_ONE_STAGE(5)) == tel.TEL_EINVAL                   # no stage 5
+    assert call(tel.TEL_SWIN_ONE_STAGE(14)) == tel.TEL_EINVAL
+    assert call(1 << 12) == tel.TEL_EINVAL
+    assert call(tel.TEL_SWIN_ONE_STAGE(0) | tel.TEL_SWIN_ATTN_ONLY) == tel.TEL_EINVAL
+    assert L.tel_window_attention_forward(ctypes.byref(d), FAKE, FAKE, y, 0, FAKE, wsb - 1,
+                                          None) == tel.TEL_EWORKSPACE

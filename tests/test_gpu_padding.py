@@ -34,10 +34,11 @@ def test_offsets_bit_exact(lens, S):
 def test_offsets_large_batch():
     """B = 65,536 sequences of U{0..512} tokens (T near 2^24): the one-workgroup scan's
     chunked path and the per-sequence fill."""
-    rng = np.random.default_rng(123)
-    lens = rng.integers(0, 513, size=65536)
-    cu, po, _ = run_offsets(lens, 512)
-    ref_cu, ref_po = enc.offsets(lens, 512)
+    import tel_inputs as ti
+    lens = ti.offsets_stress_lengths()
+    S = ti.OFFSETS_STRESS["max_seq"]
+    cu, po, _ = run_offsets(lens, S)
+    ref_cu, ref_po = enc.offsets(lens, S)
     assert np.array_equal(cu, ref_cu) and np.array_equal(po, ref_po)
 
 

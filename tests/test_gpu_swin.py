@@ -91,3 +91,34 @@ def test_swin_t_stage1_sampled_images(variant):
     ma, rel = errors(y[pick], ref)
     print(f"swin_t_stage1 images {pick}: max_abs={ma:.3e} rel_frob={rel:.3e}")
     assert_close(y[pick], ref, "f16", "swin_t_stage1 block")
+
+
+@pytest.mark.parametrize("shape", [SMALL[0], dict(batch=2, height=14, width=14, channels=96,
+                                                   heads=3, window=7, shift=3, mlp=384)])
+def test_one_stage_flags_compose_to_the_block(shape):
+    """TEL_SWIN_ONE_STAGE(k) for k = 0..4 in order, on a fresh workspace, gives the whole
+    block's output bit for bit (the per-kernel timings of the benchmark run the stages this
+    way); and one stage re-run on the workspace a whole block left behind reproduces it."""
+    cfg = dict(shape, dtype="f16", seed=7)
+    x = ti.swin_input(cfg)
+    w = ti.swin_block_weights(cfg, variant=True)
+    desc = tel.make_swin_desc(cfg["batch"], cfg["height"], cfg["width"], cfg["channels"],
+                              cfg["heads"], cfg["window"], cfg["shift"], cfg["mlp"], torch.float16,
+                              EPS)
+    packed = tel.alloc_bytes(tel.tel_swin_packed_size(desc))
+    tel.tel_swin_prepare(desc, {k: dev(v, "f16") for k, v in w.items()}, packed)
+    xd = dev(x, "f16")
+    y_full = torch.full_like(xd, float("nan"))
+    ws = tel.alloc_bytes(tel.tel_swin_workspace_size(desc))
+    tel.tel_window_attention_forward(desc, packed, xd, y_full, ws)
+    y_st = torch.full_like(xd, float("nan"))
+    ws2 = tel.alloc_bytes(tel.tel_swin_workspace_size(desc))
+    ws2.fill_(0xFF)
+    for k in range(5):
+        tel.tel_window_attention_forward(desc, packed, xd, y_st, ws2, flags=tel.TEL_SWIN_ONE_STAGE(k))
+    y_re = torch.full_like(xd, float("nan"))
+    tel.tel_window_attention_forward(desc, packed, xd, y_re, ws, flags=tel.TEL_SWIN_ONE_STAGE(4))
+    torch.cuda.synchronize()
+    assert torch.equal(y_st.view(torch.int16), y_full.view(torch.int16))
+    assert torch.equal(y_re.view(torch.int16), y_full.view(torch.int16))
+    assert torch.isfinite(y_full.float()).all()

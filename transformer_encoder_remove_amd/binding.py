@@ -40,6 +40,11 @@ EXPORTS = (
 TEL_SWIN_ATTN_ONLY = 1
 
 
+def TEL_SWIN_ONE_STAGE(k: int) -> int:
+    """tel_window_attention_forward flag: stage k (0..4) of the block alone."""
+    return (k + 1) << 8
+
+
 class TelError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed: {msg}")

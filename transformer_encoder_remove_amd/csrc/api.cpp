@@ -918,7 +918,12 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
                                  void* stream) {
   const int sup = swin_supported(d);
   if (sup != TEL_OK) return sup;
-  if (flags & ~TEL_SWIN_ATTN_ONLY) return TEL_EINVAL;
+  // flags: TEL_SWIN_ATTN_ONLY, or one stage alone (TEL_SWIN_ONE_STAGE(k), k = 0..4) on the
+  // workspace buffers a whole block leaves behind
+  const int stage = (flags >> 8) - 1;
+  if (flags & ~(TEL_SWIN_ATTN_ONLY | (0xf << 8))) return TEL_EINVAL;
+  if (stage >= 5 || (stage >= 0 && (flags & TEL_SWIN_ATTN_ONLY))) return TEL_EINVAL;
+  auto run = [stage](int k) { return stage < 0 || stage == k; };
   if (!packed || !x || !y || !workspace) return TEL_EINVAL;
   if (!aligned256(packed) || !aligned256(workspace) || !aligned16(x) || !aligned16(y))
     return TEL_EINVAL;
@@ -950,16 +955,18 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
     a.ln_eps = d->ln_eps;
     a.ln_gather = 1;
     a.geom = g;
-  } else {
+  } else if (run(0)) {
     TEL_TRY(launch_layernorm_gather(dt, x, zw, F32(L.ln1_g), F32(L.ln1_b), T, C, d->ln_eps, g,
                                     st));
   }
-  TEL_TRY(launch_gemm(dt, a, st));
-  TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh, st));
+  if (run(0)) TEL_TRY(launch_gemm(dt, a, st));
+  if (run(1))
+    TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh,
+                                    st));
   // proj + bias, window reverse + roll(+s) + residual in the epilogue
   a = GemmArgs{EPI_SWIN_SCATTER, ctx, P + L.w_proj, F32(L.b_proj), x, x1, T, C, C, nh};
   a.geom = g;
-  TEL_TRY(launch_gemm(dt, a, st));
+  if (run(2)) TEL_TRY(launch_gemm(dt, a, st));
   if (flags & TEL_SWIN_ATTN_ONLY) return TEL_OK;
   // LN2 on fc1's input rows (or a LayerNorm kernel), fc1 + bias + GELU
   a = GemmArgs{EPI_BIAS_GELU, hh, P + L.w_1, F32(L.b_1), nullptr, f, T, F, C, nh};
@@ -968,13 +975,13 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
     a.ln_g = F32(L.ln2_g);
     a.ln_b = F32(L.ln2_b);
     a.ln_eps = d->ln_eps;
-  } else {
+  } else if (run(3)) {
     TEL_TRY(launch_layernorm(dt, dt, x1, hh, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, C,
                              d->ln_eps, st));
   }
-  TEL_TRY(launch_gemm(dt, a, st));
+  if (run(3)) TEL_TRY(launch_gemm(dt, a, st));
   a = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), x1, y, T, C, F, nh};
-  TEL_TRY(launch_gemm(dt, a, st));
+  if (run(4)) TEL_TRY(launch_gemm(dt, a, st));
   return TEL_OK;
 }
 
