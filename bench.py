@@ -300,6 +300,30 @@ def main():
                 lambda: tel.tel_build_offsets(lens_s, Ss, cu_s, po_s, stream=stream),
                 4.0 * (Bs + (Bs + 1) + Ts)),
         }
+        # the same kernels at a bandwidth-bound size (~0.4 GB of packed rows)
+        Bp, Sp, Hp = (ti.PADDING_STRESS[k] for k in ("batch", "max_seq", "hidden"))
+        lens_p = ti.padding_stress_lengths()
+        Tp = int(lens_p.sum())
+        lens_pd = torch.from_numpy(lens_p).cuda()
+        cu_p = torch.empty(Bp + 1, dtype=torch.int32, device="cuda")
+        po_p = torch.empty(Bp * Sp, dtype=torch.int32, device="cuda")
+        tel.tel_build_offsets(lens_pd, Sp, cu_p, po_p)
+        xpad_p = torch.randn(Bp, Sp, Hp, device="cuda").to(tdt)
+        xpk_p = torch.empty((Tp, Hp), dtype=tdt, device="cuda")
+        ln_p = torch.empty_like(xpk_p)
+        g_p = torch.ones(Hp, device="cuda")
+        b_p = torch.zeros(Hp, device="cuda")
+        hbm_kernels.update({
+            f"remove_padding_stress_T{Tp}": (
+                lambda: tel.tel_remove_padding(xpad_p, xpk_p, po_p, Tp, stream=stream),
+                2.0 * Tp * Hp * el),
+            f"layernorm_stress_T{Tp}": (
+                lambda: tel.tel_layernorm(xpk_p, ln_p, g_p, b_p, ti.LN_EPS, stream=stream),
+                2.0 * Tp * Hp * el),
+            f"rebuild_padding_stress_T{Tp}": (
+                lambda: tel.tel_rebuild_padding(xpk_p, xpad_p, cu_p, stream=stream),
+                (Tp + Bp * Sp) * Hp * el),
+        })
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         for name, (fn, nbytes) in hbm_kernels.items():
             b2b = per_kernel[name]["us"] if name in per_kernel else back_to_back_us(
@@ -311,7 +335,7 @@ def main():
                          "frac_flushed": round(nbytes / fl / 1e3 / PEAK_HBM_GBS, 4)}
             log(f"[bench] hbm {name:28s} {b2b:8.2f} us ({nbytes / b2b / 1e3:7.1f} GB/s) "
                 f"flushed {fl:8.2f} us ({nbytes / fl / 1e3:7.1f} GB/s)")
-        del flush
+        del flush, xpad_p, xpk_p, ln_p, po_s, po_p
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -88,6 +88,16 @@ def encoder_lengths(cfg: dict, seed: int | None = None) -> np.ndarray:
 OFFSETS_STRESS = dict(batch=65536, max_seq=512, seed=123)
 
 
+# Stress shape for the padding and LayerNorm kernels alone: ~0.4 GB of packed rows.
+PADDING_STRESS = dict(batch=1024, max_seq=512, hidden=768, seed=124)
+
+
+def padding_stress_lengths(cfg: dict = PADDING_STRESS) -> np.ndarray:
+    """lens ~ U{0..max_seq} for the padding stress shape (int32)."""
+    rng = np.random.default_rng(cfg["seed"])
+    return rng.integers(0, cfg["max_seq"] + 1, size=cfg["batch"]).astype(np.int32)
+
+
 def offsets_stress_lengths(cfg: dict = OFFSETS_STRESS) -> np.ndarray:
     """lens ~ U{0..max_seq} for the offsets stress shape (int32)."""
     rng = np.random.default_rng(cfg["seed"])

@@ -31,6 +31,17 @@ def test_offsets_bit_exact(lens, S):
     assert (tail == -7).all()                      # nothing written past T
 
 
+@pytest.mark.parametrize("B", [4095, 4096, 4097, 16384, 16385, 20000])
+def test_offsets_tile_boundaries(B):
+    """Batch sizes around the scan's 4096-length tiles and its 4-tile look-ahead groups."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 65, size=B)
+    cu, po, tail = run_offsets(lens, 64)
+    ref_cu, ref_po = enc.offsets(lens, 64)
+    assert np.array_equal(cu, ref_cu) and np.array_equal(po, ref_po)
+    assert (tail == -7).all()
+
+
 def test_offsets_large_batch():
     """B = 65,536 sequences of U{0..512} tokens (T near 2^24): the one-workgroup scan's
     chunked path and the per-sequence fill."""

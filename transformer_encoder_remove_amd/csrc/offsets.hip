@@ -7,50 +7,85 @@
 namespace tel {
 
 constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_VEC = 4;                              // consecutive lengths per thread
+constexpr int SCAN_TILE = SCAN_THREADS * SCAN_VEC;      // lengths per tile
+constexpr int SCAN_AHEAD = 4;                            // tiles loaded before any is scanned
 
-// One workgroup scans any batch size: each thread sums a contiguous chunk, the chunk
-// sums are scanned across the workgroup (wavefront shuffles, then the 16 wave totals),
-// and each thread rewrites its chunk as running sums.
+// One workgroup scans any batch size, tile by tile: thread tid owns the SCAN_VEC
+// consecutive lengths tid * SCAN_VEC .. of each tile (neighbouring threads read
+// neighbouring 16-byte spans), SCAN_AHEAD tiles are requested together so the memory
+// latency is paid once per SCAN_AHEAD * SCAN_TILE lengths, and each tile is scanned in
+// registers (thread-local sums, wavefront shuffle scan, the 16 wave totals in LDS) on top
+// of the running total of the tiles before it.
 __global__ __launch_bounds__(SCAN_THREADS) void scan_lengths(const int32_t* __restrict__ lens,
                                                              int batch, int32_t* __restrict__ cu) {
   __shared__ int32_t wave_tot[SCAN_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = (batch + SCAN_THREADS - 1) / SCAN_THREADS;
-  const int b0 = min(tid * chunk, batch), b1 = min(b0 + chunk, batch);
-  int32_t s = 0;
-  for (int b = b0; b < b1; ++b) s += lens[b];
-  // inclusive scan inside the wavefront
-  int32_t inc = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int32_t v = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += v;
-  }
-  if (lane == 63) wave_tot[wave] = inc;
-  __syncthreads();
-  int32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  int32_t run = before + inc - s;   // exclusive prefix of this thread's chunk
+  const int ntiles = (batch + SCAN_TILE - 1) / SCAN_TILE;
   if (tid == 0) cu[0] = 0;
-  for (int b = b0; b < b1; ++b) {
-    run += lens[b];
-    cu[b + 1] = run;
+  int32_t carry = 0;                                     // sum of all earlier tiles
+  for (int t0 = 0; t0 < ntiles; t0 += SCAN_AHEAD) {
+    int32_t v[SCAN_AHEAD][SCAN_VEC];
+#pragma unroll
+    for (int a = 0; a < SCAN_AHEAD; ++a)
+#pragma unroll
+      for (int e = 0; e < SCAN_VEC; ++e) {
+        const long long i = (long long)(t0 + a) * SCAN_TILE + tid * SCAN_VEC + e;
+        v[a][e] = i < batch ? lens[i] : 0;
+      }
+#pragma unroll
+    for (int a = 0; a < SCAN_AHEAD; ++a) {
+      if (t0 + a >= ntiles) break;                       // uniform across the workgroup
+      int32_t inc_local[SCAN_VEC];
+      int32_t run = 0;
+#pragma unroll
+      for (int e = 0; e < SCAN_VEC; ++e) {
+        run += v[a][e];
+        inc_local[e] = run;
+      }
+      int32_t inc = run;                                 // inclusive scan inside the wavefront
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      if (lane == 63) wave_tot[wave] = inc;
+      __syncthreads();
+      int32_t before = 0, tile_total = 0;
+#pragma unroll
+      for (int w = 0; w < SCAN_THREADS / 64; ++w) {
+        const int32_t t = wave_tot[w];
+        before += w < wave ? t : 0;
+        tile_total += t;
+      }
+      const int32_t excl = carry + before + inc - run;   // lengths before this thread's first
+      const long long i0 = (long long)(t0 + a) * SCAN_TILE + tid * SCAN_VEC;
+#pragma unroll
+      for (int e = 0; e < SCAN_VEC; ++e)
+        if (i0 + e < batch) cu[i0 + e + 1] = excl + inc_local[e];
+      carry += tile_total;
+      __syncthreads();                                   // wave_tot is rewritten next tile
+    }
   }
 }
 
-// One workgroup per sequence writes the offsets of its tokens.
-__global__ __launch_bounds__(256) void fill_padding_offset(const int32_t* __restrict__ cu, int max_seq,
-                                                           int32_t* __restrict__ po) {
-  const int b = blockIdx.x;
+// One wavefront per sequence writes the offsets of its tokens (four sequences per
+// workgroup, so a batch of many short sequences is not bound by workgroup dispatch).
+constexpr int FILL_WAVES = 4;
+__global__ __launch_bounds__(64 * FILL_WAVES) void fill_padding_offset(
+    const int32_t* __restrict__ cu, int batch, int max_seq, int32_t* __restrict__ po) {
+  const int b = blockIdx.x * FILL_WAVES + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= batch) return;
   const int32_t start = cu[b], len = cu[b + 1] - start;
   const int32_t off = b * max_seq - start;
-  for (int i = threadIdx.x; i < len; i += blockDim.x) po[start + i] = off;
+  for (int i = lane; i < len; i += 64) po[start + i] = off;
 }
 
 hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* cu,
                           int32_t* padding_offset, hipStream_t stream) {
   scan_lengths<<<1, SCAN_THREADS, 0, stream>>>(lens, batch, cu);
-  fill_padding_offset<<<batch, 256, 0, stream>>>(cu, max_seq, padding_offset);
+  fill_padding_offset<<<(batch + FILL_WAVES - 1) / FILL_WAVES, 64 * FILL_WAVES, 0, stream>>>(
+      cu, batch, max_seq, padding_offset);
   return hipGetLastError();
 }
 
