@@ -174,12 +174,19 @@ def main():
     cu = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
     Lbar = float((lens.astype(np.float64) ** 2).sum() / lens.sum())
 
-    def resid_gemm(a, w, K, N):
+    reduce_ln = {}
+
+    def resid_gemm(a, w, K, N, name):
         """The output projection / FFN2 GEMM as the layer launches it: bias + residual in
-        the epilogue, or split over k (partial sums) when the layer's plan splits it."""
-        cfg_, sp_ = tel.tel_gemm_partial_plan(tel.DTYPE_CODE[tdt], T, N, K)
-        if sp_ > 1:
-            part = torch.empty((sp_, T, N), device="cuda", dtype=torch.float32)
+        the epilogue (then the LayerNorm kernel), or split over k into partial sums when the
+        layer's plan splits it (then the reduce-LayerNorm kernel, timed as `name`)."""
+        cfg_, sp_, pb_ = tel.tel_gemm_partial_plan(tel.DTYPE_CODE[tdt], T, N, K)
+        if sp_ > 1 and not (int8 or sparse):   # those layers' own GEMMs replace these below
+            part = torch.empty((sp_, T, N), device="cuda",
+                               dtype=torch.float16 if pb_ == 2 else torch.float32)
+            reduce_ln[name] = (lambda: tel.tel_layernorm_reduce(
+                part, sp_, b32(N), hid, pre, g32, b32(N), ti.LN_EPS, stream=stream),
+                part.numel() * part.element_size() + 2.0 * T * N * x.element_size())
             return lambda: tel.tel_gemm_partial(cfg_, sp_, a, w, part, stream=stream)
         return lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_RESID, a, w, b32(N), pre, resid=hid,
                                     stream=stream)
@@ -191,16 +198,19 @@ def main():
         "attention": (lambda: tel.tel_attention_varlen(qkv, ctx, cu, T, max_len, nh, H // nh,
                                                        stream=stream),
                       4.0 * T * H * Lbar, 2.0 * 4 * T * H),
-        "gemm_o_resid": (resid_gemm(ctx, layer_w["w_o"], H, H),
+        "gemm_o_resid": (resid_gemm(ctx, layer_w["w_o"], H, H, "ln1_reduce"),
                          2.0 * T * H * H, 2.0 * (3 * T * H + H * H)),
         "layernorm": (lambda: tel.tel_layernorm(pre, hid, g32, b32(H), ti.LN_EPS, stream=stream),
                       0.0, 2.0 * 2 * T * H),
         "gemm_ffn1_gelu": (lambda: tel.tel_gemm(tel.TEL_EPI_BIAS_GELU, hid, layer_w["w_1"], b32(F),
                                                 ffo, stream=stream),
                            2.0 * T * H * F, 2.0 * (T * H + F * H + T * F)),
-        "gemm_ffn2_resid": (resid_gemm(ffn, layer_w["w_2"], F, H),
+        "gemm_ffn2_resid": (resid_gemm(ffn, layer_w["w_2"], F, H, "ln2_reduce"),
                             2.0 * T * H * F, 2.0 * (T * F + F * H + 2 * T * H)),
     }
+    # the reduce-LayerNorm kernel of a split GEMM: partials read, residual read, y written
+    for name, (fn, nbytes) in reduce_ln.items():
+        kernels[name] = (fn, 0.0, nbytes)
     if int8:
         # the int8 layer's GEMMs one by one (int8 codes in, epilogues as in the layer: head
         # split, dequantise + residual, GELU written as int8 codes); random codes and scales
@@ -268,8 +278,11 @@ def main():
                 "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
     if args.calib_copy:
         calibration_copy(stream)
-    # one layer launches every kernel above once, and the LayerNorm twice
-    layer_sum_us = sum(v["us"] for v in per_kernel.values()) + per_kernel["layernorm"]["us"]
+    # one layer launches every kernel above once, and the LayerNorm kernel once more for each
+    # residual GEMM that is not split (a split one is finished by its reduce kernel)
+    n_ln = 2 - len(reduce_ln)
+    layer_sum_us = sum(v["us"] for v in per_kernel.values()) + \
+        (n_ln - 1) * per_kernel["layernorm"]["us"]
 
     # ---------------------------------------------------------------- HBM-bound kernels
     # achieved bytes/s of the memory-bound kernels against 8 TB/s: back to back (operands

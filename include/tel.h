@@ -342,37 +342,46 @@ int tel_graph_cache(int enable);
  * whose add-bias + residual + LayerNorm epilogue ([SW] section 3, the fused
  * add-bias-residual-LayerNorm) tel_layernorm_reduce finishes.
  *   partials[s][m][n] = sum over k in split s of A[m][k] * W[n][k]
- * A [M][K], W [N][K] of type dtype (TEL_F16, TEL_BF16, TEL_F32, or TEL_I8 codes); partials
- * are float32 for float operands and exact int32 for TEL_I8, splits * M * N words written.
+ * A [M][K], W [N][K] of type dtype (TEL_F16, TEL_BF16, TEL_F32, or TEL_I8 codes); with
+ * partial_bytes 4 the partials are float32 for float operands and exact int32 for TEL_I8;
+ * with partial_bytes 2 (TEL_F16 only, else TEL_EUNSUPPORTED) each partial sum is rounded to
+ * fp16. splits * M * N values written.
  * K is cut into `splits` equal runs of whole 128-byte slices. tile_config as in tel_gemm_ex
  * except -2 (no automatic choice here: see tel_gemm_partial_plan); splits > 1 needs
  * tile_config >= 0 and (K * element size / 128) % splits == 0. K % 8 == 0 (16 for int8),
  * N % 4 == 0, 16-byte aligned pointers. */
 int tel_gemm_partial(int dtype, int tile_config, int splits, const void* A, const void* W,
-                     void* partials, int M, int N, int K, void* stream);
+                     void* partials, int partial_bytes, int M, int N, int K, void* stream);
 
-/* [host] The tile configuration and number of k-splits the encoder layer uses for a
- * partial GEMM of this shape. splits > 1 only when the unsplit tile grid has fewer than
- * about 100 workgroups (few tokens): then the smallest power of two (at most 8) that
- * reaches that many, keeping at least 8 k-slices of 128 bytes per split. The layer runs
- * its output projection and FFN2 split (tel_gemm_partial + tel_layernorm_reduce) exactly
- * when splits > 1. No device work. */
-int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits);
+/* [host] The tile configuration, number of k-splits and partial-sum width (4: float32 /
+ * int32, 2: fp16) the encoder layer uses for a partial GEMM of this shape. splits > 1 when
+ * the unsplit tile grid has fewer than about 100 workgroups (few tokens): the smallest
+ * power of two (at most 8) that reaches that many, keeping at least 8 k-slices of 128 bytes
+ * per split, 32-bit partials. Also, for TEL_F16 only: K >= 2048 where the best unsplit tile
+ * has 64 rows and fills one round of 256 workgroups, and a 128 x 128 tile split in two
+ * still does (BERT-base FFN2): tile 2, splits 2, fp16 partials. The layer runs its output
+ * projection and FFN2 split (tel_gemm_partial + tel_layernorm_reduce) exactly when
+ * splits > 1. No device work. */
+int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits,
+                          int* partial_bytes);
 
 /* LayerNorm of a split GEMM's unfinished sum ([KS] Fig. 11 and [SW] section 3: add-bias,
  * residual and LayerNorm fused after the GEMM):
- *   x[r][n] = sum_s partials[s][r][n] (int32 partials: times dq[n]) + bias[n] + resid[r][n]
+ *   x[r][n] = sum_s partials[s][r][n] (int32 partials: times dq[n]; fp16 partials added in
+ *             float32) + bias[n] + resid[r][n]
  *   x rounded to out_dtype first when round_pre != 0 (the int8 layer's stored values)
  *   y[r][:] = LN(x[r][:]) * gamma + beta, written as out_dtype; also as float32 to y32
  *   and as int8 codes clamp(rne(float(y) * *qinv), +-127) to yq when those are non-null.
- * partials [splits][rows][width] float32 (dq == NULL) or int32 (dq != NULL), 1 <= splits
- * <= 8; bias, dq,
+ * partials [splits][rows][width]: partial_bytes 4: float32 (dq == NULL) or int32 (dq !=
+ * NULL); partial_bytes 2: fp16 (dq == NULL and out_dtype TEL_F16, else TEL_EUNSUPPORTED);
+ * 1 <= splits <= 8; bias, dq,
  * gamma, beta float32 [width]; resid [rows][width] of resid_dtype. (resid_dtype,
  * out_dtype) in {(F16, F16), (BF16, BF16), (F32, BF16), (F32, F32)}; qinv a device scalar. */
-int tel_layernorm_reduce(const void* partials, int splits, const float* dq, const float* bias,
-                         const void* resid, int resid_dtype, void* y, int out_dtype, float* y32,
-                         int8_t* yq, const float* qinv, const float* gamma, const float* beta,
-                         int rows, int width, float eps, int round_pre, void* stream);
+int tel_layernorm_reduce(const void* partials, int splits, int partial_bytes, const float* dq,
+                         const float* bias, const void* resid, int resid_dtype, void* y,
+                         int out_dtype, float* y32, int8_t* yq, const float* qinv,
+                         const float* gamma, const float* beta, int rows, int width, float eps,
+                         int round_pre, void* stream);
 
 #ifdef __cplusplus
 }

@@ -118,9 +118,11 @@ def test_kernel_entry_validation():
 
 
 def test_partial_plan_invariants():
-    """The k-split plan of the output projection / FFN2 GEMMs (host logic): splits only
-    when the unsplit tile grid is under 100 workgroups, a power of two up to 8, whole
-    128-byte slices with at least 8 per split, and never more than needed."""
+    """The k-split plan of the output projection / FFN2 GEMMs (host logic): 32-bit partial
+    sums only when the unsplit tile grid is under 100 workgroups, a power of two up to 8,
+    whole 128-byte slices with at least 8 per split, and never more than needed; fp16
+    partials only for fp16 operands, K >= 2048, a 64-row unsplit tile filling one round of
+    256 workgroups, and then two splits of the 128 x 128 tile that still fill one round."""
     # (BM, BN) of the pipelined tile table, in its order (gemm.hip PIPE_CFGS)
     cfgs = [(128, 256), (128, 192), (128, 128), (64, 128), (64, 64), (128, 256), (256, 128),
             (128, 128), (64, 128), (192, 192), (96, 128)]
@@ -128,25 +130,34 @@ def test_partial_plan_invariants():
     for dt, es in ((tel.TEL_F16, 2), (tel.TEL_BF16, 2), (tel.TEL_F32, 4), (tel.TEL_I8, 1)):
         for M in (1, 17, 128, 640, 2557, 14336, 24576):
             for N, K in ((768, 768), (768, 3072), (1024, 1024), (1024, 4096), (64, 256)):
-                cfg, sp = tel.tel_gemm_partial_plan(dt, M, N, K)
+                cfg, sp, pb = tel.tel_gemm_partial_plan(dt, M, N, K)
                 nk = K * es // 128
                 assert 0 <= cfg < tel.tel_gemm_tile_configs() and sp in (1, 2, 4, 8), \
                     (dt, M, N, K, cfg, sp)
+                assert pb in (2, 4) and (pb == 4 or dt == tel.TEL_F16)
                 bm, bn = cfgs[cfg]
                 tiles = -(-M // bm) * -(-N // bn)
-                if sp > 1:
+                if pb == 2:
+                    assert (cfg, sp) == (2, 2) and K >= 2048 and 2 * tiles <= 256
+                    assert nk % 2 == 0 and nk // 2 >= 8
+                elif sp > 1:
                     assert tiles < 100 and nk % sp == 0 and nk // sp >= 8
                     assert tiles * sp // 2 < 100          # the smallest split that suffices
                 else:
                     assert tiles >= 100 or nk % 2 or nk // 2 < 8
     # a 128-token batch at BERT-large shape: output projection split in 2, FFN2 in 4
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (4, 2)
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (4, 4)
-    # 2557 tokens at BERT-base shape: no split
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (4, 2, 4)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (4, 4, 4)
+    # 2557 tokens at BERT-base shape: output projection unsplit; FFN2 (K 3072, 240 tiles of
+    # 64 x 128) as 2 x 120 tiles of 128 x 128 with fp16 partials; bf16 and int8 unsplit
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 768)[1] == 1
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 3072)[1] == 1
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 3072) == (2, 2, 2)
+    assert tel.tel_gemm_partial_plan(tel.TEL_BF16, 2557, 768, 3072)[1:] == (1, 4)
+    assert tel.tel_gemm_partial_plan(tel.TEL_I8, 2900, 768, 3072)[1:] == (1, 4)
+    # BERT-large throughput batch: many rounds of 128 x 256 tiles, no split
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 13537, 1024, 4096)[1] == 1
     # K not a whole number of 128-byte slices: register-staged kernel, no split
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 100, 64, 72) == (-1, 1)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 100, 64, 72) == (-1, 1, 4)
 
 
 def test_workspace_non_decreasing_in_tokens():
@@ -162,22 +173,25 @@ def test_workspace_non_decreasing_in_tokens():
 def test_partial_gemm_and_reduce_validation():
     f16, bf16, f32 = tel.TEL_F16, tel.TEL_BF16, tel.TEL_F32
     P = L.tel_gemm_partial
-    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 0, 64, 64, None) == tel.TEL_OK          # empty
-    assert P(f16, 0, 0, FAKE, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL     # splits
-    assert P(f16, -2, 1, FAKE, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL    # no auto
-    assert P(f16, -1, 2, FAKE, FAKE, FAKE, 16, 64, 128, None) == tel.TEL_EUNSUPPORTED
-    assert P(f16, 0, 3, FAKE, FAKE, FAKE, 16, 64, 256, None) == tel.TEL_EUNSUPPORTED  # 4 slices
-    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 16, 64, 72, None) == tel.TEL_EUNSUPPORTED   # 144 B
-    assert P(tel.TEL_I8, -1, 1, FAKE, FAKE, FAKE, 16, 64, 24, None) == tel.TEL_EUNSUPPORTED
-    assert P(f16, 0, 1, FAKE_ODD, FAKE, FAKE, 16, 64, 64, None) == tel.TEL_EINVAL
+    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 4, 0, 64, 64, None) == tel.TEL_OK          # empty
+    assert P(f16, 0, 0, FAKE, FAKE, FAKE, 4, 16, 64, 64, None) == tel.TEL_EINVAL     # splits
+    assert P(f16, -2, 1, FAKE, FAKE, FAKE, 4, 16, 64, 64, None) == tel.TEL_EINVAL    # no auto
+    assert P(f16, -1, 2, FAKE, FAKE, FAKE, 4, 16, 64, 128, None) == tel.TEL_EUNSUPPORTED
+    assert P(f16, 0, 3, FAKE, FAKE, FAKE, 4, 16, 64, 256, None) == tel.TEL_EUNSUPPORTED
+    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 4, 16, 64, 72, None) == tel.TEL_EUNSUPPORTED   # 144 B
+    assert P(tel.TEL_I8, -1, 1, FAKE, FAKE, FAKE, 4, 16, 64, 24, None) == tel.TEL_EUNSUPPORTED
+    assert P(f16, 0, 1, FAKE_ODD, FAKE, FAKE, 4, 16, 64, 64, None) == tel.TEL_EINVAL
+    assert P(f16, 0, 1, FAKE, FAKE, FAKE, 3, 16, 64, 64, None) == tel.TEL_EINVAL     # width
+    assert P(bf16, 0, 1, FAKE, FAKE, FAKE, 2, 16, 64, 64, None) == tel.TEL_EUNSUPPORTED
+    assert P(tel.TEL_I8, 0, 1, FAKE, FAKE, FAKE, 2, 16, 64, 128, None) == tel.TEL_EUNSUPPORTED
     R = L.tel_layernorm_reduce
-    ok = [FAKE, 1, None, FAKE, FAKE, f16, FAKE, f16, None, None, None, FAKE, FAKE, 4, 64,
+    ok = [FAKE, 1, 4, None, FAKE, FAKE, f16, FAKE, f16, None, None, None, FAKE, FAKE, 4, 64,
           1e-5, 0, None]
 
     def call(**kw):
         a = list(ok)
-        names = ["part", "splits", "dq", "bias", "resid", "rdt", "y", "odt", "y32", "yq",
-                 "qinv", "g", "b", "rows", "width", "eps", "round", "stream"]
+        names = ["part", "splits", "pbytes", "dq", "bias", "resid", "rdt", "y", "odt", "y32",
+                 "yq", "qinv", "g", "b", "rows", "width", "eps", "round", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return R(*a)
@@ -191,6 +205,9 @@ def test_partial_gemm_and_reduce_validation():
     assert call(yq=FAKE) == tel.TEL_EINVAL                                     # no qinv
     assert call(resid=FAKE_ODD) == tel.TEL_EINVAL
     assert call(eps=float("nan")) == tel.TEL_EINVAL
+    assert call(pbytes=8) == tel.TEL_EINVAL
+    assert call(pbytes=2, rdt=bf16, odt=bf16) == tel.TEL_EUNSUPPORTED          # fp16 only
+    assert call(pbytes=2, dq=FAKE) == tel.TEL_EUNSUPPORTED                     # not int32
 
 
 def test_sparse_2of4_validation():

@@ -63,7 +63,7 @@ def test_partial_gemm_int8_exact(M, N, K):
     A, W = torch.from_numpy(qa).cuda(), torch.from_numpy(qw).cuda()
     ref = q8.int8_matmul(qa, qw)
     nk = K // 128
-    cfgs = [tel.tel_gemm_partial_plan(tel.TEL_I8, M, N, K)] + \
+    cfgs = [tel.tel_gemm_partial_plan(tel.TEL_I8, M, N, K)[:2]] + \
         [(c, s) for c in range(5) for s in (1, 2, 4) if nk % s == 0]
     for cfg, sp in cfgs:
         P = _partials(A, W, cfg, sp, M, N, dtype=torch.int32)
@@ -78,10 +78,56 @@ def test_partial_gemm_bert_base_plan(dtype, K):
     the encoder layer takes."""
     M, N = 2557, 768
     a, w = _fp_operands(M, N, K, dtype, seed=K)
-    cfg, sp = tel.tel_gemm_partial_plan(tel.DTYPE_CODE[TORCH_DT[dtype]], M, N, K)
-    P = _partials(dev(a, dtype), dev(w, dtype), cfg, sp, M, N)
-    assert_close(host(P).sum(axis=0), enc.linear(a, w, np.zeros(N)), "f32",
-                 f"plan ({cfg}, {sp})")
+    cfg, sp, pb = tel.tel_gemm_partial_plan(tel.DTYPE_CODE[TORCH_DT[dtype]], M, N, K)
+    P = _partials(dev(a, dtype), dev(w, dtype), cfg, sp, M, N,
+                  dtype=torch.float16 if pb == 2 else torch.float32)
+    parts = host(P).astype(np.float64)
+    # fp16 partial sums: each split is its k range's product rounded once to fp16
+    tol = "f16" if pb == 2 else "f32"
+    assert_close(parts.sum(axis=0), enc.linear(a, w, np.zeros(N)), tol, f"plan ({cfg}, {sp})")
+    kr = K // sp
+    for i in range(sp):
+        ref_i = enc.linear(a[:, i * kr:(i + 1) * kr], w[:, i * kr:(i + 1) * kr], np.zeros(N))
+        assert_close(parts[i], ref_i, tol, f"split {i} of plan ({cfg}, {sp})")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 400, 512), (17, 1028, 1024), (2557, 768, 3072)])
+def test_partial_gemm_fp16_partials(M, N, K):
+    """16-bit partial sums (fp16 operands): every pipelined tile configuration and split
+    count; each split's sums are its k range's product rounded to fp16."""
+    a, w = _fp_operands(M, N, K, "f16", seed=3 * M + K)
+    A, W = dev(a, "f16"), dev(w, "f16")
+    nk = K * 2 // 128
+    refs = {}
+    for sp in (1, 2, 4):
+        kr = K // sp
+        for i in {0, sp - 1}:
+            refs[sp, i] = enc.linear(a[:, i * kr:(i + 1) * kr], w[:, i * kr:(i + 1) * kr],
+                                     np.zeros(N))
+    for cfg in range(tel.tel_gemm_tile_configs()):
+        for sp in (1, 2, 4):
+            if nk % sp:
+                continue
+            parts = host(_partials(A, W, cfg, sp, M, N, dtype=torch.float16)).astype(np.float64)
+            assert np.isfinite(parts).all(), (cfg, sp)
+            for i in {0, sp - 1}:
+                assert_close(parts[i], refs[sp, i], "f16", f"fp16 split {i}/{sp} cfg {cfg}")
+
+
+@pytest.mark.parametrize("width", [768, 1024])
+@pytest.mark.parametrize("sp", [1, 2, 3])
+def test_layernorm_reduce_fp16_partials(width, sp):
+    rows = 301
+    parts, bias, gamma, beta, resid = _ln_case(rows, width, sp, seed=5 * width + sp)
+    p16 = parts.astype(np.float16)
+    r = ti.to_storage(resid, "f16")
+    ref = enc.layer_norm(p16.astype(np.float64).sum(axis=0) + bias + r.astype(np.float64),
+                         gamma, beta, EPS)
+    y = torch.full((rows, width), float("nan"), dtype=torch.float16, device="cuda")
+    tel.tel_layernorm_reduce(torch.from_numpy(p16).cuda(), sp, dev_f32(bias), dev(r, "f16"), y,
+                             dev_f32(gamma), dev_f32(beta), EPS)
+    torch.cuda.synchronize()
+    assert_close(host(y), ref, "f16", f"reduce LN, fp16 partials, width {width} splits {sp}")
 
 
 def _ln_case(rows, width, sp, seed):

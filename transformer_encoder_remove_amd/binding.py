@@ -116,9 +116,10 @@ _SIG = {
     "tel_swin_workspace_size": (SZ, [ctypes.POINTER(tel_swin_desc)]),
     "tel_window_attention_forward": (I, [ctypes.POINTER(tel_swin_desc), P, P, P, I, P, SZ, P]),
     "tel_window_partition_layernorm": (I, [P, P, P, P, I, I, I, I, I, I, F, I, P]),
-    "tel_gemm_partial": (I, [I, I, I, P, P, P, I, I, I, P]),
-    "tel_gemm_partial_plan": (I, [I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
-    "tel_layernorm_reduce": (I, [P, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
+    "tel_gemm_partial": (I, [I, I, I, P, P, P, I, I, I, I, P]),
+    "tel_gemm_partial_plan": (I, [I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I),
+                                  ctypes.POINTER(I)]),
+    "tel_layernorm_reduce": (I, [P, I, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
     "tel_graph_cache": (I, [I]),
     "tel_gemm_i8": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, P]),
     "tel_prune_2of4": (I, [P, P, P, I, I, I, P]),
@@ -318,20 +319,22 @@ def tel_graph_cache(enable: int = -1) -> int:
     return lib.tel_graph_cache(enable)
 
 
-def tel_gemm_partial_plan(dtype: int, M: int, N: int, K: int) -> tuple[int, int]:
-    """(tile_config, splits) the encoder layer uses for a partial GEMM of this shape."""
-    cfg, sp = I(), I()
-    _check("tel_gemm_partial_plan", lib.tel_gemm_partial_plan(dtype, M, N, K, ctypes.byref(cfg),
-                                                               ctypes.byref(sp)))
-    return cfg.value, sp.value
+def tel_gemm_partial_plan(dtype: int, M: int, N: int, K: int) -> tuple[int, int, int]:
+    """(tile_config, splits, partial_bytes) the encoder layer uses for a partial GEMM of
+    this shape; partial_bytes 4 = float32 (int32 for int8), 2 = fp16."""
+    cfg, sp, pb = I(), I(), I()
+    _check("tel_gemm_partial_plan", lib.tel_gemm_partial_plan(
+        dtype, M, N, K, ctypes.byref(cfg), ctypes.byref(sp), ctypes.byref(pb)))
+    return cfg.value, sp.value, pb.value
 
 
 def tel_gemm_partial(tile_config: int, splits: int, A, W, partials, stream=None):
+    """partials float32 / int32 (4-byte partial sums) or float16 (fp16 partial sums)."""
     M, K = A.shape
     N = W.shape[0]
     _check("tel_gemm_partial", lib.tel_gemm_partial(
-        dtype_code(A.dtype), tile_config, splits, _ptr(A), _ptr(W), _ptr(partials), M, N, K,
-        _stream(stream)))
+        dtype_code(A.dtype), tile_config, splits, _ptr(A), _ptr(W), _ptr(partials),
+        partials.element_size(), M, N, K, _stream(stream)))
 
 
 def tel_layernorm_reduce(partials, splits: int, bias, resid, y, gamma, beta, eps: float,
@@ -339,7 +342,8 @@ def tel_layernorm_reduce(partials, splits: int, bias, resid, y, gamma, beta, eps
                          stream=None):
     rows, width = y.shape
     _check("tel_layernorm_reduce", lib.tel_layernorm_reduce(
-        _ptr(partials), splits, _ptr(dq), _ptr(bias), _ptr(resid), dtype_code(resid.dtype),
+        _ptr(partials), splits, partials.element_size(), _ptr(dq), _ptr(bias), _ptr(resid),
+        dtype_code(resid.dtype),
         _ptr(y), dtype_code(y.dtype), _ptr(y32), _ptr(yq), _ptr(qinv), _ptr(gamma), _ptr(beta),
         rows, width, eps, int(round_pre), _stream(stream)))
 

@@ -129,9 +129,9 @@ inline int gemm_dtype(const tel_encoder_desc* d) { return d->int8_gemm ? (int)DT
 size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
   const int dt = gemm_dtype(d), H = d->hidden, F = d->ffn;
   auto need = [&](size_t t) {
-    int cfg;
-    const int sp = std::max(gemm_partial_plan(dt, (int)t, H, H, &cfg),
-                            gemm_partial_plan(dt, (int)t, H, F, &cfg));
+    int cfg, p16;
+    const int sp = std::max(gemm_partial_plan(dt, (int)t, H, H, &cfg, &p16),
+                            gemm_partial_plan(dt, (int)t, H, F, &cfg, &p16));
     return sp > 1 ? (size_t)sp * t : 0;
   };
   // tile counts, hence plans, change only at multiples of 64 rows: the largest need
@@ -225,9 +225,9 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   void* pre = ws + W.pre;
   void* part = ws + W.part;
   void* h1 = ws + W.h1;
-  int cfg_o, cfg_2;
-  const int sp_o = gemm_partial_plan(DT_I8, T, H, H, &cfg_o);
-  const int sp_2 = gemm_partial_plan(DT_I8, T, H, F, &cfg_2);
+  int cfg_o, cfg_2, p16;   // int8 partials are int32 (p16 stays 0)
+  const int sp_o = gemm_partial_plan(DT_I8, T, H, H, &cfg_o, &p16);
+  const int sp_2 = gemm_partial_plan(DT_I8, T, H, F, &cfg_2, &p16);
 
   if (!link.xq_in)
     TEL_TRY(launch_quantize_act(DT_F16, x, (int8_t*)(ws + W.xq), (size_t)T * H, inv + 0, 0.f, st));
@@ -300,9 +300,9 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   // 2:4 layers: compressed weights on the sparse MFMA, never split over k
   const bool sparse = d->sparse_2of4 != 0;
   auto IDX = [&](size_t off) { return sparse ? (const uint16_t*)(P + off) : nullptr; };
-  int cfg_o, cfg_2;
-  const int sp_o = sparse ? 1 : gemm_partial_plan(dt, T, H, H, &cfg_o);
-  const int sp_2 = sparse ? 1 : gemm_partial_plan(dt, T, H, F, &cfg_2);
+  int cfg_o, cfg_2, p16_o = 0, p16_2 = 0;
+  const int sp_o = sparse ? 1 : gemm_partial_plan(dt, T, H, H, &cfg_o, &p16_o);
+  const int sp_2 = sparse ? 1 : gemm_partial_plan(dt, T, H, F, &cfg_2, &p16_2);
 
   GemmArgs g{};
   // QKV projection + bias, written head-split for the attention kernel
@@ -311,15 +311,17 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   TEL_TRY(launch_gemm(dt, g, st));
   TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
   const int pre_dt = f32s ? (int)DT_F32 : dt;
-  // output projection + bias + residual, then LayerNorm; split over k (float32
-  // partials, bias + residual + LayerNorm in the reduce kernel) when few tokens leave
-  // the GPU idle
+  // output projection + bias + residual, then LayerNorm; split over k (float32 partials,
+  // or fp16 ones for long-K fp16 shapes; bias + residual + LayerNorm in the reduce kernel)
+  // when the plan says the split pays
   if (sp_o > 1) {
     g = GemmArgs{EPI_PARTIAL, ctx, P + L.w_o, nullptr, nullptr, part, T, H, H, nh};
     g.splits = sp_o;
+    g.part16 = p16_o;
     TEL_TRY(launch_gemm_cfg(dt, cfg_o, g, st));
-    const LnReduceArgs r{part, sp_o, nullptr, F32(L.b_o), x, dt, h1, dt, h1f, nullptr, nullptr,
-                         F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, 0};
+    LnReduceArgs r{part, sp_o, nullptr, F32(L.b_o), x, dt, h1, dt, h1f, nullptr, nullptr,
+                   F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, 0};
+    r.part16 = p16_o;
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
@@ -336,10 +338,11 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   if (sp_2 > 1) {
     g = GemmArgs{EPI_PARTIAL, f, P + L.w_2, nullptr, nullptr, part, T, H, F, nh};
     g.splits = sp_2;
+    g.part16 = p16_2;
     TEL_TRY(launch_gemm_cfg(dt, cfg_2, g, st));
-    const LnReduceArgs r{part, sp_2, nullptr, F32(L.b_2), res2, f32s ? (int)DT_F32 : dt, y, dt,
-                         nullptr, nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps,
-                         0};
+    LnReduceArgs r{part, sp_2, nullptr, F32(L.b_2), res2, f32s ? (int)DT_F32 : dt, y, dt,
+                   nullptr, nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, 0};
+    r.part16 = p16_2;
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), res2, pre, T, H, F, nh, f32s, f32s};
@@ -1021,9 +1024,11 @@ int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seq
 }
 
 int tel_gemm_partial(int dtype, int tile_config, int splits, const void* A, const void* W,
-                     void* partials, int M, int N, int K, void* stream) {
+                     void* partials, int partial_bytes, int M, int N, int K, void* stream) {
   if (!float_type(dtype) && dtype != DT_I8) return TEL_EUNSUPPORTED;
   if (M < 0 || N <= 0 || K <= 0 || splits < 1) return TEL_EINVAL;
+  if (partial_bytes != 4 && partial_bytes != 2) return TEL_EINVAL;
+  if (partial_bytes == 2 && dtype != DT_F16) return TEL_EUNSUPPORTED;
   if (tile_config < -1 || tile_config >= gemm_tile_configs()) return TEL_EINVAL;
   if (M == 0) return TEL_OK;
   if (!A || !W || !partials) return TEL_EINVAL;
@@ -1034,22 +1039,29 @@ int tel_gemm_partial(int dtype, int tile_config, int splits, const void* A, cons
   if (splits > 1 && (tile_config < 0 || (kb / 128) % splits)) return TEL_EUNSUPPORTED;
   GemmArgs g{EPI_PARTIAL, A, W, nullptr, nullptr, partials, M, N, K, 1};
   g.splits = splits;
+  g.part16 = partial_bytes == 2;
   return status_of(launch_gemm_cfg(dtype, tile_config, g, as_stream(stream)));
 }
 
-int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits) {
-  if (!tile_config || !splits) return TEL_EINVAL;
+int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits,
+                          int* partial_bytes) {
+  if (!tile_config || !splits || !partial_bytes) return TEL_EINVAL;
   if (!float_type(dtype) && dtype != DT_I8) return TEL_EUNSUPPORTED;
   if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
-  *splits = gemm_partial_plan(dtype, M, N, K, tile_config);
+  int p16 = 0;
+  *splits = gemm_partial_plan(dtype, M, N, K, tile_config, &p16);
+  *partial_bytes = p16 ? 2 : 4;
   return TEL_OK;
 }
 
-int tel_layernorm_reduce(const void* partials, int splits, const float* dq, const float* bias,
-                         const void* resid, int resid_dtype, void* y, int out_dtype, float* y32,
-                         int8_t* yq, const float* qinv, const float* gamma, const float* beta,
-                         int rows, int width, float eps, int round_pre, void* stream) {
+int tel_layernorm_reduce(const void* partials, int splits, int partial_bytes, const float* dq,
+                         const float* bias, const void* resid, int resid_dtype, void* y,
+                         int out_dtype, float* y32, int8_t* yq, const float* qinv,
+                         const float* gamma, const float* beta, int rows, int width, float eps,
+                         int round_pre, void* stream) {
   if (rows < 0 || width <= 0 || splits < 1 || splits > 8 || !(eps >= 0.f)) return TEL_EINVAL;
+  if (partial_bytes != 4 && partial_bytes != 2) return TEL_EINVAL;
+  if (partial_bytes == 2 && (out_dtype != DT_F16 || dq)) return TEL_EUNSUPPORTED;
   const bool combo = (resid_dtype == DT_F16 && out_dtype == DT_F16) ||
                      (resid_dtype == DT_BF16 && out_dtype == DT_BF16) ||
                      (resid_dtype == DT_F32 && (out_dtype == DT_BF16 || out_dtype == DT_F32));
@@ -1061,8 +1073,9 @@ int tel_layernorm_reduce(const void* partials, int splits, const float* dq, cons
     if (!aligned16(q)) return TEL_EINVAL;
   if ((dq && !aligned16(dq)) || (y32 && !aligned16(y32)) || (yq && ((uintptr_t)yq % 8)))
     return TEL_EINVAL;
-  const LnReduceArgs a{partials, splits, dq, bias, resid, resid_dtype, y, out_dtype, y32, yq,
-                       qinv, gamma, beta, rows, width, eps, round_pre ? 1 : 0};
+  LnReduceArgs a{partials, splits, dq, bias, resid, resid_dtype, y, out_dtype, y32, yq,
+                 qinv, gamma, beta, rows, width, eps, round_pre ? 1 : 0};
+  a.part16 = partial_bytes == 2;
   return status_of(launch_layernorm_reduce(a, as_stream(stream)));
 }
 

@@ -57,7 +57,14 @@ __device__ __forceinline__ int8_t quantize_code(float v, float inv) {
 template <int EPI, typename T, typename TR, typename TO, typename ACC>
 __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
                                                ACC acc) {
-  if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
+  if constexpr (EPI == EPI_PARTIAL && sizeof(TO) == 2) {
+    // partial sums rounded to the 16-bit output type
+    Vec4<TO> out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(acc[i]);
+    *reinterpret_cast<Vec4<TO>*>(e.C + (size_t)m * e.N + n) = out;
+    return;
+  } else if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
     // the raw 32-bit accumulators (int32 for int8 operands), no epilogue arithmetic
     *reinterpret_cast<ACC*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
     return;
@@ -122,7 +129,13 @@ template <int EPI, typename T, typename TR, typename TO>
 __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int m, int n,
                                                 const float* acc, const float* bb,
                                                 const float* dd, const Vec8<TR>& r) {
-  if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
+  if constexpr (EPI == EPI_PARTIAL && sizeof(TO) == 2) {
+    Vec8<TO> o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.v[i] = from_f32<TO>(acc[i]);
+    *reinterpret_cast<Vec8<TO>*>(e.C + (size_t)m * e.N + n) = o;
+    return;
+  } else if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
     Vec8<int32_t> o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.v[i] = __float_as_int(acc[i]);   // staged as raw bits
@@ -1145,7 +1158,16 @@ static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
     case EPI_BIAS_GELU: launch_cfg<T, EPI_BIAS_GELU, T, T>(cfg, a, stream); break;
     case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, T, T>(cfg, a, stream); break;
     case EPI_SWIN_SCATTER: launch_cfg<T, EPI_SWIN_SCATTER, T, T>(cfg, a, stream); break;
-    case EPI_PARTIAL: launch_cfg<T, EPI_PARTIAL, T, float>(cfg, a, stream); break;
+    case EPI_PARTIAL:
+      if constexpr (std::is_same<T, f16>::value) {
+        if (a.part16) {
+          launch_cfg<T, EPI_PARTIAL, T, T>(cfg, a, stream);
+          break;
+        }
+      }
+      if (a.part16) return hipErrorInvalidValue;
+      launch_cfg<T, EPI_PARTIAL, T, float>(cfg, a, stream);
+      break;
     case EPI_BIAS_RESID:
       if constexpr (std::is_same<T, bf16>::value) {
         if (a.resid_f32 && a.out_f32) {
@@ -1224,19 +1246,43 @@ static int pick_cfg(const GemmArgs& a, int elem_bytes) {
 // partial-sum traffic dominate). Returns 1 when splitting does not pay.
 constexpr int SPLIT_MIN_TILES = 100, SPLIT_MIN_SLICES = 8, SPLIT_MAX = 8;
 
-int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg) {
+//
+// A second rule, for fp16 operands: long-K, narrow-N shapes whose best unsplit tile is a
+// 64-row one filling a single round (BERT-base FFN2: 2557 x 768, K 3072, 240 tiles of
+// 64 x 128). With every compute unit streaming its operands at once the loop is bound by
+// that stream (measured: the per-slice time follows the bytes copied per compute unit,
+// ~65 GB/s each, not the MFMA count), and a 64 x BN tile streams (64 + BN) rows per
+// 64 x BN outputs. A 128 x 128 tile split in two over k keeps the single round (the same
+// number of workgroups) and streams 2/3 of the bytes per flop; its partial sums are
+// stored as fp16 (half the bytes of float32 for the GEMM to write and the reduce kernel
+// to read) and added in float32 by the reduce-LayerNorm kernel.
+constexpr int SPLIT16_MIN_K = 2048, SPLIT16_CFG = 2;
+
+static int tiles_of(int cfg, int M, int N) {
+  const PipeCfg& p = PIPE_CFGS[cfg];
+  return ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+}
+
+int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16) {
   const int es = dtype_size(dtype);
+  *part16 = 0;
   GemmArgs a{};
   a.M = M; a.N = N; a.K = K;
   *cfg = (M > 0 && N > 0 && K > 0) ? pick_cfg(a, es) : -1;
   if (*cfg < 0) return 1;
-  const PipeCfg& p = PIPE_CFGS[*cfg];
-  const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  const long tiles = tiles_of(*cfg, M, N);
   const int nk = (int)((long long)K * es / 128);
   int sp = 1;
   while (sp < SPLIT_MAX && tiles * sp < SPLIT_MIN_TILES && nk % (2 * sp) == 0 &&
          nk / (2 * sp) >= SPLIT_MIN_SLICES)
     sp *= 2;
+  if (sp == 1 && dtype == DT_F16 && K >= SPLIT16_MIN_K && PIPE_CFGS[*cfg].bm == 64 &&
+      tiles <= 256 && 2L * tiles_of(SPLIT16_CFG, M, N) <= 256 && nk % 2 == 0 &&
+      nk / 2 >= SPLIT_MIN_SLICES) {
+    *cfg = SPLIT16_CFG;
+    *part16 = 1;
+    return 2;
+  }
   return sp;
 }
 
@@ -1309,6 +1355,7 @@ hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t st
   if (a.splits < 1 || (a.splits > 1 && (cfg < 0 || ((long long)a.K * es / 128) % a.splits)))
     return hipErrorInvalidValue;
   if (a.splits > 1 && a.epi != EPI_PARTIAL) return hipErrorInvalidValue;
+  if (a.part16 && (a.epi != EPI_PARTIAL || dtype != DT_F16)) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_I8: return run_epi_i8(cfg, a, stream);
     case DT_F16: return run_epi<f16>(cfg, a, stream);

@@ -13,7 +13,8 @@ enum Epi {
   EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4,
   EPI_SWIN_SCATTER = 5,  // bias + residual, row m written to image row geom.src_row(m)
   EPI_PARTIAL = 6        // raw 32-bit accumulators (float32, or int32 for int8 operands) of
-                         // k-split s at C + s * M * N; a reduce kernel finishes the sum
+                         // k-split s at C + s * M * N, or those sums rounded to fp16
+                         // (GemmArgs::part16, fp16 operands); a reduce kernel finishes the sum
 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
@@ -49,6 +50,7 @@ struct GemmArgs {
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
   SwinGeom geom{};              // EPI_SWIN_SCATTER
   int splits = 1;               // pipelined kernel only: K split over this many workgroups
+  int part16 = 0;               // EPI_PARTIAL, fp16 operands: partial sums stored as fp16
   // LayerNorm applied to each row of A before the product (skinny kernel only, see
   // gemm_rows_supported): A row r is LN(A[r]) * ln_g + ln_b, read from row geom.src_row(r)
   // when ln_gather is set (the shifted-window partition)
@@ -68,8 +70,9 @@ hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t st
 int gemm_tile_configs();
 int gemm_sparse_tile_configs();   // tile table of the 2:4-sparse kernel
 // Tile configuration and number of k-splits for a partial-sum GEMM (EPI_PARTIAL) of this
-// shape; returns the splits (>= 1) and sets *cfg.
-int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg);
+// shape; returns the splits (>= 1), sets *cfg, and *part16 = 1 when the partial sums are
+// to be stored as fp16 (fp16 operands only), else 0.
+int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16);
 
 // attention.hip
 bool attention_supported(int dtype, int head_dim);
@@ -90,6 +93,7 @@ struct LnReduceArgs {
   const void* resid; int resid_dt;
   void* y; int out_dt; float* y32; int8_t* yq; const float* qinv;
   const float* gamma; const float* beta; int rows, width; float eps; int round_pre;
+  int part16 = 0;   // partial sums stored as fp16 (out type fp16 only), else 32-bit
 };
 hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream);
 hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,

@@ -111,7 +111,8 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
 }
 
 // LayerNorm of a sum that a split GEMM left unfinished: the row is assembled from the
-// k-split partial sums (float32, or int32 dequantised by dq[n]), the bias and the residual,
+// k-split partial sums (float32, fp16 (part16) added in float32, or int32 dequantised by
+// dq[n]), the bias and the residual,
 // then normalised as above. This is where the output projection's and FFN2's bias +
 // residual + LayerNorm epilogue ([SW] section 3, the fused add-bias-residual-LayerNorm)
 // happens once the GEMM's k-splits are summed.
@@ -120,12 +121,13 @@ constexpr int LNR_MAX_SPLITS = 8;
 struct LnRedParams {
   const void* part; int nsplit; const float* dq; const float* bias; const void* resid;
   void* y; float* y32; int8_t* yq; const float* qinv;
-  const float* gamma; const float* beta; int rows; float eps; int round_pre;
+  const float* gamma; const float* beta; int rows; float eps; int round_pre; int part16;
 };
 
 template <typename TR, typename TO, int G, int NV>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_reduce_kernel(LnRedParams p) {
   constexpr int H = G * NV * 8;
+  constexpr bool TO_HALF = std::is_same<TO, f16>::value;
   const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
   if (row >= p.rows) return;
@@ -160,6 +162,20 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_reduce_kernel(LnRedParam
       load8(p.bias + c0, b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] = (float)acc[e] * dq[e] + b[e];
+    } else if (TO_HALF && p.part16) {   // fp16 partial sums, added in float32
+      load8((const f16*)p.part + off, a);
+#pragma unroll
+      for (int sp = 1; sp < LNR_MAX_SPLITS; ++sp) {
+        if (sp >= p.nsplit) break;
+        float t[8];
+        load8((const f16*)p.part + sp * split_stride + off, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += t[e];
+      }
+      float b[8];
+      load8(p.bias + c0, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += b[e];
     } else {
       load8((const float*)p.part + off, a);
 #pragma unroll
@@ -395,8 +411,9 @@ hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream) {
   int G, nv;
   if (!pick_ln(a.width, &G, &nv) || a.nsplit < 1 || a.nsplit > LNR_MAX_SPLITS)
     return hipErrorInvalidValue;
+  if (a.part16 && (a.out_dt != DT_F16 || a.dq)) return hipErrorInvalidValue;
   const LnRedParams p{a.part, a.nsplit, a.dq, a.bias, a.resid, a.y, a.y32, a.yq, a.qinv,
-                      a.gamma, a.beta, a.rows, a.eps, a.round_pre};
+                      a.gamma, a.beta, a.rows, a.eps, a.round_pre, a.part16};
   bool ok = false;
   if (a.resid_dt == DT_F16 && a.out_dt == DT_F16) ok = run_lnr<f16, f16>(G, nv, p, stream);
   else if (a.resid_dt == DT_BF16 && a.out_dt == DT_BF16) ok = run_lnr<bf16, bf16>(G, nv, p, stream);
