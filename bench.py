@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-hbm", action="store_true",
                     help="skip the memory-bound kernels' flushed-cache timings")
+    ap.add_argument("--summarise-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TABLE"),
+                    help="no GPU work: turn the rocprofv3 FETCH_SIZE and WRITE_SIZE runs of "
+                         "`bench.py --calib-copy` (output directories) and the kernel table "
+                         "that run wrote (gpurun_out/kernel_table.json) into "
+                         "profiles/hbm_traffic.json")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the scale of HBM counters)")
     return ap.parse_args()
@@ -60,6 +65,8 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.summarise_traffic:
+        return summarise_traffic(*args.summarise_traffic)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the encoder "
               "forward shards by sequence with no collectives, and this build measures one "
@@ -277,6 +284,7 @@ def main():
                 "traffic": measured_traffic(args.workload, "i8" if int8 else dt, dom),
                 "avg_us": round(d["us"], 3), "flops_per_launch": d["flops"]}
     if args.calib_copy:
+        write_kernel_table(args, "i8" if int8 else dt, per_kernel)
         calibration_copy(stream)
     # one layer launches every kernel above once, and the LayerNorm kernel once more for each
     # residual GEMM that is not split (a split one is finished by its reduce kernel)
@@ -359,9 +367,11 @@ def main():
                 layer_sum_us, step_ms=step_ms, hbm=hbm)
 
 
-KERNEL_SOURCES = ("transformer_encoder_remove_amd/csrc/gemm.hip",
-                  "transformer_encoder_remove_amd/csrc/device.h",
-                  "transformer_encoder_remove_amd/csrc/launch.h")
+# every kernel source: counters taken on other sources than the ones built now are stale
+KERNEL_SOURCES = tuple(sorted(
+    os.path.join("transformer_encoder_remove_amd", "csrc", f)
+    for f in os.listdir(os.path.join(ROOT, "transformer_encoder_remove_amd", "csrc"))
+    if f.endswith((".hip", ".h", ".cpp"))))
 
 
 def kernel_sources_digest() -> str:
@@ -389,6 +399,106 @@ def measured_traffic(workload: str, dtype: str, kernel: str):
                 r.get("kernel") == kernel and r.get("sources_sha256") == kernel_sources_digest():
             return r.get("bytes_per_launch")
     return None
+
+
+KERNEL_TABLE = os.path.join(ROOT, "gpurun_out", "kernel_table.json")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def write_kernel_table(args, dtype: str, per_kernel: dict):
+    """What the counter runs need to attribute dispatches: the per-kernel timing launches
+    each kernel 1 + kernel_reps times, in this order, after the timed steps; then the
+    calibration copies follow. Library kernels only (torch's spin and fill kernels are
+    filtered out by name when the counters are summarised)."""
+    os.makedirs(os.path.dirname(KERNEL_TABLE), exist_ok=True)
+    rec = {"workload": args.workload, "dtype": dtype, "reps": args.kernel_reps,
+           "kernels": [{"name": k, "bytes": v["bytes"]} for k, v in per_kernel.items()]}
+    with open(KERNEL_TABLE, "w") as f:
+        json.dump(rec, f, indent=1)
+
+
+def _counter_rows(d: str, counter: str):
+    """(kernel name, value) per dispatch, in dispatch order, from a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(name, v) for (_, name), v in sorted(per.items())]
+
+
+def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str = KERNEL_TABLE):
+    """profiles/hbm_traffic.json from two `rocprofv3 --pmc` runs (FETCH_SIZE, WRITE_SIZE)
+    of `bench.py --calib-copy --steps 1 --warmup 1 --no-cpu --no-hbm`: each kernel's counters
+    averaged over its kernel_reps timed launches, scaled by what the same counters read for
+    the calibration copies (256 MiB read and 256 MiB written each); entries of other
+    workloads or dtypes already in the file are kept."""
+    with open(table_path) as f:
+        table = json.load(f)
+    reps, names = table["reps"], [k["name"] for k in table["kernels"]]
+    out = {"kernels": []}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as f:
+            old = json.load(f)
+        out["kernels"] = [k for k in old.get("kernels", [])
+                          if (k.get("workload"), k.get("dtype")) != (table["workload"],
+                                                                    table["dtype"])]
+    calib, per_kernel = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        if len(copies) < 3:
+            raise SystemExit(f"{counter}: calibration copies not found in {d}")
+        calib[counter] = sum(copies[-3:]) / 3
+        lib = [(n, v) for n, v in rows if n.startswith("_ZN3tel") or n.startswith("tel::")]
+        block = lib[-(1 + reps) * len(names):]
+        for i, name in enumerate(names):
+            launches = block[i * (1 + reps) + 1:(i + 1) * (1 + reps)]
+            per_kernel.setdefault(name, {})[counter] = sum(v for _, v in launches) / reps
+            per_kernel[name]["symbol"] = launches[0][0]
+    true_kib = 256 * 1024
+    ff, wf = true_kib / calib["FETCH_SIZE"], true_kib / calib["WRITE_SIZE"]
+    digest = kernel_sources_digest()
+    for k in table["kernels"]:
+        c = per_kernel[k["name"]]
+        total = (c["FETCH_SIZE"] * ff + c["WRITE_SIZE"] * wf) * 1024
+        out["kernels"].append({
+            "workload": table["workload"], "dtype": table["dtype"], "kernel": k["name"],
+            "symbol": c["symbol"], "fetch_size_kib": round(c["FETCH_SIZE"], 2),
+            "write_size_kib": round(c["WRITE_SIZE"], 2), "bytes_per_launch": int(total),
+            "algorithmic_bytes": int(k["bytes"]), "ratio": round(total / k["bytes"], 2),
+            "sources_sha256": digest})
+    out["description"] = (
+        "HBM traffic per launch of the layer / block kernels, launched one by one as bench.py's "
+        "per-kernel timing does; counters per dispatch, averaged over the timed launches. "
+        "bytes_per_launch = FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor (KiB), the "
+        "factors being what a plain 256 MiB device copy reads on the same counters. "
+        "sources_sha256: SHA-256 of " + " + ".join(KERNEL_SOURCES) + " when the counters were "
+        "taken; bench.py reports a figure only while it matches.")
+    out["calibration"] = {"copy": "__amd_rocclr_copyBuffer, 256 MiB device to device",
+                          "fetch_size_kib": round(calib["FETCH_SIZE"], 1),
+                          "write_size_kib": round(calib["WRITE_SIZE"], 1),
+                          "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
+    out["commands"] = [
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE "
+        "--output-format csv -d $REPO/gpurun_out/pmc_fetch -o bench -- python3 $REPO/bench.py "
+        "--steps 1 --warmup 1 --no-cpu --no-hbm --kernel-reps 3 --calib-copy [--workload W]",
+        "the same with --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write",
+        "python3 bench.py --summarise-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write "
+        "gpurun_out/kernel_table.json (the table the counter runs wrote)"]
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    for k in out["kernels"]:
+        print(f"{k['workload']:16s} {k['dtype']:4s} {k['kernel']:28s} {k['bytes_per_launch'] / 1e6:9.2f} MB"
+              f" (algorithmic {k['algorithmic_bytes'] / 1e6:9.2f} MB, x{k['ratio']})")
 
 
 def calibration_copy(stream, mib: int = 256, reps: int = 3):
@@ -531,6 +641,9 @@ def bench_swin(args):
         per_kernel[name] = dict(us=us, bytes=bpt * T, flops=fpt * T)
         log(f"[bench] kernel {name:28s} {us:9.2f} us  {bpt * T / us / 1e3:8.1f} GB/s"
             f"  {fpt * T / us / 1e6:7.1f} TFLOP/s")
+    if args.calib_copy:
+        write_kernel_table(args, "f16", per_kernel)
+        calibration_copy(stream)
     dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
     d = per_kernel[dom]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(d["bytes"] / d["us"] / 1e3, 1),
