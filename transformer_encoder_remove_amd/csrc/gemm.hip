@@ -297,7 +297,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 // ------------------------------------------------------------------ pipelined variant
 // Same contract as gemm_nt_kernel, for K % (128 bytes) == 0. Warp-specialised:
 //  * WM x WN compute wavefronts read MFMA fragments from LDS and run the MFMAs;
-//  * 2 producer wavefronts copy k-slices from global memory straight into LDS with the
+//  * DENSE_PRODUCERS producer wavefronts copy k-slices from global memory straight into LDS with the
 //    gfx950 direct path (global_load_lds_dwordx4: lane i's 16 bytes land at LDS base +
 //    16 * i, no VGPR staging), keeping S - 1 slices in flight in an S-stage LDS ring.
 // One barrier per slice: a producer passes barrier kt once slice kt has landed (its own
@@ -307,8 +307,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 // compiler's wait-count analysis waits for every outstanding LDS read before each MFMA
 // block, serialising LDS reads and MFMAs. Compute wavefronts double-buffer fragments in
 // registers: the next k-step's reads (also across a slice boundary) are issued before
-// the current k-step's MFMAs. Two producers, because one wavefront can have at most 63
-// copies outstanding.
+// the current k-step's MFMAs. Several producers: one wavefront can have at most 63 copies
+// outstanding, and the loops are bound by how fast each compute unit streams its operands,
+// which more copies in flight raise.
 //
 // LDS rows are 128 bytes (8 chunks of 16 bytes) with no padding; bank conflicts are avoided
 // by an XOR swizzle: chunk c of row r is stored in slot c ^ (r % 8). A copy instruction
@@ -319,7 +320,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 // the 8 XCDs in turn, so ids are regrouped so that each XCD walks a contiguous run of
 // tiles (M-fastest), i.e. the tiles that share weight columns share that XCD's L2.
 
+// Producer wavefronts per workgroup: four in the dense kernel (measured against two at
+// BERT-base shapes, bit-identical results: FFN2's 64x128 tile 21.3 -> 18.4 us, QKV 15.7 ->
+// 14.8, O 8.4 -> 7.7, FFN1 19.4 -> 18.8), two in the 2:4-sparse kernel, whose stages are
+// split between exactly two (a 59-block stage as 30 + 29).
 constexpr int PIPE_PRODUCERS = 2;
+constexpr int DENSE_PRODUCERS = 4;
 
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -449,7 +455,7 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
-__global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
+__global__ __launch_bounds__((WM * WN + DENSE_PRODUCERS) * 64) void gemm_nt_pipe_kernel(
     const T* __restrict__ A, const T* __restrict__ W, int K, int splits, int gn,
     EpiArgs<T, TR, TO> e) {
   using MF = Mfma<T>;
@@ -462,10 +468,10 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int NB = (BM + BN) / 8;                 // 1 KiB blocks per slice
-  constexpr int LJ = NB / PIPE_PRODUCERS;           // copies per producer per slice
+  constexpr int LJ = NB / DENSE_PRODUCERS;           // copies per producer per slice
   constexpr int STAGE = (BM + BN) * 128;
   constexpr int INFLIGHT = LJ * (S - 2) < 63 ? LJ * (S - 2) : 63;
-  static_assert(NB % PIPE_PRODUCERS == 0 && BM % 8 == 0 && BN % 8 == 0, "copy split");
+  static_assert(NB % DENSE_PRODUCERS == 0 && BM % 8 == 0 && BN % 8 == 0, "copy split");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
   static_assert(KS % 2 == 0, "k-steps per slice must be even");
   static_assert(S >= 2, "stages");
@@ -493,13 +499,13 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
   if constexpr (EPI == EPI_PARTIAL) e.C += (size_t)split * M * N;
 
   if (wave >= NW) {
-    // ---------------- producer: block b = p + PIPE_PRODUCERS * j of every slice
+    // ---------------- producer: block b = p + DENSE_PRODUCERS * j of every slice
     const int p = wave - NW;
     const T* src[LJ];
     const int chunk = (lane & 7) ^ (lane >> 3);
 #pragma unroll
     for (int j = 0; j < LJ; ++j) {
-      const int b = p + PIPE_PRODUCERS * j;
+      const int b = p + DENSE_PRODUCERS * j;
       if (b < BM / 8) {
         src[j] = A + (size_t)min(m0 + b * 8 + (lane >> 3), M - 1) * K + chunk * VEC;
       } else {
@@ -514,7 +520,7 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_nt_pipe_
       for (int j = 0; j < LJ; ++j)
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1)))*)(src[j] + koff),
-            (void __attribute__((address_space(3)))*)(dst + j * PIPE_PRODUCERS * 1024), 16, 0, 0);
+            (void __attribute__((address_space(3)))*)(dst + j * DENSE_PRODUCERS * 1024), 16, 0, 0);
     };
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) issue(s, min(s, nk - 1));
@@ -1081,7 +1087,7 @@ static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
   const int grid = tm * tn * a.splits;
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
-      <<<grid, (c.wm * c.wn + PIPE_PRODUCERS) * 64, 0, stream>>>(
+      <<<grid, (c.wm * c.wn + DENSE_PRODUCERS) * 64, 0, stream>>>(
           (const T*)a.A, (const T*)a.W, a.K, a.splits, xcd_group_width(tm, tn, c.bm, c.bn), e);
 }
 
