@@ -612,13 +612,14 @@ def bench_swin(args):
     for _ in range(args.warmup):
         tel.tel_window_attention_forward(desc, packed, x, y, ws, stream=stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for i in range(args.steps):
+        evs[i].record(stream)
         tel.tel_window_attention_forward(desc, packed, x, y, ws, stream=stream)
-    e1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = step_stats([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     value = T / (ms / 1e3)
     log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {value / 1e9:.3f} G tokens/s per block")
 
@@ -674,7 +675,7 @@ def bench_swin(args):
         "config": {"workload": f"{args.workload}: shifted-window block, LN1 + shift + partition, "
                                "QKV, window attention (bias + mask), proj + unshift + residual, "
                                "LN2, MLP", **{k: v for k, v in cfg.items() if k != "dtype"}},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "step_ms": step_ms,
         "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},
         "block_kernel_sum_us": round(sum(v["us"] for v in per_kernel.values()), 3),
     }
