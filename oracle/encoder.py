@@ -15,7 +15,8 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = [
-    "offsets", "remove_padding", "rebuild_padding", "linear", "softmax", "attention",
+    "offsets", "remove_padding", "rebuild_padding", "offsets_from_mask", "remove_padding_mask",
+    "rebuild_padding_mask", "linear", "softmax", "attention",
     "layer_norm", "gelu", "encoder_layer", "encoder_stack", "encoder_forward",
 ]
 
@@ -62,6 +63,41 @@ def rebuild_padding(x_packed: np.ndarray, lens, max_seq: int) -> np.ndarray:
         out[b, :lens[b]] = x_packed[t:t + lens[b]]
         t += lens[b]
     return out
+
+
+def offsets_from_mask(mask):
+    """Offset mask of padding removal in its general form ([KS] Fig. 9: tokens are removed
+    where the mask says so, wherever they sit): mask [B, S], nonzero = valid, holes
+    allowed. Packed order is sequence by sequence, positions increasing. cu[b+1] = cu[b] +
+    (valid positions of b); the packed token t that sits at position s of sequence b has
+    padding_offset[t] = b * S + s - t, so its padded row is t + padding_offset[t] as in
+    offsets() (to which this reduces for right-padded masks).
+    Returns (cu_seqlens[B+1], padding_offset[T]) as int64."""
+    m = np.asarray(mask) != 0
+    if m.ndim != 2:
+        raise ValueError("mask must be [B, S]")
+    B, S = m.shape
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(m.sum(axis=1))
+    rows = np.flatnonzero(m.reshape(-1)).astype(np.int64)   # b * S + s, b-major, s increasing
+    return cu, rows - np.arange(rows.shape[0], dtype=np.int64)
+
+
+def remove_padding_mask(x_pad: np.ndarray, mask) -> np.ndarray:
+    """Packed rows of a [B, S, W] batch: its valid positions in packed order."""
+    m = np.asarray(mask) != 0
+    B, S, W = x_pad.shape
+    return x_pad.reshape(B * S, W)[np.flatnonzero(m.reshape(-1))]
+
+
+def rebuild_padding_mask(x_packed: np.ndarray, mask) -> np.ndarray:
+    """Inverse of remove_padding_mask: packed rows back to their positions, every position
+    the mask marks invalid zero."""
+    m = np.asarray(mask) != 0
+    B, S = m.shape
+    out = np.zeros((B * S, x_packed.shape[-1]), dtype=x_packed.dtype)
+    out[np.flatnonzero(m.reshape(-1))] = x_packed
+    return out.reshape(B, S, -1)
 
 
 def linear(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:

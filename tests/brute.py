@@ -47,10 +47,11 @@ def _lists(w):
     return {k: np.asarray(v, np.float64).tolist() for k, v in w.items()}
 
 
-def encoder_layer_padded(x_pad, lens, w, heads, eps):
+def encoder_layer_padded(x_pad, lens, w, heads, eps, mask=None):
     """Post-LN encoder layer on the padded batch [B, S, H]: every position is projected,
-    keys at positions >= lens[b] are masked out. Returns [B, S, H] (pad rows computed
-    too, but only valid rows are meaningful)."""
+    keys at positions >= lens[b] are masked out (or, with mask [B, S], keys where the mask
+    is zero). Returns [B, S, H] (pad rows computed too, but only valid rows are
+    meaningful)."""
     x_pad = np.asarray(x_pad, np.float64)
     B, S, H = x_pad.shape
     d = H // heads
@@ -66,7 +67,7 @@ def encoder_layer_padded(x_pad, lens, w, heads, eps):
                 q = qkv[i][h * d:(h + 1) * d]
                 scores = [_dot(q, qkv[j][H + h * d:H + (h + 1) * d]) / math.sqrt(d)
                           for j in range(S)]
-                valid = [j < L for j in range(S)]
+                valid = [bool(mask[b][j]) if mask is not None else j < L for j in range(S)]
                 if not any(valid):
                     continue
                 p = _softmax_masked(scores, valid)

@@ -61,6 +61,79 @@ def test_offsets_brute_force_random():
             assert cu[b] == sum(lens[:b])
 
 
+def test_offsets_mask_golden():
+    """Hand-worked offset masks with holes (tests/golden/offsets_mask.txt, after [KS] Fig. 9)."""
+    cases, cur = [], None
+    for tok in golden_rows("offsets_mask.txt"):
+        if tok[0] == "case":
+            cur = {"mask": []}
+            cases.append(cur)
+        elif tok[0] == "mask":
+            cur["mask"].append([int(v) for v in tok[1:]])
+        else:
+            cur[tok[0]] = [int(v) for v in tok[1:]]
+    assert len(cases) == 4
+    for c in cases:
+        assert all(len(r) == c["S"][0] for r in c["mask"])
+        cu, po = enc.offsets_from_mask(np.array(c["mask"]))
+        assert cu.tolist() == c["cu_seqlens"], c
+        assert po.tolist() == c["padding_offset"], c
+
+
+def test_offsets_mask_brute_force_and_right_padded_case():
+    rng = np.random.default_rng(12)
+    for _ in range(30):
+        B, S = int(rng.integers(1, 9)), int(rng.integers(1, 17))
+        mask = rng.random((B, S)) < rng.random()
+        cu, po = enc.offsets_from_mask(mask)
+        rows, t, cu_ref = [], 0, [0]           # walk the batch position by position
+        for b in range(B):
+            for s in range(S):
+                if mask[b, s]:
+                    rows.append(b * S + s)
+                    t += 1
+            cu_ref.append(t)
+        assert cu.tolist() == cu_ref
+        assert (np.arange(len(po)) + po).tolist() == rows
+        lens = rng.integers(0, S + 1, size=B)  # a right-padded mask is the lengths form
+        right = np.arange(S)[None, :] < lens[:, None]
+        for a, b_ in zip(enc.offsets_from_mask(right), enc.offsets(lens, S)):
+            assert a.tolist() == b_.tolist()
+
+
+def test_remove_rebuild_mask_roundtrip():
+    rng = np.random.default_rng(13)
+    mask = rng.random((4, 7)) < 0.6
+    x = rng.standard_normal((4, 7, 5))
+    xp = enc.remove_padding_mask(x, mask)
+    assert xp.shape == (int(mask.sum()), 5)
+    y = enc.rebuild_padding_mask(xp, mask)
+    assert np.array_equal(y[mask], x[mask]) and not y[~mask].any()
+    assert np.array_equal(enc.remove_padding_mask(y, mask), xp)
+
+
+def test_layer_with_holes_matches_masked_padded_layer():
+    """A layer on the packed tokens of a mask with holes equals, on the valid positions,
+    the textbook layer over the padded batch with those keys masked out: the pure-Python
+    brute force and torch's nn.TransformerEncoderLayer with src_key_padding_mask."""
+    B, S, H, nh, F = 3, 7, 32, 2, 64
+    rng = np.random.default_rng(14)
+    mask = rng.random((B, S)) < 0.6
+    mask[:, 3] = True                                  # no sequence fully masked
+    cfg = ti.custom_encoder_config(B, S, [S] * B, H, nh, F, dtype="f32", seed=15)
+    _, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets_from_mask(mask)
+    y = enc.encoder_layer(enc.remove_padding_mask(x.astype(np.float64), mask), cu, w, nh, EPS)
+    ref = brute.encoder_layer_padded(x, [S] * B, w, nh, EPS, mask=mask.tolist())
+    assert np.abs(ref[mask] - y).max() <= 1e-10
+    layer = _torch_layer(w, H, nh, F)
+    with torch.no_grad():
+        t = layer(torch.from_numpy(x.astype(np.float64)),
+                  src_key_padding_mask=torch.from_numpy(~mask)).numpy()
+    assert np.abs(t[mask] - y).max() <= 1e-10
+
+
 def test_offsets_reject_bad_lengths():
     with pytest.raises(ValueError):
         enc.offsets([3, 9], 8)
