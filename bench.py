@@ -309,7 +309,16 @@ def main():
         lens_s = torch.from_numpy(stress).cuda()
         cu_s = torch.empty(Bs + 1, dtype=torch.int32, device="cuda")
         po_s = torch.empty(Bs * Ss, dtype=torch.int32, device="cuda")
+        # the mask form at the same stress shape: random holes, about half the positions valid
+        mask_s = torch.from_numpy(
+            (np.random.default_rng(ti.OFFSETS_STRESS["seed"]).random((Bs, Ss)) < 0.5)
+            .astype(np.uint8)).cuda()
+        Tm = int(mask_s.sum().item())
+        cu_m = torch.empty(Bs + 1, dtype=torch.int32, device="cuda")
         hbm_kernels = {
+            f"offsets_mask_stress_B{Bs}_T{Tm}": (
+                lambda: tel.tel_build_offsets_mask(mask_s, cu_m, po_s, stream=stream),
+                1.0 * Bs * Ss + 4.0 * ((Bs + 1) + Tm)),
             "attention": (kernels["attention"][0], per_kernel["attention"]["bytes"]),
             "layernorm": (kernels["layernorm"][0], per_kernel["layernorm"]["bytes"]),
             "remove_padding": (lambda: tel.tel_remove_padding(x, xp_o, pad_o, T, stream=stream),
@@ -356,7 +365,7 @@ def main():
                          "frac_flushed": round(nbytes / fl / 1e3 / PEAK_HBM_GBS, 4)}
             log(f"[bench] hbm {name:28s} {b2b:8.2f} us ({nbytes / b2b / 1e3:7.1f} GB/s) "
                 f"flushed {fl:8.2f} us ({nbytes / fl / 1e3:7.1f} GB/s)")
-        del flush, xpad_p, xpk_p, ln_p, po_s, po_p
+        del flush, xpad_p, xpk_p, ln_p, po_s, po_p, mask_s
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -86,6 +86,28 @@ int tel_remove_padding(const void* x_pad, void* x_packed, const int32_t* padding
 int tel_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu_seqlens,
                         int batch, int max_seq, int width, int dtype, void* stream);
 
+/* The offset mask in its general form ([KS] Fig. 9: tokens removed wherever the mask says,
+ * holes allowed). mask [batch][max_seq] uint8 (device; 0 = padding, anything else = valid).
+ * Packed order: sequence by sequence, positions increasing.
+ *   cu_seqlens[b+1] = cu_seqlens[b] + (valid positions of sequence b), cu_seqlens[0] = 0;
+ *   padding_offset[t] = b*max_seq + s - t for the packed token t at position s of sequence b,
+ *   so tel_remove_padding gathers the valid rows unchanged and cu_seqlens feeds the layer.
+ * padding_offset: capacity batch*max_seq int32 (the first batch entries also serve as
+ * scratch during the call; T = cu_seqlens[batch] entries hold the result). The caller learns
+ * T (and the longest sequence) from the mask or by reading cu_seqlens back.
+ * batch >= 1, max_seq >= 1, batch*max_seq < 2^31 (else TEL_EUNSUPPORTED). Three launches
+ * (per-sequence counts, the tiled scan of tel_build_offsets, per-sequence compaction). */
+int tel_build_offsets_mask(const uint8_t* mask, int batch, int max_seq, int32_t* cu_seqlens,
+                           int32_t* padding_offset, void* stream);
+
+/* Padding rebuild for the mask form, inverse of tel_remove_padding with the offsets of
+ * tel_build_offsets_mask: x_pad[t + padding_offset[t]][:] = x_packed[t][:] for t < total_tokens,
+ * and 0 for every row whose mask byte is 0. x_pad [batch*max_seq][width]; type and alignment
+ * rules as tel_remove_padding; total_tokens == 0 zeroes every masked row only. */
+int tel_rebuild_padding_mask(const void* x_packed, void* x_pad, const uint8_t* mask,
+                             const int32_t* padding_offset, int total_tokens, int batch,
+                             int max_seq, int width, int dtype, void* stream);
+
 /* ------------------------------------------------------------------ encoder layer */
 
 /* Post-LN BERT encoder layer ([SW] section 1; [KS] Fig. 6):

@@ -267,3 +267,20 @@ def test_swin_flag_validation():
     assert call(tel.TEL_SWIN_ONE_STAGE(0) | tel.TEL_SWIN_ATTN_ONLY) == tel.TEL_EINVAL
     assert L.tel_window_attention_forward(ctypes.byref(d), FAKE, FAKE, y, 0, FAKE, wsb - 1,
                                           None) == tel.TEL_EWORKSPACE
+
+
+def test_offsets_mask_validation():
+    f16 = tel.TEL_F16
+    assert L.tel_build_offsets_mask(None, 2, 8, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets_mask(FAKE, 0, 8, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets_mask(FAKE, 2, 0, FAKE, FAKE, None) == tel.TEL_EINVAL
+    assert L.tel_build_offsets_mask(FAKE, 1 << 20, 1 << 12, FAKE, FAKE, None) == \
+        tel.TEL_EUNSUPPORTED
+    R = L.tel_rebuild_padding_mask
+    assert R(FAKE, FAKE, FAKE, FAKE, -1, 2, 8, 64, f16, None) == tel.TEL_EINVAL
+    assert R(FAKE, FAKE, FAKE, FAKE, 17, 2, 8, 64, f16, None) == tel.TEL_EINVAL    # T > B*S
+    assert R(FAKE, FAKE, None, FAKE, 3, 2, 8, 64, f16, None) == tel.TEL_EINVAL     # no mask
+    assert R(FAKE, FAKE, FAKE, None, 3, 2, 8, 64, f16, None) == tel.TEL_EINVAL
+    assert R(FAKE, FAKE_ODD, FAKE, FAKE, 3, 2, 8, 64, f16, None) == tel.TEL_EINVAL
+    assert R(FAKE, FAKE, FAKE, FAKE, 3, 2, 8, 12, f16, None) == tel.TEL_EUNSUPPORTED
+    assert R(FAKE, FAKE, FAKE, FAKE, 3, 2, 8, 64, 9, None) == tel.TEL_EINVAL

@@ -35,7 +35,8 @@ EXPORTS = (
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
     "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
-    "tel_gemm_2of4_tile_configs", "tel_gemm_2of4",
+    "tel_gemm_2of4_tile_configs", "tel_gemm_2of4", "tel_build_offsets_mask",
+    "tel_rebuild_padding_mask",
 )
 TEL_SWIN_ATTN_ONLY = 1
 
@@ -125,6 +126,8 @@ _SIG = {
     "tel_prune_2of4": (I, [P, P, P, I, I, I, P]),
     "tel_gemm_2of4_tile_configs": (I, []),
     "tel_gemm_2of4": (I, [I, I, I, P, P, P, P, P, P, I, I, I, I, P]),
+    "tel_build_offsets_mask": (I, [P, I, I, P, P, P]),
+    "tel_rebuild_padding_mask": (I, [P, P, P, P, I, I, I, I, I, P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -189,6 +192,21 @@ def tel_rebuild_padding(x_packed, x_pad, cu_seqlens, stream=None):
     _check("tel_rebuild_padding", lib.tel_rebuild_padding(
         _ptr(x_packed), _ptr(x_pad), _ptr(cu_seqlens), B, S, W, dtype_code(x_pad.dtype),
         _stream(stream)))
+
+
+def tel_build_offsets_mask(mask, cu_seqlens, padding_offset, stream=None):
+    """mask [B, S] uint8/bool device tensor; cu_seqlens [B+1], padding_offset [>= B*S] int32."""
+    B, S = mask.shape
+    _check("tel_build_offsets_mask", lib.tel_build_offsets_mask(
+        _ptr(mask), B, S, _ptr(cu_seqlens), _ptr(padding_offset), _stream(stream)))
+
+
+def tel_rebuild_padding_mask(x_packed, x_pad, mask, padding_offset, total_tokens: int,
+                             stream=None):
+    B, S, W = x_pad.shape
+    _check("tel_rebuild_padding_mask", lib.tel_rebuild_padding_mask(
+        _ptr(x_packed), _ptr(x_pad), _ptr(mask), _ptr(padding_offset), total_tokens, B, S, W,
+        dtype_code(x_pad.dtype), _stream(stream)))
 
 
 def make_encoder_desc(hidden, heads, ffn, dtype: torch.dtype, eps=1e-5, int8_gemm=False,

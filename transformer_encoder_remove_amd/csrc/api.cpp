@@ -484,6 +484,30 @@ int tel_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu_seq
                                           (int)row_bytes, as_stream(stream)));
 }
 
+int tel_build_offsets_mask(const uint8_t* mask, int batch, int max_seq, int32_t* cu_seqlens,
+                           int32_t* padding_offset, void* stream) {
+  if (!mask || !cu_seqlens || !padding_offset) return TEL_EINVAL;
+  if (batch <= 0 || max_seq <= 0) return TEL_EINVAL;
+  if ((long long)batch * max_seq > INT32_MAX) return TEL_EUNSUPPORTED;
+  return status_of(launch_offsets_mask(mask, batch, max_seq, cu_seqlens, padding_offset,
+                                       as_stream(stream)));
+}
+
+int tel_rebuild_padding_mask(const void* x_packed, void* x_pad, const uint8_t* mask,
+                             const int32_t* padding_offset, int total_tokens, int batch,
+                             int max_seq, int width, int dtype, void* stream) {
+  if (batch <= 0 || max_seq <= 0 || width <= 0 || total_tokens < 0) return TEL_EINVAL;
+  if ((long long)total_tokens > (long long)batch * max_seq) return TEL_EINVAL;
+  if (!float_type(dtype) && dtype != DT_I8) return TEL_EINVAL;
+  if (!x_pad || !mask || (total_tokens > 0 && (!x_packed || !padding_offset))) return TEL_EINVAL;
+  if (!aligned16(x_pad) || (x_packed && !aligned16(x_packed))) return TEL_EINVAL;
+  const long long row_bytes = (long long)width * dtype_size(dtype);
+  if (row_bytes % 16) return TEL_EUNSUPPORTED;
+  return status_of(launch_rebuild_padding_mask(x_packed, x_pad, mask, padding_offset,
+                                               total_tokens, batch, max_seq, (int)row_bytes,
+                                               as_stream(stream)));
+}
+
 size_t tel_encoder_packed_size(const tel_encoder_desc* d) {
   if (desc_supported(d) != TEL_OK) return 0;
   return layer_layout(d).total;

@@ -22,7 +22,15 @@ inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
 // offsets.hip
 hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* cu,
                           int32_t* padding_offset, hipStream_t stream);
+// Offsets from a 0/1 mask [batch][max_seq] (holes allowed); padding_offset capacity
+// batch * max_seq, its first batch entries also scratch for the per-sequence counts.
+hipError_t launch_offsets_mask(const uint8_t* mask, int batch, int max_seq, int32_t* cu,
+                               int32_t* padding_offset, hipStream_t stream);
 // padding.hip (row_bytes % 16 == 0)
+// Rebuild for the mask form: rows with mask 0 zeroed, packed row t to row t + po[t].
+hipError_t launch_rebuild_padding_mask(const void* x_packed, void* x_pad, const uint8_t* mask,
+                                       const int32_t* po, int total_tokens, int batch,
+                                       int max_seq, int row_bytes, hipStream_t stream);
 hipError_t launch_remove_padding(const void* x_pad, void* x_packed, const int32_t* padding_offset,
                                  int total_tokens, int row_bytes, hipStream_t stream);
 hipError_t launch_rebuild_padding(const void* x_packed, void* x_pad, const int32_t* cu, int batch,

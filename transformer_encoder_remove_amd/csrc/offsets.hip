@@ -81,6 +81,60 @@ __global__ __launch_bounds__(64 * FILL_WAVES) void fill_padding_offset(
   for (int i = lane; i < len; i += 64) po[start + i] = off;
 }
 
+// The offset mask in its general form: valid positions anywhere in a sequence (holes
+// allowed), packed sequence by sequence with positions increasing. One wavefront per
+// sequence (four per workgroup, so many short sequences are not bound by workgroup
+// dispatch) counts its valid positions 64 at a time with a ballot; the counts are scanned
+// as lengths; then one wavefront per sequence gives each valid position its packed index
+// t = cu[b] + (valid positions before it) from the same ballots and writes
+// padding_offset[t] = b*S + s - t.
+constexpr int MASK_WAVES = 4;
+
+__global__ __launch_bounds__(64 * MASK_WAVES) void count_mask_kernel(
+    const uint8_t* __restrict__ mask, int batch, int max_seq, int32_t* __restrict__ counts) {
+  const int b = blockIdx.x * MASK_WAVES + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= batch) return;
+  const uint8_t* row = mask + (size_t)b * max_seq;
+  int32_t c = 0;
+  for (int s0 = 0; s0 < max_seq; s0 += 64) {
+    const int s = s0 + lane;
+    c += __popcll(__ballot(s < max_seq && row[s] != 0));
+  }
+  if (lane == 0) counts[b] = c;
+}
+
+__global__ __launch_bounds__(64 * MASK_WAVES) void compact_mask_kernel(
+    const uint8_t* __restrict__ mask, int batch, int max_seq, const int32_t* __restrict__ cu,
+    int32_t* __restrict__ po) {
+  const int b = blockIdx.x * MASK_WAVES + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= batch) return;
+  const uint8_t* row = mask + (size_t)b * max_seq;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int32_t base = cu[b];
+  for (int s0 = 0; s0 < max_seq; s0 += 64) {
+    const int s = s0 + lane;
+    const bool valid = s < max_seq && row[s] != 0;
+    const unsigned long long ballot = __ballot(valid);
+    if (valid) {
+      const int32_t t = base + __popcll(ballot & below);
+      po[t] = b * max_seq + s - t;
+    }
+    base += __popcll(ballot);
+  }
+}
+
+hipError_t launch_offsets_mask(const uint8_t* mask, int batch, int max_seq, int32_t* cu,
+                               int32_t* padding_offset, hipStream_t stream) {
+  // the counts go to padding_offset[0, batch) (capacity batch * max_seq), which the
+  // compaction overwrites only after the scan has read them
+  const int grid = (batch + MASK_WAVES - 1) / MASK_WAVES;
+  count_mask_kernel<<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, padding_offset);
+  scan_lengths<<<1, SCAN_THREADS, 0, stream>>>(padding_offset, batch, cu);
+  compact_mask_kernel<<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, cu,
+                                                              padding_offset);
+  return hipGetLastError();
+}
+
 hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* cu,
                           int32_t* padding_offset, hipStream_t stream) {
   scan_lengths<<<1, SCAN_THREADS, 0, stream>>>(lens, batch, cu);

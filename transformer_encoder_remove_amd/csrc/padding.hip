@@ -92,6 +92,29 @@ __global__ __launch_bounds__(PAD_THREADS) void offsets_remove_padding_kernel(
   }
 }
 
+// Rebuild for any offsets (the mask form, holes allowed): rows the mask marks invalid
+// are zeroed, then every packed row t is written to padded row t + padding_offset[t].
+__global__ __launch_bounds__(PAD_THREADS) void zero_masked_rows_kernel(
+    const uint8_t* __restrict__ mask, u32x4* __restrict__ x_pad, size_t rows, int vec_per_row) {
+  const size_t n = rows * vec_per_row;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * PAD_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * PAD_THREADS)
+    if (mask[i / vec_per_row] == 0) __builtin_nontemporal_store(zero, &x_pad[i]);
+}
+
+__global__ __launch_bounds__(PAD_THREADS) void scatter_rows_kernel(
+    const u32x4* __restrict__ x_packed, u32x4* __restrict__ x_pad,
+    const int32_t* __restrict__ po, int total_tokens, int vec_per_row) {
+  const size_t n = (size_t)total_tokens * vec_per_row;
+  for (size_t i = (size_t)blockIdx.x * PAD_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * PAD_THREADS) {
+    const int t = (int)(i / vec_per_row), v = (int)(i - (size_t)t * vec_per_row);
+    const size_t dst_row = (size_t)t + po[t];
+    __builtin_nontemporal_store(x_packed[i], &x_pad[dst_row * vec_per_row + v]);
+  }
+}
+
 static int grid_for(size_t n) {
   size_t blocks = (n + PAD_THREADS - 1) / PAD_THREADS;
   const size_t cap = 256 * 32;   // enough waves to fill 256 CUs; the loop covers the rest
@@ -116,6 +139,21 @@ hipError_t launch_rebuild_padding(const void* x_packed, void* x_pad, const int32
   if (n == 0) return hipSuccess;
   rebuild_padding_kernel<<<grid_for(n), PAD_THREADS, 0, stream>>>(
       (const u32x4*)x_packed, (u32x4*)x_pad, cu, max_seq, batch, vpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_rebuild_padding_mask(const void* x_packed, void* x_pad, const uint8_t* mask,
+                                       const int32_t* po, int total_tokens, int batch,
+                                       int max_seq, int row_bytes, hipStream_t stream) {
+  const int vpr = row_bytes / 16;
+  const size_t rows = (size_t)batch * max_seq, nz = rows * vpr;
+  if (nz == 0) return hipSuccess;
+  zero_masked_rows_kernel<<<grid_for(nz), PAD_THREADS, 0, stream>>>(mask, (u32x4*)x_pad, rows,
+                                                                     vpr);
+  const size_t ns = (size_t)total_tokens * vpr;
+  if (ns > 0)
+    scatter_rows_kernel<<<grid_for(ns), PAD_THREADS, 0, stream>>>(
+        (const u32x4*)x_packed, (u32x4*)x_pad, po, total_tokens, vpr);
   return hipGetLastError();
 }
 
