@@ -90,36 +90,79 @@ __global__ __launch_bounds__(64 * FILL_WAVES) void fill_padding_offset(
 // padding_offset[t] = b*S + s - t.
 constexpr int MASK_WAVES = 4;
 
+// Mask bytes of one lane: W4 reads 4 consecutive positions as one 32-bit word (rows whose
+// length is a multiple of 4), else one byte. nonzero_bytes marks the nonzero bytes of a word
+// in their top bits (x & 0x7f7f7f7f plus 0x7f7f7f7f carries into bit 7 exactly when one of
+// bits 0-6 is set; bit 7 itself is or-ed in).
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+  return (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+}
+
+template <bool W4>
 __global__ __launch_bounds__(64 * MASK_WAVES) void count_mask_kernel(
     const uint8_t* __restrict__ mask, int batch, int max_seq, int32_t* __restrict__ counts) {
   const int b = blockIdx.x * MASK_WAVES + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= batch) return;
   const uint8_t* row = mask + (size_t)b * max_seq;
   int32_t c = 0;
-  for (int s0 = 0; s0 < max_seq; s0 += 64) {
-    const int s = s0 + lane;
-    c += __popcll(__ballot(s < max_seq && row[s] != 0));
+  if constexpr (W4) {
+    const uint32_t* row4 = reinterpret_cast<const uint32_t*>(row);
+    for (int w0 = 0; w0 < max_seq / 4; w0 += 64) {
+      const int w = w0 + lane;
+      if (w < max_seq / 4) c += __popc(nonzero_bytes(row4[w]));
+    }
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  } else {
+    for (int s0 = 0; s0 < max_seq; s0 += 64) {
+      const int s = s0 + lane;
+      c += __popcll(__ballot(s < max_seq && row[s] != 0));
+    }
   }
   if (lane == 0) counts[b] = c;
 }
 
+template <bool W4>
 __global__ __launch_bounds__(64 * MASK_WAVES) void compact_mask_kernel(
     const uint8_t* __restrict__ mask, int batch, int max_seq, const int32_t* __restrict__ cu,
     int32_t* __restrict__ po) {
   const int b = blockIdx.x * MASK_WAVES + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= batch) return;
   const uint8_t* row = mask + (size_t)b * max_seq;
-  const unsigned long long below = (1ull << lane) - 1ull;
   int32_t base = cu[b];
-  for (int s0 = 0; s0 < max_seq; s0 += 64) {
-    const int s = s0 + lane;
-    const bool valid = s < max_seq && row[s] != 0;
-    const unsigned long long ballot = __ballot(valid);
-    if (valid) {
-      const int32_t t = base + __popcll(ballot & below);
-      po[t] = b * max_seq + s - t;
+  if constexpr (W4) {
+    // each lane: 4 positions; its valid count scanned across the wavefront (shuffles)
+    const uint32_t* row4 = reinterpret_cast<const uint32_t*>(row);
+    for (int w0 = 0; w0 < max_seq / 4; w0 += 64) {
+      const int w = w0 + lane;
+      const uint32_t nz = w < max_seq / 4 ? nonzero_bytes(row4[w]) : 0u;
+      const int32_t c = __popc(nz);
+      int32_t inc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      int32_t t = base + inc - c;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (nz & (0x80u << (8 * k))) {
+          po[t] = b * max_seq + 4 * w + k - t;
+          ++t;
+        }
+      base += __shfl(inc, 63, 64);
     }
-    base += __popcll(ballot);
+  } else {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int s0 = 0; s0 < max_seq; s0 += 64) {
+      const int s = s0 + lane;
+      const bool valid = s < max_seq && row[s] != 0;
+      const unsigned long long ballot = __ballot(valid);
+      if (valid) {
+        const int32_t t = base + __popcll(ballot & below);
+        po[t] = b * max_seq + s - t;
+      }
+      base += __popcll(ballot);
+    }
   }
 }
 
@@ -128,10 +171,20 @@ hipError_t launch_offsets_mask(const uint8_t* mask, int batch, int max_seq, int3
   // the counts go to padding_offset[0, batch) (capacity batch * max_seq), which the
   // compaction overwrites only after the scan has read them
   const int grid = (batch + MASK_WAVES - 1) / MASK_WAVES;
-  count_mask_kernel<<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, padding_offset);
+  const bool w4 = max_seq % 4 == 0 && reinterpret_cast<uintptr_t>(mask) % 4 == 0;
+  if (w4)
+    count_mask_kernel<true><<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq,
+                                                                   padding_offset);
+  else
+    count_mask_kernel<false><<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq,
+                                                                    padding_offset);
   scan_lengths<<<1, SCAN_THREADS, 0, stream>>>(padding_offset, batch, cu);
-  compact_mask_kernel<<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, cu,
-                                                              padding_offset);
+  if (w4)
+    compact_mask_kernel<true><<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, cu,
+                                                                     padding_offset);
+  else
+    compact_mask_kernel<false><<<grid, 64 * MASK_WAVES, 0, stream>>>(mask, batch, max_seq, cu,
+                                                                      padding_offset);
   return hipGetLastError();
 }
 
