@@ -52,8 +52,10 @@ def parse():
     ap.add_argument("--summarise-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TABLE"),
                     help="no GPU work: turn the rocprofv3 FETCH_SIZE and WRITE_SIZE runs of "
                          "`bench.py --calib-copy` (output directories) and the kernel table "
-                         "that run wrote (gpurun_out/kernel_table.json) into "
-                         "profiles/hbm_traffic.json")
+                         "that run wrote (--kernel-table) into profiles/hbm_traffic.json")
+    ap.add_argument("--kernel-table", default="kernel_table.json",
+                    help="with --calib-copy: where to write the order of the per-kernel "
+                         "launches, for --summarise-traffic")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the scale of HBM counters)")
     return ap.parse_args()
@@ -69,7 +71,7 @@ def main():
         return summarise_traffic(*args.summarise_traffic)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the encoder "
-              "forward shards by sequence with no collectives, and this build measures one "
+              "forward shards by sequence with no collectives, and this benchmark measures one "
               "GPU's share.", file=sys.stderr)
         sys.exit(2)
 
@@ -410,7 +412,6 @@ def measured_traffic(workload: str, dtype: str, kernel: str):
     return None
 
 
-KERNEL_TABLE = os.path.join(ROOT, "gpurun_out", "kernel_table.json")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -419,10 +420,11 @@ def write_kernel_table(args, dtype: str, per_kernel: dict):
     each kernel 1 + kernel_reps times, in this order, after the timed steps; then the
     calibration copies follow. Library kernels only (torch's spin and fill kernels are
     filtered out by name when the counters are summarised)."""
-    os.makedirs(os.path.dirname(KERNEL_TABLE), exist_ok=True)
+    path = os.path.abspath(args.kernel_table)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
     rec = {"workload": args.workload, "dtype": dtype, "reps": args.kernel_reps,
            "kernels": [{"name": k, "bytes": v["bytes"]} for k, v in per_kernel.items()]}
-    with open(KERNEL_TABLE, "w") as f:
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
 
 
@@ -444,7 +446,7 @@ def _counter_rows(d: str, counter: str):
     return [(name, v) for (_, name), v in sorted(per.items())]
 
 
-def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str = KERNEL_TABLE):
+def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str):
     """profiles/hbm_traffic.json from two `rocprofv3 --pmc` runs (FETCH_SIZE, WRITE_SIZE)
     of `bench.py --calib-copy --steps 1 --warmup 1 --no-cpu --no-hbm`: each kernel's counters
     averaged over its kernel_reps timed launches, scaled by what the same counters read for
@@ -498,11 +500,12 @@ def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str = KERNEL_T
                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
     out["commands"] = [
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE "
-        "--output-format csv -d $REPO/gpurun_out/pmc_fetch -o bench -- python3 $REPO/bench.py "
-        "--steps 1 --warmup 1 --no-cpu --no-hbm --kernel-reps 3 --calib-copy [--workload W]",
-        "the same with --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write",
-        "python3 bench.py --summarise-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write "
-        "gpurun_out/kernel_table.json (the table the counter runs wrote)"]
+        "--output-format csv -d $OUT/pmc_fetch -o bench -- python3 $REPO/bench.py "
+        "--steps 1 --warmup 1 --no-cpu --no-hbm --kernel-reps 3 --calib-copy "
+        "--kernel-table $OUT/kernel_table.json [--workload W]",
+        "the same with --pmc WRITE_SIZE -d $OUT/pmc_write",
+        "python3 bench.py --summarise-traffic $OUT/pmc_fetch $OUT/pmc_write "
+        "$OUT/kernel_table.json ($REPO: the repository, $OUT: any output directory)"]
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     for k in out["kernels"]:
