@@ -47,16 +47,22 @@ def _lists(w):
     return {k: np.asarray(v, np.float64).tolist() for k, v in w.items()}
 
 
-def encoder_layer_padded(x_pad, lens, w, heads, eps, mask=None):
+def encoder_layer_padded(x_pad, lens, w, heads, eps, mask=None, trace=None):
     """Post-LN encoder layer on the padded batch [B, S, H]: every position is projected,
     keys at positions >= lens[b] are masked out (or, with mask [B, S], keys where the mask
     is zero). Returns [B, S, H] (pad rows computed too, but only valid rows are
-    meaningful)."""
+    meaningful). With ``trace`` (a dict), the layer's intermediate rows are appended to
+    trace["x"], ["ctx"], ["h1"] and ["f"] for the valid positions only (the inputs of the
+    four projection GEMMs: the layer input, the attention output, the first LayerNorm's
+    output and the GELU output)."""
     x_pad = np.asarray(x_pad, np.float64)
     B, S, H = x_pad.shape
     d = H // heads
     W = _lists(w)
     out = np.zeros((B, S, H))
+    if trace is not None:
+        for key in ("x", "ctx", "h1", "f"):
+            trace.setdefault(key, [])
     for b in range(B):
         L = int(lens[b])
         rows = [x_pad[b, i].tolist() for i in range(S)]
@@ -78,6 +84,12 @@ def encoder_layer_padded(x_pad, lens, w, heads, eps, mask=None):
             f = [_gelu(z) for z in _matvec(W["w_1"], W["b_1"], h1)]
             o = _matvec(W["w_2"], W["b_2"], f)
             out[b, i] = _ln([o[c] + h1[c] for c in range(H)], W["ln2_g"], W["ln2_b"], eps)
+            valid_row = bool(mask[b][i]) if mask is not None else i < L
+            if trace is not None and valid_row:
+                trace["x"].append(rows[i])
+                trace["ctx"].append(ctx)
+                trace["h1"].append(h1)
+                trace["f"].append(f)
     return out
 
 

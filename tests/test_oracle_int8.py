@@ -90,3 +90,78 @@ def test_int8_layer_close_to_float_layer():
     y8 = q8.encoder_layer_int8(xp, cu, w, 4, EPS, amax)
     y = enc.encoder_layer(xp, cu, w, 4, EPS)
     assert np.linalg.norm(y8 - y) / np.linalg.norm(y) < 0.05
+
+
+def _tiny_int8_case(seed=5, lens=(6, 3, 5), S=6, H=32, heads=2, F=64):
+    cfg = ti.custom_encoder_config(len(lens), S, list(lens), H, heads, F, dtype="f16", seed=seed)
+    lens, x = ti.encoder_input(cfg)
+    return cfg, lens, x
+
+
+def test_calibrate_matches_brute_force_gemm_inputs():
+    """calibrate() returns the max-abs of the four projection GEMMs' inputs over the valid
+    tokens only: the layer input, the attention output, the first LayerNorm's output and the
+    GELU output, each taken from the pure-Python padded brute force (pad rows excluded).
+    Pad rows of x are scaled up so that a statistic taken over padded rows would differ."""
+    cfg, lens, x = _tiny_int8_case()
+    x = x.astype(np.float64)
+    for b, L in enumerate(lens):
+        x[b, L:] *= 9.0                                        # pads larger than any valid row
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    trace = {}
+    brute.encoder_layer_padded(x, lens, w, cfg["heads"], EPS, trace=trace)
+    want = [max(abs(v) for row in trace[k] for v in row) for k in ("x", "ctx", "h1", "f")]
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    got = q8.calibrate(enc.remove_padding(x, lens), cu, w, cfg["heads"], EPS)
+    assert len(got) == 4
+    for g, r, name in zip(got, want, ("x", "ctx", "h1", "gelu")):
+        assert abs(g - r) <= 1e-12 * max(1.0, r), (name, g, r)
+    # the four statistics are distinct quantities here, so a swapped or mis-sourced one
+    # (e.g. FFN1's input taken before the LayerNorm) cannot pass
+    assert len({round(v, 9) for v in want}) == 4
+
+
+def _brute_stack_int8(x_pad, lens, layers, amaxes, heads):
+    """Two or more int8 layers, each the pure-Python padded brute force, the output of each
+    layer stored as fp16 before the next one reads it (pad rows stay zero)."""
+    y = np.asarray(x_pad, np.float64)
+    for w, a in zip(layers, amaxes):
+        y = brute.encoder_layer_int8_padded(y, lens, w, heads, EPS, a)
+        for b, L in enumerate(lens):
+            y[b, L:] = 0.0
+        y = y.astype(np.float16).astype(np.float64)
+    return y
+
+
+def test_int8_stack_matches_two_layer_brute_force():
+    cfg, lens, x = _tiny_int8_case(seed=7)
+    heads = cfg["heads"]
+    layers = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(2)]
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    amaxes, h = [], xp
+    for w in layers:
+        amaxes.append(q8.calibrate(h, cu, w, heads, EPS))
+        h = enc.encoder_layer(h, cu, w, heads, EPS)
+    got = q8.encoder_stack_int8(xp, cu, layers, amaxes, heads, EPS)
+    ref = enc.remove_padding(_brute_stack_int8(x, lens, layers, amaxes, heads), lens)
+    assert np.abs(got - ref).max() <= 1e-9
+    # the stored output of each layer is fp16: the result is on the fp16 grid
+    assert np.array_equal(got, got.astype(np.float16).astype(np.float64))
+    # the pin is sharp: the same two layers chained without the fp16 store in between (a
+    # dropped rounding in the stack loop) move the result far beyond the 1e-9 above
+    chained = xp
+    for w, a in zip(layers, amaxes):
+        chained = q8.encoder_layer_int8(chained, cu, w, heads, EPS, a)
+    assert np.abs(chained - ref).max() > 1e-4
+
+
+def test_int8_stack_of_one_is_the_rounded_layer():
+    cfg, lens, x = _tiny_int8_case(seed=9)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    a = q8.calibrate(xp, cu, w, cfg["heads"], EPS)
+    one = q8.encoder_stack_int8(xp, cu, [w], [a], cfg["heads"], EPS)
+    ref = enc.remove_padding(brute.encoder_layer_int8_padded(x, lens, w, cfg["heads"], EPS, a), lens)
+    assert np.array_equal(one, ref.astype(np.float16).astype(np.float64))
