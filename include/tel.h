@@ -32,9 +32,12 @@
  *     and weight storage type is TEL_F32, TEL_F16 or TEL_BF16; accumulation,
  *     softmax, LayerNorm statistics and GELU are float32.
  *   - Caller obligations not checked on the device: 0 <= seq_lens[b] <= max_seq,
- *     total_tokens == sum(seq_lens), max_len >= max(seq_lens).
+ *     total_tokens == sum(seq_lens), max_len >= max(seq_lens). With the environment
+ *     variable TEL_DEBUG=1 (read on every call), tel_encoder_forward checks all three on the device
+ *     before any kernel reads the padded batch and returns TEL_EINVAL when one fails; that
+ *     check synchronises the caller's stream (this mode only).
  *   - Thread safety: calls on different streams may run concurrently; there is no
- *     global mutable state.
+ *     global mutable state except the graph cache (mutex-guarded).
  */
 #ifndef TEL_H
 #define TEL_H

@@ -284,3 +284,19 @@ def test_offsets_mask_validation():
     assert R(FAKE, FAKE_ODD, FAKE, FAKE, 3, 2, 8, 64, f16, None) == tel.TEL_EINVAL
     assert R(FAKE, FAKE, FAKE, FAKE, 3, 2, 8, 12, f16, None) == tel.TEL_EUNSUPPORTED
     assert R(FAKE, FAKE, FAKE, FAKE, 3, 2, 8, 64, 9, None) == tel.TEL_EINVAL
+
+
+def test_binding_refuses_non_int32_lengths_and_wrong_activation_type():
+    import torch
+    with pytest.raises(TypeError):
+        tel.tel_build_offsets(torch.zeros(4, dtype=torch.int64), 8, torch.zeros(5, dtype=torch.int32),
+                              torch.zeros(32, dtype=torch.int32))
+    desc = tel.make_encoder_desc(64, 4, 256, torch.float16, 1e-5)
+    with pytest.raises(TypeError):
+        tel.tel_encoder_layer_forward(desc, None, torch.zeros((3, 64), dtype=torch.float32),
+                                      torch.zeros((3, 64), dtype=torch.float32),
+                                      torch.tensor([0, 3], dtype=torch.int32), 3, 3, None)
+    with pytest.raises(TypeError):
+        tel.tel_encoder_layer_forward(desc, None, torch.zeros((3, 64), dtype=torch.float16),
+                                      torch.zeros((3, 64), dtype=torch.float16),
+                                      torch.tensor([0, 3], dtype=torch.int64), 3, 3, None)

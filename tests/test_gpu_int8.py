@@ -224,12 +224,6 @@ def test_gemm_i8_epilogues(epi, M, N, K):
         # against the oracle a code can differ by one where the kernel's fp16 GELU value
         # itself differs from the oracle's by a rounding step
         assert d.max() <= 1 and (d > 0).mean() < 5e-3, (d.max(), (d > 0).mean())
-        # bit-exact: the codes are those of the kernel's own fp16 GELU output (the same
-        # epilogue storing fp16 values instead of codes)
-        C16 = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
-        tel.tel_gemm_i8(code, A, W, dq_d, b_d, C16)
-        torch.cuda.synchronize()
-        assert np.array_equal(C.cpu().numpy(), q8.quantize_act(C16.cpu().numpy(), inv))
         return
     C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
     tel.tel_gemm_i8(code, A, W, dq_d, b_d, C, resid=dev(r, "f16") if epi == "resid" else None,

@@ -165,6 +165,22 @@ def dtype_code(t: torch.dtype) -> int:
     return DTYPE_CODE[t]
 
 
+def _i32(name: str, *ts):
+    """Lengths, offsets and cu_seqlens are int32 on the C side: refuse other integer types
+    rather than let the library read them as int32."""
+    for t in ts:
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError(f"{name}: expected an int32 tensor, got {t.dtype}")
+
+
+def _act(name: str, desc, *ts):
+    """Activations of an encoder call have the descriptor's storage type."""
+    for t in ts:
+        if t is not None and DTYPE_CODE.get(t.dtype) != desc.dtype:
+            raise TypeError(f"{name}: tensor of {t.dtype} does not match the descriptor's "
+                            f"storage type {CODE_DTYPE.get(desc.dtype)}")
+
+
 # ------------------------------------------------------------------ entry points
 def tel_version() -> str:
     return lib.tel_version().decode()
@@ -175,6 +191,7 @@ def tel_status_str(status: int) -> str:
 
 
 def tel_build_offsets(seq_lens, max_seq: int, cu_seqlens, padding_offset, stream=None):
+    _i32("tel_build_offsets", seq_lens, cu_seqlens, padding_offset)
     _check("tel_build_offsets", lib.tel_build_offsets(
         _ptr(seq_lens), seq_lens.numel(), max_seq, _ptr(cu_seqlens), _ptr(padding_offset),
         _stream(stream)))
@@ -182,6 +199,7 @@ def tel_build_offsets(seq_lens, max_seq: int, cu_seqlens, padding_offset, stream
 
 def tel_remove_padding(x_pad, x_packed, padding_offset, total_tokens: int, stream=None):
     width = x_pad.shape[-1]
+    _i32("tel_remove_padding", padding_offset)
     _check("tel_remove_padding", lib.tel_remove_padding(
         _ptr(x_pad), _ptr(x_packed), _ptr(padding_offset), total_tokens, width,
         dtype_code(x_pad.dtype), _stream(stream)))
@@ -189,6 +207,7 @@ def tel_remove_padding(x_pad, x_packed, padding_offset, total_tokens: int, strea
 
 def tel_rebuild_padding(x_packed, x_pad, cu_seqlens, stream=None):
     B, S, W = x_pad.shape
+    _i32("tel_rebuild_padding", cu_seqlens)
     _check("tel_rebuild_padding", lib.tel_rebuild_padding(
         _ptr(x_packed), _ptr(x_pad), _ptr(cu_seqlens), B, S, W, dtype_code(x_pad.dtype),
         _stream(stream)))
@@ -197,6 +216,7 @@ def tel_rebuild_padding(x_packed, x_pad, cu_seqlens, stream=None):
 def tel_build_offsets_mask(mask, cu_seqlens, padding_offset, stream=None):
     """mask [B, S] uint8/bool device tensor; cu_seqlens [B+1], padding_offset [>= B*S] int32."""
     B, S = mask.shape
+    _i32("tel_build_offsets_mask", cu_seqlens, padding_offset)
     _check("tel_build_offsets_mask", lib.tel_build_offsets_mask(
         _ptr(mask), B, S, _ptr(cu_seqlens), _ptr(padding_offset), _stream(stream)))
 
@@ -204,6 +224,7 @@ def tel_build_offsets_mask(mask, cu_seqlens, padding_offset, stream=None):
 def tel_rebuild_padding_mask(x_packed, x_pad, mask, padding_offset, total_tokens: int,
                              stream=None):
     B, S, W = x_pad.shape
+    _i32("tel_rebuild_padding_mask", padding_offset)
     _check("tel_rebuild_padding_mask", lib.tel_rebuild_padding_mask(
         _ptr(x_packed), _ptr(x_pad), _ptr(mask), _ptr(padding_offset), total_tokens, B, S, W,
         dtype_code(x_pad.dtype), _stream(stream)))
@@ -241,6 +262,8 @@ def tel_encoder_prepare(desc, weights: dict, packed, act_amax=(0.0, 0.0, 0.0, 0.
 
 def tel_encoder_layer_forward(desc, packed, x, y, cu_seqlens, total_tokens: int, max_len: int,
                               workspace, stream=None):
+    _i32("tel_encoder_layer_forward", cu_seqlens)
+    _act("tel_encoder_layer_forward", desc, x, y)
     _check("tel_encoder_layer_forward", lib.tel_encoder_layer_forward(
         ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
         cu_seqlens.numel() - 1, total_tokens, max_len, _ptr(workspace),
@@ -249,6 +272,8 @@ def tel_encoder_layer_forward(desc, packed, x, y, cu_seqlens, total_tokens: int,
 
 def tel_encoder_calibrate(desc, packed, x, y, cu_seqlens, total_tokens: int, max_len: int, amax,
                           workspace, stream=None):
+    _i32("tel_encoder_calibrate", cu_seqlens)
+    _act("tel_encoder_calibrate", desc, x, y)
     _check("tel_encoder_calibrate", lib.tel_encoder_calibrate(
         ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
         cu_seqlens.numel() - 1, total_tokens, max_len, _ptr(amax), _ptr(workspace),
@@ -259,6 +284,8 @@ def tel_encoder_forward(desc, packed_layers: list, x_pad, y_pad, seq_lens, total
                         max_len: int, workspace, stream=None):
     B, S, _ = x_pad.shape
     arr = (P * max(1, len(packed_layers)))(*[_ptr(p) for p in packed_layers])
+    _i32("tel_encoder_forward", seq_lens)
+    _act("tel_encoder_forward", desc, x_pad, y_pad)
     _check("tel_encoder_forward", lib.tel_encoder_forward(
         ctypes.byref(desc), arr, len(packed_layers), _ptr(x_pad), _ptr(y_pad), _ptr(seq_lens),
         B, S, total_tokens, max_len, _ptr(workspace),
@@ -308,6 +335,7 @@ def tel_gemm_ex(epilogue: int, tile_config: int, A, W, bias, C, resid=None, head
 
 def tel_attention_varlen(qkv_split, ctx, cu_seqlens, total_tokens: int, max_len: int,
                          heads: int, head_dim: int, stream=None):
+    _i32("tel_attention_varlen", cu_seqlens)
     _check("tel_attention_varlen", lib.tel_attention_varlen(
         _ptr(qkv_split), _ptr(ctx), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total_tokens,
         max_len, heads, head_dim, dtype_code(ctx.dtype), _stream(stream)))

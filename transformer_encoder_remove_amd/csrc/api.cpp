@@ -134,10 +134,11 @@ size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
                             gemm_partial_plan(dt, (int)t, H, F, &cfg, &p16));
     return sp > 1 ? (size_t)sp * t : 0;
   };
-  // tile counts, hence plans, change only at multiples of 64 rows: the largest need
-  // inside each run of equal plans is at its top
+  // Plans change only where a tile count does, i.e. just past a multiple of some tile
+  // height (64, 96, 128 or 192 rows: all multiples of 32), so the largest need inside each
+  // run of equal plans is at its top, a multiple of 32 (or T itself).
   size_t rows = need(T);
-  for (size_t t = 64; t < T; t += 64) rows = std::max(rows, need(t));
+  for (size_t t = 32; t < T; t += 32) rows = std::max(rows, need(t));
   return rows;
 }
 
@@ -175,8 +176,8 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
 }
 
 struct StackWs {
-  size_t cu, po, xa, xb, qa, qb, layer, total;   // qa, qb: int8 stack, codes of xa / xb
-};
+  size_t cu, po, xa, xb, qa, qb, dbg, layer, total;   // qa, qb: int8 stack, codes of xa / xb
+};                                                    // dbg: TEL_DEBUG length-check result
 
 StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
   const size_t T = (size_t)batch * max_seq, H = d->hidden, es = dtype_size(d->dtype);
@@ -189,6 +190,7 @@ StackWs stack_ws(const tel_encoder_desc* d, int batch, int max_seq) {
   s.xb = take(T * H * es);
   s.qa = d->int8_gemm ? take(T * H) : 0;
   s.qb = d->int8_gemm ? take(T * H) : 0;
+  s.dbg = take(4);
   s.layer = take(layer_ws(d, T).total);
   s.total = o;
   return s;
@@ -623,6 +625,9 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
                            const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
                            int max_len, void* workspace, hipStream_t st) {
   const StackWs S = stack_ws(d, batch, max_seq);
+  // the layer workspace is laid out for batch * max_seq tokens; a layer at total_tokens
+  // (<= batch * max_seq) re-derives its offsets from its own token count and must fit
+  if (layer_ws(d, (size_t)total_tokens).total > S.total - S.layer) return TEL_EWORKSPACE;
   char* ws = (char*)workspace;
   int32_t* cu = (int32_t*)(ws + S.cu);
   int32_t* po = (int32_t*)(ws + S.po);
@@ -688,6 +693,11 @@ std::vector<hipStream_t> g_capture_streams;       // per device, created on firs
 int g_graphs_on = -1;                              // -1: read TEL_GRAPHS once
 constexpr size_t GRAPH_CACHE_MAX = 8;
 
+bool debug_checks() {   // read on every call, so a process can switch it on and off
+  const char* e = getenv("TEL_DEBUG");
+  return e && e[0] == '1';
+}
+
 bool graphs_on_locked() {
   if (g_graphs_on < 0) {
     const char* e = getenv("TEL_GRAPHS");
@@ -724,6 +734,16 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   const StackWs S = stack_ws(d, batch, max_seq);
   if (ws_bytes < S.total) return TEL_EWORKSPACE;
   hipStream_t st = as_stream(stream);
+  if (debug_checks()) {
+    // TEL_DEBUG=1: the caller's obligations on the lengths checked on the device before any
+    // kernel reads the padded batch (a synchronisation of `stream`, in this mode only)
+    int32_t* flag = (int32_t*)((char*)workspace + S.dbg);
+    int32_t bad = 0;
+    TEL_TRY(launch_check_lengths(seq_lens, batch, max_seq, total_tokens, max_len, flag, st));
+    TEL_TRY(hipMemcpyAsync(&bad, flag, 4, hipMemcpyDeviceToHost, st));
+    TEL_TRY(hipStreamSynchronize(st));
+    if (bad) return TEL_EINVAL;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TEL_EDEVICE;
   std::unique_lock<std::mutex> lk(g_graph_mu);

@@ -26,6 +26,10 @@ hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* 
 // batch * max_seq, its first batch entries also scratch for the per-sequence counts.
 hipError_t launch_offsets_mask(const uint8_t* mask, int batch, int max_seq, int32_t* cu,
                                int32_t* padding_offset, hipStream_t stream);
+// Debug check of a forward's lengths (one workgroup): out[0] = bit 0 some length outside
+// [0, max_seq], bit 1 sum != total, bit 2 max > max_len; 0 when all hold.
+hipError_t launch_check_lengths(const int32_t* lens, int batch, int max_seq, long long total,
+                                int max_len, int32_t* out, hipStream_t stream);
 // padding.hip (row_bytes % 16 == 0)
 // Rebuild for the mask form: rows with mask 0 zeroed, packed row t to row t + po[t].
 hipError_t launch_rebuild_padding_mask(const void* x_packed, void* x_pad, const uint8_t* mask,

@@ -197,3 +197,55 @@ hipError_t launch_offsets(const int32_t* lens, int batch, int max_seq, int32_t* 
 }
 
 }  // namespace tel
+
+namespace tel {
+
+// Debug check of a forward's lengths before anything reads the padded batch: every length
+// in [0, max_seq], their sum equal to total_tokens and their maximum at most max_len. One
+// workgroup; out[0] receives the failed conditions as bits (0 = all hold).
+__global__ __launch_bounds__(1024) void check_lengths_kernel(const int32_t* __restrict__ lens,
+                                                             int batch, int max_seq,
+                                                             long long total, int max_len,
+                                                             int32_t* __restrict__ out) {
+  __shared__ long long wsum[16];
+  __shared__ int wmax[16], wbad[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long s = 0;
+  int mx = 0, bad = 0;
+  for (int b = tid; b < batch; b += 1024) {
+    const int l = lens[b];
+    bad |= (l < 0 || l > max_seq) ? 1 : 0;
+    s += l;
+    mx = max(mx, l);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o, 64);
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    bad |= __shfl_xor(bad, o, 64);
+  }
+  if (lane == 0) {
+    wsum[wave] = s;
+    wmax[wave] = mx;
+    wbad[wave] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long ts = 0;
+    int tm = 0, tb = 0;
+    for (int w = 0; w < 16; ++w) {
+      ts += wsum[w];
+      tm = max(tm, wmax[w]);
+      tb |= wbad[w];
+    }
+    out[0] = tb | (ts != total ? 2 : 0) | (tm > max_len ? 4 : 0);
+  }
+}
+
+hipError_t launch_check_lengths(const int32_t* lens, int batch, int max_seq, long long total,
+                                int max_len, int32_t* out, hipStream_t stream) {
+  check_lengths_kernel<<<1, 1024, 0, stream>>>(lens, batch, max_seq, total, max_len, out);
+  return hipGetLastError();
+}
+
+}  // namespace tel
