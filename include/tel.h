@@ -21,7 +21,8 @@
  * Conventions (every entry point):
  *   - Pointers are DEVICE pointers unless marked [host]. The caller owns every buffer
  *     (inputs, outputs, packed weights, workspace); the library never allocates or
- *     frees device memory.
+ *     frees device memory. The one exception is the fixed scratch array of
+ *     tel_encoder_layer_forward_noalloc, part of the library's image on each GPU.
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only enqueues
  *     work on it and returns; there is no hidden synchronisation. Buffers must stay
  *     valid until the stream has consumed them. Outputs must not alias inputs.
@@ -37,7 +38,8 @@
  *     before any kernel reads the padded batch and returns TEL_EINVAL when one fails; that
  *     check synchronises the caller's stream (this mode only).
  *   - Thread safety: calls on different streams may run concurrently; there is no
- *     global mutable state except the graph cache (mutex-guarded).
+ *     global mutable state except the graph cache (mutex-guarded) and the scratch array
+ *     of tel_encoder_layer_forward_noalloc (see there).
  */
 #ifndef TEL_H
 #define TEL_H
@@ -163,6 +165,24 @@ int tel_encoder_layer_forward(const tel_encoder_desc* desc, const void* packed,
                               const void* x, void* y, const int32_t* cu_seqlens, int batch,
                               int total_tokens, int max_len, void* workspace,
                               size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): tel_encoder_layer_forward with the
+ * workspace taken from a scratch array the library owns, one per GPU, of
+ * TEL_NOALLOC_SCRATCH_BYTES, held until the process ends. Nothing is allocated or freed
+ * by the call; the caller still passes inputs, output and packed weights as for
+ * tel_encoder_layer_forward (same arguments, same results).
+ *   Limit: tel_encoder_workspace_size(desc, total_tokens) must not exceed
+ *   TEL_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a BERT-base fp16 layer up to ~3,100 tokens),
+ *   else TEL_EWORKSPACE and nothing is enqueued.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last call's contents:
+ *   calls that can overlap on the same GPU (different streams, or host threads without
+ *   ordering) race on it and must be serialised by the caller. The first call on a device
+ *   looks up the array's address there (hipGetSymbolAddress; TEL_EDEVICE on failure). */
+#define TEL_NOALLOC_SCRATCH_BYTES (64u << 20)
+int tel_encoder_layer_forward_noalloc(const tel_encoder_desc* desc, const void* packed,
+                                      const void* x, void* y, const int32_t* cu_seqlens,
+                                      int batch, int total_tokens, int max_len, void* stream);
 
 /* Post-training calibration of the int8 variant's static activation scales: runs one
  * floating-point layer (desc->int8_gemm == 0) exactly as tel_encoder_layer_forward and

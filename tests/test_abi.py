@@ -286,6 +286,28 @@ def test_offsets_mask_validation():
     assert R(FAKE, FAKE, FAKE, FAKE, 3, 2, 8, 64, 9, None) == tel.TEL_EINVAL
 
 
+def test_noalloc_layer_validation():
+    """tel_encoder_layer_forward_noalloc checks its arguments and the scratch limit on the
+    host before looking up the scratch or enqueueing anything."""
+    desc = tel.make_encoder_desc(768, 12, 3072, __import__("torch").float16, 1e-5)
+    pd = ctypes.byref(desc)
+    F = tel.lib.tel_encoder_layer_forward_noalloc
+    A256 = ctypes.c_void_p(1 << 20)
+    ok_T = 2557
+    assert tel.tel_encoder_workspace_size(desc, ok_T) <= tel.TEL_NOALLOC_SCRATCH_BYTES
+    big_T = 4096
+    assert tel.tel_encoder_workspace_size(desc, big_T) > tel.TEL_NOALLOC_SCRATCH_BYTES
+    assert F(pd, A256, A256, ctypes.c_void_p((1 << 20) + 4096), A256, 2, big_T, 128, None) == \
+        tel.TEL_EWORKSPACE
+    assert F(pd, A256, A256, A256, A256, 2, 100, 64, None) == tel.TEL_EINVAL        # x == y
+    assert F(pd, None, A256, ctypes.c_void_p(2 << 20), A256, 2, 100, 64, None) == tel.TEL_EINVAL
+    assert F(pd, A256, A256, ctypes.c_void_p(2 << 20), A256, 0, 100, 64, None) == tel.TEL_EINVAL
+    assert F(pd, A256, A256, ctypes.c_void_p(2 << 20), A256, 2, 0, 0, None) == tel.TEL_OK
+    assert tel.TEL_NOALLOC_SCRATCH_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert "#define TEL_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+
+
 def test_binding_refuses_non_int32_lengths_and_wrong_activation_type():
     import torch
     with pytest.raises(TypeError):

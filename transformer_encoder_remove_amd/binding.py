@@ -36,8 +36,9 @@ EXPORTS = (
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
     "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
     "tel_gemm_2of4_tile_configs", "tel_gemm_2of4", "tel_build_offsets_mask",
-    "tel_rebuild_padding_mask",
+    "tel_rebuild_padding_mask", "tel_encoder_layer_forward_noalloc",
 )
+TEL_NOALLOC_SCRATCH_BYTES = 64 << 20
 TEL_SWIN_ATTN_ONLY = 1
 
 
@@ -98,6 +99,8 @@ _SIG = {
     "tel_encoder_workspace_size": (SZ, [ctypes.POINTER(tel_encoder_desc), I]),
     "tel_encoder_layer_forward": (I, [ctypes.POINTER(tel_encoder_desc), P, P, P, P, I, I, I, P,
                                       SZ, P]),
+    "tel_encoder_layer_forward_noalloc": (I, [ctypes.POINTER(tel_encoder_desc), P, P, P, P, I,
+                                              I, I, P]),
     "tel_encoder_calibrate": (I, [ctypes.POINTER(tel_encoder_desc), P, P, P, P, I, I, I, P, P, SZ,
                                   P]),
     "tel_encoder_forward_workspace_size": (SZ, [ctypes.POINTER(tel_encoder_desc), I, I]),
@@ -268,6 +271,15 @@ def tel_encoder_layer_forward(desc, packed, x, y, cu_seqlens, total_tokens: int,
         ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
         cu_seqlens.numel() - 1, total_tokens, max_len, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tel_encoder_layer_forward_noalloc(desc, packed, x, y, cu_seqlens, total_tokens: int,
+                                      max_len: int, stream=None):
+    _i32("tel_encoder_layer_forward_noalloc", cu_seqlens)
+    _act("tel_encoder_layer_forward_noalloc", desc, x, y)
+    _check("tel_encoder_layer_forward_noalloc", lib.tel_encoder_layer_forward_noalloc(
+        ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(y), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, total_tokens, max_len, _stream(stream)))
 
 
 def tel_encoder_calibrate(desc, packed, x, y, cu_seqlens, total_tokens: int, max_len: int, amax,

@@ -592,6 +592,25 @@ int tel_encoder_layer_forward(const tel_encoder_desc* d, const void* packed, con
                        (char*)workspace, as_stream(stream));
 }
 
+int tel_encoder_layer_forward_noalloc(const tel_encoder_desc* d, const void* packed,
+                                      const void* x, void* y, const int32_t* cu_seqlens,
+                                      int batch, int total_tokens, int max_len, void* stream) {
+  const int sup = desc_supported(d);
+  if (sup != TEL_OK) return sup;
+  if (batch <= 0 || total_tokens < 0 || max_len < 0) return TEL_EINVAL;
+  if (total_tokens == 0) return TEL_OK;
+  if (max_len == 0) return TEL_EINVAL;
+  if (!packed || !x || !y || !cu_seqlens) return TEL_EINVAL;
+  if (!aligned256(packed) || !aligned16(x) || !aligned16(y)) return TEL_EINVAL;
+  if (x == y) return TEL_EINVAL;
+  if (layer_ws(d, (size_t)total_tokens).total > TEL_NOALLOC_SCRATCH_BYTES) return TEL_EWORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return TEL_EDEVICE;
+  return layer_forward(d, (const char*)packed, x, y, cu_seqlens, batch, total_tokens, max_len,
+                       (char*)ws, as_stream(stream));
+}
+
 int tel_encoder_calibrate(const tel_encoder_desc* d, const void* packed, const void* x, void* y,
                           const int32_t* cu_seqlens, int batch, int total_tokens, int max_len,
                           float* amax, void* workspace, size_t ws_bytes, void* stream) {

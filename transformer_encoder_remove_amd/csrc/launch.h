@@ -137,6 +137,10 @@ hipError_t launch_expand_rel_bias(int dtype, const void* table, float* bias_exp,
 hipError_t launch_prune_2of4(int dtype, const void* w, void* values, uint16_t* index, int N,
                              int K, hipStream_t stream);
 
+// noalloc.hip: device address (on the current device) and size of the library-owned
+// scratch array of tel_encoder_layer_forward_noalloc; looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // prepare.hip
 hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipStream_t stream);
 hipError_t launch_store_f32(float* dst, const float* vals, int n, hipStream_t stream);
