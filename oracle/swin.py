@@ -25,7 +25,8 @@ import numpy as np
 from . import encoder as enc
 
 __all__ = ["cyclic_shift", "window_partition", "window_reverse", "relative_position_index",
-           "region_ids", "window_mask", "window_attention", "swin_block"]
+           "region_ids", "window_mask", "window_attention", "swin_block", "patch_merge_gather",
+           "patch_merging", "stage_shifts", "swin_stage", "swin_two_stages"]
 
 
 def cyclic_shift(img: np.ndarray, s: int) -> np.ndarray:
@@ -114,3 +115,61 @@ def swin_block(x: np.ndarray, w: dict, Hs: int, Ws: int, heads: int, M: int, s: 
     hid = enc.gelu(enc.linear(enc.layer_norm(x1, w["ln2_g"], w["ln2_b"], eps).reshape(-1, C),
                               w["w_1"], w["b_1"]))
     return x1 + enc.linear(hid, w["w_2"], w["b_2"]).reshape(B, L, C)
+
+
+# ------------------------------------------------------------------ stages and downsampling
+# [SW] section 1: the network is a sequence of stages with a downsampling step between
+# them, so the resolution halves from stage to stage (a resolution pyramid); section 3,
+# INT8 paragraph, names that step's GEMM (PatchMerge). The page gives no formula; the
+# reading taken is the standard Swin patch merging:
+#   * every 2 x 2 neighbourhood of the image becomes one token whose 4C features are the
+#     four tokens' features concatenated in the order (row offset, column offset) =
+#     (0, 0), (1, 0), (0, 1), (1, 1);
+#   * a LayerNorm over the 4C features, then a linear map 4C -> 2C without bias;
+#   * inside a stage, blocks alternate regular windows (shift 0) and shifted windows.
+
+MERGE_ORDER = ((0, 0), (1, 0), (0, 1), (1, 1))   # (row offset, column offset) of part k
+
+
+def patch_merge_gather(x: np.ndarray, Hs: int, Ws: int) -> np.ndarray:
+    """[B, Hs*Ws, C] (row-major image order) -> [B, (Hs/2)*(Ws/2), 4C]: output token (i, j)
+    holds the features of image tokens (2i + dy, 2j + dx) for (dy, dx) in MERGE_ORDER."""
+    B, L, C = x.shape
+    if Hs % 2 or Ws % 2 or L != Hs * Ws:
+        raise ValueError("patch merging needs an even image height and width")
+    img = np.asarray(x).reshape(B, Hs, Ws, C)
+    parts = [img[:, dy::2, dx::2] for dy, dx in MERGE_ORDER]
+    return np.concatenate(parts, axis=-1).reshape(B, (Hs // 2) * (Ws // 2), 4 * C)
+
+
+def patch_merging(x: np.ndarray, w: dict, Hs: int, Ws: int, eps: float) -> np.ndarray:
+    """Downsampling between stages: y = LN(gather(x); norm_g, norm_b) W_red^T, with W_red
+    [2C, 4C] and no bias. Returns [B, (Hs/2)*(Ws/2), 2C]."""
+    v = patch_merge_gather(np.asarray(x, np.float64), Hs, Ws)
+    B, L2, C4 = v.shape
+    z = enc.layer_norm(v.reshape(-1, C4), w["norm_g"], w["norm_b"], eps)
+    return (z @ np.asarray(w["w_red"], np.float64).T).reshape(B, L2, -1)
+
+
+def stage_shifts(n_blocks: int, Hs: int, Ws: int, M: int) -> list:
+    """Shift of each block of a stage: 0 for even blocks, M // 2 for odd ones; 0 throughout
+    when one window covers the image (nothing to shift)."""
+    s = M // 2 if min(Hs, Ws) > M else 0
+    return [0 if i % 2 == 0 else s for i in range(n_blocks)]
+
+
+def swin_stage(x: np.ndarray, blocks: list, Hs: int, Ws: int, heads: int, M: int,
+               eps: float) -> np.ndarray:
+    """The blocks of one stage in order on x [B, Hs*Ws, C], shifts as stage_shifts."""
+    for w, s in zip(blocks, stage_shifts(len(blocks), Hs, Ws, M)):
+        x = swin_block(x, w, Hs, Ws, heads, M, s, eps)
+    return x
+
+
+def swin_two_stages(x: np.ndarray, stage1: list, merge: dict, stage2: list, Hs: int, Ws: int,
+                    heads1: int, heads2: int, M: int, eps: float) -> np.ndarray:
+    """Stage 1 at Hs x Ws, patch merging, stage 2 at (Hs/2) x (Ws/2) with twice the
+    channels; every tensor between the pieces stays float64 (no storage rounding)."""
+    x = swin_stage(x, stage1, Hs, Ws, heads1, M, eps)
+    x = patch_merging(x, merge, Hs, Ws, eps)
+    return swin_stage(x, stage2, Hs // 2, Ws // 2, heads2, M, eps)

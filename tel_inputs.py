@@ -50,6 +50,14 @@ SWIN_CONFIGS = {
                           shift=3, mlp=384, dtype="f16", seed=5),
 }
 
+# Swin-T's first two stages with the downsampling between them: stage 1 (56 x 56, C 96,
+# 3 heads) and stage 2 (28 x 28, C 192, 6 heads), two blocks each (regular, then shifted
+# windows), window 7, MLP ratio 4; patch merging 4C = 384 -> 2C = 192.
+SWIN_STAGES = {
+    "swin_t_stage12": dict(batch=64, height=56, width=56, channels=96, heads=(3, 6), window=7,
+                           blocks=(2, 2), mlp_ratio=4, dtype="f16", seed=6),
+}
+
 LN_EPS = 1e-5
 
 
@@ -208,3 +216,38 @@ def int8_operands(M: int, N: int, K: int, seed: int) -> tuple[np.ndarray, np.nda
     a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
     b = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
     return a, b
+
+
+def swin_stage_block_config(cfg: dict, stage: int, shift: int) -> dict:
+    """The block config (as SWIN_CONFIGS entries) of stage 0 or 1 of a SWIN_STAGES entry."""
+    f = 2 ** stage
+    C = cfg["channels"] * f
+    return dict(batch=cfg["batch"], height=cfg["height"] // f, width=cfg["width"] // f,
+                channels=C, heads=cfg["heads"][stage], window=cfg["window"], shift=shift,
+                mlp=C * cfg["mlp_ratio"], dtype=cfg["dtype"], seed=cfg["seed"])
+
+
+def swin_stage_weights(cfg: dict, variant: bool = False):
+    """(stage-1 block weights, patch-merging weights, stage-2 block weights) of a
+    SWIN_STAGES entry; every block draws from its own seed tuple."""
+    s = cfg["seed"]
+    out = []
+    for stage in range(2):
+        blocks = []
+        for i in range(cfg["blocks"][stage]):
+            bc = swin_stage_block_config(cfg, stage, 0)
+            blocks.append(swin_block_weights(bc, variant, seed=1000 * s + 100 * stage + i))
+        out.append(blocks)
+    return out[0], patch_merge_weights(cfg["channels"], variant, seed=s), out[1]
+
+
+def patch_merge_weights(C: int, variant: bool = False, seed: int = 0, dtype: str = "f16") -> dict:
+    """norm_g, norm_b [4C] (1 and 0, or 1 + N(0, 0.1) and N(0, 0.1) with variant) and
+    w_red [2C, 4C] ~ N(0, 0.02), rounded to the storage type."""
+    rng = np.random.default_rng([seed, 7])
+    w = {"w_red": rng.standard_normal((2 * C, 4 * C)) * 0.02,
+         "norm_g": np.ones(4 * C), "norm_b": np.zeros(4 * C)}
+    if variant:
+        w["norm_g"] = 1.0 + rng.standard_normal(4 * C) * 0.1
+        w["norm_b"] = rng.standard_normal(4 * C) * 0.1
+    return {k: to_storage(v, dtype) for k, v in w.items()}

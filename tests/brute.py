@@ -207,3 +207,24 @@ def swin_block_direct(x, w, Hs, Ws, heads, M, s, eps):
             f = _matvec(W["w_2"], W["b_2"], hdn)
             out[b, t] = [x1[c] + f[c] for c in range(C)]
     return out
+
+
+def patch_merging_direct(x, w, Hs, Ws, eps):
+    """Patch merging by loops over output positions: part k of output token (i, j) is the
+    image token at row 2i + (k % 2), column 2j + (k // 2); the 4C values are normalised
+    together, then multiplied by W_red [2C][4C] (no bias). x is [B, Hs*Ws, C]."""
+    x = np.asarray(x, np.float64)
+    B, L, C = x.shape
+    W = np.asarray(w["w_red"], np.float64).tolist()
+    g = np.asarray(w["norm_g"], np.float64).tolist()
+    be = np.asarray(w["norm_b"], np.float64).tolist()
+    out = np.zeros((B, (Hs // 2) * (Ws // 2), len(W)))
+    for b in range(B):
+        for i in range(Hs // 2):
+            for j in range(Ws // 2):
+                v = []
+                for k in range(4):
+                    y, xx = 2 * i + k % 2, 2 * j + k // 2
+                    v.extend(x[b, y * Ws + xx].tolist())
+                out[b, i * (Ws // 2) + j] = _matvec(W, [0.0] * len(W), _ln(v, g, be, eps))
+    return out

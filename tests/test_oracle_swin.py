@@ -110,3 +110,75 @@ def test_single_window_is_global_attention_with_bias():
                         t(w["w_1"]), t(w["b_1"])))
     ref = (x1 + F.linear(h, t(w["w_2"]), t(w["b_2"]))).numpy()
     assert np.abs(y - ref).max() <= 1e-12
+
+
+# ------------------------------------------------------------------ stages, patch merging
+def test_patch_merge_gather_golden():
+    """tests/golden/patch_merge_order_4x6.txt: the 2 x 2 gather of a 4 x 6 image, by hand."""
+    img = np.array([[10 * y + x for x in range(6)] for y in range(4)], np.float64)
+    got = swin.patch_merge_gather(img.reshape(1, 24, 1), 4, 6)
+    want = np.array([[float(v) for v in r] for r in golden_rows("patch_merge_order_4x6.txt")])
+    assert got.shape == (1, 6, 4)
+    assert np.array_equal(got[0], want)
+
+
+def test_patch_merge_gather_is_a_rearrangement():
+    """The gather is einops' rearrangement b (h p1) (w p2) c -> b (h w) (p2 p1 c): the
+    column offset p2 is the slower of the two offsets in the concatenated features."""
+    from einops import rearrange
+    rng = np.random.default_rng(3)
+    B, Hs, Ws, C = 2, 6, 10, 5
+    x = rng.standard_normal((B, Hs * Ws, C))
+    want = rearrange(x.reshape(B, Hs, Ws, C), "b (h p1) (w p2) c -> b (h w) (p2 p1 c)", p1=2, p2=2)
+    assert np.array_equal(swin.patch_merge_gather(x, Hs, Ws), want)
+    with pytest.raises(ValueError):
+        swin.patch_merge_gather(x[:, :55], 5, 11)
+
+
+@pytest.mark.parametrize("Hs,Ws,C", [(4, 6, 3), (8, 8, 4), (2, 2, 8)])
+def test_patch_merging_matches_brute_force(Hs, Ws, C):
+    rng = np.random.default_rng(Hs * Ws + C)
+    x = rng.standard_normal((2, Hs * Ws, C))
+    w = ti.patch_merge_weights(C, variant=True, seed=C, dtype="f32")
+    y = swin.patch_merging(x, w, Hs, Ws, EPS)
+    assert y.shape == (2, (Hs // 2) * (Ws // 2), 2 * C)
+    assert np.abs(y - brute.patch_merging_direct(x, w, Hs, Ws, EPS)).max() <= 1e-12
+
+
+def test_patch_merging_normalises_all_four_parts_together():
+    """Parts of very different scale: a LayerNorm per part (or per channel group) would map
+    each part to unit variance; over all 4C the small parts stay small."""
+    C = 4
+    x = np.zeros((1, 4, C))
+    x[0, 0] = [1, 2, 3, 4]          # part 0 of the single output token
+    x[0, 1:] = 1e-3 * np.arange(12).reshape(3, C)
+    w = {"w_red": np.eye(2 * C, 4 * C), "norm_g": np.ones(4 * C), "norm_b": np.zeros(4 * C)}
+    v = np.concatenate([x[0, 0], x[0, 2], x[0, 1], x[0, 3]])   # order (0,0), (1,0), (0,1), (1,1)
+    z = (v - v.mean()) / np.sqrt(v.var() + EPS)
+    assert np.abs(swin.patch_merging(x, w, 2, 2, EPS)[0, 0] - z[:2 * C]).max() <= 1e-12
+
+
+def test_stage_shifts():
+    assert swin.stage_shifts(2, 56, 56, 7) == [0, 3]
+    assert swin.stage_shifts(4, 28, 28, 7) == [0, 3, 0, 3]
+    assert swin.stage_shifts(2, 7, 7, 7) == [0, 0]          # one window covers the image
+
+
+def test_two_stages_match_brute_force_composition():
+    """Stage 1 (two blocks), patch merging, stage 2 (two blocks) against the direct block
+    brute force and the patch-merging brute force chained by hand."""
+    B, Hs, M = 1, 8, 2
+    c1 = ti.custom_swin_config(B, Hs, Hs, 8, 2, M, 1, 16, dtype="f32", seed=71)
+    c2 = ti.custom_swin_config(B, Hs // 2, Hs // 2, 16, 4, M, 1, 32, dtype="f32", seed=72)
+    s1 = [ti.swin_block_weights(c1, variant=True, seed=80 + i) for i in range(2)]
+    s2 = [ti.swin_block_weights(c2, variant=True, seed=90 + i) for i in range(2)]
+    mw = ti.patch_merge_weights(8, variant=True, seed=5, dtype="f32")
+    x = ti.swin_input(c1)
+    got = swin.swin_two_stages(x, s1, mw, s2, Hs, Hs, 2, 4, M, EPS)
+    ref = brute.swin_block_direct(x, s1[0], Hs, Hs, 2, M, 0, EPS)
+    ref = brute.swin_block_direct(ref, s1[1], Hs, Hs, 2, M, 1, EPS)
+    ref = brute.patch_merging_direct(ref, mw, Hs, Hs, EPS)
+    ref = brute.swin_block_direct(ref, s2[0], Hs // 2, Hs // 2, 4, M, 0, EPS)
+    ref = brute.swin_block_direct(ref, s2[1], Hs // 2, Hs // 2, 4, M, 1, EPS)
+    assert got.shape == (B, (Hs // 2) ** 2, 16)
+    assert np.abs(got - ref).max() <= 1e-10
