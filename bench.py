@@ -11,7 +11,8 @@ bert_large_latency (24 fp16 layers), bert_base_int8 (int8 GEMMs; static activati
 scales from tel_encoder_calibrate on the same batch, i.e. post-training calibration,
 outside the timed region), bert_base_sparse (the bert_base layers with their projection
 matrices pruned 2:4 when prepared, on the sparse MFMA), swin_t_stage1 (one shifted-window
-block, tokens/s per block).
+block, tokens/s per block), swin_t_stage12 (Swin-T stages 1 and 2, two blocks each, with the
+patch merging between them; stage-1 tokens/s).
 
 Also measured here, each with HIP events on the stream its kernel is launched on:
 the average duration of every kernel of one layer (same shapes, launched through the
@@ -82,6 +83,8 @@ def main():
 
     if args.workload in ti.SWIN_CONFIGS:
         return bench_swin(args)
+    if args.workload in ti.SWIN_STAGES:
+        return bench_swin_stages(args)
     cfg = dict(ti.ENCODER_CONFIGS[args.workload])
     if args.dtype:
         cfg["dtype"] = args.dtype
@@ -690,6 +693,109 @@ def bench_swin(args):
         "roofline": roofline, "cpu_baseline": cpu, "step_ms": step_ms,
         "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},
         "block_kernel_sum_us": round(sum(v["us"] for v in per_kernel.values()), 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_swin_stages(args):
+    """Swin-T stage 1 (two blocks), patch merging, stage 2 (two blocks) per step; stage-1
+    input tokens/s of the whole pipeline, and the patch-merging kernel against HBM."""
+    import torch
+
+    import tel_inputs as ti
+    import transformer_encoder_remove_amd as tel
+    from oracle import swin as sw_shifts   # block shift pattern only (stage_shifts)
+    cfg = ti.SWIN_STAGES[args.workload]
+    torch.cuda.set_device(0)
+    tdt = torch.float16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).cuda().to(tdt)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).cuda()
+    B, H, W, C, M = cfg["batch"], cfg["height"], cfg["width"], cfg["channels"], cfg["window"]
+    x_np = ti.swin_input(cfg)
+    s1, mw, s2 = ti.swin_stage_weights(cfg)
+    blocks = []   # (stage, desc, packed, workspace, input buffer, output buffer)
+    x = dev(x_np)
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    half = [torch.empty((B, (H // 2) * (W // 2), 2 * C), dtype=tdt, device="cuda")
+            for _ in range(3)]
+    for stage, ws_list in ((0, s1), (1, s2)):
+        f = 2 ** stage
+        for i, (w, s) in enumerate(zip(ws_list, sw_shifts.stage_shifts(len(ws_list), H // f,
+                                                                       W // f, M))):
+            bc = ti.swin_stage_block_config(cfg, stage, s)
+            desc = tel.make_swin_desc(bc["batch"], bc["height"], bc["width"], bc["channels"],
+                                      bc["heads"], bc["window"], bc["shift"], bc["mlp"], tdt,
+                                      ti.LN_EPS)
+            packed = tel.alloc_bytes(tel.tel_swin_packed_size(desc))
+            tel.tel_swin_prepare(desc, {k: dev(v) for k, v in w.items()}, packed)
+            ws = tel.alloc_bytes(tel.tel_swin_workspace_size(desc))
+            src = (x if i == 0 else bufs[0]) if stage == 0 else half[i]
+            dst = bufs[i] if stage == 0 else half[i + 1]
+            blocks.append((stage, desc, packed, ws, src, dst))
+    mg, mb, mwr = f32(mw["norm_g"]), f32(mw["norm_b"]), dev(mw["w_red"])
+    T = B * H * W
+    stream = torch.cuda.current_stream()
+    log(f"[bench] workload {args.workload}: {cfg} stage-1 tokens={T}")
+
+    def merge():
+        tel.tel_patch_merging(bufs[1], half[0], mg, mb, mwr, H, W, ti.LN_EPS, stream=stream)
+
+    def step():
+        for stage, desc, packed, ws, src, dst in blocks:
+            if stage == 1 and src is half[0]:
+                merge()
+            tel.tel_window_attention_forward(desc, packed, src, dst, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for i in range(args.steps):
+        evs[i].record(stream)
+        step()
+    evs[-1].record(stream)
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = step_stats([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    value = T / (ms / 1e3)
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {value / 1e9:.3f} G stage-1 tokens/s, "
+        f"{B / (ms / 1e3):.0f} images/s")
+    per_piece = {}
+    for n, (stage, desc, packed, ws, src, dst) in enumerate(blocks):
+        fn = lambda d=desc, p=packed, w=ws, a=src, b=dst: tel.tel_window_attention_forward(
+            d, p, a, b, w, stream=stream)
+        per_piece[f"stage{stage + 1}_block{n % 2}_shift{desc.shift}"] = back_to_back_us(
+            fn, stream, args.kernel_reps)
+    mus = back_to_back_us(merge, stream, args.kernel_reps)
+    per_piece["patch_merging"] = mus
+    for k, v in per_piece.items():
+        log(f"[bench] piece {k:28s} {v:9.2f} us")
+    m_bytes = 2 * (T * C + (T // 4) * 2 * C + 2 * C * 4 * C)   # read x and W_red, write y
+    roofline = {"kernel": "patch_merging (2x2 gather + LN 4C + 4C->2C)", "bound": "hbm",
+                "achieved": round(m_bytes / mus / 1e3, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(m_bytes / mus / 1e3 / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_us": round(mus, 3), "bytes_per_launch": m_bytes}
+    cpu = None
+    if not args.no_cpu:
+        from oracle import swin
+        t0 = time.perf_counter()
+        swin.swin_two_stages(x_np[:1], s1, mw, s2, H, W, cfg["heads"][0], cfg["heads"][1], M,
+                             ti.LN_EPS)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(H * W / t_cpu, 1), "unit": "stage-1 tokens/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"1 image through both stages and the merge, float64 NumPy, {t_cpu:.1f} s"}
+    out = {
+        "metric": "stage-1 tokens/sec through Swin-T stages 1 and 2 with patch merging (fp16)",
+        "value": round(value, 1), "unit": "stage-1 tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights and bias tables)",
+        "config": {"workload": f"{args.workload}: two shifted-window stages with the downsampling "
+                               "between them", **{k: v for k, v in cfg.items() if k != "dtype"}},
+        "images_per_s": round(B / (ms / 1e3), 1),
+        "roofline": roofline, "cpu_baseline": cpu, "step_ms": step_ms,
+        "pieces_us": {k: round(v, 3) for k, v in per_piece.items()},
     }
     print(json.dumps(out), flush=True)
 

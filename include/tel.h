@@ -368,6 +368,20 @@ int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, c
                                    int batch, int height, int width, int channels, int window,
                                    int shift, float eps, int dtype, void* stream);
 
+/* Patch merging, the downsampling between two Swin stages ([SW] section 1: stages with a
+ * downsampling step between them, halving the resolution; section 3, INT8 paragraph: the
+ * PatchMerge GEMM). One kernel: the 2 x 2 gather, a LayerNorm over the 4C gathered
+ * features and the linear map 4C -> 2C (no bias):
+ *   v(i, j) = [x(2i, 2j), x(2i+1, 2j), x(2i, 2j+1), x(2i+1, 2j+1)]     (4 * channels values)
+ *   y(i, j) = (LN(v(i, j)) * gamma + beta) W_red^T
+ * x [batch][height * width][channels] (row-major image order), y [batch][(height/2) *
+ * (width/2)][2 * channels], W_red [2 * channels][4 * channels] of type dtype; gamma, beta
+ * float32 [4 * channels]. height and width even; dtype TEL_F16 or TEL_BF16; channels 96
+ * (Swin-T's stage 1 -> stage 2), else TEL_EUNSUPPORTED. 16-byte aligned pointers, x != y. */
+int tel_patch_merging(const void* x, void* y, const float* gamma, const float* beta,
+                      const void* w_red, int batch, int height, int width, int channels,
+                      float eps, int dtype, void* stream);
+
 /* y[r][:] = LN(x[r][:]) * gamma + beta over rows of width `width` (float32 gamma/beta). */
 int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta, int rows,
                   int width, float eps, int dtype, void* stream);

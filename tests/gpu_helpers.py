@@ -81,3 +81,48 @@ def gpu_encoder_forward(tel, cfg: dict, lens, x_pad, layer_weights: list, int8=F
     tel.tel_encoder_forward(desc, packed, x, y, lens_d, T, max_len, ws)
     torch.cuda.synchronize()
     return host(y)
+
+
+def swin_block_gpu(tel, cfg: dict, w: dict):
+    """(desc, packed, workspace) of one shifted-window block of config cfg."""
+    dt = cfg["dtype"]
+    desc = tel.make_swin_desc(cfg["batch"], cfg["height"], cfg["width"], cfg["channels"],
+                              cfg["heads"], cfg["window"], cfg["shift"], cfg["mlp"], TORCH_DT[dt],
+                              ti.LN_EPS)
+    packed = tel.alloc_bytes(tel.tel_swin_packed_size(desc))
+    tel.tel_swin_prepare(desc, {k: dev(v, dt) for k, v in w.items()}, packed)
+    ws = tel.alloc_bytes(tel.tel_swin_workspace_size(desc))
+    return desc, packed, ws
+
+
+def swin_two_stages_gpu(tel, cfg: dict, x: np.ndarray, stage1: list, merge: dict, stage2: list,
+                        keep_intermediates: bool = True):
+    """Swin stage 1 (blocks alternating shift 0 / 3), patch merging, stage 2 on the GPU,
+    through the C ABI. Returns the output and, with keep_intermediates, the input of every
+    piece (host float64 copies), in order."""
+    from oracle import swin as _sw   # only for the block shift pattern (stage_shifts)
+    dt = cfg["dtype"]
+    H, W, M = cfg["height"], cfg["width"], cfg["window"]
+    cur = dev(x, dt)
+    ins = []
+    for stage, blocks in ((0, stage1), (1, stage2)):
+        f = 2 ** stage
+        for w, s in zip(blocks, _sw.stage_shifts(len(blocks), H // f, W // f, M)):
+            bc = ti.swin_stage_block_config(cfg, stage, s)
+            desc, packed, ws = swin_block_gpu(tel, bc, w)
+            out = torch.empty_like(cur)
+            if keep_intermediates:
+                ins.append(host(cur))
+            tel.tel_window_attention_forward(desc, packed, cur, out, ws)
+            cur = out
+        if stage == 0:
+            C = cfg["channels"]
+            out = torch.empty((cfg["batch"], (H // 2) * (W // 2), 2 * C), dtype=TORCH_DT[dt],
+                              device="cuda")
+            if keep_intermediates:
+                ins.append(host(cur))
+            tel.tel_patch_merging(cur, out, dev_f32(merge["norm_g"]), dev_f32(merge["norm_b"]),
+                                  dev(merge["w_red"], dt), H, W, ti.LN_EPS)
+            cur = out
+    torch.cuda.synchronize()
+    return host(cur), ins

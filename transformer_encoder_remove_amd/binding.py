@@ -36,7 +36,7 @@ EXPORTS = (
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
     "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
     "tel_gemm_2of4_tile_configs", "tel_gemm_2of4", "tel_build_offsets_mask",
-    "tel_rebuild_padding_mask", "tel_encoder_layer_forward_noalloc",
+    "tel_rebuild_padding_mask", "tel_encoder_layer_forward_noalloc", "tel_patch_merging",
 )
 TEL_NOALLOC_SCRATCH_BYTES = 64 << 20
 TEL_SWIN_ATTN_ONLY = 1
@@ -111,6 +111,7 @@ _SIG = {
     "tel_gemm_ex": (I, [I, I, I, P, P, P, P, P, I, I, I, I, P]),
     "tel_attention_varlen": (I, [P, P, P, I, I, I, I, I, I, P]),
     "tel_layernorm": (I, [P, P, P, P, I, I, F, I, P]),
+    "tel_patch_merging": (I, [P, P, P, P, P, I, I, I, I, F, I, P]),
     "tel_quantize_i8": (I, [P, P, SZ, F, I, P]),
     "tel_quantize_weight_i8": (I, [P, P, P, I, I, I, P]),
     "tel_gemm_i8_i32": (I, [P, P, P, I, I, I, P]),
@@ -351,6 +352,16 @@ def tel_attention_varlen(qkv_split, ctx, cu_seqlens, total_tokens: int, max_len:
     _check("tel_attention_varlen", lib.tel_attention_varlen(
         _ptr(qkv_split), _ptr(ctx), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total_tokens,
         max_len, heads, head_dim, dtype_code(ctx.dtype), _stream(stream)))
+
+
+def tel_patch_merging(x, y, gamma, beta, w_red, height: int, width: int, eps: float,
+                      stream=None):
+    """x [B, height*width, C] -> y [B, (height/2)*(width/2), 2C]; gamma, beta float32 [4C];
+    w_red [2C, 4C] of x's type."""
+    B, L, C = x.shape
+    _check("tel_patch_merging", lib.tel_patch_merging(
+        _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), _ptr(w_red), B, height, width, C, eps,
+        dtype_code(x.dtype), _stream(stream)))
 
 
 def tel_layernorm(x, y, gamma, beta, eps: float, stream=None):

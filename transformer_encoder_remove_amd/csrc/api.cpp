@@ -1072,6 +1072,29 @@ int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, c
                                            channels, eps, swin_geom(&d), as_stream(stream)));
 }
 
+int tel_patch_merging(const void* x, void* y, const float* gamma, const float* beta,
+                      const void* w_red, int batch, int height, int width, int channels,
+                      float eps, int dtype, void* stream) {
+  if (batch <= 0 || height <= 0 || width <= 0 || channels <= 0 || !(eps >= 0.f))
+    return TEL_EINVAL;
+  if (height % 2 || width % 2) return TEL_EINVAL;
+  if (!patch_merging_supported(dtype, channels)) return TEL_EUNSUPPORTED;
+  if ((long long)batch * height * width > INT32_MAX / 4) return TEL_EUNSUPPORTED;
+  if (!x || !y || !gamma || !beta || !w_red) return TEL_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta) || !aligned16(w_red))
+    return TEL_EINVAL;
+  if (x == y) return TEL_EINVAL;
+  const int M = batch * (height / 2) * (width / 2);
+  GemmArgs a{EPI_PLAIN, x, w_red, nullptr, nullptr, y, M, 2 * channels, 4 * channels, 1};
+  a.ln_g = gamma;
+  a.ln_b = beta;
+  a.ln_eps = eps;
+  a.ln_merge = 1;
+  a.geom.Hs = height;
+  a.geom.Ws = width;
+  return status_of(launch_gemm(dtype, a, as_stream(stream)));
+}
+
 int tel_attention_varlen(const void* qkv_split, void* ctx, const int32_t* cu_seqlens, int batch,
                          int total_tokens, int max_len, int heads, int head_dim, int dtype,
                          void* stream) {

@@ -134,6 +134,15 @@ struct SwinGeom {
     if (x >= Ws) x -= Ws;
     return b * Hs * Ws + y * Ws + x;
   }
+  // Patch merging (the downsampling between stages): merged token r of the (Hs/2) x (Ws/2)
+  // grid, part k = 0..3, reads image row (2i + (k & 1), 2j + (k >> 1)) of the Hs x Ws
+  // image, i.e. the parts in (row, column) offset order (0,0), (1,0), (0,1), (1,1).
+  __device__ __forceinline__ int merge_src(int r, int k) const {
+    const int Wo = Ws >> 1, per_img = (Hs >> 1) * Wo;
+    const int b = r / per_img, rem = r - b * per_img;
+    const int i = rem / Wo, j = rem - i * Wo;
+    return b * Hs * Ws + (2 * i + (k & 1)) * Ws + 2 * j + (k >> 1);
+  }
   // Shift-mask region of window-order token p of window w (image-local window index):
   // per axis, [0, L-M) -> 0, [L-M, L-s) -> 1, [L-s, L) -> 2 in the shifted frame; no mask
   // (one region) when s == 0.

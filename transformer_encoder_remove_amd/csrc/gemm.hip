@@ -69,7 +69,8 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
     *reinterpret_cast<ACC*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
     return;
   } else {
-    const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
+    const float4 b = EPI == EPI_PLAIN ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                      : *reinterpret_cast<const float4*>(e.bias + n);
     float v[4];
     if constexpr (std::is_same<T, int8_t>::value) {
       const float4 d = *reinterpret_cast<const float4*>(e.dq + n);
@@ -835,24 +836,42 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
 // 4-column epilogue above (bias, GELU, QKV split, window scatter, residual) applies as is.
 constexpr int ROWS_WG = 64;
 
-template <typename T, int KS, bool GATHER>
+// Input-row modes of the skinny kernel: rows as stored, the shifted-window partition
+// (row r reads image row geom.src_row(r)), or patch merging (row r is the concatenation of
+// the four image rows geom.merge_src(r, k), each K / 4 wide).
+enum RowMode { ROWS_PLAIN = 0, ROWS_WINDOW = 1, ROWS_MERGE = 2 };
+
+template <typename T, int KS, int MODE>
 __device__ __forceinline__ void rows_load(typename Mfma<T>::frag (&buf)[KS], const T* A, int M,
                                           int row0, int lr, int lg, const SwinGeom& geom) {
   constexpr int K = KS * 32;
   int row = min(row0 + lr, M - 1);
-  if constexpr (GATHER) row = geom.src_row(row);
-  const T* src = A + (size_t)row * K + lg * 8;
+  if constexpr (MODE == ROWS_MERGE) {
+    constexpr int C = K / 4, TP = KS / 4;           // 32-wide k chunks per part
+    static_assert(KS % 4 == 0, "a k chunk must not straddle two parts");
 #pragma unroll
-  for (int t = 0; t < KS; ++t) buf[t] = *reinterpret_cast<const typename Mfma<T>::frag*>(src + t * 32);
+    for (int k = 0; k < 4; ++k) {
+      const T* src = A + (size_t)geom.merge_src(row, k) * C + lg * 8;
+#pragma unroll
+      for (int t = 0; t < TP; ++t)
+        buf[k * TP + t] = *reinterpret_cast<const typename Mfma<T>::frag*>(src + t * 32);
+    }
+    return;
+  } else {
+    if constexpr (MODE == ROWS_WINDOW) row = geom.src_row(row);
+    const T* src = A + (size_t)row * K + lg * 8;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) buf[t] = *reinterpret_cast<const typename Mfma<T>::frag*>(src + t * 32);
+  }
 }
 
 // LayerNorm of the rows held in fragments: the 4 lanes lg = 0..3 of a row hold its K values
 // (8 per k-step each), so the two-pass statistics are the lane's own sums plus butterflies
 // over xor 16 and xor 32; the normalised values replace the fragments (rounded to T, as a
 // stored LayerNorm output would be). g, b: the lane's gamma/beta for its K/4 positions.
-template <typename T, int KS>
-__device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS],
-                                               const float (&g)[KS][8], const float (&b)[KS][8],
+// gb(t, e, &g, &b) gives the lane's gamma and beta of its value e of k-step t.
+template <typename T, int KS, typename GB>
+__device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS], const GB& gb,
                                                float eps) {
   constexpr int K = KS * 32;
   float v[KS][8];
@@ -881,7 +900,11 @@ __device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS]
 #pragma unroll
   for (int t = 0; t < KS; ++t)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) buf[t][e] = from_f32<T>(v[t][e] * rstd * g[t][e] + b[t][e]);
+    for (int e = 0; e < 8; ++e) {
+      float g, b;
+      gb(t, e, g, b);
+      buf[t][e] = from_f32<T>(v[t][e] * rstd * g + b);
+    }
 }
 
 // Output fragments in groups of 6 and k in chunks of 3 steps, with scheduling barriers
@@ -921,7 +944,18 @@ __device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS]
   }
 }
 
-template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, bool GATHER>
+// LayerNorm parameters of the A operand: up to K = 96 the lane keeps its gamma / beta in
+// registers; wider rows (patch merging, K = 384) would need 2 * K / 4 registers, so they
+// are staged in LDS beside the weights and read per value (lanes of one lg read the same
+// address: a broadcast).
+template <int KS> constexpr bool ln_in_lds() { return KS > 3; }
+
+template <typename T, int NF, int KS, bool LNA>
+constexpr int rows_lds_bytes() {
+  return NF * 16 * (KS * 32 + 8) * (int)sizeof(T) + (LNA && ln_in_lds<KS>() ? 2 * KS * 32 * 4 : 0);
+}
+
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, int MODE>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
                                                         const T* __restrict__ W,
                                                         EpiArgs<T, TR, TO> e,
@@ -931,7 +965,11 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
   using MF = Mfma<T>;
   static_assert(MF::KPL == 8, "16-bit operands");
   constexpr int N = NF * 16, K = KS * 32, LDW = K + 8;
-  __shared__ __attribute__((aligned(16))) T sW[N * LDW];
+  constexpr bool GB_LDS = LNA && ln_in_lds<KS>();
+  __shared__ __attribute__((aligned(16))) char smem_rows[rows_lds_bytes<T, NF, KS, LNA>()];
+  T* sW = reinterpret_cast<T*>(smem_rows);
+  float* sG = reinterpret_cast<float*>(smem_rows + N * LDW * sizeof(T));
+  float* sB = sG + K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   for (int idx = tid; idx < N * (K / 8); idx += 256) {
@@ -939,11 +977,18 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
     *reinterpret_cast<u32x4*>(sW + r * LDW + c * 8) =
         *reinterpret_cast<const u32x4*>(W + (size_t)r * K + c * 8);
   }
+  if constexpr (GB_LDS) {
+    for (int k = tid; k < K; k += 256) {
+      sG[k] = ln_g[k];
+      sB[k] = ln_b[k];
+    }
+  }
   __syncthreads();
   const int M = e.M, stride = gridDim.x * ROWS_WG;
   // the lane's gamma / beta of the A-operand LayerNorm: k = t * 32 + lg * 8 + j
-  float lg_g[KS][8], lg_b[KS][8];
-  if constexpr (LNA) {
+  constexpr int KR = LNA && !GB_LDS ? KS : 1;
+  float lg_g[KR][8], lg_b[KR][8];
+  if constexpr (LNA && !GB_LDS) {
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
@@ -954,38 +999,55 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
         lg_b[t][j] = bv.x; lg_b[t][j + 1] = bv.y; lg_b[t][j + 2] = bv.z; lg_b[t][j + 3] = bv.w;
       }
   }
+  auto gb = [&](int t, int j, float& g, float& b) {
+    if constexpr (GB_LDS) {
+      g = sG[t * 32 + lg * 8 + j];
+      b = sB[t * 32 + lg * 8 + j];
+    } else {
+      g = lg_g[t][j];
+      b = lg_b[t][j];
+    }
+  };
   typename MF::frag a0[KS], a1[KS];
   int rb = blockIdx.x * ROWS_WG + wave * 16;   // this wavefront's 16 rows of the block
-  if (rb < M) rows_load<T, KS, GATHER>(a0, A, M, rb, lr, lg, e.geom);
-  if (rb + stride < M) rows_load<T, KS, GATHER>(a1, A, M, rb + stride, lr, lg, e.geom);
+  if (rb < M) rows_load<T, KS, MODE>(a0, A, M, rb, lr, lg, e.geom);
+  if (rb + stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + stride, lr, lg, e.geom);
   for (; rb < M; rb += 2 * stride) {
-    if constexpr (LNA) rows_layernorm<T, KS>(a0, lg_g, lg_b, ln_eps);
+    if constexpr (LNA) rows_layernorm<T, KS>(a0, gb, ln_eps);
     rows_block<T, NF, KS, EPI, TR, TO>(a0, sW, e, rb, lr, lg);
-    if (rb + 2 * stride < M) rows_load<T, KS, GATHER>(a0, A, M, rb + 2 * stride, lr, lg, e.geom);
+    if (rb + 2 * stride < M) rows_load<T, KS, MODE>(a0, A, M, rb + 2 * stride, lr, lg, e.geom);
     if (rb + stride >= M) break;
-    if constexpr (LNA) rows_layernorm<T, KS>(a1, lg_g, lg_b, ln_eps);
+    if constexpr (LNA) rows_layernorm<T, KS>(a1, gb, ln_eps);
     rows_block<T, NF, KS, EPI, TR, TO>(a1, sW, e, rb + stride, lr, lg);
-    if (rb + 3 * stride < M) rows_load<T, KS, GATHER>(a1, A, M, rb + 3 * stride, lr, lg, e.geom);
+    if (rb + 3 * stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + 3 * stride, lr, lg, e.geom);
   }
 }
 
 template <typename T, int NF, int KS>
 static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
   const int blocks = (a.M + ROWS_WG - 1) / ROWS_WG;
-  const int grid = std::min(blocks, 512);   // two workgroups per CU (<= 80 KiB of LDS each)
-#define TEL_ROWS_LN(EPI, LNA, GATHER)                                                        \
+  // persistent: two workgroups per CU when one takes <= 80 KiB of LDS, else one
+  const int per_cu = rows_lds_bytes<T, NF, KS, true>() <= 80 * 1024 ? 2 : 1;
+  const int grid = std::min(blocks, 256 * per_cu);
+#define TEL_ROWS_LN(EPI, LNA, MODE)                                                          \
   do {                                                                                       \
     EpiArgs<T, T, T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, \
                        a.geom};                                                              \
-    gemm_rows_kernel<T, NF, KS, EPI, T, T, LNA, GATHER><<<grid, 256, 0, stream>>>(          \
+    gemm_rows_kernel<T, NF, KS, EPI, T, T, LNA, MODE><<<grid, 256, 0, stream>>>(            \
         (const T*)a.A, (const T*)a.W, e, a.ln_g, a.ln_b, a.ln_eps);                         \
   } while (0)
-#define TEL_ROWS(EPI) TEL_ROWS_LN(EPI, false, false)
+#define TEL_ROWS(EPI) TEL_ROWS_LN(EPI, false, ROWS_PLAIN)
+  if constexpr (NF == 12 && KS == 12) {   // patch merging only: gather of four rows, LN, no bias
+    if (!a.ln_g || !a.ln_b || !a.ln_merge || a.epi != EPI_PLAIN) return hipErrorInvalidValue;
+    TEL_ROWS_LN(EPI_PLAIN, true, ROWS_MERGE);
+    return hipGetLastError();
+  } else {
   if (a.ln_g) {   // A-operand LayerNorm: the shifted-window block's LN1 (+ partition) and LN2
     if (!a.ln_b) return hipErrorInvalidValue;
-    if (a.epi == EPI_QKV_SPLIT && a.ln_gather) TEL_ROWS_LN(EPI_QKV_SPLIT, true, true);
-    else if (a.epi == EPI_QKV_SPLIT) TEL_ROWS_LN(EPI_QKV_SPLIT, true, false);
-    else if (a.epi == EPI_BIAS_GELU && !a.ln_gather) TEL_ROWS_LN(EPI_BIAS_GELU, true, false);
+    if (a.ln_merge) return hipErrorInvalidValue;
+    if (a.epi == EPI_QKV_SPLIT && a.ln_gather) TEL_ROWS_LN(EPI_QKV_SPLIT, true, ROWS_WINDOW);
+    else if (a.epi == EPI_QKV_SPLIT) TEL_ROWS_LN(EPI_QKV_SPLIT, true, ROWS_PLAIN);
+    else if (a.epi == EPI_BIAS_GELU && !a.ln_gather) TEL_ROWS_LN(EPI_BIAS_GELU, true, ROWS_PLAIN);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
@@ -997,15 +1059,20 @@ static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
     case EPI_SWIN_SCATTER: TEL_ROWS(EPI_SWIN_SCATTER); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+  }
 #undef TEL_ROWS
 #undef TEL_ROWS_LN
-  return hipGetLastError();
 }
 
 bool gemm_rows_supported(int dtype, int N, int K) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   return (N == 288 && K == 96) || (N == 96 && K == 96) || (N == 384 && K == 96) ||
          (N == 96 && K == 384);
+}
+
+bool patch_merging_supported(int dtype, int channels) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && channels == 96;
 }
 
 // The (N, K) shapes the skinny kernel is built for; false: use the tiled kernels.
@@ -1016,6 +1083,7 @@ static bool launch_rows(const GemmArgs& a, hipStream_t stream, hipError_t* err) 
   else if (a.N == 96 && a.K == 96) *err = launch_rows_nk<T, 6, 3>(a, stream);
   else if (a.N == 384 && a.K == 96) *err = launch_rows_nk<T, 24, 3>(a, stream);
   else if (a.N == 96 && a.K == 384) *err = launch_rows_nk<T, 6, 12>(a, stream);
+  else if (a.N == 192 && a.K == 384 && a.ln_merge) *err = launch_rows_nk<T, 12, 12>(a, stream);
   else return false;
   return true;
 }

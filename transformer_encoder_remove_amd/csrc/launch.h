@@ -12,9 +12,10 @@ enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
 enum Epi {
   EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESID = 2, EPI_QKV_SPLIT = 3, EPI_RAW_I32 = 4,
   EPI_SWIN_SCATTER = 5,  // bias + residual, row m written to image row geom.src_row(m)
-  EPI_PARTIAL = 6        // raw 32-bit accumulators (float32, or int32 for int8 operands) of
+  EPI_PARTIAL = 6,       // raw 32-bit accumulators (float32, or int32 for int8 operands) of
                          // k-split s at C + s * M * N, or those sums rounded to fp16
                          // (GemmArgs::part16, fp16 operands); a reduce kernel finishes the sum
+  EPI_PLAIN = 7          // C = A W^T in the storage type, no bias (skinny kernel only)
 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
@@ -70,12 +71,17 @@ struct GemmArgs {
   const float* ln_b = nullptr;
   float ln_eps = 0.f;
   int ln_gather = 0;
+  // patch merging (skinny kernel, with ln_g): A row r is the concatenation of the four
+  // image rows geom.merge_src(r, k), k = 0..3, of the Hs x Ws image in geom
+  int ln_merge = 0;
   // 2:4-sparse weights (f16/bf16, K % 128 == 0): W holds the kept values [N][K/2] and
   // w_idx the 16-bit index words [N][K/16] (the form launch_prune_2of4 writes)
   const uint16_t* w_idx = nullptr;
 };
 // The (dtype, N, K) the skinny row kernel serves (the shifted-window block's projections).
 bool gemm_rows_supported(int dtype, int N, int K);
+// Patch merging of an image of `channels` channels runs on the skinny kernel (N = 2C, K = 4C).
+bool patch_merging_supported(int dtype, int channels);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
