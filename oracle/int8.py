@@ -25,12 +25,15 @@ implementations make the same decision.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from . import encoder as enc
 
 __all__ = ["quantize_weight", "quantize_act", "int8_matmul", "dequantize", "calibrate",
-           "act_scale", "encoder_layer_int8", "encoder_stack_int8"]
+           "calibrate_attention", "act_scale", "attention_int8", "encoder_layer_int8",
+           "encoder_stack_int8"]
 
 
 def _rne_clamp(v32: np.ndarray) -> np.ndarray:
@@ -85,15 +88,67 @@ def calibrate(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float) -> lis
             float(np.abs(mid["h1"]).max()), float(np.abs(mid["f"]).max())]
 
 
+def calibrate_attention(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float) -> list:
+    """Max-abs of the Q, K and V parts of the QKV projection in a float64 run of the
+    floating-point layer on a calibration batch (the static scales of int8 attention)."""
+    _, mid = enc.encoder_layer(x, cu_seqlens, w, heads, eps, return_intermediates=True)
+    H = mid["qkv"].shape[1] // 3
+    return [float(np.abs(mid["qkv"][:, i * H:(i + 1) * H]).max()) for i in range(3)]
+
+
+def attention_int8(qkv_storage: np.ndarray, cu_seqlens, heads: int, attn_amax: list):
+    """Multi-head attention with both products on int8 codes ([SW] section 3, INT8
+    paragraph: all matrix multiplications in int8). Reading of the steps the page leaves
+    open, per sequence b, head h and query i (keys j of sequence b only):
+      * Q, K, V codes from the stored (fp16) projection at static per-tensor scales
+        s_q, s_k, s_v (calibration max-abs / 127), the quantize_act rule;
+      * S[i, j] = sum_c q[i, c] k[j, c], exact integers;
+      * t[i, j] = float32(S) * a2 with a2 = float32(float32(s_q * s_k) / sqrt(d)) *
+        log2(e), one float32 multiply (scores in base 2);
+      * p[i, j] = 2^(t[i, j] - max_j t[i, j]) in float32, in (0, 1];
+      * P codes r[i, j] = rne(127 p[i, j]) in [0, 127] (fixed scale 1/127);
+      * ctx[i, h d + c] = s_v * (sum_j r[i, j] v[j, c]) / (sum_j r[i, j]): both sums exact
+        integers (the largest p gives r = 127, so the denominator is >= 127).
+    Decisions that turn floats into codes are taken in float32, as the kernel takes them.
+    Returns ctx [T, H] in float64 (not rounded)."""
+    qkv = np.asarray(qkv_storage)
+    T, H3 = qkv.shape
+    H = H3 // 3
+    d = H // heads
+    f32 = np.float32
+    sc = [act_scale(a) for a in attn_amax]
+    q = quantize_act(qkv[:, :H], sc[0][1]).astype(np.int64)
+    k = quantize_act(qkv[:, H:2 * H], sc[1][1]).astype(np.int64)
+    v = quantize_act(qkv[:, 2 * H:], sc[2][1]).astype(np.int64)
+    a2 = f32(f32(f32(sc[0][0] * sc[1][0]) / f32(math.sqrt(d))) * f32(1.4426950408889634))
+    out = np.zeros((T, H), np.float64)
+    cu = np.asarray(cu_seqlens, np.int64)
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        for h in range(heads):
+            cs = slice(h * d, (h + 1) * d)
+            S = q[s0:s1, cs] @ k[s0:s1, cs].T                       # exact
+            t = S.astype(f32) * a2
+            p = np.exp2((t - t.max(axis=1, keepdims=True)).astype(f32)).astype(f32)
+            r = np.clip(np.rint((p * f32(127.0)).astype(f32)), 0, 127).astype(np.int64)
+            num = r @ v[s0:s1, cs]                                  # exact
+            out[s0:s1, cs] = float(sc[2][0]) * num / r.sum(axis=1, keepdims=True)
+    return out
+
+
 def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float,
-                       amax: list, storage=np.float16):
+                       amax: list, storage=np.float16, attn_amax=None):
     """Post-LN encoder layer with the four projection GEMMs in int8.
 
     ``w`` holds the floating-point weights; they are quantised here per
     quantize_weight. ``amax`` are the four calibration max-abs values.
     ``storage`` is the type every activation is stored in (fp16): the dequantised
     QKV, the attention output, the two pre-LayerNorm sums, h1 and the GELU output.
-    The returned output is not rounded.
+    With ``attn_amax`` (the Q, K, V max-abs of calibrate_attention) attention runs on
+    int8 codes too (attention_int8); the QKV projection's fp16 value is then only the
+    value its codes are taken from. The returned output is not rounded.
     """
     scales = [act_scale(a) for a in amax]
 
@@ -108,18 +163,23 @@ def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: floa
 
     x = np.asarray(x, np.float64)
     qkv = st(qlinear(x, "w_qkv", "b_qkv", 0))
-    ctx = st(enc.attention(qkv, cu_seqlens, heads))
+    if attn_amax is not None:
+        ctx = st(attention_int8(qkv.astype(storage), cu_seqlens, heads, attn_amax))
+    else:
+        ctx = st(enc.attention(qkv, cu_seqlens, heads))
     h1 = st(enc.layer_norm(st(qlinear(ctx, "w_o", "b_o", 1) + x), w["ln1_g"], w["ln1_b"], eps))
     f = st(enc.gelu(qlinear(h1, "w_1", "b_1", 2)))
     return enc.layer_norm(st(qlinear(f, "w_2", "b_2", 3) + h1), w["ln2_g"], w["ln2_b"], eps)
 
 
 def encoder_stack_int8(x, cu_seqlens, layers: list, amaxes: list, heads: int, eps: float,
-                       storage=np.float16):
-    """Layers in order, each with its own calibration max-abs list; the output of
-    every layer is rounded to ``storage`` as the stored activation."""
+                       storage=np.float16, attn_amaxes=None):
+    """Layers in order, each with its own calibration max-abs list (and, for int8
+    attention, its own Q/K/V max-abs list); the output of every layer is rounded to
+    ``storage`` as the stored activation."""
     y = np.asarray(x, np.float64)
-    for w, a in zip(layers, amaxes):
-        y = encoder_layer_int8(y, cu_seqlens, w, heads, eps, a, storage)
+    for i, (w, a) in enumerate(zip(layers, amaxes)):
+        aa = attn_amaxes[i] if attn_amaxes is not None else None
+        y = encoder_layer_int8(y, cu_seqlens, w, heads, eps, a, storage, attn_amax=aa)
         y = y.astype(storage).astype(np.float64)
     return y

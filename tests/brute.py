@@ -98,7 +98,48 @@ def _q8(v32):
     return int(max(-127, min(127, r)))
 
 
-def encoder_layer_int8_padded(x_pad, lens, w, heads, eps, amax):
+def attention_int8_padded(qkv_pad, lens, heads, attn_amax):
+    """Int8 attention on the padded batch by loops: codes of the fp16 Q, K, V values at
+    scales amax / 127; integer score sums over the valid keys only; base-2 scores and the
+    probabilities in float32 scalars; probability codes rne(127 p); the context as s_v times
+    the ratio of two integer sums. qkv_pad [B, S, 3H] fp16 values; returns [B, S, H] (rows
+    past each length stay 0)."""
+    f32 = np.float32
+    qkv_pad = np.asarray(qkv_pad)
+    B, S, H3 = qkv_pad.shape
+    H = H3 // 3
+    d = H // heads
+    s_ = [f32(f32(a) / f32(127.0)) for a in attn_amax]
+    inv = [f32(f32(127.0) / f32(a)) for a in attn_amax]
+    a2 = f32(f32(f32(s_[0] * s_[1]) / f32(math.sqrt(d))) * f32(1.4426950408889634))
+    code = lambda v, g: _q8(f32(f32(np.float16(v)) * inv[g]))
+    out = np.zeros((B, S, H))
+    for b in range(B):
+        L = int(lens[b])
+        qc = [[code(qkv_pad[b, i, c], 0) for c in range(H)] for i in range(L)]
+        kc = [[code(qkv_pad[b, j, H + c], 1) for c in range(H)] for j in range(L)]
+        vc = [[code(qkv_pad[b, j, 2 * H + c], 2) for c in range(H)] for j in range(L)]
+        for h in range(heads):
+            for i in range(L):
+                t = []
+                for j in range(L):
+                    acc = 0
+                    for c in range(h * d, (h + 1) * d):
+                        acc += qc[i][c] * kc[j][c]
+                    t.append(f32(f32(acc) * a2))
+                m = max(t)
+                r = [int(max(0, min(127, np.rint(f32(f32(np.exp2(f32(tj - m))) * f32(127.0))))))
+                     for tj in t]
+                den = sum(r)
+                for c in range(h * d, (h + 1) * d):
+                    num = 0
+                    for j in range(L):
+                        num += r[j] * vc[j][c]
+                    out[b, i, c] = float(s_[2]) * num / den
+    return out
+
+
+def encoder_layer_int8_padded(x_pad, lens, w, heads, eps, amax, attn_amax=None):
     """Int8-GEMM layer, padded formulation, loops. Weights: per-row scale
     max|W|/127 (float32), codes rne(W/s) clamped; activations: fp16 storage, then
     one float32 multiply by 127/amax, rne, clamp; int accumulate; y = acc*(s_a*s_w)+b.
@@ -143,9 +184,13 @@ def encoder_layer_int8_padded(x_pad, lens, w, heads, eps, amax):
         L = int(lens[b])
         rows = [x_pad[b, i].tolist() for i in range(S)]
         qkv = [[h(v) for v in qlin(r, "w_qkv", "b_qkv", 0)] for r in rows]
+        if attn_amax is not None:
+            ctx8 = attention_int8_padded(np.asarray(qkv)[None], [L], heads, attn_amax)[0]
         for i in range(L):
             ctx = [0.0] * H
-            for hh in range(heads):
+            if attn_amax is not None:
+                ctx = [h(v) for v in ctx8[i]]
+            for hh in range(heads if attn_amax is None else 0):
                 q = qkv[i][hh * d:(hh + 1) * d]
                 sc = [_dot(q, qkv[j][H + hh * d:H + (hh + 1) * d]) / math.sqrt(d) for j in range(S)]
                 p = _softmax_masked(sc, [j < L for j in range(S)])

@@ -165,3 +165,97 @@ def test_int8_stack_of_one_is_the_rounded_layer():
     one = q8.encoder_stack_int8(xp, cu, [w], [a], cfg["heads"], EPS)
     ref = enc.remove_padding(brute.encoder_layer_int8_padded(x, lens, w, cfg["heads"], EPS, a), lens)
     assert np.array_equal(one, ref.astype(np.float16).astype(np.float64))
+
+
+# ------------------------------------------------------------------ int8 attention
+def _qkv_case(seed, lens, H=32, heads=2):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    qkv = (rng.standard_normal((T, 3 * H)) * 0.7).astype(np.float16)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    amax = [float(np.abs(qkv[:, i * H:(i + 1) * H].astype(np.float64)).max()) for i in range(3)]
+    return qkv, cu, amax
+
+
+def test_attention_int8_matches_padded_brute_force():
+    lens = [5, 1, 0, 9]
+    qkv, cu, amax = _qkv_case(11, lens)
+    got = q8.attention_int8(qkv, cu, 2, amax)
+    S = max(lens)
+    pad = np.zeros((len(lens), S, qkv.shape[1]), np.float16)
+    for b in range(len(lens)):
+        pad[b, :lens[b]] = qkv[cu[b]:cu[b + 1]]
+        pad[b, lens[b]:] = 9.0                                    # pads must not matter
+    ref = brute.attention_int8_padded(pad, lens, 2, amax)
+    assert np.abs(enc.remove_padding(ref, lens) - got).max() <= 1e-12
+
+
+def test_attention_int8_special_cases():
+    H, heads = 32, 2
+    rng = np.random.default_rng(12)
+    # identical keys: every probability is 1 (code 127), the output is the mean of V's codes
+    L = 6
+    qkv = (rng.standard_normal((L, 3 * H)) * 0.7).astype(np.float16)
+    qkv[:, H:2 * H] = qkv[0, H:2 * H]
+    amax = [float(np.abs(qkv[:, i * H:(i + 1) * H].astype(np.float64)).max()) for i in range(3)]
+    cu = np.array([0, L])
+    got = q8.attention_int8(qkv, cu, heads, amax)
+    s_v, inv_v = q8.act_scale(amax[2])
+    vq = q8.quantize_act(qkv[:, 2 * H:], inv_v).astype(np.float64)
+    assert np.abs(got - float(s_v) * vq.mean(axis=0)).max() <= 1e-12
+    # a single token attends to itself: its own V codes times s_v
+    one = q8.attention_int8(qkv[:1], np.array([0, 1]), heads, amax)
+    assert np.abs(one[0] - float(s_v) * vq[0]).max() <= 1e-12
+    # V codes all equal c: the output is c * s_v whatever the probabilities
+    qkv2 = qkv.copy()
+    qkv2[:, 2 * H:] = np.float16(0.5)
+    qkv2[:, H:2 * H] = (rng.standard_normal((L, H)) * 0.7).astype(np.float16)
+    amax2 = [amax[0], float(np.abs(qkv2[:, H:2 * H].astype(np.float64)).max()), 1.0]
+    got2 = q8.attention_int8(qkv2, cu, heads, amax2)
+    assert np.abs(got2 - float(q8.act_scale(1.0)[0]) * 64).max() <= 1e-12   # rne(0.5 * 127) = 64
+
+
+def test_attention_int8_sequences_are_isolated_and_close_to_float():
+    lens = [7, 30, 12]
+    qkv, cu, amax = _qkv_case(13, lens, H=64, heads=4)
+    got = q8.attention_int8(qkv, cu, 4, amax)
+    qkv2 = qkv.copy()
+    qkv2[cu[1]:cu[2]] = (np.random.default_rng(1).standard_normal((30, 192)) * 0.7).astype(np.float16)
+    got2 = q8.attention_int8(qkv2, cu, 4, amax)
+    for b in (0, 2):
+        assert np.array_equal(got[cu[b]:cu[b + 1]], got2[cu[b]:cu[b + 1]])
+    ref = enc.attention(qkv.astype(np.float64), cu, 4)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 0.03
+
+
+def test_int8_layer_with_int8_attention_matches_brute_force():
+    cfg = ti.custom_encoder_config(2, 6, [6, 4], 32, 2, 64, dtype="f16", seed=14)
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets(lens, 6)
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    amax = q8.calibrate(xp, cu, w, 2, EPS)
+    aa = q8.calibrate_attention(xp, cu, w, 2, EPS)
+    y = q8.encoder_layer_int8(xp, cu, w, 2, EPS, amax, attn_amax=aa)
+    ref = brute.encoder_layer_int8_padded(x, lens, w, 2, EPS, amax, attn_amax=aa)
+    assert np.abs(enc.remove_padding(ref, lens) - y).max() <= 1e-9
+    # and the float-attention int8 layer differs from it (the option is not a no-op)
+    y_f = q8.encoder_layer_int8(xp, cu, w, 2, EPS, amax)
+    assert np.abs(y_f - y).max() > 1e-6
+
+
+def test_calibrate_attention_matches_brute_force_projection():
+    cfg, lens, x = _tiny_int8_case(seed=15)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    H = cfg["hidden"]
+    cu, _ = enc.offsets(lens, cfg["max_seq"])
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    got = q8.calibrate_attention(xp, cu, w, cfg["heads"], EPS)
+    Wq = np.asarray(w["w_qkv"], np.float64)
+    bq = np.asarray(w["b_qkv"], np.float64)
+    want = [0.0, 0.0, 0.0]
+    for row in xp:
+        for n in range(3 * H):
+            v = abs(sum(Wq[n, k] * row[k] for k in range(H)) + bq[n])
+            want[n // H] = max(want[n // H], v)
+    assert np.abs(np.array(got) - np.array(want)).max() <= 1e-12
