@@ -89,6 +89,7 @@ def main():
     if args.dtype:
         cfg["dtype"] = args.dtype
     int8 = bool(cfg.get("int8"))
+    int8_mode = int(cfg.get("int8", 0))   # 1: int8 GEMMs, 2: and int8 attention
     sparse = bool(cfg.get("sparse"))
     dt = cfg["dtype"]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
@@ -124,19 +125,20 @@ def main():
         po = torch.empty(B * S, dtype=torch.int32, device="cuda")
         tel.tel_build_offsets(lens_d, S, cu_d, po)
         tel.tel_remove_padding(x, from_pad, po, T)
-        amax = torch.zeros((NL, 4), dtype=torch.float32, device="cuda")
+        amax = torch.zeros((NL, 7), dtype=torch.float32, device="cuda")
         lws = tel.alloc_bytes(tel.tel_encoder_workspace_size(desc, T))
         cur, nxt = from_pad, torch.empty_like(from_pad)
         for i in range(NL):
             tel.tel_encoder_calibrate(desc, packed[i], cur, nxt, cu_d, T, max_len, amax[i], lws)
             cur, nxt = nxt, cur
         amax_h = amax.cpu().numpy()
-        desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS, int8_gemm=True)
+        desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS, int8_gemm=int8_mode)
         psize = tel.tel_encoder_packed_size(desc)
         packed = []
         for i in range(NL):
             p = tel.alloc_bytes(psize)
-            tel.tel_encoder_prepare(desc, dws[i], p, act_amax=tuple(float(a) for a in amax_h[i]))
+            tel.tel_encoder_prepare(desc, dws[i], p, act_amax=tuple(float(a) for a in amax_h[i][:4]),
+                                    attn_amax=tuple(float(a) for a in amax_h[i][4:7]))
             packed.append(p)
         log(f"[bench] calibrated act_amax layer 0: {amax_h[0]}")
     del dws
@@ -246,6 +248,23 @@ def main():
             "gemm_ffn2_resid": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_BIAS_RESID, fq, wq["2"], dqs[H],
                                                         b32(H), pre, resid=hid, stream=stream),
                                 2.0 * T * H * F, T * F + F * H + 2.0 * 2 * T * H),
+        })
+    if int8_mode == 2:
+        # int8 attention: the QKV GEMM writes the codes of Q, K, V; attention reads codes and
+        # writes the codes of its output (1 byte per value in and out)
+        qkv8 = torch.empty(3 * T * H, dtype=torch.int8, device="cuda")
+        qinv3 = torch.full((3,), 40.0, device="cuda")
+        codes = rnd(3 * T * H)
+        scl = torch.tensor([1e-3, 1e-2, 40.0], dtype=torch.float32, device="cuda")
+        ctx8 = torch.empty(T, H, dtype=torch.int8, device="cuda")
+        kernels.update({
+            "gemm_qkv": (lambda: tel.tel_gemm_i8(tel.TEL_EPI_QKV_SPLIT, xq, wq["qkv"], dqs[3 * H],
+                                                 b32(3 * H), qkv8, qinv=qinv3, out_int8=True,
+                                                 heads=nh, stream=stream),
+                         2.0 * T * H * 3 * H, T * H + 3 * H * H + 1.0 * 3 * T * H),
+            "attention": (lambda: tel.tel_attention_int8(codes, ctx8, scl, cu, T, max_len, nh,
+                                                         H // nh, stream=stream),
+                          4.0 * T * H * Lbar, 1.0 * 4 * T * H),
         })
     if sparse:
         # the 2:4 layer's GEMMs (compressed weights of layer 0's matrices, as prepared);
@@ -825,9 +844,11 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     while elapsed < seconds:
         w = weights[done % len(weights)]
         amax = q8.calibrate(xp, cu, w, cfg["heads"], ti.LN_EPS) if int8 else None
+        aa = (q8.calibrate_attention(xp, cu, w, cfg["heads"], ti.LN_EPS)
+              if cfg.get("int8") == 2 else None)
         t0 = time.perf_counter()
         if int8:
-            xp = q8.encoder_layer_int8(xp, cu, w, cfg["heads"], ti.LN_EPS, amax)
+            xp = q8.encoder_layer_int8(xp, cu, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa)
         else:
             xp = enc.encoder_layer(xp, cu, w, cfg["heads"], ti.LN_EPS)
         elapsed += time.perf_counter() - t0
@@ -850,9 +871,11 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     w = weights[0]
     with threadpool_limits(limits=1):
         amax = q8.calibrate(x1, cu1, w, cfg["heads"], ti.LN_EPS) if int8 else None
+        aa = (q8.calibrate_attention(x1, cu1, w, cfg["heads"], ti.LN_EPS)
+              if cfg.get("int8") == 2 else None)
         t0 = time.perf_counter()
         if int8:
-            q8.encoder_layer_int8(x1, cu1, w, cfg["heads"], ti.LN_EPS, amax)
+            q8.encoder_layer_int8(x1, cu1, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa)
         else:
             enc.encoder_layer(x1, cu1, w, cfg["heads"], ti.LN_EPS)
         t1 = time.perf_counter() - t0

@@ -125,7 +125,8 @@ typedef struct {
   int ffn;         /* F, multiple of 8                                         */
   int dtype;       /* storage type of activations and weights                 */
   int int8_gemm;   /* 1: the four projection GEMMs run in int8 (dtype TEL_F16; H and F
-                      multiples of 16); see the int8 section below                 */
+                      multiples of 16); 2: attention's two products in int8 as well
+                      (tel_attention_int8); see the int8 section below               */
   float ln_eps;
   int sparse_2of4; /* 1: the four projection matrices are pruned 2:4 when prepared and run
                       on the sparse MFMA (dtype TEL_F16 or TEL_BF16, not int8_gemm; H and F
@@ -141,6 +142,9 @@ typedef struct {
   /* [host] int8 only: calibration max-abs of the inputs of the QKV, O, FFN1 and FFN2
    * GEMMs (static per-tensor activation scales a/127). Ignored otherwise. */
   float act_amax[4];
+  /* [host] int8_gemm == 2 only: calibration max-abs of the Q, K and V parts of the QKV
+   * projection (the static scales of the codes attention multiplies). Ignored otherwise. */
+  float attn_amax[3];
 } tel_encoder_weights;
 
 /* Bytes of the packed (preprocessed) form of one layer's weights. 0 on a bad desc. */
@@ -186,10 +190,11 @@ int tel_encoder_layer_forward_noalloc(const tel_encoder_desc* desc, const void* 
 
 /* Post-training calibration of the int8 variant's static activation scales: runs one
  * floating-point layer (desc->int8_gemm == 0) exactly as tel_encoder_layer_forward and
- * raises amax[0..3] (device float[4], caller-initialised, e.g. to 0) to the max-abs of
- * the inputs of its QKV, O, FFN1 and FFN2 GEMMs (x, attention output, h1, GELU output).
- * Calls accumulate, so a stack is calibrated layer by layer on one or more batches;
- * the results become tel_encoder_weights.act_amax of the int8 layer. */
+ * raises amax[0..6] (device float[7], caller-initialised, e.g. to 0) to the max-abs of
+ * the inputs of its QKV, O, FFN1 and FFN2 GEMMs (x, attention output, h1, GELU output)
+ * and of the Q, K and V parts of its QKV projection ([4..6]). Calls accumulate, so a stack
+ * is calibrated layer by layer on one or more batches; [0..3] become
+ * tel_encoder_weights.act_amax of the int8 layer, [4..6] its attn_amax. */
 int tel_encoder_calibrate(const tel_encoder_desc* desc, const void* packed, const void* x,
                           void* y, const int32_t* cu_seqlens, int batch, int total_tokens,
                           int max_len, float* amax, void* workspace, size_t ws_bytes,
@@ -353,12 +358,26 @@ int tel_gemm_i8_i32(const int8_t* A, const int8_t* B, int32_t* C, int M, int N, 
  * exact in int32, then v = acc * dq[n] + bias[n] (float32 arithmetic; dq[n] = activation
  * scale * weight scale of column n) and the epilogue of tel_gemm: TEL_EPI_BIAS, _BIAS_GELU,
  * _BIAS_RESID (resid fp16 [M][N]) or _QKV_SPLIT. C is fp16 ([M][N], or the head-split
- * layout), except out_int8 != 0 (TEL_EPI_BIAS_GELU only): C receives int8 codes
- * clamp(rne(float(fp16(v)) * *qinv), -127, 127), qinv a device scalar. A [M][K], W [N][K];
+ * layout), except out_int8 != 0 (TEL_EPI_BIAS_GELU or TEL_EPI_QKV_SPLIT): C receives int8
+ * codes clamp(rne(float(fp16(v)) * qinv), -127, 127), qinv a device scalar (GELU) or three,
+ * one each for the Q, K and V columns (head split, int8 attention). A [M][K], W [N][K];
  * K % 16 == 0, N % 4 == 0, 16-byte aligned pointers. */
 int tel_gemm_i8(int epilogue, const int8_t* A, const int8_t* W, const float* dq,
                 const float* bias, const void* resid, void* C, const float* qinv, int out_int8,
                 int M, int N, int K, int heads, void* stream);
+
+/* Attention with both products on int8 codes ([SW] section 3, INT8 paragraph: all matrix
+ * multiplications in int8), the attention of an int8_gemm == 2 layer. qkv_codes
+ * [3][heads][total_tokens][head_dim] int8 (codes of Q, K, V at scales s_q, s_k, s_v);
+ * scales: device float[3] = {s_q * s_k / sqrt(head_dim) * log2(e), s_v, 1 / s_o}. Per query
+ * i of sequence b and head h, keys of sequence b only: S = q . k exact in int32; t = S *
+ * scales[0] (float32); p = 2^(t - max_j t) in float32; P codes r = rne(127 p); ctx = s_v *
+ * (sum_j r v_j) / (sum_j r), both sums exact int32. out: ctx [total_tokens][heads *
+ * head_dim] fp16 (out_codes 0), or the int8 codes clamp(rne(float(fp16(ctx)) / s_o), +-127)
+ * (out_codes 1). head_dim in {16, 32, 64, 128}; qkv_codes and out 16-byte aligned. */
+int tel_attention_int8(const int8_t* qkv_codes, void* out, int out_codes, const float* scales,
+                       const int32_t* cu_seqlens, int batch, int total_tokens, int max_len,
+                       int heads, int head_dim, void* stream);
 
 /* Shifted-window partition with LayerNorm, one gather ([SW] section 3, the hand-written
  * shift-window-partition kernel): y row r (window order: images, windows row-major,

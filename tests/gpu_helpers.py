@@ -48,7 +48,8 @@ def dev_f32(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).to("cuda")
 
 
-def prepare_layers(tel, desc, layer_weights: list, dtype: str, act_amax=None) -> list:
+def prepare_layers(tel, desc, layer_weights: list, dtype: str, act_amax=None,
+                   attn_amax=None) -> list:
     packed = []
     n = tel.tel_encoder_packed_size(desc)
     assert n > 0
@@ -57,21 +58,26 @@ def prepare_layers(tel, desc, layer_weights: list, dtype: str, act_amax=None) ->
         p = tel.alloc_bytes(n)
         if act_amax is None:
             tel.tel_encoder_prepare(desc, dw, p)
-        else:
+        elif attn_amax is None:
             tel.tel_encoder_prepare(desc, dw, p, act_amax=tuple(float(a) for a in act_amax[i]))
+        else:
+            tel.tel_encoder_prepare(desc, dw, p, act_amax=tuple(float(a) for a in act_amax[i]),
+                                    attn_amax=tuple(float(a) for a in attn_amax[i]))
         packed.append(p)
     torch.cuda.synchronize()
     return packed
 
 
 def gpu_encoder_forward(tel, cfg: dict, lens, x_pad, layer_weights: list, int8=False,
-                        act_amax=None) -> np.ndarray:
+                        act_amax=None, attn_amax=None) -> np.ndarray:
     """Whole stack (offsets, remove, layers, rebuild) on the GPU; returns y_pad (float64).
-    int8: the projection GEMMs in int8 with per-layer calibration max-abs act_amax[layer]."""
+    int8: the projection GEMMs in int8 with per-layer calibration max-abs act_amax[layer];
+    int8 = 2: attention on int8 codes too, with the Q/K/V max-abs attn_amax[layer]."""
     dt = cfg["dtype"]
     desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT[dt], ti.LN_EPS,
                                  int8_gemm=int8)
-    packed = prepare_layers(tel, desc, layer_weights, dt, act_amax if int8 else None)
+    packed = prepare_layers(tel, desc, layer_weights, dt, act_amax if int8 else None,
+                            attn_amax if int8 == 2 else None)
     B, S, H = x_pad.shape
     x = dev(x_pad, dt)
     y = torch.full_like(x, float("nan"))

@@ -141,12 +141,13 @@ def test_calibrate_matches_oracle():
     cu, _ = enc.offsets(lens, cfg["max_seq"])
     xd = dev(xp, "f16")
     yd = torch.empty_like(xd)
-    amax = torch.zeros(4, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(7, dtype=torch.float32, device="cuda")
     ws = tel.alloc_bytes(tel.tel_encoder_workspace_size(desc, T))
     tel.tel_encoder_calibrate(desc, packed, xd, yd, torch.tensor(cu.astype(np.int32), device="cuda"),
                               T, int(lens.max()), amax, ws)
     torch.cuda.synchronize()
-    ref = np.array(q8.calibrate(xp, cu, w, cfg["heads"], EPS))
+    ref = np.array(q8.calibrate(xp, cu, w, cfg["heads"], EPS) +
+                   q8.calibrate_attention(xp, cu, w, cfg["heads"], EPS))
     got = amax.cpu().numpy().astype(np.float64)
     assert got[0] == ref[0]                               # the input itself: exact
     assert np.all(np.abs(got - ref) <= 5e-3 * ref), (got, ref)

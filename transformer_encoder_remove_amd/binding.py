@@ -37,6 +37,7 @@ EXPORTS = (
     "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
     "tel_gemm_2of4_tile_configs", "tel_gemm_2of4", "tel_build_offsets_mask",
     "tel_rebuild_padding_mask", "tel_encoder_layer_forward_noalloc", "tel_patch_merging",
+    "tel_attention_int8",
 )
 TEL_NOALLOC_SCRATCH_BYTES = 64 << 20
 TEL_SWIN_ATTN_ONLY = 1
@@ -84,7 +85,7 @@ class tel_swin_weights(ctypes.Structure):
 class tel_encoder_weights(ctypes.Structure):
     _fields_ = [(n, P) for n in ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
                                  "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")] + \
-               [("act_amax", F * 4)]
+               [("act_amax", F * 4), ("attn_amax", F * 3)]
 
 
 _SIG = {
@@ -112,6 +113,7 @@ _SIG = {
     "tel_attention_varlen": (I, [P, P, P, I, I, I, I, I, I, P]),
     "tel_layernorm": (I, [P, P, P, P, I, I, F, I, P]),
     "tel_patch_merging": (I, [P, P, P, P, P, I, I, I, I, F, I, P]),
+    "tel_attention_int8": (I, [P, P, I, P, P, I, I, I, I, I, P]),
     "tel_quantize_i8": (I, [P, P, SZ, F, I, P]),
     "tel_quantize_weight_i8": (I, [P, P, P, I, I, I, P]),
     "tel_gemm_i8_i32": (I, [P, P, P, I, I, I, P]),
@@ -236,6 +238,7 @@ def tel_rebuild_padding_mask(x_packed, x_pad, mask, padding_offset, total_tokens
 
 def make_encoder_desc(hidden, heads, ffn, dtype: torch.dtype, eps=1e-5, int8_gemm=False,
                       sparse_2of4=False):
+    """int8_gemm: False/0, True/1 (int8 GEMMs) or 2 (int8 GEMMs and int8 attention)."""
     return tel_encoder_desc(hidden, heads, ffn, dtype_code(dtype), int(int8_gemm), eps,
                             int(sparse_2of4))
 
@@ -256,9 +259,11 @@ _WNAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2"
            "ln2_g", "ln2_b")
 
 
-def tel_encoder_prepare(desc, weights: dict, packed, act_amax=(0.0, 0.0, 0.0, 0.0), stream=None):
+def tel_encoder_prepare(desc, weights: dict, packed, act_amax=(0.0, 0.0, 0.0, 0.0),
+                        attn_amax=(0.0, 0.0, 0.0), stream=None):
     """weights: dict of device tensors (storage type) named as in tel_encoder_weights."""
-    w = tel_encoder_weights(*[_ptr(weights[n]) for n in _WNAMES], (F * 4)(*act_amax))
+    w = tel_encoder_weights(*[_ptr(weights[n]) for n in _WNAMES], (F * 4)(*act_amax),
+                            (F * 3)(*attn_amax))
     _check("tel_encoder_prepare", lib.tel_encoder_prepare(
         ctypes.byref(desc), ctypes.byref(w), _ptr(packed), packed.numel() * packed.element_size(),
         _stream(stream)))
@@ -352,6 +357,16 @@ def tel_attention_varlen(qkv_split, ctx, cu_seqlens, total_tokens: int, max_len:
     _check("tel_attention_varlen", lib.tel_attention_varlen(
         _ptr(qkv_split), _ptr(ctx), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total_tokens,
         max_len, heads, head_dim, dtype_code(ctx.dtype), _stream(stream)))
+
+
+def tel_attention_int8(qkv_codes, out, scales, cu_seqlens, total_tokens: int, max_len: int,
+                       heads: int, head_dim: int, stream=None):
+    """qkv_codes int8 [3*heads*T*head_dim]; out fp16 [T, heads*head_dim] (the context) or
+    int8 (its codes at scales[2]); scales float32 device [3]."""
+    _i32("tel_attention_int8", cu_seqlens)
+    _check("tel_attention_int8", lib.tel_attention_int8(
+        _ptr(qkv_codes), _ptr(out), int(out.dtype == torch.int8), _ptr(scales), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, total_tokens, max_len, heads, head_dim, _stream(stream)))
 
 
 def tel_patch_merging(x, y, gamma, beta, w_red, height: int, width: int, eps: float,

@@ -33,6 +33,11 @@ inline bool float_type(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT
   } while (0)
 
 // ------------------------------------------------------------------ packed layer layout
+// Activation-scale table of an int8 layer (float32): [0..3] s_a of the QKV, O, FFN1, FFN2
+// inputs, [4..7] their 1 / s_a; int8 attention: [8..10] 1 / s of the Q, K, V codes the QKV
+// epilogue writes, then the attention kernel's [11] s_q s_k / sqrt(d) * log2 e, [12] s_v,
+// [13] 1 / s_a of the O projection's input (= [5]).
+constexpr int ACT_FLOATS = 16;
 // Storage-type weights first (GEMM operands, [N][K] as given), then float32 vectors.
 // An int8 layer stores int8 weight codes instead, followed by the per-row weight scales,
 // the per-column dequantisation scales and the activation scales s_a[4], inv_a[4].
@@ -55,7 +60,9 @@ bool desc_ok(const tel_encoder_desc* d) {
 int desc_supported(const tel_encoder_desc* d) {
   if (!desc_ok(d)) return TEL_EINVAL;
   if (!float_type(d->dtype)) return TEL_EUNSUPPORTED;
+  if (d->int8_gemm < 0 || d->int8_gemm > 2) return TEL_EINVAL;
   if (d->int8_gemm && (d->dtype != DT_F16 || d->hidden % 16 || d->ffn % 16)) return TEL_EUNSUPPORTED;
+  if (d->int8_gemm == 2 && !attention_int8_supported(d->hidden / d->heads)) return TEL_EUNSUPPORTED;
   if (d->sparse_2of4 && (d->int8_gemm || (d->dtype != DT_F16 && d->dtype != DT_BF16) ||
                          d->hidden % 128 || d->ffn % 128))
     return TEL_EUNSUPPORTED;
@@ -102,7 +109,7 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
     L.dq_o = take(H * 4);
     L.dq_1 = take(F * 4);
     L.dq_2 = take(H * 4);
-    L.act = take(8 * 4);
+    L.act = take(ACT_FLOATS * 4);
   }
   L.total = o;
   return L;
@@ -218,6 +225,7 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   const int H = d->hidden, F = d->ffn, nh = d->heads;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
   const float* inv = F32(L.act) + 4;
+  const bool attn8 = d->int8_gemm == 2;
   const int8_t* xq = link.xq_in ? link.xq_in : (const int8_t*)(ws + W.xq);
   int8_t* ctxq = (int8_t*)(ws + W.ctxq);
   int8_t* h1q = (int8_t*)(ws + W.h1q);
@@ -235,10 +243,18 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
     TEL_TRY(launch_quantize_act(DT_F16, x, (int8_t*)(ws + W.xq), (size_t)T * H, inv + 0, 0.f, st));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.dq = F32(L.dq_qkv);
+  if (attn8) {   // int8 attention: the QKV epilogue writes the codes of Q, K and V
+    g.out_i8 = 1;
+    g.qinv = F32(L.act) + 8;
+  }
   TEL_TRY(launch_gemm(DT_I8, g, st));
   // attention writes the int8 codes of its fp16 output directly (the O projection's input)
-  TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, ctxq,
-                           inv + 1));
+  if (attn8)
+    TEL_TRY(launch_attention_int8((const int8_t*)qkv, ctxq, 1, cu, batch, T, max_len, nh, H / nh,
+                                  F32(L.act) + 11, st));
+  else
+    TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, ctxq,
+                             inv + 1));
   // output projection + dequantise + bias + residual (stored fp16), LayerNorm and the
   // int8 codes of h1; split over k (int32 partials, all of that in the reduce kernel)
   // when few tokens leave the GPU idle
@@ -538,8 +554,21 @@ int tel_encoder_prepare(const tel_encoder_desc* d, const tel_encoder_weights* w,
       sa[i] = a / 127.0f;
       inv[i] = 127.0f / a;
     }
-    float act[8] = {sa[0], sa[1], sa[2], sa[3], inv[0], inv[1], inv[2], inv[3]};
-    TEL_TRY(launch_store_f32((float*)(P + L.act), act, 8, st));
+    float act[ACT_FLOATS] = {sa[0], sa[1], sa[2], sa[3], inv[0], inv[1], inv[2], inv[3]};
+    if (d->int8_gemm == 2) {   // int8 attention: Q, K, V code scales and the kernel's constants
+      float sqkv[3];
+      for (int i = 0; i < 3; ++i) {
+        const float a = w->attn_amax[i];
+        if (!(a > 0.f) || !(a < 3.0e38f)) return TEL_EINVAL;
+        sqkv[i] = a / 127.0f;
+        act[8 + i] = 127.0f / a;
+      }
+      const int hd = d->hidden / d->heads;
+      act[11] = ((sqkv[0] * sqkv[1]) / sqrtf((float)hd)) * 1.4426950408889634f;
+      act[12] = sqkv[2];
+      act[13] = inv[1];
+    }
+    TEL_TRY(launch_store_f32((float*)(P + L.act), act, ACT_FLOATS, st));
     TEL_TRY(launch_quantize_weight(dt, w->w_qkv, (int8_t*)(P + L.w_qkv), (float*)(P + L.sw_qkv),
                                    (float*)(P + L.dq_qkv), sa[0], 3 * H, H, st));
     TEL_TRY(launch_quantize_weight(dt, w->w_o, (int8_t*)(P + L.w_o), (float*)(P + L.sw_o),
@@ -624,11 +653,15 @@ int tel_encoder_calibrate(const tel_encoder_desc* d, const void* packed, const v
   const char* ws = (const char*)workspace;
   const int dt = d->dtype;
   hipStream_t st = as_stream(stream);
-  // inputs of the QKV, O, FFN1 and FFN2 GEMMs: x, ctx, h1 and the GELU output
+  // inputs of the QKV, O, FFN1 and FFN2 GEMMs: x, ctx, h1 and the GELU output; then the
+  // Q, K and V parts of the projection (head-split: three contiguous [heads][T][d] blocks)
+  const size_t es = dtype_size(dt);
   TEL_TRY(launch_absmax(dt, x, T * H, amax + 0, st));
   TEL_TRY(launch_absmax(dt, ws + W.ctx, T * H, amax + 1, st));
   TEL_TRY(launch_absmax(dt, ws + W.h1, T * H, amax + 2, st));
   TEL_TRY(launch_absmax(dt, ws + W.f, T * F, amax + 3, st));
+  for (int i = 0; i < 3; ++i)
+    TEL_TRY(launch_absmax(dt, ws + W.qkv + i * T * H * es, T * H, amax + 4 + i, st));
   return TEL_OK;
 }
 
@@ -920,7 +953,7 @@ int tel_gemm_i8(int epilogue, const int8_t* A, const int8_t* W, const float* dq,
                 int M, int N, int K, int heads, void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return TEL_EINVAL;
   if (epilogue < TEL_EPI_BIAS || epilogue > TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
-  if (out_int8 && epilogue != TEL_EPI_BIAS_GELU) return TEL_EINVAL;
+  if (out_int8 && epilogue != TEL_EPI_BIAS_GELU && epilogue != TEL_EPI_QKV_SPLIT) return TEL_EINVAL;
   if (M == 0) return TEL_OK;
   if (!A || !W || !dq || !bias || !C || (out_int8 && !qinv)) return TEL_EINVAL;
   if (epilogue == TEL_EPI_BIAS_RESID && !resid) return TEL_EINVAL;
@@ -1070,6 +1103,21 @@ int tel_window_partition_layernorm(const void* x, void* y, const float* gamma, c
   d.shift = shift;
   return status_of(launch_layernorm_gather(dtype, x, y, gamma, beta, batch * height * width,
                                            channels, eps, swin_geom(&d), as_stream(stream)));
+}
+
+int tel_attention_int8(const int8_t* qkv_codes, void* out, int out_codes, const float* scales,
+                       const int32_t* cu_seqlens, int batch, int total_tokens, int max_len,
+                       int heads, int head_dim, void* stream) {
+  if (batch <= 0 || total_tokens < 0 || max_len < 0 || heads <= 0 || head_dim <= 0)
+    return TEL_EINVAL;
+  if (!attention_int8_supported(head_dim)) return TEL_EUNSUPPORTED;
+  if (total_tokens == 0) return TEL_OK;
+  if (max_len == 0) return TEL_EINVAL;
+  if (!qkv_codes || !out || !scales || !cu_seqlens) return TEL_EINVAL;
+  if (!aligned16(qkv_codes) || !aligned16(out) || ((uintptr_t)scales & 3u)) return TEL_EINVAL;
+  return status_of(launch_attention_int8(qkv_codes, out, out_codes ? 1 : 0, cu_seqlens, batch,
+                                         total_tokens, max_len, heads, head_dim, scales,
+                                         as_stream(stream)));
 }
 
 int tel_patch_merging(const void* x, void* y, const float* gamma, const float* beta,

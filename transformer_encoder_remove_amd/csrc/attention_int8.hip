@@ -1,0 +1,230 @@
+// Variable-length multi-head attention with both products on int8 codes (the Swin talk
+// "大規模なビジュアル モデル…", section 3, INT8 paragraph: every matrix multiplication in
+// int8, INT8 outputs where no value is needed). Steps per (sequence b, head h, query i),
+// keys of sequence b only:
+//   S = q . k over int8 codes, exact int32 (v_mfma_i32_16x16x64_i8);
+//   t = float32(S) * a2, a2 = s_q s_k / sqrt(d) * log2 e (base-2 scores);
+//   m = max over the sequence's keys of t (a first pass over the keys);
+//   p = 2^(t - m) in (0, 1]; P codes r = rne(127 p) in [0, 127];
+//   ctx = s_v * (sum_j r v_j) / (sum_j r), both sums exact int32.
+// The exact maximum comes first so that no code depends on the order the key blocks are
+// visited in. Output: the context as the storage type (fp16), or directly as the int8
+// codes of that fp16 value at the O projection's input scale.
+//
+// Input: Q, K, V codes head-split as [3][heads][T][D] int8 (the int8 QKV epilogue's layout).
+// Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid = (ceil(max_len / 64),
+// heads, batch). Per 64-key block, K [64][D] and V^T [D][64] are staged in LDS. Each
+// wavefront computes S^T = K Q^T for its 16 queries, so a lane holds the scores of one query
+// for 16 keys (keys 16 j + 4 lg + i, j, i = 0..3). For P V the MFMA k index e of lane group lg
+// is mapped to key 16 (e / 4) + 4 lg + e % 4, the keys that lane already holds, so its 16 P
+// codes are its B fragment as they stand; V^T is staged with that key order, so the A
+// fragment is one 16-byte LDS read.
+#include <math.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace tel {
+
+constexpr int A8_QB = 64, A8_KB = 64;
+
+// LDS column of key `key` (0..63) in the permuted V^T rows: lane group g = (key % 16) / 4
+// reads columns 16 g .. 16 g + 15, holding keys 4 g + 16 jj + i at column 16 g + 4 jj + i.
+__device__ __forceinline__ int a8_vcol(int key) {
+  return ((key & 15) >> 2) * 16 + (key >> 4) * 4 + (key & 3);
+}
+
+template <int D, bool CODES>
+__global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict__ qkv,
+                                                        void* __restrict__ out,
+                                                        const int32_t* __restrict__ cu,
+                                                        int total_tokens, int heads,
+                                                        const float* __restrict__ scales) {
+  using MF = Mfma<int8_t>;
+  typedef MF::frag frag;                            // 16 int8 codes per lane
+  constexpr int NKS = (D + 63) / 64;                // 64-deep k steps of q . k
+  constexpr int NCB = D / 16;                       // 16-channel blocks of the output
+  constexpr int LDK = (D < 64 ? 64 : D) + 16;       // bytes per staged K row
+  constexpr int LDV = A8_KB + 16;                   // bytes per staged V^T row
+  static_assert(D % 16 == 0, "head_dim");
+  __shared__ __attribute__((aligned(16))) int8_t sK[A8_KB * LDK];
+  __shared__ __attribute__((aligned(16))) int8_t sVt[D * LDV];
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int start = cu[b], L = cu[b + 1] - start;
+  const int q0 = blockIdx.x * A8_QB;
+  if (q0 >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const size_t hs = (size_t)total_tokens * D;
+  const int8_t* Qh = qkv + (size_t)h * hs + (size_t)start * D;
+  const int8_t* Kh = qkv + (size_t)(heads + h) * hs + (size_t)start * D;
+  const int8_t* Vh = qkv + (size_t)(2 * heads + h) * hs + (size_t)start * D;
+  const float a2 = scales[0], s_v = scales[1];
+
+  const int qi = q0 + wave * 16 + lr;
+  const int qc = min(qi, L - 1);
+  frag qf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int d0 = s * 64 + lg * 16;
+    qf[s] = d0 < D ? *reinterpret_cast<const frag*>(Qh + (size_t)qc * D + d0) : frag{};
+  }
+  // K (and V) of a 64-key block: 16-byte vectors, thread tid owns vectors tid + 256 p;
+  // rows past the sequence end are clamped to its last key (their scores are masked)
+  constexpr int VPR = D / 16, NVEC = A8_KB * VPR, PER = (NVEC + 255) / 256;
+  auto stage_k = [&](int kb0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPR, c = idx - r * VPR;
+        *reinterpret_cast<u32x4*>(&sK[r * LDK + c * 16]) =
+            *reinterpret_cast<const u32x4*>(Kh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
+      }
+    }
+    if constexpr (D < 64) {   // zero the k padding of the rows once per block
+      for (int r = tid; r < A8_KB; r += 256)
+#pragma unroll
+        for (int c = D; c < 64; c += 16)
+          *reinterpret_cast<u32x4*>(&sK[r * LDK + c]) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_v = [&](int kb0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p;
+      if (NVEC % 256 == 0 || idx < NVEC) {
+        const int r = idx / VPR, c = idx - r * VPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Vh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
+        int8_t e[16];
+        __builtin_memcpy(e, &v, 16);
+        const int col = a8_vcol(r);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sVt[(c * 16 + k) * LDV + col] = e[k];
+      }
+    }
+  };
+  // scores of the staged block in base 2, -inf for keys past the end
+  auto scores = [&](int kb0, float (&t)[4][4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      MF::acc s = MF::acc{0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const frag kf = *reinterpret_cast<const frag*>(&sK[(j * 16 + lr) * LDK + k * 64 + lg * 16]);
+        s = MF::mma(kf, qf[k], s);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb0 + j * 16 + lg * 4 + i;
+        t[j][i] = key < L ? (float)s[i] * a2 : -INFINITY;
+      }
+    }
+  };
+
+  // pass 1: the exact row maximum over all keys of the sequence
+  float m = -INFINITY;
+  for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
+    __syncthreads();
+    stage_k(kb0);
+    __syncthreads();
+    float t[4][4];
+    scores(kb0, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, t[j][i]);
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+
+  // pass 2: P codes and P V, exact int32
+  MF::acc o[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) o[c] = MF::acc{0, 0, 0, 0};
+  int lsum = 0;
+  for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
+    __syncthreads();
+    stage_k(kb0);
+    stage_v(kb0);
+    __syncthreads();
+    float t[4][4];
+    scores(kb0, t);
+    int8_t r[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(t[j][i] - m);                    // 0 for masked keys
+        const int code = (int)fminf(__builtin_rintf(p * 127.0f), 127.0f);
+        r[4 * j + i] = (int8_t)code;
+        lsum += code;
+      }
+    frag pf;
+    __builtin_memcpy(&pf, r, 16);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const frag vf = *reinterpret_cast<const frag*>(&sVt[(c * 16 + lr) * LDV + lg * 16]);
+      o[c] = MF::mma(vf, pf, o[c]);
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+
+  if (qi < L) {
+    const size_t base = (size_t)(start + qi) * (heads * D) + h * D;
+    const float inv_l = s_v / (float)lsum;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      // O^T block c: lane holds channels c * 16 + 4 lg + i of query qi
+      if constexpr (CODES) {
+        const float inv = scales[2];
+        int8_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (float)(f16)((float)o[c][i] * inv_l);
+          q[i] = (int8_t)fminf(fmaxf(__builtin_rintf(v * inv), -127.f), 127.f);
+        }
+        uint32_t packed;
+        __builtin_memcpy(&packed, q, 4);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(out) + base + c * 16 + 4 * lg) = packed;
+      } else {
+        Vec4<f16> w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.v[i] = (f16)((float)o[c][i] * inv_l);
+        *reinterpret_cast<Vec4<f16>*>(reinterpret_cast<f16*>(out) + base + c * 16 + 4 * lg) = w;
+      }
+    }
+  }
+}
+
+bool attention_int8_supported(int head_dim) {
+  return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
+}
+
+template <int D>
+static void run_attn8(const int8_t* qkv, void* out, bool codes, const int32_t* cu, int batch,
+                      int total, int max_len, int heads, const float* scales, hipStream_t st) {
+  const dim3 grid((max_len + A8_QB - 1) / A8_QB, heads, batch);
+  if (codes)
+    attn_int8_kernel<D, true><<<grid, 256, 0, st>>>(qkv, out, cu, total, heads, scales);
+  else
+    attn_int8_kernel<D, false><<<grid, 256, 0, st>>>(qkv, out, cu, total, heads, scales);
+}
+
+hipError_t launch_attention_int8(const int8_t* qkv, void* out, int out_codes, const int32_t* cu,
+                                 int batch, int total, int max_len, int heads, int head_dim,
+                                 const float* scales, hipStream_t stream) {
+  if (total == 0 || max_len == 0) return hipSuccess;
+  switch (head_dim) {
+    case 16: run_attn8<16>(qkv, out, out_codes, cu, batch, total, max_len, heads, scales, stream); break;
+    case 32: run_attn8<32>(qkv, out, out_codes, cu, batch, total, max_len, heads, scales, stream); break;
+    case 64: run_attn8<64>(qkv, out, out_codes, cu, batch, total, max_len, heads, scales, stream); break;
+    case 128: run_attn8<128>(qkv, out, out_codes, cu, batch, total, max_len, heads, scales, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tel

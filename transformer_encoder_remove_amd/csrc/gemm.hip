@@ -109,7 +109,8 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
       idx = (size_t)m * e.N + n;
     }
     if constexpr (std::is_same<TO, int8_t>::value) {
-      const float inv = *e.qinv;
+      // head-split int8 output (int8 attention): Q, K and V each at its own scale
+      const float inv = EPI == EPI_QKV_SPLIT ? e.qinv[n / (e.N / 3)] : *e.qinv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) out.v[i] = quantize_code(v[i], inv);
     } else {
@@ -169,7 +170,7 @@ __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int
     }
     Vec8<TO> out;
     if constexpr (std::is_same<TO, int8_t>::value) {
-      const float inv = *e.qinv;
+      const float inv = EPI == EPI_QKV_SPLIT ? e.qinv[n / (e.N / 3)] : *e.qinv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) out.v[i] = quantize_code(v[i], inv);
     } else {
@@ -1267,7 +1268,10 @@ static hipError_t run_epi(int cfg, const GemmArgs& a, hipStream_t stream) {
 static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
   typedef int8_t T;
   switch (a.epi) {
-    case EPI_QKV_SPLIT: launch_cfg<T, EPI_QKV_SPLIT, f16, f16>(cfg, a, stream); break;
+    case EPI_QKV_SPLIT:   // int8 codes of Q, K, V (int8 attention), or fp16 values
+      if (a.out_i8) launch_cfg<T, EPI_QKV_SPLIT, f16, int8_t>(cfg, a, stream);
+      else launch_cfg<T, EPI_QKV_SPLIT, f16, f16>(cfg, a, stream);
+      break;
     case EPI_BIAS_RESID: launch_cfg<T, EPI_BIAS_RESID, f16, f16>(cfg, a, stream); break;
     case EPI_BIAS: launch_cfg<T, EPI_BIAS, f16, f16>(cfg, a, stream); break;
     case EPI_BIAS_GELU:

@@ -59,8 +59,9 @@ struct GemmArgs {
   int resid_f32 = 0;    // EPI_BIAS_RESID, bf16 operands only: residual is float32
   int out_f32 = 0;      // EPI_BIAS_RESID, bf16 operands only: output is float32
   const float* dq = nullptr;    // int8 operands: per-column dequantisation scale [N]
-  const float* qinv = nullptr;  // int8 output (EPI_BIAS_GELU): device scalar 1 / scale
-  int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU: write int8 codes
+  const float* qinv = nullptr;  // int8 output: device scalar 1 / scale (EPI_BIAS_GELU), or
+                                // three of them, for Q, K and V (EPI_QKV_SPLIT)
+  int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU / EPI_QKV_SPLIT: int8 codes
   SwinGeom geom{};              // EPI_SWIN_SCATTER
   int splits = 1;               // pipelined kernel only: K split over this many workgroups
   int part16 = 0;               // EPI_PARTIAL, fp16 operands: partial sums stored as fp16
@@ -98,6 +99,14 @@ bool attention_supported(int dtype, int head_dim);
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
                             int8_t* ctxq = nullptr, const float* qinv = nullptr);
+
+// attention_int8.hip: attention on int8 Q, K, V codes ([3][heads][T][D]); scales (device):
+// [0] = s_q s_k / sqrt(D) * log2 e, [1] = s_v, [2] = 1 / (input scale of the O projection);
+// out = fp16 context (out_codes 0) or its int8 codes at scales[2] (out_codes 1).
+bool attention_int8_supported(int head_dim);
+hipError_t launch_attention_int8(const int8_t* qkv, void* out, int out_codes, const int32_t* cu,
+                                 int batch, int total, int max_len, int heads, int head_dim,
+                                 const float* scales, hipStream_t stream);
 
 // layernorm.hip: y = LN(x) in type dtype_out from x in type dtype_in; when y_f32 is not
 // null the same result is also written there in float32.

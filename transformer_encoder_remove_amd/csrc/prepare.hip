@@ -23,19 +23,20 @@ hipError_t launch_widen_f32(int dtype, const void* src, float* dst, int n, hipSt
   return hipGetLastError();
 }
 
-struct F32x8 { float v[8]; };
+constexpr int STORE_F32_MAX = 16;
+struct F32xN { float v[STORE_F32_MAX]; };
 
-__global__ void store_f32x8_kernel(float* __restrict__ dst, F32x8 vals, int n) {
+__global__ void store_f32_kernel(float* __restrict__ dst, F32xN vals, int n) {
   if (threadIdx.x < n) dst[threadIdx.x] = vals.v[threadIdx.x];
 }
 
 // Small host-known constants into device memory through kernel arguments (no host buffer
 // has to outlive the call).
 hipError_t launch_store_f32(float* dst, const float* vals, int n, hipStream_t stream) {
-  if (n <= 0 || n > 8) return hipErrorInvalidValue;
-  F32x8 a{};
+  if (n <= 0 || n > STORE_F32_MAX) return hipErrorInvalidValue;
+  F32xN a{};
   for (int i = 0; i < n; ++i) a.v[i] = vals[i];
-  store_f32x8_kernel<<<1, 64, 0, stream>>>(dst, a, n);
+  store_f32_kernel<<<1, 64, 0, stream>>>(dst, a, n);
   return hipGetLastError();
 }
 
