@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--dtype", default=None, help="override storage type (f16, bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graphs", action="store_true",
+                    help="run the timed steps through the forward's HIP-graph cache")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="split the batch into this many parts balanced by valid tokens, each "
+                         "part's forward on its own stream (default priority), joined per step")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-hbm", action="store_true",
                     help="skip the memory-bound kernels' flushed-cache timings")
@@ -118,7 +123,16 @@ def main():
     y = torch.empty_like(x)
     lens_d = torch.from_numpy(lens).cuda()
     cu_d = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
-    if int8:
+    if int8 and cfg.get("dynamic"):
+        # dynamic activation scales: no calibration, the weights quantised once
+        desc = tel.make_encoder_desc(H, nh, F, tdt, ti.LN_EPS, int8_gemm=1, dynamic_scales=True)
+        psize = tel.tel_encoder_packed_size(desc)
+        packed = []
+        for i in range(NL):
+            p = tel.alloc_bytes(psize)
+            tel.tel_encoder_prepare(desc, dws[i], p)
+            packed.append(p)
+    elif int8:
         # post-training calibration on this batch (the float stack, layer by layer), then
         # the int8 layers prepared with those static scales
         from_pad = torch.empty((T, H), dtype=tdt, device="cuda")
@@ -146,9 +160,41 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    if args.graphs:
+        tel.tel_graph_cache(1)
 
     def step():
         tel.tel_encoder_forward(desc, packed, x, y, lens_d, T, max_len, ws, stream=stream)
+
+    if args.streams > 1:
+        # the batch cut into contiguous runs of sequences with about equal valid tokens, each
+        # run's whole forward on its own stream; the main stream waits for all of them
+        cum = np.cumsum(lens)
+        cuts = [0] + [int(np.searchsorted(cum, T * k / args.streams)) + 1
+                      for k in range(1, args.streams)] + [B]
+        parts = []
+        for k in range(args.streams):
+            b0, b1 = cuts[k], cuts[k + 1]
+            if b1 <= b0:
+                continue
+            pl = lens[b0:b1]
+            parts.append(dict(x=x[b0:b1], y=y[b0:b1], lens=lens_d[b0:b1], T=int(pl.sum()),
+                              max_len=int(pl.max()), st=torch.cuda.Stream(),
+                              ws=tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(
+                                  desc, b1 - b0, S))))
+        log(f"[bench] {len(parts)} streams: valid tokens per part "
+            f"{[p['T'] for p in parts]}")
+
+        def step():
+            start = torch.cuda.Event()
+            start.record(stream)
+            for p in parts:
+                p["st"].wait_event(start)
+                tel.tel_encoder_forward(desc, packed, p["x"], p["y"], p["lens"], p["T"],
+                                        p["max_len"], p["ws"], stream=p["st"])
+                done = torch.cuda.Event()
+                done.record(p["st"])
+                stream.wait_event(done)
 
     for _ in range(args.warmup):
         step()
@@ -603,12 +649,16 @@ def emit(args, cfg, value, ms_per_step, T, max_len, roofline, per_kernel, cpu, l
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
         "config": {"workload": f"{args.workload}: {NL}-layer post-LN encoder"
                                f"{' with int8 GEMMs' if int8 else ''}"
+                               f"{' and int8 attention' if cfg.get('int8') == 2 else ''}"
+                               f"{' (dynamic activation scales)' if cfg.get('dynamic') else ''}"
                                f"{' with 2:4-sparse projection weights' if cfg.get('sparse') else ''}"
                                f", offsets + padding removal "
                                f"+ layers + rebuild", "batch": cfg["batch"],
                    "max_seq": cfg["max_seq"], "valid_tokens": T, "max_len": max_len,
                    "hidden": cfg["hidden"], "heads": cfg["heads"], "ffn": cfg["ffn"],
-                   "layers": NL, "parallelism": "single GPU"},
+                   "layers": NL, "parallelism": "single GPU",
+                   **({"graph_replay": True} if args.graphs else {}),
+                   **({"streams": args.streams} if args.streams > 1 else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_ms": step_ms,
@@ -843,12 +893,14 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     elapsed, done = 0.0, 0
     while elapsed < seconds:
         w = weights[done % len(weights)]
-        amax = q8.calibrate(xp, cu, w, cfg["heads"], ti.LN_EPS) if int8 else None
+        dyn = bool(cfg.get("dynamic"))
+        amax = q8.calibrate(xp, cu, w, cfg["heads"], ti.LN_EPS) if int8 and not dyn else None
         aa = (q8.calibrate_attention(xp, cu, w, cfg["heads"], ti.LN_EPS)
               if cfg.get("int8") == 2 else None)
         t0 = time.perf_counter()
         if int8:
-            xp = q8.encoder_layer_int8(xp, cu, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa)
+            xp = q8.encoder_layer_int8(xp, cu, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa,
+                                       dynamic=dyn)
         else:
             xp = enc.encoder_layer(xp, cu, w, cfg["heads"], ti.LN_EPS)
         elapsed += time.perf_counter() - t0
@@ -870,12 +922,14 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     x1 = enc.remove_padding(x_pad[:nb].astype(np.float64), sub_lens)
     w = weights[0]
     with threadpool_limits(limits=1):
-        amax = q8.calibrate(x1, cu1, w, cfg["heads"], ti.LN_EPS) if int8 else None
+        dyn = bool(cfg.get("dynamic"))
+        amax = q8.calibrate(x1, cu1, w, cfg["heads"], ti.LN_EPS) if int8 and not dyn else None
         aa = (q8.calibrate_attention(x1, cu1, w, cfg["heads"], ti.LN_EPS)
               if cfg.get("int8") == 2 else None)
         t0 = time.perf_counter()
         if int8:
-            q8.encoder_layer_int8(x1, cu1, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa)
+            q8.encoder_layer_int8(x1, cu1, w, cfg["heads"], ti.LN_EPS, amax, attn_amax=aa,
+                                  dynamic=dyn)
         else:
             enc.encoder_layer(x1, cu1, w, cfg["heads"], ti.LN_EPS)
         t1 = time.perf_counter() - t0

@@ -131,6 +131,13 @@ typedef struct {
   int sparse_2of4; /* 1: the four projection matrices are pruned 2:4 when prepared and run
                       on the sparse MFMA (dtype TEL_F16 or TEL_BF16, not int8_gemm; H and F
                       multiples of 128); see the 2:4 section below                   */
+  int dynamic_scales; /* 1 (int8_gemm == 1 only): dynamic activation scales ("揭秘Transformer
+                         模型：速度优化与量化技术", section 3.3, dynamic quantisation): each int8
+                         GEMM's activation scale is max-abs / 127 of that GEMM's fp16 input over
+                         the batch being run, reduced on the device; act_amax is ignored.
+                         After tel_encoder_layer_forward the first 16 bytes of its workspace
+                         hold the four max-abs values it used (float32: the QKV, O, FFN1 and
+                         FFN2 inputs); the layer never splits a GEMM over k              */
 } tel_encoder_desc;
 
 /* Canonical weights of one layer, storage type desc->dtype, device pointers:

@@ -139,7 +139,8 @@ def attention_int8(qkv_storage: np.ndarray, cu_seqlens, heads: int, attn_amax: l
 
 
 def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: float,
-                       amax: list, storage=np.float16, attn_amax=None):
+                       amax: list, storage=np.float16, attn_amax=None, dynamic=False,
+                       dyn_amax=None, dyn_trace=None):
     """Post-LN encoder layer with the four projection GEMMs in int8.
 
     ``w`` holds the floating-point weights; they are quantised here per
@@ -148,17 +149,31 @@ def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: floa
     QKV, the attention output, the two pre-LayerNorm sums, h1 and the GELU output.
     With ``attn_amax`` (the Q, K, V max-abs of calibrate_attention) attention runs on
     int8 codes too (attention_int8); the QKV projection's fp16 value is then only the
-    value its codes are taken from. The returned output is not rounded.
+    value its codes are taken from.
+    With ``dynamic`` the activation scales are not static ([P5] section 3.3, dynamic
+    quantisation: the quantisation parameters follow the data at inference time): each
+    GEMM's scale comes from the max-abs of that GEMM's stored input over the batch being
+    run (amax is then unused). ``dyn_amax`` optionally gives those four maxima instead of
+    computing them (a caller that must take the same scale decision as another
+    implementation feeds that implementation's maxima); ``dyn_trace`` (a list) receives the
+    maxima this run found, in GEMM order. The returned output is not rounded.
     """
-    scales = [act_scale(a) for a in amax]
+    scales = None if dynamic else [act_scale(a) for a in amax]
 
     def st(a):
         return np.asarray(a, np.float64).astype(storage).astype(np.float64)
 
     def qlinear(a, wname, bname, g):
         wq, sw = quantize_weight(w[wname])
-        s, inv = scales[g]
-        q = quantize_act(np.asarray(a, np.float64).astype(storage), inv)
+        a_st = np.asarray(a, np.float64).astype(storage)
+        if dynamic:
+            a_run = float(np.abs(a_st.astype(np.float64)).max())
+            s, inv = act_scale(dyn_amax[g] if dyn_amax is not None else a_run)
+        else:
+            s, inv = scales[g]
+        if dynamic and dyn_trace is not None:
+            dyn_trace.append(a_run)
+        q = quantize_act(a_st, inv)
         return dequantize(int8_matmul(q, wq), s, sw, w[bname])
 
     x = np.asarray(x, np.float64)
@@ -173,13 +188,16 @@ def encoder_layer_int8(x: np.ndarray, cu_seqlens, w: dict, heads: int, eps: floa
 
 
 def encoder_stack_int8(x, cu_seqlens, layers: list, amaxes: list, heads: int, eps: float,
-                       storage=np.float16, attn_amaxes=None):
+                       storage=np.float16, attn_amaxes=None, dynamic=False):
     """Layers in order, each with its own calibration max-abs list (and, for int8
     attention, its own Q/K/V max-abs list); the output of every layer is rounded to
     ``storage`` as the stored activation."""
     y = np.asarray(x, np.float64)
+    if amaxes is None:
+        amaxes = [None] * len(layers)
     for i, (w, a) in enumerate(zip(layers, amaxes)):
         aa = attn_amaxes[i] if attn_amaxes is not None else None
-        y = encoder_layer_int8(y, cu_seqlens, w, heads, eps, a, storage, attn_amax=aa)
+        y = encoder_layer_int8(y, cu_seqlens, w, heads, eps, a, storage, attn_amax=aa,
+                               dynamic=dynamic)
         y = y.astype(storage).astype(np.float64)
     return y

@@ -40,6 +40,10 @@ ENCODER_CONFIGS = {
                             heads=16, ffn=4096, layers=24, dtype="f16", seed=3),
     "bert_base_int8": dict(batch=32, max_seq=128, len_range=(32, 128), hidden=768, heads=12,
                            ffn=3072, layers=12, dtype="f16", seed=4, int8=True),
+    # the same int8 batch with dynamic activation scales (from each batch's own max-abs)
+    "bert_base_int8_dyn": dict(batch=32, max_seq=128, len_range=(32, 128), hidden=768,
+                               heads=12, ffn=3072, layers=12, dtype="f16", seed=4, int8=True,
+                               dynamic=True),
     # the same int8 batch with attention's two products on int8 codes as well
     "bert_base_int8_attn": dict(batch=32, max_seq=128, len_range=(32, 128), hidden=768,
                                 heads=12, ffn=3072, layers=12, dtype="f16", seed=4, int8=2),

@@ -273,3 +273,66 @@ def patch_merging_direct(x, w, Hs, Ws, eps):
                     v.extend(x[b, y * Ws + xx].tolist())
                 out[b, i * (Ws // 2) + j] = _matvec(W, [0.0] * len(W), _ln(v, g, be, eps))
     return out
+
+
+def encoder_layer_int8_dynamic_padded(x_pad, lens, w, heads, eps):
+    """Int8-GEMM layer with dynamic activation scales, stage by stage over every valid
+    position of the padded batch: each GEMM's input is stored as fp16, its scale is the
+    max-abs of those stored values over all valid positions (divided by 127), then codes,
+    integer sums and the dequantised result as in encoder_layer_int8_padded."""
+    f32 = np.float32
+    h = lambda v: float(np.float16(v))
+    x_pad = np.asarray(x_pad, np.float64)
+    B, S, H = x_pad.shape
+    d = H // heads
+    W = {k: np.asarray(v) for k, v in w.items()}
+    L64 = lambda n: np.asarray(W[n], np.float64).tolist()
+    pos = [(b, i) for b in range(B) for i in range(int(lens[b]))]
+
+    def qweights(Wm):
+        Wm = np.asarray(Wm, np.float32)
+        codes, scales = [], []
+        for row in Wm:
+            mx = max(abs(f32(v)) for v in row)
+            s = f32(mx / f32(127.0)) if mx > 0 else f32(1.0)
+            scales.append(s)
+            codes.append([_q8(f32(f32(v) / s)) for v in row])
+        return codes, scales
+
+    def qlin_all(rows, wn, bn):
+        """rows: fp16 values of every valid position; the scale from their max-abs."""
+        mx = max(abs(v) for r in rows for v in r)
+        s, inv = (f32(f32(mx) / f32(127.0)), f32(f32(127.0) / f32(mx))) if mx > 0 else \
+            (f32(1.0), f32(1.0))
+        codes, scales = qweights(W[wn])
+        bias = np.asarray(W[bn], np.float64)
+        out = []
+        for r in rows:
+            qa = [_q8(f32(f32(v) * inv)) for v in r]
+            out.append([sum(qa[k] * codes[n][k] for k in range(len(qa))) * float(f32(s * scales[n]))
+                        + float(bias[n]) for n in range(len(codes))])
+        return out
+
+    xs = [[h(v) for v in x_pad[b, i]] for b, i in pos]
+    qkv = [[h(v) for v in r] for r in qlin_all(xs, "w_qkv", "b_qkv")]
+    row_of = {p: n for n, p in enumerate(pos)}
+    ctx = []
+    for b, i in pos:
+        c = [0.0] * H
+        keys = [row_of[(b, j)] for j in range(int(lens[b]))]
+        for hh in range(heads):
+            q = qkv[row_of[(b, i)]][hh * d:(hh + 1) * d]
+            sc = [_dot(q, qkv[k][H + hh * d:H + (hh + 1) * d]) / math.sqrt(d) for k in keys]
+            p = _softmax_masked(sc, [True] * len(keys))
+            for cc in range(d):
+                c[hh * d + cc] = h(sum(p[j] * qkv[k][2 * H + hh * d + cc] for j, k in enumerate(keys)))
+        ctx.append(c)
+    a = qlin_all(ctx, "w_o", "b_o")
+    h1 = [[h(v) for v in _ln([h(a[n][c] + x_pad[b, i, c]) for c in range(H)], L64("ln1_g"),
+                             L64("ln1_b"), eps)] for n, (b, i) in enumerate(pos)]
+    f = [[h(_gelu(z)) for z in r] for r in qlin_all(h1, "w_1", "b_1")]
+    o = qlin_all(f, "w_2", "b_2")
+    out = np.zeros((B, S, H))
+    for n, (b, i) in enumerate(pos):
+        out[b, i] = _ln([h(o[n][c] + h1[n][c]) for c in range(H)], L64("ln2_g"), L64("ln2_b"), eps)
+    return out

@@ -322,3 +322,16 @@ def test_binding_refuses_non_int32_lengths_and_wrong_activation_type():
         tel.tel_encoder_layer_forward(desc, None, torch.zeros((3, 64), dtype=torch.float16),
                                       torch.zeros((3, 64), dtype=torch.float16),
                                       torch.tensor([0, 3], dtype=torch.int64), 3, 3, None)
+
+
+def test_dynamic_scales_descriptor_validation():
+    import torch
+    ok = tel.make_encoder_desc(768, 12, 3072, torch.float16, 1e-5, int8_gemm=1, dynamic_scales=True)
+    assert tel.tel_encoder_packed_size(ok) > 0
+    assert tel.tel_encoder_workspace_size(ok, 2557) > 0
+    for bad in (tel.make_encoder_desc(768, 12, 3072, torch.float16, 1e-5, dynamic_scales=True),
+                tel.make_encoder_desc(768, 12, 3072, torch.float16, 1e-5, int8_gemm=2,
+                                      dynamic_scales=True)):
+        assert tel.tel_encoder_packed_size(bad) == 0
+        assert tel.lib.tel_encoder_prepare(ctypes.byref(bad), None, None, 0, None) == \
+            tel.TEL_EUNSUPPORTED

@@ -259,3 +259,38 @@ def test_calibrate_attention_matches_brute_force_projection():
             v = abs(sum(Wq[n, k] * row[k] for k in range(H)) + bq[n])
             want[n // H] = max(want[n // H], v)
     assert np.abs(np.array(got) - np.array(want)).max() <= 1e-12
+
+
+# ------------------------------------------------------------------ dynamic activation scales
+def test_dynamic_int8_layer_matches_brute_force():
+    cfg = ti.custom_encoder_config(3, 6, [6, 2, 5], 32, 2, 64, dtype="f16", seed=17)
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    cu, _ = enc.offsets(lens, 6)
+    xp = enc.remove_padding(x.astype(np.float64), lens)
+    y = q8.encoder_layer_int8(xp, cu, w, 2, EPS, None, dynamic=True)
+    ref = brute.encoder_layer_int8_dynamic_padded(x, lens, w, 2, EPS)
+    assert np.abs(enc.remove_padding(ref, lens) - y).max() <= 1e-9
+
+
+def test_dynamic_scales_follow_the_batch():
+    """The dynamic layer depends on the batch it runs: the same sequence run alone or beside
+    a sequence of much larger activations gets other codes (its scales grow), while a static
+    layer gives that sequence the same output either way; and the dynamic layer on the
+    loud batch matches the stage-wise brute force."""
+    cfg = ti.custom_encoder_config(2, 6, [6, 6], 32, 2, 64, dtype="f16", seed=18)
+    lens, x = ti.encoder_input(cfg)
+    w = ti.encoder_layer_weights(cfg, 0, variant=True)
+    x = x.astype(np.float64)
+    x[1] *= 8.0                                                   # a loud second sequence
+    x = x.astype(np.float16).astype(np.float64)
+    cu2, _ = enc.offsets(lens, 6)
+    both = q8.encoder_layer_int8(enc.remove_padding(x, lens), cu2, w, 2, EPS, None, dynamic=True)
+    alone = q8.encoder_layer_int8(x[0], np.array([0, 6]), w, 2, EPS, None, dynamic=True)
+    assert np.abs(both[:6] - alone).max() > 1e-4
+    a_static = [8.0, 1.0, 4.0, 0.5]
+    s_both = q8.encoder_layer_int8(enc.remove_padding(x, lens), cu2, w, 2, EPS, a_static)
+    s_alone = q8.encoder_layer_int8(x[0], np.array([0, 6]), w, 2, EPS, a_static)
+    assert np.array_equal(s_both[:6], s_alone)
+    dyn_ref = brute.encoder_layer_int8_dynamic_padded(x, lens, w, 2, EPS)
+    assert np.abs(enc.remove_padding(dyn_ref, lens) - both).max() <= 1e-9

@@ -66,7 +66,7 @@ F = ctypes.c_float
 
 class tel_encoder_desc(ctypes.Structure):
     _fields_ = [("hidden", I), ("heads", I), ("ffn", I), ("dtype", I), ("int8_gemm", I),
-                ("ln_eps", F), ("sparse_2of4", I)]
+                ("ln_eps", F), ("sparse_2of4", I), ("dynamic_scales", I)]
 
 
 class tel_swin_desc(ctypes.Structure):
@@ -237,10 +237,11 @@ def tel_rebuild_padding_mask(x_packed, x_pad, mask, padding_offset, total_tokens
 
 
 def make_encoder_desc(hidden, heads, ffn, dtype: torch.dtype, eps=1e-5, int8_gemm=False,
-                      sparse_2of4=False):
-    """int8_gemm: False/0, True/1 (int8 GEMMs) or 2 (int8 GEMMs and int8 attention)."""
+                      sparse_2of4=False, dynamic_scales=False):
+    """int8_gemm: False/0, True/1 (int8 GEMMs) or 2 (int8 GEMMs and int8 attention);
+    dynamic_scales: int8 activation scales from each batch's own max-abs (int8_gemm 1)."""
     return tel_encoder_desc(hidden, heads, ffn, dtype_code(dtype), int(int8_gemm), eps,
-                            int(sparse_2of4))
+                            int(sparse_2of4), int(dynamic_scales))
 
 
 def tel_encoder_packed_size(desc) -> int:

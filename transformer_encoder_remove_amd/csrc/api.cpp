@@ -63,6 +63,8 @@ int desc_supported(const tel_encoder_desc* d) {
   if (d->int8_gemm < 0 || d->int8_gemm > 2) return TEL_EINVAL;
   if (d->int8_gemm && (d->dtype != DT_F16 || d->hidden % 16 || d->ffn % 16)) return TEL_EUNSUPPORTED;
   if (d->int8_gemm == 2 && !attention_int8_supported(d->hidden / d->heads)) return TEL_EUNSUPPORTED;
+  if (d->dynamic_scales < 0 || d->dynamic_scales > 1) return TEL_EINVAL;
+  if (d->dynamic_scales && d->int8_gemm != 1) return TEL_EUNSUPPORTED;
   if (d->sparse_2of4 && (d->int8_gemm || (d->dtype != DT_F16 && d->dtype != DT_BF16) ||
                          d->hidden % 128 || d->ffn % 128))
     return TEL_EUNSUPPORTED;
@@ -125,6 +127,7 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
 struct LayerWs {
   size_t qkv, ctx, pre, part, h1, h1f, f, total;
   size_t xq, ctxq, h1q;   // int8 layer: codes of the inputs of the QKV, O and FFN1 GEMMs
+  size_t fq, dyn;         // dynamic scales: codes of the GELU output, the four max-abs
 };
 
 inline bool f32_stream(const tel_encoder_desc* d) { return d->dtype == DT_BF16; }
@@ -134,6 +137,7 @@ inline int gemm_dtype(const tel_encoder_desc* d) { return d->int8_gemm ? (int)DT
 // projection and FFN2 at every token count up to T (fewer tokens may mean more splits),
 // so a workspace sized for T also serves any smaller batch.
 size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
+  if (d->dynamic_scales) return 0;   // that layer never splits over k
   const int dt = gemm_dtype(d), H = d->hidden, F = d->ffn;
   auto need = [&](size_t t) {
     int cfg, p16;
@@ -152,12 +156,14 @@ size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
 // The workspace layout is computed on every layer call; remember the last answer per
 // thread so a stack of layers at one token count pays for the plan scan once.
 size_t partial_rows(const tel_encoder_desc* d, size_t T) {
-  struct Key { int dt, H, F; size_t T; size_t rows; };
-  thread_local Key last{-1, 0, 0, 0, 0};
+  struct Key { int dt, H, F, dyn; size_t T; size_t rows; };
+  thread_local Key last{-1, 0, 0, 0, 0, 0};
   const int dt = gemm_dtype(d);
-  if (last.dt == dt && last.H == d->hidden && last.F == d->ffn && last.T == T) return last.rows;
+  if (last.dt == dt && last.H == d->hidden && last.F == d->ffn && last.dyn == d->dynamic_scales &&
+      last.T == T)
+    return last.rows;
   const size_t rows = partial_rows_uncached(d, T);
-  last = Key{dt, d->hidden, d->ffn, T, rows};
+  last = Key{dt, d->hidden, d->ffn, d->dynamic_scales, T, rows};
   return rows;
 }
 
@@ -166,18 +172,23 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  // dynamic scales: the four max-abs values first (documented: bytes 0..15 of the workspace)
+  if (d->dynamic_scales) w.dyn = take(4 * 4);
   w.qkv = take(3 * T * H * es);
   w.ctx = take(T * H * es);
   w.pre = take(T * H * (f32_stream(d) ? 4 : es));
   w.part = take(partial_rows(d, T) * H * 4);
   w.h1 = take(T * H * es);
   w.h1f = f32_stream(d) ? take(T * H * 4) : 0;
-  w.f = take(T * F * (d->int8_gemm ? 1 : es));   // int8 layer: GELU output as codes
+  // int8 layer: GELU output as codes (static scales), or as fp16 values and then codes
+  // (dynamic scales: the scale needs the whole tensor's max-abs first)
+  w.f = take(T * F * (d->int8_gemm && !d->dynamic_scales ? 1 : es));
   if (d->int8_gemm) {
     w.xq = take(T * H);
     w.ctxq = take(T * H);
     w.h1q = take(T * H);
   }
+  if (d->dynamic_scales) w.fq = take(T * F);
   w.total = o;
   return w;
 }
@@ -212,6 +223,65 @@ struct Int8Link {
   const float* next_qinv = nullptr;
 };
 
+// Int8 layer with dynamic activation scales ("揭秘Transformer模型…", section 3.3: the
+// quantisation parameters follow the data at inference time): each GEMM input is stored as
+// fp16 by its producer, its max-abs over the batch is reduced on the device, the quantise
+// kernel takes 127 / max-abs as its inverse scale, and the GEMM epilogue forms the
+// dequantisation scale (max-abs / 127) * s_w[n] per column. The layer never splits over k.
+int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const void* x, void* y,
+                               const int32_t* cu, int batch, int T, int max_len, char* ws,
+                               hipStream_t st) {
+  const LayerLayout L = layer_layout(d);
+  const LayerWs W = layer_ws(d, (size_t)T);
+  const int H = d->hidden, F = d->ffn, nh = d->heads;
+  auto F32 = [&](size_t off) { return (const float*)(P + off); };
+  float* amax = (float*)(ws + W.dyn);
+  int8_t* xq = (int8_t*)(ws + W.xq);
+  int8_t* ctxq = (int8_t*)(ws + W.ctxq);
+  int8_t* h1q = (int8_t*)(ws + W.h1q);
+  int8_t* fq = (int8_t*)(ws + W.fq);
+  void* qkv = ws + W.qkv;
+  void* ctx = ws + W.ctx;
+  void* pre = ws + W.pre;
+  void* h1 = ws + W.h1;
+  void* f = ws + W.f;
+  const float zeros[4] = {0.f, 0.f, 0.f, 0.f};
+  TEL_TRY(launch_store_f32(amax, zeros, 4, st));   // a kernel, not a memset (graph capture)
+  auto codes = [&](const void* a, size_t n, int8_t* q, int g) -> hipError_t {
+    hipError_t e = launch_absmax(DT_F16, a, n, amax + g, st);
+    if (e != hipSuccess) return e;
+    return launch_quantize_act(DT_F16, a, q, n, nullptr, 0.f, st, amax + g);
+  };
+  TEL_TRY(codes(x, (size_t)T * H, xq, 0));
+  GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
+  g.dq = F32(L.sw_qkv);
+  g.dyn_amax = amax + 0;
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  // P split as in the static int8 layer: ctx's codes follow P's rounding closely
+  TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, nullptr,
+                           nullptr, true));
+  TEL_TRY(codes(ctx, (size_t)T * H, ctxq, 1));
+  g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
+  g.dq = F32(L.sw_o);
+  g.dyn_amax = amax + 1;
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, h1, nullptr, F32(L.ln1_g), F32(L.ln1_b), T, H,
+                           d->ln_eps, st));
+  TEL_TRY(codes(h1, (size_t)T * H, h1q, 2));
+  g = GemmArgs{EPI_BIAS_GELU, h1q, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
+  g.dq = F32(L.sw_1);
+  g.dyn_amax = amax + 2;
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(codes(f, (size_t)T * F, fq, 3));
+  g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
+  g.dq = F32(L.sw_2);
+  g.dyn_amax = amax + 3;
+  TEL_TRY(launch_gemm(DT_I8, g, st));
+  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                           d->ln_eps, st));
+  return TEL_OK;
+}
+
 // Int8 layer ([SW] section 3, INT8: quantise -> INT8 GEMM -> INT32 -> dequantise; bias,
 // residual and LayerNorm stay floating point; attention runs in fp16 on the dequantised
 // Q, K, V). Codes are produced where the value is made: the attention kernel for ctx, the
@@ -220,6 +290,8 @@ struct Int8Link {
 int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, void* y,
                        const int32_t* cu, int batch, int T, int max_len, char* ws,
                        hipStream_t st, const Int8Link& link = Int8Link{}) {
+  if (d->dynamic_scales)
+    return layer_forward_int8_dynamic(d, P, x, y, cu, batch, T, max_len, ws, st);
   const LayerLayout L = layer_layout(d);
   const LayerWs W = layer_ws(d, (size_t)T);
   const int H = d->hidden, F = d->ffn, nh = d->heads;
@@ -546,7 +618,16 @@ int tel_encoder_prepare(const tel_encoder_desc* d, const tel_encoder_weights* w,
   char* P = (char*)packed;
   hipStream_t st = as_stream(stream);
   const int dt = d->dtype;
-  if (d->int8_gemm) {
+  if (d->int8_gemm && d->dynamic_scales) {   // weights only: activation scales at run time
+    TEL_TRY(launch_quantize_weight(dt, w->w_qkv, (int8_t*)(P + L.w_qkv), (float*)(P + L.sw_qkv),
+                                   nullptr, 0.f, 3 * H, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_o, (int8_t*)(P + L.w_o), (float*)(P + L.sw_o), nullptr,
+                                   0.f, H, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_1, (int8_t*)(P + L.w_1), (float*)(P + L.sw_1), nullptr,
+                                   0.f, F, H, st));
+    TEL_TRY(launch_quantize_weight(dt, w->w_2, (int8_t*)(P + L.w_2), (float*)(P + L.sw_2), nullptr,
+                                   0.f, H, F, st));
+  } else if (d->int8_gemm) {
     float sa[4], inv[4];
     for (int i = 0; i < 4; ++i) {
       const float a = w->act_amax[i];
@@ -698,7 +779,7 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
   const size_t act_off = d->int8_gemm ? layer_layout(d).act : 0;
   for (int i = 0; i < n_layers; ++i) {
     int r;
-    if (d->int8_gemm && total_tokens > 0) {
+    if (d->int8_gemm && !d->dynamic_scales && total_tokens > 0) {
       // each LN2 writes the codes of its output at the next layer's input scale
       Int8Link link;
       link.xq_in = i > 0 ? qa : nullptr;

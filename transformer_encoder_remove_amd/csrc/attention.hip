@@ -306,10 +306,10 @@ bool attention_supported(int dtype, int head_dim) {
 template <typename T, int D>
 static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                            int max_len, int heads, int8_t* ctxq, const float* qinv,
-                           hipStream_t stream) {
+                           bool psplit, hipStream_t stream) {
   const dim3 grid((max_len + ATT_QB - 1) / ATT_QB, heads, batch);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  if (ctxq || !std::is_same<T, f16>::value)   // P split (see attn_block)
+  if (ctxq || psplit || !std::is_same<T, f16>::value)   // P split (see attn_block)
     attn_varlen_kernel<T, D, true><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total,
                                                              heads, scale_log2, ctxq, qinv);
   else
@@ -321,28 +321,28 @@ static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int ba
 template <typename T>
 static hipError_t run_attn_d(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                              int max_len, int heads, int d, int8_t* ctxq, const float* qinv,
-                             hipStream_t stream) {
+                             bool ps, hipStream_t stream) {
   switch (d) {
-    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
-    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
-    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
-    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, stream);
+    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
+    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
+    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
+    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
-                            int8_t* ctxq, const float* qinv) {
+                            int8_t* ctxq, const float* qinv, bool psplit) {
   if (total == 0 || max_len == 0) return hipSuccess;
   if (ctxq && !qinv) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_F16:
-      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
+      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
     case DT_BF16:
-      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
+      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
     case DT_F32:
-      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, stream);
+      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
     default: return hipErrorInvalidValue;
   }
 }

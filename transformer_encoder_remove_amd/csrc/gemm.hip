@@ -47,7 +47,14 @@ template <typename T, typename TR, typename TO> struct EpiArgs {
   const float* dq;     // int8 operands: per-column dequantisation scale [N]
   const float* qinv;   // int8 output: device scalar, 1 / activation scale of the consumer
   SwinGeom geom;       // EPI_SWIN_SCATTER: window order -> image order
+  const float* dyn_amax = nullptr;   // int8 operands, dynamic scale: dq = s_w, s_a from max-abs
 };
+
+// Activation scale of a dynamically scaled int8 GEMM: max-abs / 127 (1 for an all-zero input).
+__device__ __forceinline__ float dyn_act_scale(const float* amax) {
+  const float a = *amax;
+  return a > 0.f ? a / 127.f : 1.f;
+}
 
 __device__ __forceinline__ int8_t quantize_code(float v, float inv) {
   const float r = __builtin_rintf((float)(f16)v * inv);
@@ -73,7 +80,11 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
                                       : *reinterpret_cast<const float4*>(e.bias + n);
     float v[4];
     if constexpr (std::is_same<T, int8_t>::value) {
-      const float4 d = *reinterpret_cast<const float4*>(e.dq + n);
+      float4 d = *reinterpret_cast<const float4*>(e.dq + n);
+      if (e.dyn_amax) {   // per-column dequantisation scale s_a * s_w[n], formed here
+        const float sa = dyn_act_scale(e.dyn_amax);
+        d = make_float4(sa * d.x, sa * d.y, sa * d.z, sa * d.w);
+      }
       v[0] = (float)acc[0] * d.x + b.x;
       v[1] = (float)acc[1] * d.y + b.y;
       v[2] = (float)acc[2] * d.z + b.z;
@@ -408,6 +419,11 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
         const float4 d1 = *reinterpret_cast<const float4*>(e.dq + n + 4);
         dd[0] = d0.x; dd[1] = d0.y; dd[2] = d0.z; dd[3] = d0.w;
         dd[4] = d1.x; dd[5] = d1.y; dd[6] = d1.z; dd[7] = d1.w;
+        if (e.dyn_amax) {   // dynamic activation scale: s_a * s_w[n]
+          const float sa = dyn_act_scale(e.dyn_amax);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dd[i] = sa * dd[i];
+        }
       }
     }
   }
@@ -563,7 +579,7 @@ __global__ __launch_bounds__((WM * WN + DENSE_PRODUCERS) * 64) void gemm_nt_pipe
   // Materialise the epilogue's kernel arguments before the loop: a scalar load still in
   // flight there would make the compiler wait for every LDS read before each MFMA block.
   asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads),
-               "s"(e.dq), "s"(e.qinv));
+               "s"(e.dq), "s"(e.qinv), "s"(e.dyn_amax));
   if constexpr (EPI == EPI_SWIN_SCATTER)
     asm volatile("" ::"s"(e.geom.Hs), "s"(e.geom.Ws), "s"(e.geom.M), "s"(e.geom.s),
                  "s"(e.geom.nWx), "s"(e.geom.nW), "s"(e.geom.N));
@@ -1123,6 +1139,7 @@ template <typename T, int BM, int BN, int WM, int WN, int EPI, typename TR, type
 static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
+  e.dyn_amax = a.dyn_amax;
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI, TR, TO><<<grid, WM * WN * 64, 0, stream>>>(
       (const T*)a.A, (const T*)a.W, a.K, e);
@@ -1153,6 +1170,7 @@ template <typename T, int C, int EPI, typename TR, typename TO>
 static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
+  e.dyn_amax = a.dyn_amax;
   const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
   const int grid = tm * tn * a.splits;
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>

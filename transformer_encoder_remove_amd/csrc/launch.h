@@ -59,6 +59,9 @@ struct GemmArgs {
   int resid_f32 = 0;    // EPI_BIAS_RESID, bf16 operands only: residual is float32
   int out_f32 = 0;      // EPI_BIAS_RESID, bf16 operands only: output is float32
   const float* dq = nullptr;    // int8 operands: per-column dequantisation scale [N]
+  const float* dyn_amax = nullptr;  // int8 operands, dynamic activation scale: dq holds the
+                                    // weight scales s_w and the activation scale is
+                                    // *dyn_amax / 127 (1 when 0), applied per column
   const float* qinv = nullptr;  // int8 output: device scalar 1 / scale (EPI_BIAS_GELU), or
                                 // three of them, for Q, K and V (EPI_QKV_SPLIT)
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU / EPI_QKV_SPLIT: int8 codes
@@ -95,10 +98,13 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16);
 
 // attention.hip
 bool attention_supported(int dtype, int head_dim);
-// ctxq != nullptr: write only the int8 codes of the stored-type output (scale *qinv)
+// ctxq != nullptr: write only the int8 codes of the stored-type output (scale *qinv);
+// psplit: P enters P V split into two 16-bit parts also for fp16 values (the int8 layers,
+// whose codes of the context are sensitive to P's rounding; always so for bf16 and codes)
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
-                            int8_t* ctxq = nullptr, const float* qinv = nullptr);
+                            int8_t* ctxq = nullptr, const float* qinv = nullptr,
+                            bool psplit = false);
 
 // attention_int8.hip: attention on int8 Q, K, V codes ([3][heads][T][D]); scales (device):
 // [0] = s_q s_k / sqrt(D) * log2 e, [1] = s_v, [2] = 1 / (input scale of the O projection);
@@ -164,9 +170,11 @@ hipError_t launch_store_f32(float* dst, const float* vals, int n, hipStream_t st
 hipError_t launch_quantize_weight(int dtype, const void* w, int8_t* q, float* s_w, float* dq,
                                   float act_scale, int N, int K, hipStream_t stream);
 // q[i] = clamp(rne(float(x[i]) * inv), -127, 127); inv is a device scalar when inv_dev is
-// not null, else the host value inv_host.
+// not null, else the host value inv_host; with amax_dev (dynamic scales) inv = 127 / *amax_dev
+// (1 when it is 0).
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
-                               float inv_host, hipStream_t stream);
+                               float inv_host, hipStream_t stream,
+                               const float* amax_dev = nullptr);
 // *out = max(*out, max |x[i]|) (calibration statistic; out is a device float >= 0)
 hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream);
 

@@ -66,8 +66,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__ x,
                                                            int8_t* __restrict__ q, size_t n,
                                                            const float* __restrict__ inv_dev,
-                                                           float inv_host) {
-  const float inv = inv_dev ? *inv_dev : inv_host;
+                                                           float inv_host,
+                                                           const float* __restrict__ amax_dev) {
+  // dynamic scale: 1 / s = 127 / max-abs of the tensor (1 for an all-zero tensor)
+  float inv = inv_dev ? *inv_dev : inv_host;
+  if (amax_dev) {
+    const float a = *amax_dev;
+    inv = a > 0.f ? 127.f / a : 1.f;
+  }
   const size_t nv = n / 8;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (size_t)gridDim.x * 256) {
     int8_t c[8];
@@ -89,20 +95,20 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
 }
 
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
-                               float inv_host, hipStream_t stream) {
+                               float inv_host, hipStream_t stream, const float* amax_dev) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n / 8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
   switch (dtype) {
     case DT_F16:
-      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host);
+      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host, amax_dev);
       break;
     case DT_BF16:
-      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host);
+      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host, amax_dev);
       break;
     case DT_F32:
-      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev, inv_host);
+      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev, inv_host, amax_dev);
       break;
     default:
       return hipErrorInvalidValue;
