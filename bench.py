@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--dtype", default=None, help="override storage type (f16, bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every GEMM tile configuration on the encoder's projection "
+                         "shapes (back to back, fp16) and print a table")
     ap.add_argument("--graphs", action="store_true",
                     help="run the timed steps through the forward's HIP-graph cache")
     ap.add_argument("--streams", type=int, default=1,
@@ -86,6 +89,8 @@ def main():
     import tel_inputs as ti
     import transformer_encoder_remove_amd as tel
 
+    if args.tile_sweep:
+        return tile_sweep(args)
     if args.workload in ti.SWIN_CONFIGS:
         return bench_swin(args)
     if args.workload in ti.SWIN_STAGES:
@@ -764,6 +769,39 @@ def bench_swin(args):
         "block_kernel_sum_us": round(sum(v["us"] for v in per_kernel.values()), 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def tile_sweep(args):
+    """Back-to-back time of every tile configuration of the pipelined GEMM (and of the
+    register-staged kernel, -1, and the automatic choice, -2) on the projection shapes of
+    BERT-base (2557 tokens), the BERT-large latency batch (128 tokens) and BERT-large FFN1
+    (13537 tokens), fp16, each with the epilogue the layer uses."""
+    import torch
+
+    import transformer_encoder_remove_amd as tel
+    torch.manual_seed(0)
+    st = torch.cuda.current_stream()
+    E = {"bias": tel.TEL_EPI_BIAS, "gelu": tel.TEL_EPI_BIAS_GELU, "resid": tel.TEL_EPI_BIAS_RESID,
+         "qkv": tel.TEL_EPI_QKV_SPLIT}
+    shapes = [("base_qkv", 2557, 2304, 768, "qkv", 12), ("base_o", 2557, 768, 768, "resid", 12),
+              ("base_ffn1", 2557, 3072, 768, "gelu", 12), ("base_ffn2", 2557, 768, 3072, "resid", 12),
+              ("lat_qkv", 128, 3072, 1024, "qkv", 16), ("lat_ffn1", 128, 4096, 1024, "gelu", 16),
+              ("lat_o", 128, 1024, 1024, "resid", 16), ("lat_ffn2", 128, 1024, 4096, "resid", 16),
+              ("large_ffn1", 13537, 4096, 1024, "gelu", 16)]
+    cfgs = [-2, -1] + list(range(tel.tel_gemm_tile_configs()))
+    print("shape " + " ".join(f"{c:>7d}" for c in cfgs), flush=True)
+    for name, M, N, K, epi, heads in shapes:
+        A = torch.randn(M, K, device="cuda").half()
+        W = (torch.randn(N, K, device="cuda") * 0.02).half()
+        b = torch.zeros(N, device="cuda")
+        R = torch.randn(M, N, device="cuda").half() if epi == "resid" else None
+        C = torch.empty(M * N, device="cuda", dtype=torch.half)
+        row = []
+        for cfg in cfgs:
+            fn = lambda cfg=cfg: tel.tel_gemm_ex(E[epi], cfg, A, W, b, C, resid=R, heads=heads,
+                                                 stream=st)
+            row.append(back_to_back_us(fn, st, args.kernel_reps))
+        print(f"{name} " + " ".join(f"{t:7.2f}" for t in row), flush=True)
 
 
 def bench_swin_stages(args):
