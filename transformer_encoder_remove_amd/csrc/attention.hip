@@ -7,8 +7,11 @@
 // Input: Q, K, V head-split as [3][heads][T][D] (the QKV GEMM's epilogue layout), so a
 // head's keys are one contiguous [len][D] block. Output: ctx [T][heads * D].
 //
-// Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid =
-// (ceil(max_len / 64), heads, batch), workgroups past a sequence's end exit at once.
+// Workgroup = QB / 16 wavefronts = QB queries of one (sequence, head), QB = 128 for 16-bit
+// types up to head_dim 64 (8 wavefronts: each K/V block is loaded once for up to 128 queries)
+// and 64 otherwise; grid = (ceil(max_len / QB), heads, batch), workgroups past a sequence's
+// end exit at once, and wavefronts whose queries all lie past it skip the arithmetic (they
+// still stage K/V and meet every barrier).
 // K and V blocks travel through a two-block register ring: Q and the first two key
 // blocks are requested together at the start, and each later block two blocks ahead of
 // its use, so the memory latency is paid about once per workgroup. Per 64-key block:
@@ -31,8 +34,8 @@
 
 namespace tel {
 
-constexpr int ATT_QB = 64;   // queries per workgroup
 constexpr int ATT_KB = 64;   // keys per LDS block
+constexpr int KV_THREADS = 256;   // threads that stage K/V (KvRegs' layout)
 
 // Scores, online-softmax update and O update for one 64-key block staged in LDS.
 template <typename T, int D, int LDK, int LDV, bool PSPLIT>
@@ -194,8 +197,8 @@ template <typename T, int D> struct KvRegs {
   }
 };
 
-template <typename T, int D, bool PSPLIT>
-__global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ qkv,
+template <typename T, int D, bool PSPLIT, int QB>
+__global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict__ qkv,
                                                           T* __restrict__ ctx,
                                                           const int32_t* __restrict__ cu,
                                                           int total_tokens, int heads,
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int start = cu[b], L = cu[b + 1] - start;
-  const int q0 = blockIdx.x * ATT_QB;
+  const int q0 = blockIdx.x * QB;
   if (q0 >= L) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -232,11 +235,13 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
   // workgroup pays one memory latency for Q and the first two key blocks together;
   // later blocks are fetched two blocks ahead of their use.
   KvRegs<T, D> kv0, kv1;
-  kv0.load(Kh, Vh, 0, L, tid);
-  if (ATT_KB < L) kv1.load(Kh, Vh, ATT_KB, L, tid);
+  const bool stager = tid < KV_THREADS;
+  if (stager) kv0.load(Kh, Vh, 0, L, tid);
+  if (stager && ATT_KB < L) kv1.load(Kh, Vh, ATT_KB, L, tid);
 
   const int qi = q0 + wave * 16 + lr;
   const int qc = min(qi, L - 1);
+  const bool wave_on = q0 + wave * 16 < L;    // some query of this wavefront is valid
   frag qf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
@@ -254,11 +259,12 @@ __global__ __launch_bounds__(256) void attn_varlen_kernel(const T* __restrict__ 
 #define TEL_ATT_BLOCK(KV, kb0)                                                              \
   do {                                                                                      \
     __syncthreads();                        /* the previous block's LDS reads are done */   \
-    KV.template store<LDK, LDV>(sK, sVt, tid);                                              \
-    if ((kb0) + 2 * ATT_KB < L) KV.load(Kh, Vh, (kb0) + 2 * ATT_KB, L, tid);                \
+    if (stager) KV.template store<LDK, LDV>(sK, sVt, tid);                                  \
+    if (stager && (kb0) + 2 * ATT_KB < L) KV.load(Kh, Vh, (kb0) + 2 * ATT_KB, L, tid);      \
     __syncthreads();                                                                        \
-    attn_block<T, D, LDK, LDV, PSPLIT>(sK, sVt, qf, o, m_run, l_run, (kb0), L, scale_log2, lr, \
-                                       lg);                                                 \
+    if (wave_on)                                                                            \
+      attn_block<T, D, LDK, LDV, PSPLIT>(sK, sVt, qf, o, m_run, l_run, (kb0), L, scale_log2, \
+                                         lr, lg);                                           \
   } while (0)
 
   for (int kb0 = 0; kb0 < L; kb0 += 2 * ATT_KB) {
@@ -307,14 +313,17 @@ template <typename T, int D>
 static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                            int max_len, int heads, int8_t* ctxq, const float* qinv,
                            bool psplit, hipStream_t stream) {
-  const dim3 grid((max_len + ATT_QB - 1) / ATT_QB, heads, batch);
+  // 128 queries per workgroup where the registers allow two such workgroups per compute
+  // unit (16-bit types, head_dim <= 64), else 64
+  constexpr int QB = (sizeof(T) == 2 && D <= 64) ? 128 : 64;
+  const dim3 grid((max_len + QB - 1) / QB, heads, batch);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (ctxq || psplit || !std::is_same<T, f16>::value)   // P split (see attn_block)
-    attn_varlen_kernel<T, D, true><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total,
-                                                             heads, scale_log2, ctxq, qinv);
+    attn_varlen_kernel<T, D, true, QB><<<grid, QB * 4, 0, stream>>>(
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv);
   else
-    attn_varlen_kernel<T, D, false><<<grid, 256, 0, stream>>>((const T*)qkv, (T*)ctx, cu, total,
-                                                              heads, scale_log2, ctxq, qinv);
+    attn_varlen_kernel<T, D, false, QB><<<grid, QB * 4, 0, stream>>>(
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv);
   return hipGetLastError();
 }
 
