@@ -851,8 +851,6 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
 // next two blocks in registers while it computes the current one. The weight tile is the
 // MFMA A operand, so each lane ends with 4 consecutive columns of one token and the
 // 4-column epilogue above (bias, GELU, QKV split, window scatter, residual) applies as is.
-constexpr int ROWS_WG = 64;
-
 // Input-row modes of the skinny kernel: rows as stored, the shifted-window partition
 // (row r reads image row geom.src_row(r)), or patch merging (row r is the concatenation of
 // the four image rows geom.merge_src(r, k), each K / 4 wide).
@@ -886,6 +884,47 @@ __device__ __forceinline__ void rows_load(typename Mfma<T>::frag (&buf)[KS], con
 // (8 per k-step each), so the two-pass statistics are the lane's own sums plus butterflies
 // over xor 16 and xor 32; the normalised values replace the fragments (rounded to T, as a
 // stored LayerNorm output would be). g, b: the lane's gamma/beta for its K/4 positions.
+// Wide rows (K > 96): the same two-pass statistics without a float copy of the values (each
+// value is converted again where it is needed: the same float operations, bit-identical
+// results, 8 * KS fewer registers), gamma / beta read from LDS as float4 vectors.
+template <typename T, int KS>
+__device__ __forceinline__ void rows_layernorm_wide(typename Mfma<T>::frag (&buf)[KS],
+                                                    const float* sG, const float* sB, int lg,
+                                                    float eps) {
+  constexpr int K = KS * 32;
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += to_f32(buf[t][e]);
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  const float mean = s * (1.f / K);
+  float q = 0.f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = to_f32(buf[t][e]) - mean;
+      q += c * c;
+    }
+  q += __shfl_xor(q, 16, 64);
+  q += __shfl_xor(q, 32, 64);
+  const float rstd = rsqrtf(q * (1.f / K) + eps);
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // four values at a time: 8 live gamma / beta floats
+      const float4 g4 = *reinterpret_cast<const float4*>(sG + t * 32 + lg * 8 + 4 * h);
+      const float4 b4 = *reinterpret_cast<const float4*>(sB + t * 32 + lg * 8 + 4 * h);
+      const float g[4] = {g4.x, g4.y, g4.z, g4.w};
+      const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        buf[t][4 * h + e] = from_f32<T>((to_f32(buf[t][4 * h + e]) - mean) * rstd * g[e] + b[e]);
+    }
+}
+
 // gb(t, e, &g, &b) gives the lane's gamma and beta of its value e of k-step t.
 template <typename T, int KS, typename GB>
 __device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS], const GB& gb,
@@ -924,15 +963,16 @@ __device__ __forceinline__ void rows_layernorm(typename Mfma<T>::frag (&buf)[KS]
     }
 }
 
-// Output fragments in groups of 6 and k in chunks of 3 steps, with scheduling barriers
-// between them: the live weight fragments stay at 6 x 3 (72 VGPRs) instead of the whole
-// weight slice, which keeps two or three wavefronts per SIMD resident.
-template <typename T, int NF, int KS, int EPI, typename TR, typename TO>
+// Output fragments in groups of G and k in chunks of KC steps (6 and 3; 4 and 1 for the
+// 8-wavefront patch-merging workgroup), with scheduling barriers between them: the live
+// weight fragments stay at G x KC instead of the whole weight slice, which keeps two or three
+// wavefronts per SIMD resident.
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO, int KC = 3, int G = 6>
 __device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS], const T* sW,
                                            const EpiArgs<T, TR, TO>& e, int row0, int lr,
                                            int lg) {
   using MF = Mfma<T>;
-  constexpr int LDW = KS * 32 + 8, G = 6, KC = 3;
+  constexpr int LDW = KS * 32 + 8;
   static_assert(NF % G == 0 && KS % KC == 0, "fragment groups");
   const int m = row0 + lr;
 #pragma unroll
@@ -972,8 +1012,11 @@ constexpr int rows_lds_bytes() {
   return NF * 16 * (KS * 32 + 8) * (int)sizeof(T) + (LNA && ln_in_lds<KS>() ? 2 * KS * 32 * 4 : 0);
 }
 
-template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, int MODE>
-__global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
+// NTH threads: 256 (4 wavefronts, 64 rows per step), or 512 for the fp16 patch-merging shape,
+// whose workgroup has a compute unit's LDS to itself and needs more rows in flight.
+template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, int MODE,
+          int NTH = 256>
+__global__ __launch_bounds__(NTH) void gemm_rows_kernel(const T* __restrict__ A,
                                                         const T* __restrict__ W,
                                                         EpiArgs<T, TR, TO> e,
                                                         const float* __restrict__ ln_g,
@@ -989,19 +1032,20 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
   float* sB = sG + K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  for (int idx = tid; idx < N * (K / 8); idx += 256) {
+  constexpr int RWG = NTH / 64 * 16;   // rows per workgroup step
+  for (int idx = tid; idx < N * (K / 8); idx += NTH) {
     const int r = idx / (K / 8), c = idx - r * (K / 8);
     *reinterpret_cast<u32x4*>(sW + r * LDW + c * 8) =
         *reinterpret_cast<const u32x4*>(W + (size_t)r * K + c * 8);
   }
   if constexpr (GB_LDS) {
-    for (int k = tid; k < K; k += 256) {
+    for (int k = tid; k < K; k += NTH) {
       sG[k] = ln_g[k];
       sB[k] = ln_b[k];
     }
   }
   __syncthreads();
-  const int M = e.M, stride = gridDim.x * ROWS_WG;
+  const int M = e.M, stride = gridDim.x * RWG;
   // the lane's gamma / beta of the A-operand LayerNorm: k = t * 32 + lg * 8 + j
   constexpr int KR = LNA && !GB_LDS ? KS : 1;
   float lg_g[KR][8], lg_b[KR][8];
@@ -1025,16 +1069,31 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
       b = lg_b[t][j];
     }
   };
+  auto layernorm = [&](typename MF::frag (&buf)[KS]) {
+    if constexpr (GB_LDS) rows_layernorm_wide<T, KS>(buf, sG, sB, lg, ln_eps);
+    else rows_layernorm<T, KS>(buf, gb, ln_eps);
+  };
+  int rb = blockIdx.x * RWG + wave * 16;   // this wavefront's 16 rows of the block
+  if constexpr (NTH == 512) {
+    // 8 wavefronts per compute unit: one row block in registers per wavefront, the other
+    // wavefronts' work covers the load latency
+    typename MF::frag a0[KS];
+    for (; rb < M; rb += stride) {
+      rows_load<T, KS, MODE>(a0, A, M, rb, lr, lg, e.geom);
+      if constexpr (LNA) layernorm(a0);
+      rows_block<T, NF, KS, EPI, TR, TO, 1, 4>(a0, sW, e, rb, lr, lg);
+    }
+    return;
+  }
   typename MF::frag a0[KS], a1[KS];
-  int rb = blockIdx.x * ROWS_WG + wave * 16;   // this wavefront's 16 rows of the block
   if (rb < M) rows_load<T, KS, MODE>(a0, A, M, rb, lr, lg, e.geom);
   if (rb + stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + stride, lr, lg, e.geom);
   for (; rb < M; rb += 2 * stride) {
-    if constexpr (LNA) rows_layernorm<T, KS>(a0, gb, ln_eps);
+    if constexpr (LNA) layernorm(a0);
     rows_block<T, NF, KS, EPI, TR, TO>(a0, sW, e, rb, lr, lg);
     if (rb + 2 * stride < M) rows_load<T, KS, MODE>(a0, A, M, rb + 2 * stride, lr, lg, e.geom);
     if (rb + stride >= M) break;
-    if constexpr (LNA) rows_layernorm<T, KS>(a1, gb, ln_eps);
+    if constexpr (LNA) layernorm(a1);
     rows_block<T, NF, KS, EPI, TR, TO>(a1, sW, e, rb + stride, lr, lg);
     if (rb + 3 * stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + 3 * stride, lr, lg, e.geom);
   }
@@ -1042,15 +1101,19 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(const T* __restrict__ A,
 
 template <typename T, int NF, int KS>
 static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
-  const int blocks = (a.M + ROWS_WG - 1) / ROWS_WG;
-  // persistent: two workgroups per CU when one takes <= 80 KiB of LDS, else one
+  // persistent: two workgroups per CU when one takes <= 80 KiB of LDS, else one; the
+  // one-per-CU shape (patch merging) runs 8 wavefronts per workgroup in fp16 (bf16's
+  // conversions need a few more registers than 8 wavefronts leave: 4 wavefronts there)
   const int per_cu = rows_lds_bytes<T, NF, KS, true>() <= 80 * 1024 ? 2 : 1;
+  constexpr int NTH = (NF == 12 && KS == 12 && std::is_same<T, f16>::value) ? 512 : 256;
+  const int rows_wg = NTH / 64 * 16;
+  const int blocks = (a.M + rows_wg - 1) / rows_wg;
   const int grid = std::min(blocks, 256 * per_cu);
 #define TEL_ROWS_LN(EPI, LNA, MODE)                                                          \
   do {                                                                                       \
     EpiArgs<T, T, T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, \
                        a.geom};                                                              \
-    gemm_rows_kernel<T, NF, KS, EPI, T, T, LNA, MODE><<<grid, 256, 0, stream>>>(            \
+    gemm_rows_kernel<T, NF, KS, EPI, T, T, LNA, MODE, NTH><<<grid, NTH, 0, stream>>>(       \
         (const T*)a.A, (const T*)a.W, e, a.ln_g, a.ln_b, a.ln_eps);                         \
   } while (0)
 #define TEL_ROWS(EPI) TEL_ROWS_LN(EPI, false, ROWS_PLAIN)
