@@ -13,7 +13,8 @@
 //
 // Input: Q, K, V codes head-split as [3][heads][T][D] int8 (the int8 QKV epilogue's layout).
 // Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid = (ceil(max_len / 64),
-// heads, batch). Per 64-key block, K [64][D] and V^T [D][64] are staged in LDS. Each
+// heads, batch). Per 64-key block, K [64][D] and V^T [D][64] are staged in LDS; a sequence of up
+// to 128 keys has both blocks staged at once and its scores kept in registers (one pass). Each
 // wavefront computes S^T = K Q^T for its 16 queries, so a lane holds the scores of one query
 // for 16 keys (keys 16 j + 4 lg + i, j, i = 0..3). For P V the MFMA k index e of lane group lg
 // is mapped to key 16 (e / 4) + 4 lg + e % 4, the keys that lane already holds, so its 16 P
@@ -45,9 +46,10 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
   constexpr int NKS = (D + 63) / 64;                // 64-deep k steps of q . k
   constexpr int NCB = D / 16;                       // 16-channel blocks of the output
   constexpr int LDK = (D < 64 ? 64 : D) + 16;       // bytes per staged K row
-  constexpr int LDV = A8_KB + 16;                   // bytes per staged V^T row
+  constexpr int LDV = 2 * A8_KB + 16;               // bytes per staged V^T row (two blocks)
   static_assert(D % 16 == 0, "head_dim");
-  __shared__ __attribute__((aligned(16))) int8_t sK[A8_KB * LDK];
+  // room for two key blocks: a sequence of up to 128 keys is staged once (one pass)
+  __shared__ __attribute__((aligned(16))) int8_t sK[2 * A8_KB * LDK];
   __shared__ __attribute__((aligned(16))) int8_t sVt[D * LDV];
 
   const int b = blockIdx.z, h = blockIdx.y;
@@ -73,13 +75,15 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
   // K (and V) of a 64-key block: 16-byte vectors, thread tid owns vectors tid + 256 p;
   // rows past the sequence end are clamped to its last key (their scores are masked)
   constexpr int VPR = D / 16, NVEC = A8_KB * VPR, PER = (NVEC + 255) / 256;
-  auto stage_k = [&](int kb0) {
+  // stage key block kb0 into LDS block slot `slot` (K rows slot * 64.., V^T columns slot * 64..)
+  auto stage_k = [&](int kb0, int slot) {
+    int8_t* dK = sK + slot * A8_KB * LDK;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = tid + 256 * p;
       if (NVEC % 256 == 0 || idx < NVEC) {
         const int r = idx / VPR, c = idx - r * VPR;
-        *reinterpret_cast<u32x4*>(&sK[r * LDK + c * 16]) =
+        *reinterpret_cast<u32x4*>(&dK[r * LDK + c * 16]) =
             *reinterpret_cast<const u32x4*>(Kh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
       }
     }
@@ -87,10 +91,10 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
       for (int r = tid; r < A8_KB; r += 256)
 #pragma unroll
         for (int c = D; c < 64; c += 16)
-          *reinterpret_cast<u32x4*>(&sK[r * LDK + c]) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&dK[r * LDK + c]) = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto stage_v = [&](int kb0) {
+  auto stage_v = [&](int kb0, int slot) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = tid + 256 * p;
@@ -99,20 +103,21 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
         const u32x4 v = *reinterpret_cast<const u32x4*>(Vh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
         int8_t e[16];
         __builtin_memcpy(e, &v, 16);
-        const int col = a8_vcol(r);
+        const int col = slot * A8_KB + a8_vcol(r);
 #pragma unroll
         for (int k = 0; k < 16; ++k) sVt[(c * 16 + k) * LDV + col] = e[k];
       }
     }
   };
-  // scores of the staged block in base 2, -inf for keys past the end
-  auto scores = [&](int kb0, float (&t)[4][4]) {
+  // scores of the block staged in slot `slot` in base 2, -inf for keys past the end
+  auto scores = [&](int kb0, int slot, float (&t)[4][4]) {
+    const int8_t* sKb = sK + slot * A8_KB * LDK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       MF::acc s = MF::acc{0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
-        const frag kf = *reinterpret_cast<const frag*>(&sK[(j * 16 + lr) * LDK + k * 64 + lg * 16]);
+        const frag kf = *reinterpret_cast<const frag*>(&sKb[(j * 16 + lr) * LDK + k * 64 + lg * 16]);
         s = MF::mma(kf, qf[k], s);
       }
 #pragma unroll
@@ -123,34 +128,19 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
     }
   };
 
-  // pass 1: the exact row maximum over all keys of the sequence
-  float m = -INFINITY;
-  for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
-    __syncthreads();
-    stage_k(kb0);
-    __syncthreads();
-    float t[4][4];
-    scores(kb0, t);
+  auto row_max = [&](float (&t)[4][4], float m) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = fmaxf(m, t[j][i]);
-  }
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
-
-  // pass 2: P codes and P V, exact int32
+    return m;
+  };
   MF::acc o[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) o[c] = MF::acc{0, 0, 0, 0};
   int lsum = 0;
-  for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
-    __syncthreads();
-    stage_k(kb0);
-    stage_v(kb0);
-    __syncthreads();
-    float t[4][4];
-    scores(kb0, t);
+  // P codes of one block's scores and their P V contribution (V^T of `slot`), exact int32
+  auto pv = [&](float (&t)[4][4], float m, int slot) {
     int8_t r[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -165,8 +155,53 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
     __builtin_memcpy(&pf, r, 16);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      const frag vf = *reinterpret_cast<const frag*>(&sVt[(c * 16 + lr) * LDV + lg * 16]);
+      const frag vf = *reinterpret_cast<const frag*>(&sVt[(c * 16 + lr) * LDV + slot * A8_KB + lg * 16]);
       o[c] = MF::mma(vf, pf, o[c]);
+    }
+  };
+  float m = -INFINITY;
+  if (L <= 2 * A8_KB) {
+    // up to 128 keys: both blocks staged at once, scores kept in registers, one pass
+    const bool two = L > A8_KB;
+    stage_k(0, 0);
+    stage_v(0, 0);
+    if (two) {
+      stage_k(A8_KB, 1);
+      stage_v(A8_KB, 1);
+    }
+    __syncthreads();
+    float t0[4][4], t1[4][4];
+    scores(0, 0, t0);
+    m = row_max(t0, m);
+    if (two) {
+      scores(A8_KB, 1, t1);
+      m = row_max(t1, m);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    pv(t0, m, 0);
+    if (two) pv(t1, m, 1);
+  } else {
+    // pass 1: the exact row maximum over all keys of the sequence
+    for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
+      __syncthreads();
+      stage_k(kb0, 0);
+      __syncthreads();
+      float t[4][4];
+      scores(kb0, 0, t);
+      m = row_max(t, m);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    // pass 2: P codes and P V
+    for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
+      __syncthreads();
+      stage_k(kb0, 0);
+      stage_v(kb0, 0);
+      __syncthreads();
+      float t[4][4];
+      scores(kb0, 0, t);
+      pv(t, m, 0);
     }
   }
   lsum += __shfl_xor(lsum, 16, 64);
