@@ -120,13 +120,24 @@ hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, co
 // their bit patterns, so an unsigned atomic max is exact and order-independent. The
 // workgroup reduces through LDS first: one atomic per workgroup, not per wavefront (atomics
 // on one address serialise).
+// Each thread reads 16 bytes per step (8 16-bit or 4 float32 values); workgroup 0 takes the
+// tail of n that does not fill a vector.
 template <typename T>
 __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, size_t n,
                                                      float* __restrict__ out) {
+  constexpr int VEC = 16 / sizeof(T);
   __shared__ float wave_max[4];
   float m = 0.f;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-    m = fmaxf(m, fabsf(to_f32(x[i])));
+  const size_t nv = n / VEC;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (size_t)gridDim.x * 256) {
+    T v[VEC];
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + i * VEC);
+    __builtin_memcpy(v, &raw, 16);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, fabsf(to_f32(v[e])));
+  }
+  if (blockIdx.x == 0)
+    for (size_t i = nv * VEC + threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(to_f32(x[i])));
   m = group_max<64>(m);
   if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -138,8 +149,10 @@ __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, si
 
 hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
+  if ((uintptr_t)x & 15u) return hipErrorInvalidValue;   // 16-byte vector loads
+  size_t blocks = (n * dtype_size(dtype) / 16 + 255) / 256;
   if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) blocks = 1;
   switch (dtype) {
     case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out); break;
     case DT_BF16: absmax_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, n, out); break;
