@@ -452,16 +452,27 @@ def main():
 
 
 # every kernel source: counters taken on other sources than the ones built now are stale
-KERNEL_SOURCES = tuple(sorted(
-    os.path.join("transformer_encoder_remove_amd", "csrc", f)
-    for f in os.listdir(os.path.join(ROOT, "transformer_encoder_remove_amd", "csrc"))
-    if f.endswith((".hip", ".h", ".cpp"))))
+# The source files each measured kernel is compiled from: its own .hip file and the two
+# headers every kernel includes. A counter record stays valid while these are unchanged.
+_HEADERS = ("device.h", "launch.h")
+_KERNEL_FILE = {"attention": "attention.hip", "layernorm": "layernorm.hip",
+                "ln1_reduce": "layernorm.hip", "ln2_reduce": "layernorm.hip",
+                "window_attention": "swin.hip"}
 
 
-def kernel_sources_digest() -> str:
+def kernel_sources(kernel: str) -> tuple:
+    """Files (relative to the repository) whose text fixes the named kernel: the GEMM-based
+    ones (every gemm_* kernel and the shifted-window block's fused projections) come from
+    gemm.hip."""
+    own = _KERNEL_FILE.get(kernel, "gemm.hip")
+    return tuple(os.path.join("transformer_encoder_remove_amd", "csrc", f)
+                 for f in (own,) + _HEADERS)
+
+
+def kernel_sources_digest(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources(kernel):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -480,7 +491,7 @@ def measured_traffic(workload: str, dtype: str, kernel: str):
         return None
     for r in rec.get("kernels", []):
         if r.get("workload") == workload and r.get("dtype") == dtype and \
-                r.get("kernel") == kernel and r.get("sources_sha256") == kernel_sources_digest():
+                r.get("kernel") == kernel and r.get("sources_sha256") == kernel_sources_digest(kernel):
             return r.get("bytes_per_launch")
     return None
 
@@ -550,7 +561,6 @@ def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str):
             per_kernel[name]["symbol"] = launches[0][0]
     true_kib = 256 * 1024
     ff, wf = true_kib / calib["FETCH_SIZE"], true_kib / calib["WRITE_SIZE"]
-    digest = kernel_sources_digest()
     for k in table["kernels"]:
         c = per_kernel[k["name"]]
         total = (c["FETCH_SIZE"] * ff + c["WRITE_SIZE"] * wf) * 1024
@@ -559,14 +569,15 @@ def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str):
             "symbol": c["symbol"], "fetch_size_kib": round(c["FETCH_SIZE"], 2),
             "write_size_kib": round(c["WRITE_SIZE"], 2), "bytes_per_launch": int(total),
             "algorithmic_bytes": int(k["bytes"]), "ratio": round(total / k["bytes"], 2),
-            "sources_sha256": digest})
+            "sources_sha256": kernel_sources_digest(k["name"])})
     out["description"] = (
         "HBM traffic per launch of the layer / block kernels, launched one by one as bench.py's "
         "per-kernel timing does; counters per dispatch, averaged over the timed launches. "
         "bytes_per_launch = FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor (KiB), the "
         "factors being what a plain 256 MiB device copy reads on the same counters. "
-        "sources_sha256: SHA-256 of " + " + ".join(KERNEL_SOURCES) + " when the counters were "
-        "taken; bench.py reports a figure only while it matches.")
+        "sources_sha256: SHA-256 of the kernel's own source file and the headers device.h and "
+        "launch.h (bench.py kernel_sources) when the counters were taken; bench.py reports a "
+        "figure only while it matches.")
     out["calibration"] = {"copy": "__amd_rocclr_copyBuffer, 256 MiB device to device",
                           "fetch_size_kib": round(calib["FETCH_SIZE"], 1),
                           "write_size_kib": round(calib["WRITE_SIZE"], 1),
