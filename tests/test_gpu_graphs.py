@@ -132,3 +132,39 @@ def test_graph_replays_match_oracle(cache_state, name, layers, int8):
         # pad rows of the rebuilt output are exactly zero
         for b in range(B):
             assert not yd[b, int(lens[b]):].any()
+
+
+def test_graph_key_tells_static_from_dynamic_scales(cache_state):
+    """Two descriptors that differ only in dynamic_scales, on the same packed weights and
+    buffers, record two graphs: each replay equals its own eager forward."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base_int8"], layers=1)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, 0, variant=True)]
+    mk = lambda dyn: tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"],
+                                           torch.float16, ti.LN_EPS, int8_gemm=True,
+                                           dynamic_scales=dyn)
+    d_static, d_dyn = mk(False), mk(True)
+    packed = prepare_layers(tel, d_static, ws, "f16", [[3.0, 2.5, 4.0, 1.5]])
+    B, S, _ = x.shape
+    xd = dev(x, "f16")
+    yd = torch.empty_like(xd)
+    lens_d = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    wsb = tel.alloc_bytes(max(tel.tel_encoder_forward_workspace_size(d, B, S)
+                              for d in (d_static, d_dyn)))
+    T, max_len = int(np.sum(lens)), int(np.max(lens))
+    run = lambda d: tel.tel_encoder_forward(d, packed, xd, yd, lens_d, T, max_len, wsb)
+    tel.tel_graph_cache(0)
+    refs = []
+    for d in (d_static, d_dyn):
+        yd.fill_(float("nan"))
+        run(d)
+        torch.cuda.synchronize()
+        refs.append(yd.clone())
+    assert not torch.equal(refs[0], refs[1])   # the two scale modes give different codes
+    tel.tel_graph_cache(1)
+    for i in range(3):
+        for d, ref in zip((d_static, d_dyn), refs):
+            yd.fill_(float("nan"))
+            run(d)
+            torch.cuda.synchronize()
+            assert torch.equal(yd, ref), f"replay {i}, dynamic={d.dynamic_scales}"

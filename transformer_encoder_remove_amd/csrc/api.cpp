@@ -887,7 +887,7 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
   }
   std::vector<uintptr_t> key = {(uintptr_t)dev, (uintptr_t)d->hidden, (uintptr_t)d->heads,
                                 (uintptr_t)d->ffn, (uintptr_t)d->dtype, (uintptr_t)d->int8_gemm,
-                                (uintptr_t)d->sparse_2of4,
+                                (uintptr_t)d->sparse_2of4, (uintptr_t)d->dynamic_scales,
                                 (uintptr_t)n_layers, (uintptr_t)x_pad, (uintptr_t)y_pad,
                                 (uintptr_t)seq_lens, (uintptr_t)batch, (uintptr_t)max_seq,
                                 (uintptr_t)total_tokens, (uintptr_t)max_len,
