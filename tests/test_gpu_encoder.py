@@ -87,6 +87,34 @@ def test_bert_base_12_layers_sampled_sequences():
                  "bert_base 12 layers")
 
 
+def test_bert_base_bf16_12_layers_sampled():
+    """12 bf16 BERT-base layers on the full batch, sampled sequences. Per layer: the output
+    of the GPU's first k+1 layers against the oracle's layer k applied to the GPU's own
+    output of the first k layers, within the fp16/bf16 bound. End to end, against the
+    float64 oracle of all 12 layers: each layer's output is stored as bf16 (unit roundoff
+    u = 2^-8) before the next one reads it, and these independent roundings add up like a
+    random walk, so the bound there is sqrt(12) times the per-layer one (max-abs 6.9e-2,
+    relative Frobenius 1.7e-2); the measured error is printed."""
+    cfg = dict(ti.ENCODER_CONFIGS["bert_base"], dtype="bf16")
+    lens, x = ti.encoder_input(cfg)
+    nl = cfg["layers"]
+    ws = [ti.encoder_layer_weights(cfg, i) for i in range(nl)]
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 31})
+    lp = lens[pick]
+    prev = x[pick]
+    for k in range(nl):
+        y = gpu_encoder_forward(tel, dict(cfg, layers=k + 1), lens, x, ws[:k + 1])[pick]
+        ref = enc.encoder_forward(prev, lp, [ws[k]], cfg["heads"], EPS)
+        got, want = enc.remove_padding(y, lp), enc.remove_padding(ref, lp)
+        assert_close(got, want, "bf16", f"bf16 layer {k} on the GPU's own input")
+        prev = y
+    ref = enc.encoder_forward(x[pick], lp, ws, cfg["heads"], EPS)
+    ma, rel = errors(enc.remove_padding(prev, lp), enc.remove_padding(ref, lp))
+    print(f"bf16 12 layers end to end vs float64: max_abs={ma:.3e} rel_frob={rel:.3e}")
+    root = np.sqrt(nl)
+    assert ma <= 2e-2 * root and rel <= 5e-3 * root, (ma, rel)
+
+
 def test_bert_large_tput_one_layer_sampled():
     """BERT-large throughput batch (B 64, S 384, lengths U{64..384}), one layer on the GPU for
     the whole batch; the oracle checks a sample of sequences."""
