@@ -173,7 +173,7 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   // dynamic scales: the four max-abs values first (documented: bytes 0..15 of the workspace)
-  if (d->dynamic_scales) w.dyn = take(4 * 4);
+  if (d->dynamic_scales) w.dyn = take(16 * 4);   // two regions of 8 maxima (DynLink)
   w.qkv = take(3 * T * H * es);
   w.ctx = take(T * H * es);
   w.pre = take(T * H * (f32_stream(d) ? 4 : es));
@@ -225,17 +225,30 @@ struct Int8Link {
 
 // Int8 layer with dynamic activation scales ("揭秘Transformer模型…", section 3.3: the
 // quantisation parameters follow the data at inference time): each GEMM input is stored as
-// fp16 by its producer, its max-abs over the batch is reduced on the device, the quantise
-// kernel takes 127 / max-abs as its inverse scale, and the GEMM epilogue forms the
+// fp16 by its producer, its max-abs over the batch is reduced on the device (folded into
+// the producer for ctx, h1 and the GELU output; a pass of its own for the layer input), the
+// quantise kernel takes 127 / max-abs as its inverse scale, and the GEMM epilogue forms the
 // dequantisation scale (max-abs / 127) * s_w[n] per column. The layer never splits over k.
+//
+// In a stack, layer i uses region i % 2 of the 16 floats at W.dyn: [0..3] its four maxima,
+// [4] the max-abs of its output, which its LN2 folds in and layer i + 1 takes as its input
+// statistic (DynLink), so only the first layer reads its input for the max-abs.
+struct DynLink {
+  int parity = 0;         // region of this layer
+  bool in_from_prev = false;   // input max-abs left by the previous layer's LN2
+  bool out_to_next = false;    // fold this layer's output max-abs for the next layer
+};
+
 int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const void* x, void* y,
                                const int32_t* cu, int batch, int T, int max_len, char* ws,
-                               hipStream_t st) {
+                               hipStream_t st, const DynLink& link = DynLink{}) {
   const LayerLayout L = layer_layout(d);
   const LayerWs W = layer_ws(d, (size_t)T);
   const int H = d->hidden, F = d->ffn, nh = d->heads;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
-  float* amax = (float*)(ws + W.dyn);
+  float* const dyn = (float*)(ws + W.dyn);
+  float* amax = dyn + 8 * link.parity;
+  const float* x_amax = link.in_from_prev ? dyn + 8 * (1 - link.parity) + 4 : amax + 0;
   int8_t* xq = (int8_t*)(ws + W.xq);
   int8_t* ctxq = (int8_t*)(ws + W.ctxq);
   int8_t* h1q = (int8_t*)(ws + W.h1q);
@@ -245,40 +258,46 @@ int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const v
   void* pre = ws + W.pre;
   void* h1 = ws + W.h1;
   void* f = ws + W.f;
-  const float zeros[4] = {0.f, 0.f, 0.f, 0.f};
-  TEL_TRY(launch_store_f32(amax, zeros, 4, st));   // a kernel, not a memset (graph capture)
-  auto codes = [&](const void* a, size_t n, int8_t* q, int g) -> hipError_t {
-    hipError_t e = launch_absmax(DT_F16, a, n, amax + g, st);
-    if (e != hipSuccess) return e;
+  const float zeros[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  TEL_TRY(launch_store_f32(amax, zeros, 5, st));   // a kernel, not a memset (graph capture)
+  // the layer input's max-abs has its own pass; ctx's, h1's and the GELU output's are folded
+  // into the kernels that store them (attention, LN1, the FFN1 epilogue)
+  auto quantize = [&](const void* a, size_t n, int8_t* q, int g) {
     return launch_quantize_act(DT_F16, a, q, n, nullptr, 0.f, st, amax + g);
   };
-  TEL_TRY(codes(x, (size_t)T * H, xq, 0));
+  if (!link.in_from_prev) TEL_TRY(launch_absmax(DT_F16, x, (size_t)T * H, amax + 0, st));
+  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, nullptr, 0.f, st, x_amax));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.dq = F32(L.sw_qkv);
-  g.dyn_amax = amax + 0;
+  g.dyn_amax = x_amax;
   TEL_TRY(launch_gemm(DT_I8, g, st));
   // P split as in the static int8 layer: ctx's codes follow P's rounding closely
   TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, nullptr,
-                           nullptr, true));
-  TEL_TRY(codes(ctx, (size_t)T * H, ctxq, 1));
+                           nullptr, true, amax + 1));
+  TEL_TRY(quantize(ctx, (size_t)T * H, ctxq, 1));
   g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
   g.dq = F32(L.sw_o);
   g.dyn_amax = amax + 1;
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, h1, nullptr, F32(L.ln1_g), F32(L.ln1_b), T, H,
-                           d->ln_eps, st));
-  TEL_TRY(codes(h1, (size_t)T * H, h1q, 2));
-  g = GemmArgs{EPI_BIAS_GELU, h1q, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
+  TEL_TRY(launch_layernorm_amax(pre, h1, amax + 2, F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps,
+                                st));
+  TEL_TRY(quantize(h1, (size_t)T * H, h1q, 2));
+  g = GemmArgs{EPI_BIAS_GELU_AMAX, h1q, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
   g.dq = F32(L.sw_1);
   g.dyn_amax = amax + 2;
+  g.out_amax = amax + 3;
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(codes(f, (size_t)T * F, fq, 3));
+  TEL_TRY(quantize(f, (size_t)T * F, fq, 3));
   g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
   g.dq = F32(L.sw_2);
   g.dyn_amax = amax + 3;
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
-                           d->ln_eps, st));
+  if (link.out_to_next)
+    TEL_TRY(launch_layernorm_amax(pre, y, amax + 4, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                                  d->ln_eps, st));
+  else
+    TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,
+                             d->ln_eps, st));
   return TEL_OK;
 }
 
@@ -792,6 +811,14 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
       int8_t* tq = qa;
       qa = qb;
       qb = tq;
+    } else if (d->int8_gemm && d->dynamic_scales && total_tokens > 0) {
+      // each LN2 folds the max-abs of its output in for the next layer's input scale
+      DynLink dl;
+      dl.parity = i & 1;
+      dl.in_from_prev = i > 0;
+      dl.out_to_next = i + 1 < n_layers;
+      r = layer_forward_int8_dynamic(d, (const char*)packed_layers[i], xa, xb, cu, batch,
+                                     total_tokens, max_len, ws + S.layer, st, dl);
     } else {
       r = layer_forward(d, (const char*)packed_layers[i], xa, xb, cu, batch, total_tokens,
                         max_len, ws + S.layer, st);

@@ -204,7 +204,8 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
                                                           int total_tokens, int heads,
                                                           float scale_log2,
                                                           int8_t* __restrict__ ctxq,
-                                                          const float* __restrict__ qinv) {
+                                                          const float* __restrict__ qinv,
+                                                          float* __restrict__ amax) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int KPL = MF::KPL, KMF = 4 * KPL;
@@ -218,11 +219,13 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
 
   __shared__ __attribute__((aligned(16))) T sK[ATT_KB * LDK];
   __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+  __shared__ unsigned int amax_lds[2];   // with amax: workgroup max-abs, counter
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int start = cu[b], L = cu[b + 1] - start;
   const int q0 = blockIdx.x * QB;
   if (q0 >= L) return;
+  if (amax && threadIdx.x == 0) amax_lds[0] = amax_lds[1] = 0u;   // before the first barrier
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -273,6 +276,7 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
   }
 #undef TEL_ATT_BLOCK
 
+  float am = 0.f;   // with amax: this lane's max-abs of its stored context values
   if (qi < L) {
     const float inv_l = 1.f / l_run;
     const size_t base = (size_t)(start + qi) * (heads * D) + h * D;
@@ -299,9 +303,15 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) w.v[i] = from_f32<T>(o[c][i] * inv_l);
         *reinterpret_cast<Vec4<T>*>(ctx + base + c * 16 + 4 * lg) = w;
+        if (amax) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(to_f32(w.v[i])));
+        }
       }
     }
   }
+  // the max-abs of the stored context, for a dynamically scaled int8 O projection
+  if (amax) wg_atomic_max(am, amax, amax_lds, QB / 16);
 }
 
 bool attention_supported(int dtype, int head_dim) {
@@ -312,7 +322,7 @@ bool attention_supported(int dtype, int head_dim) {
 template <typename T, int D>
 static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                            int max_len, int heads, int8_t* ctxq, const float* qinv,
-                           bool psplit, hipStream_t stream) {
+                           bool psplit, float* amax, hipStream_t stream) {
   // 128 queries per workgroup where the registers allow two such workgroups per compute
   // unit (16-bit types, head_dim <= 64), else 64
   constexpr int QB = (sizeof(T) == 2 && D <= 64) ? 128 : 64;
@@ -320,38 +330,39 @@ static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int ba
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (ctxq || psplit || !std::is_same<T, f16>::value)   // P split (see attn_block)
     attn_varlen_kernel<T, D, true, QB><<<grid, QB * 4, 0, stream>>>(
-        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv);
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax);
   else
     attn_varlen_kernel<T, D, false, QB><<<grid, QB * 4, 0, stream>>>(
-        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv);
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t run_attn_d(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                              int max_len, int heads, int d, int8_t* ctxq, const float* qinv,
-                             bool ps, hipStream_t stream) {
+                             bool ps, float* amax, hipStream_t stream) {
   switch (d) {
-    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
-    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
-    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
-    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, stream);
+    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
+    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
+    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
+    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
-                            int8_t* ctxq, const float* qinv, bool psplit) {
+                            int8_t* ctxq, const float* qinv, bool psplit, float* amax) {
   if (total == 0 || max_len == 0) return hipSuccess;
   if (ctxq && !qinv) return hipErrorInvalidValue;
+  if (amax && ctxq) return hipErrorInvalidValue;   // the max-abs is of the stored context
   switch (dtype) {
     case DT_F16:
-      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
+      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
     case DT_BF16:
-      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
+      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
     case DT_F32:
-      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, stream);
+      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -112,6 +112,36 @@ template <int G> __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// One wavefront's share of a tensor's max-abs: the 64 lanes' maxima (each >= 0) reduced in
+// registers, then one atomic max on *out (non-negative floats order like their bit
+// patterns, so the unsigned atomic is exact and independent of arrival order). Every lane
+// of the wavefront must call it.
+__device__ __forceinline__ void wave_atomic_max(float m, float* out) {
+  m = group_max<64>(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+// The same for a workgroup of nw wavefronts with one global atomic: each wavefront folds
+// its maximum into lds[0] with an LDS atomic max, then increments the counter lds[1]; the
+// wavefront that brings the counter to nw (its increment is ordered after every other
+// wavefront's maximum) folds lds[0] into *out. There is no barrier, so wavefronts that
+// have already left (a GEMM's producers) are not waited for. lds[0] and lds[1] must hold 0
+// before any wavefront gets here, and each of the nw wavefronts calls this once.
+__device__ __forceinline__ void wg_atomic_max(float m, float* out, unsigned int* lds, int nw) {
+  m = group_max<64>(m);
+  if ((threadIdx.x & 63) == 0) {
+    __hip_atomic_fetch_max(&lds[0], __float_as_uint(m), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    const unsigned int n = __hip_atomic_fetch_add(&lds[1], 1u, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (n == (unsigned int)nw - 1) {
+      const unsigned int v = __hip_atomic_load(&lds[0], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      atomicMax(reinterpret_cast<unsigned int*>(out), v);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ shifted windows
 // Token order maps of the shifted-window block. Image order: row b * Hs * Ws + y * Ws + x.
 // Window order: windows row-major inside each image, images outermost, tokens row-major

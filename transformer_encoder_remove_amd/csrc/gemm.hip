@@ -48,7 +48,10 @@ template <typename T, typename TR, typename TO> struct EpiArgs {
   const float* qinv;   // int8 output: device scalar, 1 / activation scale of the consumer
   SwinGeom geom;       // EPI_SWIN_SCATTER: window order -> image order
   const float* dyn_amax = nullptr;   // int8 operands, dynamic scale: dq = s_w, s_a from max-abs
+  float* out_amax = nullptr;         // EPI_BIAS_GELU_AMAX: max-abs of the stored outputs
 };
+
+constexpr bool epi_gelu(int epi) { return epi == EPI_BIAS_GELU || epi == EPI_BIAS_GELU_AMAX; }
 
 // Activation scale of a dynamically scaled int8 GEMM: max-abs / 127 (1 for an all-zero input).
 __device__ __forceinline__ float dyn_act_scale(const float* amax) {
@@ -61,20 +64,21 @@ __device__ __forceinline__ int8_t quantize_code(float v, float inv) {
   return (int8_t)fminf(fmaxf(r, -127.f), 127.f);
 }
 
+// Returns the max-abs of the stored outputs for EPI_BIAS_GELU_AMAX, 0 otherwise.
 template <int EPI, typename T, typename TR, typename TO, typename ACC>
-__device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
-                                               ACC acc) {
+__device__ __forceinline__ float epilogue_store(const EpiArgs<T, TR, TO>& e, int m, int n,
+                                                ACC acc) {
   if constexpr (EPI == EPI_PARTIAL && sizeof(TO) == 2) {
     // partial sums rounded to the 16-bit output type
     Vec4<TO> out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(acc[i]);
     *reinterpret_cast<Vec4<TO>*>(e.C + (size_t)m * e.N + n) = out;
-    return;
+    return 0.f;
   } else if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
     // the raw 32-bit accumulators (int32 for int8 operands), no epilogue arithmetic
     *reinterpret_cast<ACC*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = acc;
-    return;
+    return 0.f;
   } else {
     const float4 b = EPI == EPI_PLAIN ? make_float4(0.f, 0.f, 0.f, 0.f)
                                       : *reinterpret_cast<const float4*>(e.bias + n);
@@ -97,7 +101,7 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
     }
     Vec4<TO> out;
     size_t idx;
-    if constexpr (EPI == EPI_BIAS_GELU) {
+    if constexpr (epi_gelu(EPI)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
     }
@@ -129,6 +133,12 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
       for (int i = 0; i < 4; ++i) out.v[i] = from_f32<TO>(v[i]);
     }
     *reinterpret_cast<Vec4<TO>*>(e.C + idx) = out;
+    float am = 0.f;
+    if constexpr (EPI == EPI_BIAS_GELU_AMAX) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(to_f32(out.v[i])));
+    }
+    return am;
   }
 }
 
@@ -139,21 +149,21 @@ __device__ __forceinline__ void epilogue_store(const EpiArgs<T, TR, TO>& e, int 
 template <typename T8> struct alignas(sizeof(T8) * 8) Vec8 { T8 v[8]; };
 
 template <int EPI, typename T, typename TR, typename TO>
-__device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int m, int n,
-                                                const float* acc, const float* bb,
-                                                const float* dd, const Vec8<TR>& r) {
+__device__ __forceinline__ float epilogue_apply8(const EpiArgs<T, TR, TO>& e, int m, int n,
+                                                 const float* acc, const float* bb,
+                                                 const float* dd, const Vec8<TR>& r) {
   if constexpr (EPI == EPI_PARTIAL && sizeof(TO) == 2) {
     Vec8<TO> o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.v[i] = from_f32<TO>(acc[i]);
     *reinterpret_cast<Vec8<TO>*>(e.C + (size_t)m * e.N + n) = o;
-    return;
+    return 0.f;
   } else if constexpr (EPI == EPI_RAW_I32 || EPI == EPI_PARTIAL) {
     Vec8<int32_t> o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.v[i] = __float_as_int(acc[i]);   // staged as raw bits
     *reinterpret_cast<Vec8<int32_t>*>(reinterpret_cast<int32_t*>(e.C) + (size_t)m * e.N + n) = o;
-    return;
+    return 0.f;
   } else {
     float v[8];
 #pragma unroll
@@ -161,7 +171,7 @@ __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int
       if constexpr (std::is_same<T, int8_t>::value) v[i] = (float)__float_as_int(acc[i]) * dd[i] + bb[i];
       else v[i] = acc[i] + bb[i];
     }
-    if constexpr (EPI == EPI_BIAS_GELU) {
+    if constexpr (epi_gelu(EPI)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = gelu_erf(v[i]);
     }
@@ -201,6 +211,12 @@ __device__ __forceinline__ void epilogue_apply8(const EpiArgs<T, TR, TO>& e, int
     } else {
       *reinterpret_cast<Vec8<TO>*>(e.C + idx) = out;
     }
+    float am = 0.f;
+    if constexpr (EPI == EPI_BIAS_GELU_AMAX) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(to_f32(out.v[i])));
+    }
+    return am;
   }
 }
 
@@ -223,6 +239,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 
   __shared__ __attribute__((aligned(16))) T sA[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) T sW[2][BN * LDK];
+  __shared__ unsigned int amax_lds[2];   // EPI_BIAS_GELU_AMAX: workgroup max-abs, counter
+  if constexpr (EPI == EPI_BIAS_GELU_AMAX) {
+    if (threadIdx.x == 0) amax_lds[0] = amax_lds[1] = 0u;   // before the first barrier
+  }
 
   const int M = e.M, N = e.N;
   const int tiles_m = (M + BM - 1) / BM;
@@ -294,15 +314,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
     __syncthreads();
   }
 
+  float am = 0.f;
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
     const int n = n0 + wn * TN + i * 16 + lg * 4;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int m = m0 + wm * TM + j * 16 + lr;
-      if (m < M && n < N) epilogue_store<EPI, T, TR, TO>(e, m, n, acc[i][j]);
+      if (m < M && n < N) am = fmaxf(am, epilogue_store<EPI, T, TR, TO>(e, m, n, acc[i][j]));
     }
   }
+  if constexpr (EPI == EPI_BIAS_GELU_AMAX) wg_atomic_max(am, e.out_amax, amax_lds, WM * WN);
 #undef TEL_GEMM_FETCH
 #undef TEL_GEMM_STASH
 }
@@ -369,7 +391,8 @@ template <int EPI, typename T, typename TR, typename TO, int TM, int TN, typenam
           int FM>
 __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* smem,
                                               const EpiArgs<T, TR, TO>& e, int m0, int n0,
-                                              int wm, int wn, int wave, int lane) {
+                                              int wm, int wn, int wave, int lane,
+                                              unsigned int* amax_lds = nullptr, int nw = 0) {
   const int M = e.M, N = e.N;
   const int lr = lane & 15, lg = lane >> 4;
   constexpr int LDC = TN + 4;                       // floats per staged epilogue row
@@ -406,6 +429,7 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
   constexpr bool IS_I8 = std::is_same<T, int8_t>::value;
   constexpr bool HAS_R = EPI == EPI_BIAS_RESID || EPI == EPI_SWIN_SCATTER;
   float bb[8], dd[8];
+  float am = 0.f;   // EPI_BIAS_GELU_AMAX: this lane's max-abs of its stored outputs
 #pragma unroll
   for (int i = 0; i < 8; ++i) bb[i] = dd[i] = 0.f;
   if constexpr (EPI != EPI_RAW_I32 && EPI != EPI_PARTIAL) {
@@ -452,7 +476,7 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
       v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
       v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
       if (full8) {
-        epilogue_apply8<EPI, T, TR, TO>(e, m, n, v, bb, dd, rv[q]);
+        am = fmaxf(am, epilogue_apply8<EPI, T, TR, TO>(e, m, n, v, bb, dd, rv[q]));
       } else {   // ragged N (N % 8 == 4) or head_dim % 8 == 4: two 4-column stores
         ACC lo, hi;
 #pragma unroll
@@ -465,11 +489,12 @@ __device__ __forceinline__ void pipe_epilogue(const ACC (&acc)[FN][FM], char* sm
             hi[i] = v[4 + i];
           }
         }
-        epilogue_store<EPI, T, TR, TO>(e, m, n, lo);
-        if (n + 4 < N) epilogue_store<EPI, T, TR, TO>(e, m, n + 4, hi);
+        am = fmaxf(am, epilogue_store<EPI, T, TR, TO>(e, m, n, lo));
+        if (n + 4 < N) am = fmaxf(am, epilogue_store<EPI, T, TR, TO>(e, m, n + 4, hi));
       }
     }
   }
+  if constexpr (EPI == EPI_BIAS_GELU_AMAX) wg_atomic_max(am, e.out_amax, amax_lds, nw);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int S, int EPI, typename TR, typename TO>
@@ -497,6 +522,14 @@ __global__ __launch_bounds__((WM * WN + DENSE_PRODUCERS) * 64) void gemm_nt_pipe
   constexpr int LDC = TN + 4;                       // floats per staged epilogue row
   constexpr int STAGED = TM * LDC * 4 * NW;         // epilogue staging bytes
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE > STAGED ? S * STAGE : STAGED];
+  __shared__ unsigned int amax_lds[2];   // EPI_BIAS_GELU_AMAX: workgroup max-abs, counter
+  if constexpr (EPI == EPI_BIAS_GELU_AMAX) {
+    // compute wavefront 0 clears them; every wavefront passes the first barrier after this
+    if (threadIdx.x == 0) {
+      amax_lds[0] = amax_lds[1] = 0u;
+      wait_lgkmcnt0();
+    }
+  }
 
   const int M = e.M, N = e.N;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -580,6 +613,7 @@ __global__ __launch_bounds__((WM * WN + DENSE_PRODUCERS) * 64) void gemm_nt_pipe
   // flight there would make the compiler wait for every LDS read before each MFMA block.
   asm volatile("" ::"s"(e.bias), "s"(e.resid), "s"(e.C), "s"(e.N), "s"(e.M), "s"(e.heads),
                "s"(e.dq), "s"(e.qinv), "s"(e.dyn_amax));
+  if constexpr (EPI == EPI_BIAS_GELU_AMAX) asm volatile("" ::"s"(e.out_amax));
   if constexpr (EPI == EPI_SWIN_SCATTER)
     asm volatile("" ::"s"(e.geom.Hs), "s"(e.geom.Ws), "s"(e.geom.M), "s"(e.geom.s),
                  "s"(e.geom.nWx), "s"(e.geom.nW), "s"(e.geom.N));
@@ -611,7 +645,7 @@ __global__ __launch_bounds__((WM * WN + DENSE_PRODUCERS) * 64) void gemm_nt_pipe
   }
 #undef TEL_PIPE_FRAGS
 
-  pipe_epilogue<EPI, T, TR, TO, TM, TN>(acc, smem, e, m0, n0, wm, wn, wave, lane);
+  pipe_epilogue<EPI, T, TR, TO, TM, TN>(acc, smem, e, m0, n0, wm, wn, wave, lane, amax_lds, NW);
 }
 
 // ------------------------------------------------------------------ 2:4 sparse weights
@@ -1203,6 +1237,7 @@ static void launch_one(const GemmArgs& a, hipStream_t stream) {
   constexpr int BK = 128 / sizeof(T);   // 128-byte k slices
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
   e.dyn_amax = a.dyn_amax;
+  e.out_amax = a.out_amax;
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   gemm_nt_kernel<T, BM, BN, BK, WM, WN, EPI, TR, TO><<<grid, WM * WN * 64, 0, stream>>>(
       (const T*)a.A, (const T*)a.W, a.K, e);
@@ -1234,6 +1269,7 @@ static void launch_pipe(const GemmArgs& a, hipStream_t stream) {
   constexpr PipeCfg c = PIPE_CFGS[C];
   EpiArgs<T, TR, TO> e{a.bias, (const TR*)a.resid, (TO*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, a.geom};
   e.dyn_amax = a.dyn_amax;
+  e.out_amax = a.out_amax;
   const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
   const int grid = tm * tn * a.splits;
   gemm_nt_pipe_kernel<T, c.bm, c.bn, c.wm, c.wn, c.s, EPI, TR, TO>
@@ -1358,6 +1394,10 @@ static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
     case EPI_BIAS_GELU:
       if (a.out_i8) launch_cfg<T, EPI_BIAS_GELU, f16, int8_t>(cfg, a, stream);
       else launch_cfg<T, EPI_BIAS_GELU, f16, f16>(cfg, a, stream);
+      break;
+    case EPI_BIAS_GELU_AMAX:
+      if (!a.out_amax || a.out_i8) return hipErrorInvalidValue;
+      launch_cfg<T, EPI_BIAS_GELU_AMAX, f16, f16>(cfg, a, stream);
       break;
     case EPI_RAW_I32: launch_cfg<T, EPI_RAW_I32, f16, int32_t>(cfg, a, stream); break;
     case EPI_PARTIAL: launch_cfg<T, EPI_PARTIAL, f16, int32_t>(cfg, a, stream); break;

@@ -15,7 +15,9 @@ enum Epi {
   EPI_PARTIAL = 6,       // raw 32-bit accumulators (float32, or int32 for int8 operands) of
                          // k-split s at C + s * M * N, or those sums rounded to fp16
                          // (GemmArgs::part16, fp16 operands); a reduce kernel finishes the sum
-  EPI_PLAIN = 7          // C = A W^T in the storage type, no bias (skinny kernel only)
+  EPI_PLAIN = 7,         // C = A W^T in the storage type, no bias (skinny kernel only)
+  EPI_BIAS_GELU_AMAX = 8 // int8 operands, fp16 output: EPI_BIAS_GELU that also folds the
+                         // max-abs of its stored outputs into *out_amax (dynamic scales)
 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
@@ -65,6 +67,7 @@ struct GemmArgs {
   const float* qinv = nullptr;  // int8 output: device scalar 1 / scale (EPI_BIAS_GELU), or
                                 // three of them, for Q, K and V (EPI_QKV_SPLIT)
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU / EPI_QKV_SPLIT: int8 codes
+  float* out_amax = nullptr;    // EPI_BIAS_GELU_AMAX: atomic max of |stored output| (>= 0 before)
   SwinGeom geom{};              // EPI_SWIN_SCATTER
   int splits = 1;               // pipelined kernel only: K split over this many workgroups
   int part16 = 0;               // EPI_PARTIAL, fp16 operands: partial sums stored as fp16
@@ -100,11 +103,12 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16);
 bool attention_supported(int dtype, int head_dim);
 // ctxq != nullptr: write only the int8 codes of the stored-type output (scale *qinv);
 // psplit: P enters P V split into two 16-bit parts also for fp16 values (the int8 layers,
-// whose codes of the context are sensitive to P's rounding; always so for bf16 and codes)
+// whose codes of the context are sensitive to P's rounding; always so for bf16 and codes).
+// amax (context stored, no codes): atomic max of |stored context| into *amax (>= 0 before).
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
                             int8_t* ctxq = nullptr, const float* qinv = nullptr,
-                            bool psplit = false);
+                            bool psplit = false, float* amax = nullptr);
 
 // attention_int8.hip: attention on int8 Q, K, V codes ([3][heads][T][D]); scales (device):
 // [0] = s_q s_k / sqrt(D) * log2 e, [1] = s_v, [2] = 1 / (input scale of the O projection);
@@ -136,6 +140,11 @@ hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y,
 hipError_t launch_layernorm_gather(int dtype, const void* x, void* y, const float* gamma,
                                    const float* beta, int rows, int width, float eps,
                                    const SwinGeom& geom, hipStream_t stream);
+// fp16 LayerNorm that also folds the max-abs of its (fp16-rounded) output into *amax
+// (atomic max; *amax must hold a non-negative value, e.g. 0, beforehand).
+hipError_t launch_layernorm_amax(const void* x, void* y, float* amax, const float* gamma,
+                                 const float* beta, int rows, int width, float eps,
+                                 hipStream_t stream);
 // fp16 LayerNorm that also writes the int8 codes of its (fp16-rounded) output.
 hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* qinv,
                                const float* gamma, const float* beta, int rows, int width,

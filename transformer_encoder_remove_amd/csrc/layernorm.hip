@@ -47,7 +47,13 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
 // from the stored (TO-rounded) value: code = clamp(rne(float(y) * inv), -127, 127).
 // GATHER: output row r reads input row geom.src_row(r) (the shifted-window partition:
 // LayerNorm, cyclic shift and window partition in one pass).
-template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false, bool GATHER = false>
+// AMAX: also *amax = max(*amax, max |y|) over the stored (TO-rounded) outputs, the
+// statistic of a dynamically scaled int8 GEMM that reads y: reduced over the workgroup
+// through LDS, then one atomic max per workgroup (non-negative floats order like their
+// bit patterns, so the unsigned atomic is exact and order-independent). Rows past the end
+// then compute on the last row instead of leaving, so that every lane reaches the barrier.
+template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false, bool GATHER = false,
+          bool AMAX = false>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restrict__ x,
                                                                TO* __restrict__ y,
                                                                float* __restrict__ y32,
@@ -56,11 +62,18 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
                                                                int rows, float eps,
                                                                int8_t* __restrict__ yq = nullptr,
                                                                const float* __restrict__ qinv = nullptr,
-                                                               SwinGeom geom = SwinGeom{}) {
+                                                               SwinGeom geom = SwinGeom{},
+                                                               float* __restrict__ amax = nullptr) {
   constexpr int H = G * NV * 8;
-  const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
+  int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
-  if (row >= rows) return;   // whole G-lane groups leave together
+  const bool live = row < rows;
+  if constexpr (AMAX) {
+    row = live ? row : rows - 1;
+  } else {
+    if (!live) return;   // whole G-lane groups leave together
+  }
+  float ymax = 0.f;
   const TI* xr = x + (size_t)(GATHER ? geom.src_row(row) : row) * H;
   float v[NV][8];
   float s = 0.f;
@@ -93,7 +106,13 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
       o[e + 2] = v[k][e + 2] * rstd * g.z + b.z;
       o[e + 3] = v[k][e + 3] * rstd * g.w + b.w;
     }
-    store8(y + (size_t)row * H + c0, o);
+    if constexpr (AMAX) {
+      if (live) store8(y + (size_t)row * H + c0, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ymax = fmaxf(ymax, fabsf(to_f32(from_f32<TO>(o[e]))));
+    } else {
+      store8(y + (size_t)row * H + c0, o);
+    }
     if constexpr (COPY) store8(y32 + (size_t)row * H + c0, o);
     if constexpr (Q8) {
       const float inv = *qinv;
@@ -106,6 +125,18 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
       uint2 packed;
       __builtin_memcpy(&packed, c, 8);
       *reinterpret_cast<uint2*>(yq + (size_t)row * H + c0) = packed;
+    }
+  }
+  if constexpr (AMAX) {
+    __shared__ float wave_max[LN_THREADS / 64];
+    ymax = group_max<64>(live ? ymax : 0.f);
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = ymax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = wave_max[0];
+#pragma unroll
+      for (int w = 1; w < LN_THREADS / 64; ++w) m = fmaxf(m, wave_max[w]);
+      atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
     }
   }
 }
@@ -274,6 +305,7 @@ struct LnArgs {
   int8_t* yq = nullptr;
   const float* qinv = nullptr;
   const SwinGeom* geom = nullptr;
+  float* amax = nullptr;
 };
 
 template <typename TI, typename TO, bool COPY, int G, int NV>
@@ -284,6 +316,15 @@ static void run_ln(const LnArgs& a, hipStream_t s) {
       layernorm_kernel<TI, TO, COPY, G, NV, false, true>
           <<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>((const TI*)a.x, (TO*)a.y, a.y32, a.g, a.b,
                                                           a.rows, a.eps, nullptr, nullptr, *a.geom);
+    }
+    return;
+  }
+  if (a.amax) {
+    if constexpr (std::is_same<TI, f16>::value && std::is_same<TO, f16>::value && !COPY) {
+      layernorm_kernel<TI, TO, COPY, G, NV, false, false, true>
+          <<<(a.rows + RPB - 1) / RPB, LN_THREADS, 0, s>>>((const TI*)a.x, (TO*)a.y, a.y32, a.g,
+                                                          a.b, a.rows, a.eps, nullptr, nullptr,
+                                                          SwinGeom{}, a.amax);
     }
     return;
   }
@@ -360,6 +401,18 @@ hipError_t launch_layernorm_gather(int dtype, const void* x, void* y, const floa
     case DT_F32: ok = run_ln_g<float, float, false>(G, nv, a, stream); break;
   }
   if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_amax(const void* x, void* y, float* amax, const float* gamma,
+                                 const float* beta, int rows, int width, float eps,
+                                 hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  int G, nv;
+  if (!pick_ln(width, &G, &nv) || !amax) return hipErrorInvalidValue;
+  LnArgs a{x, y, nullptr, gamma, beta, rows, eps};
+  a.amax = amax;
+  if (!run_ln_g<f16, f16, false>(G, nv, a, stream)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
