@@ -150,8 +150,10 @@ __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, si
 hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   if ((uintptr_t)x & 15u) return hipErrorInvalidValue;   // 16-byte vector loads
+  // one workgroup per compute unit at most: atomics to the one address serialise (a few
+  // ns each), so fewer, longer workgroups finish sooner than one per 4 KiB of input
   size_t blocks = (n * dtype_size(dtype) / 16 + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
+  if (blocks > 256) blocks = 256;
   if (blocks == 0) blocks = 1;
   switch (dtype) {
     case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out); break;
