@@ -12,9 +12,12 @@
 // codes of that fp16 value at the O projection's input scale.
 //
 // Input: Q, K, V codes head-split as [3][heads][T][D] int8 (the int8 QKV epilogue's layout).
-// Workgroup = 4 wavefronts = 64 queries of one (sequence, head); grid = (ceil(max_len / 64),
-// heads, batch). Per 64-key block, K [64][D] and V^T [D][64] are staged in LDS; a sequence of up
-// to 128 keys has both blocks staged at once and its scores kept in registers (one pass). Each
+// Workgroup = QB / 16 wavefronts = QB queries of one (sequence, head), QB = 128 up to head_dim
+// 64 and 64 above (8 or 4 wavefronts; each staged K/V block serves all of them); grid =
+// (ceil(max_len / QB), heads, batch); wavefronts whose queries all lie past the sequence end
+// stage K/V and meet every barrier but skip the arithmetic. Per 64-key block, K [64][D] and
+// V^T [D][64] are staged in LDS; a sequence of up to 128 keys has both blocks staged at once
+// and its scores kept in registers (one pass). Each
 // wavefront computes S^T = K Q^T for its 16 queries, so a lane holds the scores of one query
 // for 16 keys (keys 16 j + 4 lg + i, j, i = 0..3). For P V the MFMA k index e of lane group lg
 // is mapped to key 16 (e / 4) + 4 lg + e % 4, the keys that lane already holds, so its 16 P
@@ -27,7 +30,8 @@
 
 namespace tel {
 
-constexpr int A8_QB = 64, A8_KB = 64;
+constexpr int A8_KB = 64;
+template <int D> constexpr int a8_qb() { return D <= 64 ? 128 : 64; }
 
 // LDS column of key `key` (0..63) in the permuted V^T rows: lane group g = (key % 16) / 4
 // reads columns 16 g .. 16 g + 15, holding keys 4 g + 16 jj + i at column 16 g + 4 jj + i.
@@ -35,8 +39,8 @@ __device__ __forceinline__ int a8_vcol(int key) {
   return ((key & 15) >> 2) * 16 + (key >> 4) * 4 + (key & 3);
 }
 
-template <int D, bool CODES>
-__global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict__ qkv,
+template <int D, bool CODES, int QB = a8_qb<D>()>
+__global__ __launch_bounds__(QB * 4) void attn_int8_kernel(const int8_t* __restrict__ qkv,
                                                         void* __restrict__ out,
                                                         const int32_t* __restrict__ cu,
                                                         int total_tokens, int heads,
@@ -54,7 +58,8 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int start = cu[b], L = cu[b + 1] - start;
-  const int q0 = blockIdx.x * A8_QB;
+  constexpr int NT = QB * 4;                        // threads
+  const int q0 = blockIdx.x * QB;
   if (q0 >= L) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -66,29 +71,30 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
 
   const int qi = q0 + wave * 16 + lr;
   const int qc = min(qi, L - 1);
+  const bool wave_on = q0 + wave * 16 < L;          // some query of this wavefront is valid
   frag qf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const int d0 = s * 64 + lg * 16;
     qf[s] = d0 < D ? *reinterpret_cast<const frag*>(Qh + (size_t)qc * D + d0) : frag{};
   }
-  // K (and V) of a 64-key block: 16-byte vectors, thread tid owns vectors tid + 256 p;
+  // K (and V) of a 64-key block: 16-byte vectors, thread tid owns vectors tid + NT p;
   // rows past the sequence end are clamped to its last key (their scores are masked)
-  constexpr int VPR = D / 16, NVEC = A8_KB * VPR, PER = (NVEC + 255) / 256;
+  constexpr int VPR = D / 16, NVEC = A8_KB * VPR, PER = (NVEC + NT - 1) / NT;
   // stage key block kb0 into LDS block slot `slot` (K rows slot * 64.., V^T columns slot * 64..)
   auto stage_k = [&](int kb0, int slot) {
     int8_t* dK = sK + slot * A8_KB * LDK;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p;
-      if (NVEC % 256 == 0 || idx < NVEC) {
+      const int idx = tid + NT * p;
+      if (NVEC % NT == 0 || idx < NVEC) {
         const int r = idx / VPR, c = idx - r * VPR;
         *reinterpret_cast<u32x4*>(&dK[r * LDK + c * 16]) =
             *reinterpret_cast<const u32x4*>(Kh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
       }
     }
     if constexpr (D < 64) {   // zero the k padding of the rows once per block
-      for (int r = tid; r < A8_KB; r += 256)
+      for (int r = tid; r < A8_KB; r += NT)
 #pragma unroll
         for (int c = D; c < 64; c += 16)
           *reinterpret_cast<u32x4*>(&dK[r * LDK + c]) = u32x4{0u, 0u, 0u, 0u};
@@ -97,8 +103,8 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
   auto stage_v = [&](int kb0, int slot) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p;
-      if (NVEC % 256 == 0 || idx < NVEC) {
+      const int idx = tid + NT * p;
+      if (NVEC % NT == 0 || idx < NVEC) {
         const int r = idx / VPR, c = idx - r * VPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(Vh + (size_t)min(kb0 + r, L - 1) * D + c * 16);
         int8_t e[16];
@@ -170,26 +176,30 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
       stage_v(A8_KB, 1);
     }
     __syncthreads();
-    float t0[4][4], t1[4][4];
-    scores(0, 0, t0);
-    m = row_max(t0, m);
-    if (two) {
-      scores(A8_KB, 1, t1);
-      m = row_max(t1, m);
+    if (wave_on) {
+      float t0[4][4], t1[4][4];
+      scores(0, 0, t0);
+      m = row_max(t0, m);
+      if (two) {
+        scores(A8_KB, 1, t1);
+        m = row_max(t1, m);
+      }
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      pv(t0, m, 0);
+      if (two) pv(t1, m, 1);
     }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    pv(t0, m, 0);
-    if (two) pv(t1, m, 1);
   } else {
     // pass 1: the exact row maximum over all keys of the sequence
     for (int kb0 = 0; kb0 < L; kb0 += A8_KB) {
       __syncthreads();
       stage_k(kb0, 0);
       __syncthreads();
-      float t[4][4];
-      scores(kb0, 0, t);
-      m = row_max(t, m);
+      if (wave_on) {
+        float t[4][4];
+        scores(kb0, 0, t);
+        m = row_max(t, m);
+      }
     }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
@@ -199,9 +209,11 @@ __global__ __launch_bounds__(256) void attn_int8_kernel(const int8_t* __restrict
       stage_k(kb0, 0);
       stage_v(kb0, 0);
       __syncthreads();
-      float t[4][4];
-      scores(kb0, 0, t);
-      pv(t, m, 0);
+      if (wave_on) {
+        float t[4][4];
+        scores(kb0, 0, t);
+        pv(t, m, 0);
+      }
     }
   }
   lsum += __shfl_xor(lsum, 16, 64);
@@ -241,11 +253,12 @@ bool attention_int8_supported(int head_dim) {
 template <int D>
 static void run_attn8(const int8_t* qkv, void* out, bool codes, const int32_t* cu, int batch,
                       int total, int max_len, int heads, const float* scales, hipStream_t st) {
-  const dim3 grid((max_len + A8_QB - 1) / A8_QB, heads, batch);
+  constexpr int QB = a8_qb<D>();
+  const dim3 grid((max_len + QB - 1) / QB, heads, batch);
   if (codes)
-    attn_int8_kernel<D, true><<<grid, 256, 0, st>>>(qkv, out, cu, total, heads, scales);
+    attn_int8_kernel<D, true><<<grid, QB * 4, 0, st>>>(qkv, out, cu, total, heads, scales);
   else
-    attn_int8_kernel<D, false><<<grid, 256, 0, st>>>(qkv, out, cu, total, heads, scales);
+    attn_int8_kernel<D, false><<<grid, QB * 4, 0, st>>>(qkv, out, cu, total, heads, scales);
 }
 
 hipError_t launch_attention_int8(const int8_t* qkv, void* out, int out_codes, const int32_t* cu,
