@@ -252,10 +252,11 @@ typedef struct {
 /* tel_window_attention_forward flag for per-kernel measurement: run stage k alone, reading and
  * writing the workspace buffers exactly as the whole block does (k = 0: LN1 + shift + window
  * partition + QKV; 1: window attention; 2: proj + window reverse + unshift + residual; 3: LN2 +
- * fc1 + GELU; 4: fc2 + residual, which writes y). Stage k reads what stages < k wrote into the
- * same workspace, so a whole-block call on that workspace must come first; running the five
- * stages in order equals one whole-block call. Not combinable with TEL_SWIN_ATTN_ONLY
- * (TEL_EINVAL). */
+ * fc1 + GELU; 4: fc2 + residual, which writes y; where tel_swin_mlp_fused says so, stage 3 is
+ * the whole MLP half, fc2 + residual included, and writes y, and stage 4 does nothing). Stage k
+ * reads what stages < k wrote into the same workspace, so a whole-block call on that workspace
+ * must come first; running the five stages in order equals one whole-block call. Not
+ * combinable with TEL_SWIN_ATTN_ONLY (TEL_EINVAL). */
 #define TEL_SWIN_ONE_STAGE(k) (((k) + 1) << 8)
 
 size_t tel_swin_packed_size(const tel_swin_desc* desc);
@@ -265,6 +266,11 @@ size_t tel_swin_packed_size(const tel_swin_desc* desc);
 int tel_swin_prepare(const tel_swin_desc* desc, const tel_swin_weights* w, void* packed,
                      size_t packed_bytes, void* stream);
 size_t tel_swin_workspace_size(const tel_swin_desc* desc);
+/* [host] 1 when the block runs its MLP half (LN2, fc1 + bias + GELU, fc2 + bias + residual;
+ * the Swin talk "大規模なビジュアル モデル…", section 3, fuses each of these) as one kernel
+ * whose hidden activations never reach memory: fp16, channels 96, mlp_hidden 384 (Swin-T
+ * stage 1). 0 otherwise, or for an unsupported descriptor. No device work. */
+int tel_swin_mlp_fused(const tel_swin_desc* desc);
 /* The block on x -> y (flags 0), or the attention half only (TEL_SWIN_ATTN_ONLY).
  * Workspace: 256-byte aligned, >= tel_swin_workspace_size bytes. x and y must differ. */
 int tel_window_attention_forward(const tel_swin_desc* desc, const void* packed, const void* x,

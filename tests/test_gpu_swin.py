@@ -98,7 +98,8 @@ def test_swin_t_stage1_sampled_images(variant):
 def test_one_stage_flags_compose_to_the_block(shape):
     """TEL_SWIN_ONE_STAGE(k) for k = 0..4 in order, on a fresh workspace, gives the whole
     block's output bit for bit (the per-kernel timings of the benchmark run the stages this
-    way); and one stage re-run on the workspace a whole block left behind reproduces it."""
+    way); and the stage that writes y, re-run on the workspace a whole block left behind,
+    reproduces it."""
     cfg = dict(shape, dtype="f16", seed=7)
     x = ti.swin_input(cfg)
     w = ti.swin_block_weights(cfg, variant=True)
@@ -116,8 +117,11 @@ def test_one_stage_flags_compose_to_the_block(shape):
     ws2.fill_(0xFF)
     for k in range(5):
         tel.tel_window_attention_forward(desc, packed, xd, y_st, ws2, flags=tel.TEL_SWIN_ONE_STAGE(k))
+    # the stage that writes y: fc2 + residual, or the fused MLP half (stage 4 then empty)
+    last = 3 if tel.tel_swin_mlp_fused(desc) else 4
     y_re = torch.full_like(xd, float("nan"))
-    tel.tel_window_attention_forward(desc, packed, xd, y_re, ws, flags=tel.TEL_SWIN_ONE_STAGE(4))
+    tel.tel_window_attention_forward(desc, packed, xd, y_re, ws,
+                                     flags=tel.TEL_SWIN_ONE_STAGE(last))
     torch.cuda.synchronize()
     assert torch.equal(y_st.view(torch.int16), y_full.view(torch.int16))
     assert torch.equal(y_re.view(torch.int16), y_full.view(torch.int16))

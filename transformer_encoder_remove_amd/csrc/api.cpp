@@ -1115,6 +1115,13 @@ int tel_swin_prepare(const tel_swin_desc* d, const tel_swin_weights* w, void* pa
   return TEL_OK;
 }
 
+int tel_swin_mlp_fused(const tel_swin_desc* d) {
+  if (swin_supported(d) != TEL_OK) return 0;
+  return gemm_rows_supported(d->dtype, 3 * d->channels, d->channels) &&
+         gemm_rows_supported(d->dtype, d->mlp_hidden, d->channels) &&
+         swin_mlp_supported(d->dtype, d->channels, d->mlp_hidden);
+}
+
 size_t tel_swin_workspace_size(const tel_swin_desc* d) {
   if (swin_supported(d) != TEL_OK) return 0;
   return swin_ws(d).total;
@@ -1175,6 +1182,13 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
   a.geom = g;
   if (run(2)) TEL_TRY(launch_gemm(dt, a, st));
   if (flags & TEL_SWIN_ATTN_ONLY) return TEL_OK;
+  if (fuse_ln && swin_mlp_supported(dt, C, F)) {
+    // the MLP half in one kernel (stage 3); stage 4 has nothing left to do
+    if (run(3))
+      TEL_TRY(launch_swin_mlp(dt, x1, y, P + L.w_1, F32(L.b_1), P + L.w_2, F32(L.b_2),
+                              F32(L.ln2_g), F32(L.ln2_b), d->ln_eps, T, st));
+    return TEL_OK;
+  }
   // LN2 on fc1's input rows (or a LayerNorm kernel), fc1 + bias + GELU
   a = GemmArgs{EPI_BIAS_GELU, hh, P + L.w_1, F32(L.b_1), nullptr, f, T, F, C, nh};
   if (fuse_ln) {

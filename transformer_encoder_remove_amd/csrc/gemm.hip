@@ -1179,6 +1179,147 @@ static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
 #undef TEL_ROWS_LN
 }
 
+// ------------------------------------------------------------------ fused MLP
+// The shifted-window block's MLP half in one pass over the tokens (the Swin talk "大規模な
+// ビジュアル モデル…", section 3: LayerNorm, fc1 + bias + GELU and fc2 + bias + residual
+// are each fused there; here they are one kernel):
+//   y[m] = x1[m] + W2 GELU(W1 LN2(x1[m]) + b1) + b2,  C = 96 channels, hidden 384.
+// Both weight matrices sit in LDS for the whole (persistent) workgroup, each wavefront takes
+// 16 token rows at a time, and fc1's outputs, GELU applied and rounded to the storage type
+// (as the separate fc1 kernel stores them), stay in registers as fc2's MFMA operand: the 384
+// hidden values per token never reach memory (2 x 384 x 2 bytes per token of HBM traffic
+// saved against fc1 and fc2 as two kernels).
+//
+// fc1 leaves lane (lr, lg) with hidden columns 16 i + 4 lg + q (q = 0..3) of its token row
+// lr, for each 16-column block i. fc2's k-step s (32 hidden columns) takes the lane's own
+// values of blocks 2 s and 2 s + 1 as its B fragment as they stand: MFMA k index 8 lg + e of
+// the step is hidden column 32 s + 4 lg + e for e < 4 and 32 s + 16 + 4 lg + (e - 4) for
+// e >= 4. W2 is staged in LDS with its columns in that order (whole groups of 4 move), so
+// its A fragment is one 16-byte read, and the product is the plain sum over all 384 columns.
+constexpr int MLP_C = 96, MLP_F = 384;
+constexpr int MLP_LDW1 = MLP_C + 8, MLP_LDW2 = MLP_F + 8;   // fp16 per staged row
+
+__device__ __forceinline__ int mlp_w2_col(int k) {   // LDS column of hidden column k
+  const int s = k >> 5, r = k & 31;
+  return s * 32 + (r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + (r & 3));
+}
+
+template <typename T, int NTH>
+__global__ __launch_bounds__(NTH) void swin_mlp_kernel(const T* __restrict__ X1, T* __restrict__ Y,
+                                                       const T* __restrict__ W1,
+                                                       const float* __restrict__ b1,
+                                                       const T* __restrict__ W2,
+                                                       const float* __restrict__ b2,
+                                                       const float* __restrict__ ln_g,
+                                                       const float* __restrict__ ln_b,
+                                                       float ln_eps, int M) {
+  using MF = Mfma<T>;
+  typedef typename MF::frag frag;
+  constexpr int KS1 = MLP_C / 32, NF1 = MLP_F / 16, KS2 = MLP_F / 32, NF2 = MLP_C / 16;
+  constexpr int NW = NTH / 64;
+  __shared__ __attribute__((aligned(16))) T sW1[MLP_F * MLP_LDW1];
+  __shared__ __attribute__((aligned(16))) T sW2[MLP_C * MLP_LDW2];
+  __shared__ __attribute__((aligned(16))) float sB1[MLP_F];
+  __shared__ __attribute__((aligned(16))) float sG[MLP_C];
+  __shared__ __attribute__((aligned(16))) float sB[MLP_C];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int idx = tid; idx < MLP_F * (MLP_C / 8); idx += NTH) {   // W1 rows, 16-byte vectors
+    const int r = idx / (MLP_C / 8), c = idx - r * (MLP_C / 8);
+    *reinterpret_cast<u32x4*>(sW1 + r * MLP_LDW1 + c * 8) =
+        *reinterpret_cast<const u32x4*>(W1 + (size_t)r * MLP_C + c * 8);
+  }
+  for (int idx = tid; idx < MLP_C * (MLP_F / 4); idx += NTH) {   // W2, permuted groups of 4
+    const int r = idx / (MLP_F / 4), g4 = idx - r * (MLP_F / 4);
+    *reinterpret_cast<u32x2*>(sW2 + r * MLP_LDW2 + mlp_w2_col(4 * g4)) =
+        *reinterpret_cast<const u32x2*>(W2 + (size_t)r * MLP_F + 4 * g4);
+  }
+  for (int k = tid; k < MLP_F; k += NTH) sB1[k] = b1[k];
+  for (int k = tid; k < MLP_C; k += NTH) {
+    sG[k] = ln_g[k];
+    sB[k] = ln_b[k];
+  }
+  __syncthreads();
+  // LN2's gamma / beta from LDS (lanes of one lg read the same words: broadcasts), which
+  // leaves the registers for a third wavefront per SIMD
+  auto gb = [&](int t, int j, float& g, float& b) {
+    g = sG[t * 32 + lg * 8 + j];
+    b = sB[t * 32 + lg * 8 + j];
+  };
+  EpiArgs<T, T, T> e{b2, X1, Y, M, MLP_C, 1, nullptr, nullptr, SwinGeom{}};
+  const int stride = gridDim.x * NW * 16;
+  for (int rb = (blockIdx.x * NW + wave) * 16; rb < M; rb += stride) {
+    frag a[KS1];
+    rows_load<T, KS1, ROWS_PLAIN>(a, X1, M, rb, lr, lg, e.geom);
+    rows_layernorm<T, KS1>(a, gb, ln_eps);
+    // fc1 + bias + GELU, 6 hidden blocks at a time, into fc2's B fragments
+    frag h[KS2];
+#pragma unroll
+    for (int g = 0; g < NF1 / 6; ++g) {
+      typename MF::acc acc[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) acc[i] = typename MF::acc{};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < KS1; ++t)
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const frag w = *reinterpret_cast<const frag*>(
+              sW1 + ((g * 6 + i) * 16 + lr) * MLP_LDW1 + t * 32 + lg * 8);
+          acc[i] = MF::mma(w, a[t], acc[i]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int blk = g * 6 + i;
+        const float4 bb = *reinterpret_cast<const float4*>(sB1 + blk * 16 + lg * 4);
+        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          h[blk >> 1][(blk & 1) * 4 + q] = from_f32<T>(gelu_erf(acc[i][q] + bv[q]));
+      }
+    }
+    // fc2 + bias + residual
+    typename MF::acc o[NF2];
+#pragma unroll
+    for (int i = 0; i < NF2; ++i) o[i] = typename MF::acc{};
+#pragma unroll
+    for (int s2 = 0; s2 < KS2; ++s2)
+#pragma unroll
+      for (int i = 0; i < NF2; ++i) {
+        const frag w = *reinterpret_cast<const frag*>(sW2 + (i * 16 + lr) * MLP_LDW2 + s2 * 32 +
+                                                      lg * 8);
+        o[i] = MF::mma(w, h[s2], o[i]);
+      }
+    const int m = rb + lr;
+    if (m < M) {
+#pragma unroll
+      for (int i = 0; i < NF2; ++i) epilogue_store<EPI_BIAS_RESID, T, T, T>(e, m, i * 16 + lg * 4, o[i]);
+    }
+  }
+}
+
+bool swin_mlp_supported(int dtype, int channels, int hidden) {
+  return dtype == DT_F16 && channels == MLP_C && hidden == MLP_F;
+}
+
+hipError_t launch_swin_mlp(int dtype, const void* x1, void* y, const void* w1, const float* b1,
+                           const void* w2, const float* b2, const float* ln_g, const float* ln_b,
+                           float eps, int M, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  constexpr int NTH = 768;   // 12 wavefronts: three per SIMD on the one workgroup per unit
+  const int blocks = (M + NTH / 4 - 1) / (NTH / 4);   // 16 rows per wavefront
+  const int grid = std::min(blocks, 256);              // one workgroup per compute unit (LDS)
+  switch (dtype) {
+    case DT_F16:
+      swin_mlp_kernel<f16, NTH><<<grid, NTH, 0, stream>>>((const f16*)x1, (f16*)y, (const f16*)w1,
+                                                          b1, (const f16*)w2, b2, ln_g, ln_b, eps, M);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool gemm_rows_supported(int dtype, int N, int K) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   return (N == 288 && K == 96) || (N == 96 && K == 96) || (N == 384 && K == 96) ||

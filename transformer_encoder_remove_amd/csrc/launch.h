@@ -89,6 +89,12 @@ struct GemmArgs {
 bool gemm_rows_supported(int dtype, int N, int K);
 // Patch merging of an image of `channels` channels runs on the skinny kernel (N = 2C, K = 4C).
 bool patch_merging_supported(int dtype, int channels);
+// The shifted-window block's MLP half fused (LN2, fc1 + bias + GELU, fc2 + bias + residual:
+// y = x1 + W2 GELU(W1 LN(x1) + b1) + b2), for channels 96 and hidden 384, fp16.
+bool swin_mlp_supported(int dtype, int channels, int hidden);
+hipError_t launch_swin_mlp(int dtype, const void* x1, void* y, const void* w1, const float* b1,
+                           const void* w2, const float* b2, const float* ln_g, const float* ln_b,
+                           float eps, int M, hipStream_t stream);
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t stream);
 // Explicit tile configuration: -1 = register-staged kernel, 0.. = pipelined tile table.
 hipError_t launch_gemm_cfg(int dtype, int cfg, const GemmArgs& a, hipStream_t stream);
