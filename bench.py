@@ -733,7 +733,13 @@ def bench_swin(args):
         "ln2_fc1_gelu": (3, el * (C + F), 2 * C * F),
         "fc2_resid": (4, el * (F + C + C), 2 * F * C),
     }
-    mlp_fused = tel.tel_swin_mlp_fused(desc)
+    fused = tel.tel_swin_fused_stages(desc)
+    mlp_fused = bool(fused & tel.TEL_SWIN_FUSED_MLP)
+    if fused & tel.TEL_SWIN_FUSED_ATTN:   # stage 0 is the whole attention half: x read, x1 written
+        for k in ("ln1_shift_partition_qkv", "window_attention", "proj_reverse_unshift_resid"):
+            del stages[k]
+        stages = {"attention_half": (0, el * (C + C), 2 * C * 3 * C + 4 * cfg["window"] ** 2 * C
+                                     + 2 * C * C), **stages}
     if mlp_fused:   # stage 3 is the whole MLP half (x1 read once, y written), stage 4 empty
         del stages["ln2_fc1_gelu"], stages["fc2_resid"]
         stages["ln2_mlp_resid"] = (3, el * (C + C), 4 * C * F)
@@ -751,9 +757,9 @@ def bench_swin(args):
         calibration_copy(stream)
     dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
     d = per_kernel[dom]
-    if dom == "ln2_mlp_resid":
-        # the fused MLP moves 2 x 96 x 2 bytes per token against 4 x 96 x 384 flops: far past
-        # the ridge point, so it is priced against the fp16 MFMA peak
+    if dom in ("ln2_mlp_resid", "attention_half"):
+        # a fused half moves 2 x 96 x 2 bytes per token against tens of kflops: far past the
+        # ridge point, so it is priced against the fp16 MFMA peak
         roofline = {"kernel": dom, "bound": "mfma",
                     "achieved": round(d["flops"] / d["us"] / 1e6, 2), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(d["flops"] / d["us"] / 1e6 / PEAK_FP16_TFLOPS, 4),
@@ -788,7 +794,7 @@ def bench_swin(args):
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights and bias table)",
         "config": {"workload": f"{args.workload}: shifted-window block, LN1 + shift + partition, "
                                "QKV, window attention (bias + mask), proj + unshift + residual, "
-                               "LN2, MLP" + (" (one kernel)" if mlp_fused else ""),
+                               "LN2, MLP" + (f" (fused stages {fused})" if fused else ""),
                    **{k: v for k, v in cfg.items() if k != "dtype"}},
         "roofline": roofline, "cpu_baseline": cpu, "step_ms": step_ms,
         "kernels_us": {k: round(v["us"], 3) for k, v in per_kernel.items()},

@@ -252,8 +252,9 @@ typedef struct {
 /* tel_window_attention_forward flag for per-kernel measurement: run stage k alone, reading and
  * writing the workspace buffers exactly as the whole block does (k = 0: LN1 + shift + window
  * partition + QKV; 1: window attention; 2: proj + window reverse + unshift + residual; 3: LN2 +
- * fc1 + GELU; 4: fc2 + residual, which writes y; where tel_swin_mlp_fused says so, stage 3 is
- * the whole MLP half, fc2 + residual included, and writes y, and stage 4 does nothing). Stage k
+ * fc1 + GELU; 4: fc2 + residual, which writes y; where tel_swin_fused_stages says so, stage 0
+ * is the whole attention half and writes X1 while stages 1 and 2 do nothing, and stage 3 is the
+ * whole MLP half and writes y while stage 4 does nothing). Stage k
  * reads what stages < k wrote into the same workspace, so a whole-block call on that workspace
  * must come first; running the five stages in order equals one whole-block call. Not
  * combinable with TEL_SWIN_ATTN_ONLY (TEL_EINVAL). */
@@ -266,11 +267,16 @@ size_t tel_swin_packed_size(const tel_swin_desc* desc);
 int tel_swin_prepare(const tel_swin_desc* desc, const tel_swin_weights* w, void* packed,
                      size_t packed_bytes, void* stream);
 size_t tel_swin_workspace_size(const tel_swin_desc* desc);
-/* [host] 1 when the block runs its MLP half (LN2, fc1 + bias + GELU, fc2 + bias + residual;
- * the Swin talk "大規模なビジュアル モデル…", section 3, fuses each of these) as one kernel
- * whose hidden activations never reach memory: fp16, channels 96, mlp_hidden 384 (Swin-T
- * stage 1). 0 otherwise, or for an unsupported descriptor. No device work. */
-int tel_swin_mlp_fused(const tel_swin_desc* desc);
+/* [host] Which halves of the block run as one kernel each (the Swin talk "大規模なビジュアル
+ * モデル…", section 3, fuses the steps within each half; here each half is one pass whose
+ * intermediates never reach memory): TEL_SWIN_FUSED_ATTN, the attention half (LN1 + shift +
+ * partition, QKV, window attention, proj + reverse + unshift + residual), for fp16, channels
+ * 96, 3 heads, windows of at most 64 tokens; TEL_SWIN_FUSED_MLP, the MLP half (LN2, fc1 + bias
+ * + GELU, fc2 + bias + residual), for fp16, channels 96, mlp_hidden 384 (Swin-T stage 1).
+ * 0 for an unsupported descriptor. No device work. */
+#define TEL_SWIN_FUSED_ATTN 1
+#define TEL_SWIN_FUSED_MLP 2
+int tel_swin_fused_stages(const tel_swin_desc* desc);
 /* The block on x -> y (flags 0), or the attention half only (TEL_SWIN_ATTN_ONLY).
  * Workspace: 256-byte aligned, >= tel_swin_workspace_size bytes. x and y must differ. */
 int tel_window_attention_forward(const tel_swin_desc* desc, const void* packed, const void* x,

@@ -118,7 +118,7 @@ def test_one_stage_flags_compose_to_the_block(shape):
     for k in range(5):
         tel.tel_window_attention_forward(desc, packed, xd, y_st, ws2, flags=tel.TEL_SWIN_ONE_STAGE(k))
     # the stage that writes y: fc2 + residual, or the fused MLP half (stage 4 then empty)
-    last = 3 if tel.tel_swin_mlp_fused(desc) else 4
+    last = 3 if tel.tel_swin_fused_stages(desc) & tel.TEL_SWIN_FUSED_MLP else 4
     y_re = torch.full_like(xd, float("nan"))
     tel.tel_window_attention_forward(desc, packed, xd, y_re, ws,
                                      flags=tel.TEL_SWIN_ONE_STAGE(last))

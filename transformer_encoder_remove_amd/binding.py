@@ -32,7 +32,7 @@ EXPORTS = (
     "tel_encoder_forward_workspace_size", "tel_encoder_forward", "tel_gemm",
     "tel_gemm_tile_configs", "tel_gemm_ex", "tel_attention_varlen", "tel_quantize_i8",
     "tel_quantize_weight_i8", "tel_gemm_i8_i32", "tel_layernorm", "tel_swin_packed_size",
-    "tel_swin_prepare", "tel_swin_workspace_size", "tel_swin_mlp_fused",
+    "tel_swin_prepare", "tel_swin_workspace_size", "tel_swin_fused_stages",
     "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
     "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
@@ -122,7 +122,7 @@ _SIG = {
     "tel_swin_prepare": (I, [ctypes.POINTER(tel_swin_desc), ctypes.POINTER(tel_swin_weights), P,
                              SZ, P]),
     "tel_swin_workspace_size": (SZ, [ctypes.POINTER(tel_swin_desc)]),
-    "tel_swin_mlp_fused": (I, [ctypes.POINTER(tel_swin_desc)]),
+    "tel_swin_fused_stages": (I, [ctypes.POINTER(tel_swin_desc)]),
     "tel_window_attention_forward": (I, [ctypes.POINTER(tel_swin_desc), P, P, P, I, P, SZ, P]),
     "tel_window_partition_layernorm": (I, [P, P, P, P, I, I, I, I, I, I, F, I, P]),
     "tel_gemm_partial": (I, [I, I, I, P, P, P, I, I, I, I, P]),
@@ -466,8 +466,13 @@ def tel_swin_workspace_size(desc) -> int:
     return lib.tel_swin_workspace_size(ctypes.byref(desc))
 
 
-def tel_swin_mlp_fused(desc) -> bool:
-    return bool(lib.tel_swin_mlp_fused(ctypes.byref(desc)))
+TEL_SWIN_FUSED_ATTN, TEL_SWIN_FUSED_MLP = 1, 2
+
+
+def tel_swin_fused_stages(desc) -> int:
+    """Bit mask: TEL_SWIN_FUSED_ATTN (stage 0 is the whole attention half, stages 1-2 empty),
+    TEL_SWIN_FUSED_MLP (stage 3 is the whole MLP half, stage 4 empty)."""
+    return lib.tel_swin_fused_stages(ctypes.byref(desc))
 
 
 def tel_swin_prepare(desc, weights: dict, packed, stream=None):

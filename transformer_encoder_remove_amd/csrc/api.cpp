@@ -493,6 +493,18 @@ SwinGeom swin_geom(const tel_swin_desc* d) {
   return g;
 }
 
+// Which halves of the block run as one kernel each (TEL_SWIN_FUSED_*): both need the
+// skinny-kernel shapes (C 96 here) in fp16; the attention half also 3 heads and windows of
+// at most 64 tokens.
+int swin_fused_stages(const tel_swin_desc* d) {
+  const int C = d->channels, F = d->mlp_hidden, dt = d->dtype;
+  if (!gemm_rows_supported(dt, 3 * C, C) || !gemm_rows_supported(dt, F, C)) return 0;
+  int f = 0;
+  if (swin_attn_half_supported(dt, C, d->heads, d->window * d->window)) f |= TEL_SWIN_FUSED_ATTN;
+  if (swin_mlp_supported(dt, C, F)) f |= TEL_SWIN_FUSED_MLP;
+  return f;
+}
+
 struct SwinLayout {
   size_t w_qkv, w_proj, w_1, w_2;
   size_t ln1_g, ln1_b, b_qkv, b_proj, ln2_g, ln2_b, b_1, b_2, bias;
@@ -1115,11 +1127,9 @@ int tel_swin_prepare(const tel_swin_desc* d, const tel_swin_weights* w, void* pa
   return TEL_OK;
 }
 
-int tel_swin_mlp_fused(const tel_swin_desc* d) {
+int tel_swin_fused_stages(const tel_swin_desc* d) {
   if (swin_supported(d) != TEL_OK) return 0;
-  return gemm_rows_supported(d->dtype, 3 * d->channels, d->channels) &&
-         gemm_rows_supported(d->dtype, d->mlp_hidden, d->channels) &&
-         swin_mlp_supported(d->dtype, d->channels, d->mlp_hidden);
+  return swin_fused_stages(d);
 }
 
 size_t tel_swin_workspace_size(const tel_swin_desc* d) {
@@ -1173,16 +1183,25 @@ int tel_window_attention_forward(const tel_swin_desc* d, const void* packed, con
     TEL_TRY(launch_layernorm_gather(dt, x, zw, F32(L.ln1_g), F32(L.ln1_b), T, C, d->ln_eps, g,
                                     st));
   }
-  if (run(0)) TEL_TRY(launch_gemm(dt, a, st));
-  if (run(1))
-    TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh,
-                                    st));
-  // proj + bias, window reverse + roll(+s) + residual in the epilogue
-  a = GemmArgs{EPI_SWIN_SCATTER, ctx, P + L.w_proj, F32(L.b_proj), x, x1, T, C, C, nh};
-  a.geom = g;
-  if (run(2)) TEL_TRY(launch_gemm(dt, a, st));
+  const int fused = swin_fused_stages(d);
+  if (fused & TEL_SWIN_FUSED_ATTN) {
+    // the attention half in one kernel (stage 0); stages 1 and 2 have nothing left to do
+    if (run(0))
+      TEL_TRY(launch_swin_attn_half(x, x1, P + L.w_qkv, F32(L.b_qkv), F32(L.bias),
+                                    P + L.w_proj, F32(L.b_proj), F32(L.ln1_g), F32(L.ln1_b),
+                                    d->ln_eps, g, d->batch * g.nW, st));
+  } else {
+    if (run(0)) TEL_TRY(launch_gemm(dt, a, st));
+    if (run(1))
+      TEL_TRY(launch_window_attention(dt, qkv, ctx, F32(L.bias), g, d->batch * g.nW, nh, C / nh,
+                                      st));
+    // proj + bias, window reverse + roll(+s) + residual in the epilogue
+    a = GemmArgs{EPI_SWIN_SCATTER, ctx, P + L.w_proj, F32(L.b_proj), x, x1, T, C, C, nh};
+    a.geom = g;
+    if (run(2)) TEL_TRY(launch_gemm(dt, a, st));
+  }
   if (flags & TEL_SWIN_ATTN_ONLY) return TEL_OK;
-  if (fuse_ln && swin_mlp_supported(dt, C, F)) {
+  if (fused & TEL_SWIN_FUSED_MLP) {
     // the MLP half in one kernel (stage 3); stage 4 has nothing left to do
     if (run(3))
       TEL_TRY(launch_swin_mlp(dt, x1, y, P + L.w_1, F32(L.b_1), P + L.w_2, F32(L.b_2),

@@ -89,6 +89,15 @@ struct GemmArgs {
 bool gemm_rows_supported(int dtype, int N, int K);
 // Patch merging of an image of `channels` channels runs on the skinny kernel (N = 2C, K = 4C).
 bool patch_merging_supported(int dtype, int channels);
+// The shifted-window block's attention half fused (LN1 + shift + partition, QKV, window
+// attention with the bias table and shift mask, proj + reverse + unshift + residual), for
+// fp16, channels 96, 3 heads and windows of up to 64 tokens; bias_exp as for
+// launch_window_attention.
+bool swin_attn_half_supported(int dtype, int channels, int heads, int window_tokens);
+hipError_t launch_swin_attn_half(const void* x, void* x1, const void* w_qkv, const float* b_qkv,
+                                 const float* bias_exp, const void* w_proj, const float* b_proj,
+                                 const float* ln_g, const float* ln_b, float eps,
+                                 const SwinGeom& geom, int windows, hipStream_t stream);
 // The shifted-window block's MLP half fused (LN2, fc1 + bias + GELU, fc2 + bias + residual:
 // y = x1 + W2 GELU(W1 LN(x1) + b1) + b2), for channels 96 and hidden 384, fp16.
 bool swin_mlp_supported(int dtype, int channels, int hidden);
