@@ -1,10 +1,7 @@
 """Every kernel the library builds runs without scratch memory (no register spills to
 memory, no private arrays), as the compiler reports it (-Rpass-analysis=
-kernel-resource-usage): scratch 0 and no vector-register spills. A scalar register that does
-not fit is parked in a lane of a vector register (v_writelane / v_readlane, no memory
-access); a few of those are allowed (the fused shifted-window attention half holds one). The
-build writes that report for each source; a source whose report is missing or older than the
-source is compiled here once more to get it. CPU only."""
+kernel-resource-usage). The build writes that report for each source; a source whose
+report is missing or older than the source is compiled here once more to get it. CPU only."""
 import importlib.util
 import json
 import os
@@ -44,7 +41,7 @@ def test_no_scratch_no_spills(src):
         assert kernels, f"no kernel reported for {src}"
     for k in kernels:
         assert k.get("scratch") == 0, (k["name"], k)
-        assert k.get("vgpr_spill") == 0 and k.get("sgpr_spill") <= 2, (k["name"], k)
+        assert k.get("vgpr_spill") == 0 and k.get("sgpr_spill") == 0, (k["name"], k)
 
 
 def test_parser_reads_the_remark_format():
