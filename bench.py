@@ -452,17 +452,18 @@ def main():
 
 
 # every kernel source: counters taken on other sources than the ones built now are stale
-# The source files each measured kernel is compiled from: its own .hip file and the two
-# headers every kernel includes. A counter record stays valid while these are unchanged.
-_HEADERS = ("device.h", "launch.h")
+# The source files each measured kernel is compiled from: its own .hip file and the shared
+# headers. A counter record stays valid while these are unchanged.
+_HEADERS = ("device.h", "launch.h", "rows.h")
 _KERNEL_FILE = {"attention": "attention.hip", "layernorm": "layernorm.hip",
                 "ln1_reduce": "layernorm.hip", "ln2_reduce": "layernorm.hip",
-                "window_attention": "swin.hip"}
+                "window_attention": "swin.hip", "attention_half": "swin_fused.hip",
+                "ln2_mlp_resid": "swin_fused.hip"}
 
 
 def kernel_sources(kernel: str) -> tuple:
     """Files (relative to the repository) whose text fixes the named kernel: the GEMM-based
-    ones (every gemm_* kernel and the shifted-window block's fused projections) come from
+    ones (every gemm_* kernel and the shifted-window block's skinny projections) come from
     gemm.hip."""
     own = _KERNEL_FILE.get(kernel, "gemm.hip")
     return tuple(os.path.join("transformer_encoder_remove_amd", "csrc", f)
