@@ -576,9 +576,9 @@ def summarise_traffic(fetch_dir: str, write_dir: str, table_path: str):
         "per-kernel timing does; counters per dispatch, averaged over the timed launches. "
         "bytes_per_launch = FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor (KiB), the "
         "factors being what a plain 256 MiB device copy reads on the same counters. "
-        "sources_sha256: SHA-256 of the kernel's own source file and the headers device.h and "
-        "launch.h (bench.py kernel_sources) when the counters were taken; bench.py reports a "
-        "figure only while it matches.")
+        "sources_sha256: SHA-256 of the kernel's own source file and the shared headers "
+        "device.h, launch.h and rows.h (bench.py kernel_sources) when the counters were taken; "
+        "bench.py reports a figure only while it matches.")
     out["calibration"] = {"copy": "__amd_rocclr_copyBuffer, 256 MiB device to device",
                           "fetch_size_kib": round(calib["FETCH_SIZE"], 1),
                           "write_size_kib": round(calib["WRITE_SIZE"], 1),
