@@ -435,6 +435,19 @@ int tel_layernorm(const void* x, void* y, const float* gamma, const float* beta,
  * returns the previous setting. Thread-safe. */
 int tel_graph_cache(int enable);
 
+/* Weight read-ahead of tel_encoder_forward (on by default; the environment variable
+ * TEL_PREFETCH=0 turns it off at load). For float stacks whose weights cannot all stay in
+ * the GPU's 256 MB memory-side cache and dominate what a layer reads (n_layers x packed size
+ * >= 160 MiB and packed size > 8 x the layer's activation bytes, e.g. a 24-layer BERT-large
+ * over 128 tokens), the two reduce-LayerNorm kernels of each k-split layer carry extra
+ * workgroups that read weights the next GEMMs use, once, so that those GEMMs find them
+ * cached: the layer's FFN weights after the output projection, the next layer's QKV and
+ * output-projection weights at the end of the layer. A scheduling aid of this library, not
+ * a step of the layer: same stream, no extra launch, and outputs bit-identical with and
+ * without. enable: 1 on, 0 off, -1 query only; returns the previous setting.
+ * Thread-safe. */
+int tel_weight_prefetch(int enable);
+
 /* Split-k GEMM without epilogue: the first half of a layer's output projection and FFN2,
  * whose add-bias + residual + LayerNorm epilogue ([SW] section 3, the fused
  * add-bias-residual-LayerNorm) tel_layernorm_reduce finishes.

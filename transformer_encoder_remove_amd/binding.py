@@ -35,7 +35,8 @@ EXPORTS = (
     "tel_swin_prepare", "tel_swin_workspace_size", "tel_swin_fused_stages",
     "tel_window_attention_forward",
     "tel_window_partition_layernorm", "tel_gemm_partial", "tel_gemm_partial_plan",
-    "tel_layernorm_reduce", "tel_graph_cache", "tel_gemm_i8", "tel_prune_2of4",
+    "tel_layernorm_reduce", "tel_graph_cache", "tel_weight_prefetch", "tel_gemm_i8",
+    "tel_prune_2of4",
     "tel_gemm_2of4_tile_configs", "tel_gemm_2of4", "tel_build_offsets_mask",
     "tel_rebuild_padding_mask", "tel_encoder_layer_forward_noalloc", "tel_patch_merging",
     "tel_attention_int8",
@@ -130,6 +131,7 @@ _SIG = {
                                   ctypes.POINTER(I)]),
     "tel_layernorm_reduce": (I, [P, I, I, P, P, P, I, P, I, P, P, P, P, P, I, I, F, I, P]),
     "tel_graph_cache": (I, [I]),
+    "tel_weight_prefetch": (I, [I]),
     "tel_gemm_i8": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, P]),
     "tel_prune_2of4": (I, [P, P, P, I, I, I, P]),
     "tel_gemm_2of4_tile_configs": (I, []),
@@ -404,6 +406,12 @@ def tel_graph_cache(enable: int = -1) -> int:
     """Turn tel_encoder_forward's graph cache on (1) or off (0); -1 queries. Returns the
     previous setting."""
     return lib.tel_graph_cache(enable)
+
+
+def tel_weight_prefetch(enable: int = -1) -> int:
+    """Turn tel_encoder_forward's weight read-ahead on (1) or off (0); -1 queries. Returns
+    the previous setting."""
+    return lib.tel_weight_prefetch(enable)
 
 
 def tel_gemm_partial_plan(dtype: int, M: int, N: int, K: int) -> tuple[int, int, int]:

@@ -390,8 +390,18 @@ int layer_forward_int8(const tel_encoder_desc* d, const char* P, const void* x, 
   return TEL_OK;
 }
 
+// Weights read ahead by extra workgroups of the layer's short kernels (see the weight
+// prefetch below): with `on`, FFN1's during the attention and FFN2's during the first
+// reduce-LayerNorm, and `next`'s QKV and output-projection weights (when not null) during
+// the second.
+struct LayerPrefetch {
+  bool on = false;
+  const char* next = nullptr;
+};
+
 int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void* y,
-                  const int32_t* cu, int batch, int T, int max_len, char* ws, hipStream_t st) {
+                  const int32_t* cu, int batch, int T, int max_len, char* ws, hipStream_t st,
+                  const LayerPrefetch& pf = LayerPrefetch()) {
   if (T == 0) return TEL_OK;
   if (d->int8_gemm) return layer_forward_int8(d, P, x, y, cu, batch, T, max_len, ws, st);
   const LayerLayout L = layer_layout(d);
@@ -418,7 +428,10 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
   g = GemmArgs{EPI_QKV_SPLIT, x, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.w_idx = IDX(L.wi_qkv);
   TEL_TRY(launch_gemm(dt, g, st));
-  TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st));
+  // with the read-ahead: FFN1's weights during the attention
+  TEL_TRY(launch_attention(dt, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, nullptr,
+                           nullptr, false, nullptr, pf.on ? P + L.w_1 : nullptr,
+                           pf.on ? L.w_2 - L.w_1 : 0));
   const int pre_dt = f32s ? (int)DT_F32 : dt;
   // output projection + bias + residual, then LayerNorm; split over k (float32 partials,
   // or fp16 ones for long-K fp16 shapes; bias + residual + LayerNorm in the reduce kernel)
@@ -431,6 +444,10 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
     LnReduceArgs r{part, sp_o, nullptr, F32(L.b_o), x, dt, h1, dt, h1f, nullptr, nullptr,
                    F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps, 0};
     r.part16 = p16_o;
+    if (pf.on) {   // FFN2's weights
+      r.prefetch = P + L.w_2;
+      r.prefetch_bytes = L.b_qkv - L.w_2;
+    }
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, ctx, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh, 0, f32s};
@@ -452,6 +469,10 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
     LnReduceArgs r{part, sp_2, nullptr, F32(L.b_2), res2, f32s ? (int)DT_F32 : dt, y, dt,
                    nullptr, nullptr, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H, d->ln_eps, 0};
     r.part16 = p16_2;
+    if (pf.next) {   // the next layer's QKV and output-projection weights
+      r.prefetch = pf.next + L.w_qkv;
+      r.prefetch_bytes = L.w_1 - L.w_qkv;
+    }
     TEL_TRY(launch_layernorm_reduce(r, st));
   } else {
     g = GemmArgs{EPI_BIAS_RESID, f, P + L.w_2, F32(L.b_2), res2, pre, T, H, F, nh, f32s, f32s};
@@ -782,12 +803,53 @@ size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* d, int batch, 
   return stack_ws(d, batch, max_seq).total;
 }
 
+// ------------------------------------------------------------------ weight prefetch
+// A deep stack at few tokens (BERT-large, 24 layers, one 128-token sequence: 25 MB of
+// weights per layer against 0.25 MB of activations) is bound by fetching weights: the
+// stack's 605 MB do not stay in the 256 MB memory-side cache between forwards, and each
+// GEMM pulls its weights from HBM through its few workgroups. There, the layer's short
+// kernels (using few compute units at these token counts) carry extra workgroups that read
+// weights a later GEMM needs, once, into that cache: the attention FFN1's, the first
+// reduce-LayerNorm (after the output projection) FFN2's, the second one (end of the layer)
+// the next layer's QKV and output-projection weights, about 8 MB each at BERT-large. Used
+// when the weights cannot all stay cached and dominate what a layer reads, and only on the
+// k-split path.
+namespace {
+constexpr size_t PREFETCH_MIN_STACK_BYTES = size_t(160) << 20;
+std::mutex g_prefetch_mu;
+int g_prefetch_on = -1;           // -1: read TEL_PREFETCH once (on unless it is "0")
+
+bool prefetch_on() {
+  std::lock_guard<std::mutex> lk(g_prefetch_mu);
+  if (g_prefetch_on < 0) {
+    const char* e = getenv("TEL_PREFETCH");
+    g_prefetch_on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return g_prefetch_on == 1;
+}
+
+bool prefetch_wanted(const tel_encoder_desc* d, int n_layers, int total_tokens) {
+  if (n_layers < 2 || total_tokens <= 0 || d->int8_gemm || d->sparse_2of4) return false;
+  const size_t packed = tel_encoder_packed_size(d);
+  if ((size_t)n_layers * packed < PREFETCH_MIN_STACK_BYTES) return false;
+  const size_t act = (size_t)total_tokens * d->hidden * dtype_size(d->dtype);
+  return act * 8 < packed && prefetch_on();
+}
+}  // namespace
+
+int tel_weight_prefetch(int enable) {
+  const int prev = prefetch_on() ? 1 : 0;
+  std::lock_guard<std::mutex> lk(g_prefetch_mu);
+  if (enable >= 0) g_prefetch_on = enable ? 1 : 0;
+  return prev;
+}
+
 // The whole forward (offsets, remove padding, layers, rebuild) enqueued on stream st;
 // arguments already validated.
 static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_layers,
                            int n_layers, const void* x_pad, void* y_pad,
-                           const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
-                           int max_len, void* workspace, hipStream_t st) {
+                          const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
+                          int max_len, void* workspace, hipStream_t st) {
   const StackWs S = stack_ws(d, batch, max_seq);
   // the layer workspace is laid out for batch * max_seq tokens; a layer at total_tokens
   // (<= batch * max_seq) re-derives its offsets from its own token count and must fit
@@ -808,6 +870,7 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
   int8_t* qa = (int8_t*)(ws + S.qa);
   int8_t* qb = (int8_t*)(ws + S.qb);
   const size_t act_off = d->int8_gemm ? layer_layout(d).act : 0;
+  const bool pf = prefetch_wanted(d, n_layers, total_tokens);
   for (int i = 0; i < n_layers; ++i) {
     int r;
     if (d->int8_gemm && !d->dynamic_scales && total_tokens > 0) {
@@ -832,8 +895,11 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
       r = layer_forward_int8_dynamic(d, (const char*)packed_layers[i], xa, xb, cu, batch,
                                      total_tokens, max_len, ws + S.layer, st, dl);
     } else {
+      LayerPrefetch lp;
+      lp.on = pf;
+      lp.next = pf && i + 1 < n_layers ? (const char*)packed_layers[i + 1] : nullptr;
       r = layer_forward(d, (const char*)packed_layers[i], xa, xb, cu, batch, total_tokens,
-                        max_len, ws + S.layer, st);
+                        max_len, ws + S.layer, st, lp);
     }
     if (r != TEL_OK) return r;
     void* t = xa;
@@ -930,7 +996,8 @@ int tel_encoder_forward(const tel_encoder_desc* d, const void* const* packed_lay
                                 (uintptr_t)n_layers, (uintptr_t)x_pad, (uintptr_t)y_pad,
                                 (uintptr_t)seq_lens, (uintptr_t)batch, (uintptr_t)max_seq,
                                 (uintptr_t)total_tokens, (uintptr_t)max_len,
-                                (uintptr_t)workspace};
+                                (uintptr_t)workspace,
+                                (uintptr_t)prefetch_wanted(d, n_layers, total_tokens)};
   uint32_t eps_bits;
   memcpy(&eps_bits, &d->ln_eps, 4);
   key.push_back(eps_bits);

@@ -35,6 +35,9 @@
 namespace tel {
 
 constexpr int ATT_KB = 64;   // keys per LDS block
+// read-ahead workgroups when asked for (16,384 threads: a sweep at a 128-token BERT-large
+// stack found 8,192 and 32,768 or more slower)
+constexpr int ATT_AHEAD_BLOCKS = 32;
 constexpr int KV_THREADS = 256;   // threads that stage K/V (KvRegs' layout)
 
 // Scores, online-softmax update and O update for one 64-key block staged in LDS.
@@ -205,7 +208,9 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
                                                           float scale_log2,
                                                           int8_t* __restrict__ ctxq,
                                                           const float* __restrict__ qinv,
-                                                          float* __restrict__ amax) {
+                                                          float* __restrict__ amax, int batch,
+                                                          const void* ahead,
+                                                          size_t ahead_bytes) {
   using MF = Mfma<T>;
   typedef typename MF::frag frag;
   constexpr int KPL = MF::KPL, KMF = 4 * KPL;
@@ -221,6 +226,12 @@ __global__ __launch_bounds__(QB * 4) void attn_varlen_kernel(const T* __restrict
   __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
   __shared__ unsigned int amax_lds[2];   // with amax: workgroup max-abs, counter
 
+  if ((int)blockIdx.z >= batch) {   // read-ahead workgroups (z past the batch): no barrier yet
+    read_ahead(ahead, ahead_bytes,
+               ((blockIdx.z - batch) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x,
+               (gridDim.z - batch) * gridDim.y * gridDim.x);
+    return;
+  }
   const int b = blockIdx.z, h = blockIdx.y;
   const int start = cu[b], L = cu[b + 1] - start;
   const int q0 = blockIdx.x * QB;
@@ -322,47 +333,58 @@ bool attention_supported(int dtype, int head_dim) {
 template <typename T, int D>
 static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                            int max_len, int heads, int8_t* ctxq, const float* qinv,
-                           bool psplit, float* amax, hipStream_t stream) {
+                           bool psplit, float* amax, const void* ahead, size_t ahead_bytes,
+                           hipStream_t stream) {
   // 128 queries per workgroup where the registers allow two such workgroups per compute
   // unit (16-bit types, head_dim <= 64), else 64
   constexpr int QB = (sizeof(T) == 2 && D <= 64) ? 128 : 64;
-  const dim3 grid((max_len + QB - 1) / QB, heads, batch);
+  const int gx = (max_len + QB - 1) / QB;
+  // read-ahead: extra z slices holding about ATT_AHEAD_BLOCKS workgroups
+  const int extra_z = ahead_bytes ? (ATT_AHEAD_BLOCKS + gx * heads - 1) / (gx * heads) : 0;
+  const dim3 grid(gx, heads, batch + extra_z);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (ctxq || psplit || !std::is_same<T, f16>::value)   // P split (see attn_block)
     attn_varlen_kernel<T, D, true, QB><<<grid, QB * 4, 0, stream>>>(
-        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax);
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax, batch, ahead,
+        ahead_bytes);
   else
     attn_varlen_kernel<T, D, false, QB><<<grid, QB * 4, 0, stream>>>(
-        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax);
+        (const T*)qkv, (T*)ctx, cu, total, heads, scale_log2, ctxq, qinv, amax, batch, ahead,
+        ahead_bytes);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t run_attn_d(const void* qkv, void* ctx, const int32_t* cu, int batch, int total,
                              int max_len, int heads, int d, int8_t* ctxq, const float* qinv,
-                             bool ps, float* amax, hipStream_t stream) {
+                             bool ps, float* amax, const void* ah, size_t ahb,
+                             hipStream_t stream) {
   switch (d) {
-    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
-    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
-    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
-    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, stream);
+    case 16: return run_attn<T, 16>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, ah, ahb, stream);
+    case 32: return run_attn<T, 32>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, ah, ahb, stream);
+    case 64: return run_attn<T, 64>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, ah, ahb, stream);
+    case 128: return run_attn<T, 128>(qkv, ctx, cu, batch, total, max_len, heads, ctxq, qinv, ps, amax, ah, ahb, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
-                            int8_t* ctxq, const float* qinv, bool psplit, float* amax) {
+                            int8_t* ctxq, const float* qinv, bool psplit, float* amax,
+                            const void* ahead, size_t ahead_bytes) {
   if (total == 0 || max_len == 0) return hipSuccess;
   if (ctxq && !qinv) return hipErrorInvalidValue;
   if (amax && ctxq) return hipErrorInvalidValue;   // the max-abs is of the stored context
+  if (ahead_bytes < 16) ahead_bytes = 0;
+  if (ahead_bytes && (!ahead || (uintptr_t)ahead % 16 || batch > 65535 - 256))
+    return hipErrorInvalidValue;
   switch (dtype) {
     case DT_F16:
-      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
+      return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, ahead, ahead_bytes, stream);
     case DT_BF16:
-      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
+      return run_attn_d<bf16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, ahead, ahead_bytes, stream);
     case DT_F32:
-      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, stream);
+      return run_attn_d<float>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, ahead, ahead_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -187,6 +187,28 @@ struct SwinGeom {
   }
 };
 
+// Wait until at most N of this wavefront's vector memory operations are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup `wg` of `nwg` reads its share of [p, p + bytes) (16-byte aligned; a tail under
+// 16 bytes is skipped) once and discards it: a later kernel then finds those bytes cached
+// instead of in HBM. The reads are direct global -> LDS copies into one 1 KiB scratch slot
+// that every wavefront overwrites (a copy into LDS is never dropped as unused, unlike a load
+// into registers whose value nothing reads); all of them have landed before the return.
+__device__ inline void read_ahead(const void* p, size_t bytes, int wg, int nwg) {
+  __shared__ __attribute__((aligned(1024))) char slot[1024];
+  const char* q = (const char*)p;
+  const size_t n16 = bytes / 16;
+  const size_t stride = (size_t)nwg * blockDim.x;
+  for (size_t i = (size_t)wg * blockDim.x + threadIdx.x; i < n16; i += stride)
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(q + i * 16),
+                                     (void __attribute__((address_space(3)))*)slot, 16, 0, 0);
+  wait_vmcnt<0>();
+}
+
 // GELU with the exact (erf) form, 0.5 z (1 + erf(z / sqrt 2)). erf comes from the rational
 // approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26 (after
 // Hastings): erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x),

@@ -363,10 +363,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 constexpr int PIPE_PRODUCERS = 2;
 constexpr int DENSE_PRODUCERS = 4;
 
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }

@@ -120,10 +120,13 @@ bool attention_supported(int dtype, int head_dim);
 // psplit: P enters P V split into two 16-bit parts also for fp16 values (the int8 layers,
 // whose codes of the context are sensitive to P's rounding; always so for bf16 and codes).
 // amax (context stored, no codes): atomic max of |stored context| into *amax (>= 0 before).
+// ahead (16-byte aligned): extra workgroups read [ahead, ahead + ahead_bytes) once into the
+// cache for a later kernel (read_ahead).
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
                             int total, int max_len, int heads, int head_dim, hipStream_t stream,
                             int8_t* ctxq = nullptr, const float* qinv = nullptr,
-                            bool psplit = false, float* amax = nullptr);
+                            bool psplit = false, float* amax = nullptr,
+                            const void* ahead = nullptr, size_t ahead_bytes = 0);
 
 // attention_int8.hip: attention on int8 Q, K, V codes ([3][heads][T][D]); scales (device):
 // [0] = s_q s_k / sqrt(D) * log2 e, [1] = s_v, [2] = 1 / (input scale of the O projection);
@@ -146,6 +149,10 @@ struct LnReduceArgs {
   void* y; int out_dt; float* y32; int8_t* yq; const float* qinv;
   const float* gamma; const float* beta; int rows, width; float eps; int round_pre;
   int part16 = 0;   // partial sums stored as fp16 (out type fp16 only), else 32-bit
+  // optional: extra workgroups read [prefetch, prefetch + prefetch_bytes) (16-byte aligned)
+  // once and discard it, bringing weights a later kernel needs into the memory-side cache
+  const void* prefetch = nullptr;
+  size_t prefetch_bytes = 0;
 };
 hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream);
 hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y, float* y_f32,

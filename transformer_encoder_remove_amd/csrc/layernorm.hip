@@ -153,12 +153,17 @@ struct LnRedParams {
   const void* part; int nsplit; const float* dq; const float* bias; const void* resid;
   void* y; float* y32; int8_t* yq; const float* qinv;
   const float* gamma; const float* beta; int rows; float eps; int round_pre; int part16;
-};
+  const void* ahead; size_t ahead_bytes; int main_blocks;   // workgroups past main_blocks
+};                                                           // only read ahead
 
 template <typename TR, typename TO, int G, int NV>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_reduce_kernel(LnRedParams p) {
   constexpr int H = G * NV * 8;
   constexpr bool TO_HALF = std::is_same<TO, f16>::value;
+  if ((int)blockIdx.x >= p.main_blocks) {   // no barrier below: these may leave at once
+    read_ahead(p.ahead, p.ahead_bytes, blockIdx.x - p.main_blocks, gridDim.x - p.main_blocks);
+    return;
+  }
   const int row = blockIdx.x * (LN_THREADS / G) + threadIdx.x / G;
   const int sub = threadIdx.x % G;
   if (row >= p.rows) return;
@@ -433,9 +438,15 @@ hipError_t launch_layernorm_q8(const void* x, void* y, int8_t* yq, const float* 
 
 namespace tel {
 
+// Read-ahead workgroups beside the reduce's own: 16,384 threads, each with its 16-byte
+// copies all in flight (a sweep at a 128-token BERT-large stack found 8,192 and 32,768 or
+// more threads slower: more compete with the reduce's own loads, fewer cannot cover the
+// memory latency).
+constexpr int LNR_AHEAD_BLOCKS = 64;
+
 template <typename TR, typename TO, int G>
 static bool run_lnr_nv(int nv, const LnRedParams& p, hipStream_t s) {
-  const int blocks = (p.rows + LN_THREADS / G - 1) / (LN_THREADS / G);
+  const int blocks = p.main_blocks + (p.ahead_bytes ? LNR_AHEAD_BLOCKS : 0);
   switch (nv) {
     case 1: layernorm_reduce_kernel<TR, TO, G, 1><<<blocks, LN_THREADS, 0, s>>>(p); return true;
     case 2: layernorm_reduce_kernel<TR, TO, G, 2><<<blocks, LN_THREADS, 0, s>>>(p); return true;
@@ -465,8 +476,12 @@ hipError_t launch_layernorm_reduce(const LnReduceArgs& a, hipStream_t stream) {
   if (!pick_ln(a.width, &G, &nv) || a.nsplit < 1 || a.nsplit > LNR_MAX_SPLITS)
     return hipErrorInvalidValue;
   if (a.part16 && (a.out_dt != DT_F16 || a.dq)) return hipErrorInvalidValue;
+  if (a.prefetch_bytes >= 16 && (!a.prefetch || (uintptr_t)a.prefetch % 16))
+    return hipErrorInvalidValue;
+  const int main_blocks = (a.rows + LN_THREADS / G - 1) / (LN_THREADS / G);
   const LnRedParams p{a.part, a.nsplit, a.dq, a.bias, a.resid, a.y, a.y32, a.yq, a.qinv,
-                      a.gamma, a.beta, a.rows, a.eps, a.round_pre, a.part16};
+                      a.gamma, a.beta, a.rows, a.eps, a.round_pre, a.part16, a.prefetch,
+                      a.prefetch_bytes >= 16 ? a.prefetch_bytes : 0, main_blocks};
   bool ok = false;
   if (a.resid_dt == DT_F16 && a.out_dt == DT_F16) ok = run_lnr<f16, f16>(G, nv, p, stream);
   else if (a.resid_dt == DT_BF16 && a.out_dt == DT_BF16) ok = run_lnr<bf16, bf16>(G, nv, p, stream);
