@@ -339,8 +339,10 @@ static hipError_t run_attn(const void* qkv, void* ctx, const int32_t* cu, int ba
   // unit (16-bit types, head_dim <= 64), else 64
   constexpr int QB = (sizeof(T) == 2 && D <= 64) ? 128 : 64;
   const int gx = (max_len + QB - 1) / QB;
-  // read-ahead: extra z slices holding about ATT_AHEAD_BLOCKS workgroups
-  const int extra_z = ahead_bytes ? (ATT_AHEAD_BLOCKS + gx * heads - 1) / (gx * heads) : 0;
+  // read-ahead: extra z slices holding about ATT_AHEAD_BLOCKS workgroups (none where the
+  // grid's z extent would pass its limit: the read-ahead only saves time)
+  int extra_z = ahead_bytes ? (ATT_AHEAD_BLOCKS + gx * heads - 1) / (gx * heads) : 0;
+  if (batch + extra_z > 65535) extra_z = 0;
   const dim3 grid(gx, heads, batch + extra_z);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (ctxq || psplit || !std::is_same<T, f16>::value)   // P split (see attn_block)
@@ -376,8 +378,7 @@ hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t
   if (ctxq && !qinv) return hipErrorInvalidValue;
   if (amax && ctxq) return hipErrorInvalidValue;   // the max-abs is of the stored context
   if (ahead_bytes < 16) ahead_bytes = 0;
-  if (ahead_bytes && (!ahead || (uintptr_t)ahead % 16 || batch > 65535 - 256))
-    return hipErrorInvalidValue;
+  if (ahead_bytes && (!ahead || (uintptr_t)ahead % 16)) return hipErrorInvalidValue;
   switch (dtype) {
     case DT_F16:
       return run_attn_d<f16>(qkv, ctx, cu, batch, total, max_len, heads, head_dim, ctxq, qinv, psplit, amax, ahead, ahead_bytes, stream);
