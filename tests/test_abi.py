@@ -148,10 +148,10 @@ def test_partial_plan_invariants():
     # a 128-token batch at BERT-large shape: output projection split in 2, FFN2 in 4
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (4, 2, 4)
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (4, 4, 4)
-    # 2557 tokens at BERT-base shape: output projection unsplit; FFN2 (K 3072, 240 tiles of
-    # 64 x 128) as 2 x 120 tiles of 128 x 128 with fp16 partials; bf16 and int8 unsplit
+    # 2557 tokens at BERT-base shape: output projection and FFN2 (K 3072, one round of
+    # 240 tiles of 64 x 128) unsplit, in every type
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 768)[1] == 1
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 3072) == (2, 2, 2)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 3072)[1:] == (1, 4)
     assert tel.tel_gemm_partial_plan(tel.TEL_BF16, 2557, 768, 3072)[1:] == (1, 4)
     assert tel.tel_gemm_partial_plan(tel.TEL_I8, 2900, 768, 3072)[1:] == (1, 4)
     # BERT-large throughput batch: many rounds of 128 x 256 tiles, no split
@@ -295,7 +295,7 @@ def test_noalloc_layer_validation():
     A256 = ctypes.c_void_p(1 << 20)
     ok_T = 2557
     assert tel.tel_encoder_workspace_size(desc, ok_T) <= tel.TEL_NOALLOC_SCRATCH_BYTES
-    big_T = 4096
+    big_T = 5000
     assert tel.tel_encoder_workspace_size(desc, big_T) > tel.TEL_NOALLOC_SCRATCH_BYTES
     assert F(pd, A256, A256, ctypes.c_void_p((1 << 20) + 4096), A256, 2, big_T, 128, None) == \
         tel.TEL_EWORKSPACE

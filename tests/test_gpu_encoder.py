@@ -57,10 +57,9 @@ def test_edge_shapes(shape, dtype):
     assert_close(y, _oracle(cfg, lens, x, ws), dtype, f"edge {shape}")
 
 
-def test_fp16_split_ffn2_ragged_two_layers():
-    """H 768, F 2048: FFN2 (K 2048) runs split over k with fp16 partial sums and the output
-    projection unsplit; two layers with non-trivial LayerNorm parameters over 1434 ragged
-    tokens (empty and one-token sequences, not a multiple of any tile)."""
+def test_fp16_ffn2_k2048_ragged_two_layers():
+    """H 768, F 2048 (FFN2 at K 2048): two layers with non-trivial LayerNorm parameters over
+    1434 ragged tokens (empty and one-token sequences, not a multiple of any tile)."""
     lens = [128, 97, 33, 120, 1, 64, 65, 128, 77, 100, 90, 127, 31, 80, 99, 91, 98, 2, 0, 3]
     cfg = ti.custom_encoder_config(len(lens), 128, lens, 768, 12, 2048, dtype="f16", seed=77,
                                    layers=2)

@@ -1336,16 +1336,12 @@ static int pick_cfg(const GemmArgs& a, int elem_bytes) {
 constexpr int SPLIT_MIN_TILES = 100, SPLIT_MIN_SLICES = 8, SPLIT_MAX = 8;
 
 //
-// A second rule, for fp16 operands: long-K, narrow-N shapes whose best unsplit tile is a
-// 64-row one filling a single round (BERT-base FFN2: 2557 x 768, K 3072, 240 tiles of
-// 64 x 128). With every compute unit streaming its operands at once the loop is bound by
-// that stream (measured: the per-slice time follows the bytes copied per compute unit,
-// ~65 GB/s each, not the MFMA count), and a 64 x BN tile streams (64 + BN) rows per
-// 64 x BN outputs. A 128 x 128 tile split in two over k keeps the single round (the same
-// number of workgroups) and streams 2/3 of the bytes per flop; its partial sums are
-// stored as fp16 (half the bytes of float32 for the GEMM to write and the reduce kernel
-// to read) and added in float32 by the reduce-LayerNorm kernel.
-constexpr int SPLIT16_MIN_K = 2048, SPLIT16_CFG = 2;
+// fp16 partial sums (part16, half the bytes of float32) are available to callers of
+// tel_gemm_partial; the plan itself no longer picks them. A rule that split BERT-base's FFN2
+// (2557 x 768, K 3072, one round of 64 x 128 tiles) into two k-splits of 128 x 128 tiles
+// with fp16 partials won back to back, but after the GEMM gained its four producer
+// wavefronts the unsplit tile + LayerNorm was 0.9 % faster per 12-layer step end to end
+// (three alternating runs on one box: 1.037 against 1.046 ms).
 
 static int tiles_of(int cfg, int M, int N) {
   const PipeCfg& p = PIPE_CFGS[cfg];
@@ -1365,13 +1361,6 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16) {
   while (sp < SPLIT_MAX && tiles * sp < SPLIT_MIN_TILES && nk % (2 * sp) == 0 &&
          nk / (2 * sp) >= SPLIT_MIN_SLICES)
     sp *= 2;
-  if (sp == 1 && dtype == DT_F16 && K >= SPLIT16_MIN_K && PIPE_CFGS[*cfg].bm == 64 &&
-      tiles <= 256 && 2L * tiles_of(SPLIT16_CFG, M, N) <= 256 && nk % 2 == 0 &&
-      nk / 2 >= SPLIT_MIN_SLICES) {
-    *cfg = SPLIT16_CFG;
-    *part16 = 1;
-    return 2;
-  }
   return sp;
 }
 
