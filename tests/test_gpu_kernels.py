@@ -125,10 +125,12 @@ def test_gemm_every_tile_config(dtype, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("N,K", [(288, 96), (96, 96), (384, 96), (96, 384)])
+@pytest.mark.parametrize("N,K", [(288, 96), (96, 96), (384, 96), (96, 384), (192, 192),
+                                 (576, 192), (768, 192)])
 def test_skinny_gemm_shapes(dtype, N, K):
     """The narrow projections of the shifted-window block (weights held in LDS, 8-column
-    stores after a lane exchange), every plain epilogue, a ragged token count."""
+    stores after a lane exchange), every plain epilogue, a ragged token count; at K 192
+    (stage 2) the wider outputs run as 192-column slices side by side."""
     M = 1000
     a, w, b, r = _operands(M, N, K, dtype, seed=N + K)
     A, W, R = dev(a, dtype), dev(w, dtype), dev(r, dtype)
@@ -142,11 +144,12 @@ def test_skinny_gemm_shapes(dtype, N, K):
         assert_close(host(C), ref, dtype, f"skinny epi {epi} {dtype} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("heads", [3, 24])
-def test_skinny_qkv_split(heads):
-    """QKV head split at the shifted-window block's width (N 288, K 96): head_dim 32 runs on
-    the skinny kernel, head_dim 4 (fewer than 8 columns per head) on the tiled one."""
-    M, H = 777, 96
+@pytest.mark.parametrize("H,heads", [(96, 3), (96, 24), (192, 6)])
+def test_skinny_qkv_split(H, heads):
+    """QKV head split at the shifted-window block's widths (N 288, K 96; N 576, K 192 in
+    three column slices): head_dim 32 runs on the skinny kernel, head_dim 4 (fewer than 8
+    columns per head) on the tiled one."""
+    M = 777
     a, w, b, _ = _operands(M, 3 * H, H, "f16", seed=heads)
     C = torch.full((3 * M * H,), float("nan"), dtype=torch.float16, device="cuda")
     tel.tel_gemm(tel.TEL_EPI_QKV_SPLIT, dev(a, "f16"), dev(w, "f16"), dev_f32(b), C, heads=heads)

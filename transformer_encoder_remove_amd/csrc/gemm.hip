@@ -877,7 +877,9 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
 // 96 -> 96, fc1 96 -> 384, fc2 384 -> 96, over ~2e5 tokens). A tile narrower than N
 // would re-read the token matrix once per tile column; here each workgroup keeps the
 // whole weight matrix (N x K <= 384 x 96 or 96 x 384) in LDS and owns full output rows, so
-// every token row is read exactly once. Persistent: a workgroup walks row blocks of 64
+// every token row is read exactly once. At channels 192 (stage 2: QKV 192 -> 576, proj
+// 192 -> 192, fc1 192 -> 768) a workgroup holds a 192-column slice of the weights (75 KiB),
+// and the slices run side by side, each reading the token rows once. Persistent: a workgroup walks row blocks of 64
 // tokens (16 per wavefront) with a stride of the grid, holding the token fragments of its
 // next two blocks in registers while it computes the current one. The weight tile is the
 // MFMA A operand, so each lane ends with 4 consecutive columns of one token and the
@@ -890,7 +892,7 @@ __global__ __launch_bounds__((WM * WN + PIPE_PRODUCERS) * 64) void gemm_sp_pipe_
 template <typename T, int NF, int KS, int EPI, typename TR, typename TO, int KC = 3, int G = 6>
 __device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS], const T* sW,
                                            const EpiArgs<T, TR, TO>& e, int row0, int lr,
-                                           int lg) {
+                                           int lg, int n0) {
   using MF = Mfma<T>;
   constexpr int LDW = KS * 32 + 8;
   static_assert(NF % G == 0 && KS % KC == 0, "fragment groups");
@@ -916,7 +918,7 @@ __device__ __forceinline__ void rows_block(const typename Mfma<T>::frag (&a)[KS]
     if (m < e.M) {
 #pragma unroll
       for (int i = 0; i < G; ++i)
-        epilogue_store<EPI, T, TR, TO>(e, m, (g * G + i) * 16 + lg * 4, acc[i]);
+        epilogue_store<EPI, T, TR, TO>(e, m, n0 + (g * G + i) * 16 + lg * 4, acc[i]);
     }
   }
 }
@@ -936,7 +938,7 @@ constexpr int rows_lds_bytes() {
 // whose workgroup has a compute unit's LDS to itself and needs more rows in flight.
 template <typename T, int NF, int KS, int EPI, typename TR, typename TO, bool LNA, int MODE,
           int NTH = 256>
-__global__ __launch_bounds__(NTH) void gemm_rows_kernel(const T* __restrict__ A,
+__global__ __launch_bounds__(NTH, KS == 6 ? 2 : 1) void gemm_rows_kernel(const T* __restrict__ A,
                                                         const T* __restrict__ W,
                                                         EpiArgs<T, TR, TO> e,
                                                         const float* __restrict__ ln_g,
@@ -953,6 +955,9 @@ __global__ __launch_bounds__(NTH) void gemm_rows_kernel(const T* __restrict__ A,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   constexpr int RWG = NTH / 64 * 16;   // rows per workgroup step
+  // column slice blockIdx.y: weight rows [n0, n0 + N) of an e.N-wide output
+  const int n0 = blockIdx.y * N;
+  W += (size_t)n0 * K;
   for (int idx = tid; idx < N * (K / 8); idx += NTH) {
     const int r = idx / (K / 8), c = idx - r * (K / 8);
     *reinterpret_cast<u32x4*>(sW + r * LDW + c * 8) =
@@ -1001,20 +1006,23 @@ __global__ __launch_bounds__(NTH) void gemm_rows_kernel(const T* __restrict__ A,
     for (; rb < M; rb += stride) {
       rows_load<T, KS, MODE>(a0, A, M, rb, lr, lg, e.geom);
       if constexpr (LNA) layernorm(a0);
-      rows_block<T, NF, KS, EPI, TR, TO, 1, 4>(a0, sW, e, rb, lr, lg);
+      rows_block<T, NF, KS, EPI, TR, TO, 1, 4>(a0, sW, e, rb, lr, lg, 0);   // never sliced
     }
     return;
   }
+  // K 192 holds 12 token fragments in registers: output groups of 4 keep the QKV split's
+  // epilogue within two wavefronts per SIMD
+  constexpr int GR = KS == 6 ? 4 : 6;
   typename MF::frag a0[KS], a1[KS];
   if (rb < M) rows_load<T, KS, MODE>(a0, A, M, rb, lr, lg, e.geom);
   if (rb + stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + stride, lr, lg, e.geom);
   for (; rb < M; rb += 2 * stride) {
     if constexpr (LNA) layernorm(a0);
-    rows_block<T, NF, KS, EPI, TR, TO>(a0, sW, e, rb, lr, lg);
+    rows_block<T, NF, KS, EPI, TR, TO, 3, GR>(a0, sW, e, rb, lr, lg, n0);
     if (rb + 2 * stride < M) rows_load<T, KS, MODE>(a0, A, M, rb + 2 * stride, lr, lg, e.geom);
     if (rb + stride >= M) break;
     if constexpr (LNA) layernorm(a1);
-    rows_block<T, NF, KS, EPI, TR, TO>(a1, sW, e, rb + stride, lr, lg);
+    rows_block<T, NF, KS, EPI, TR, TO, 3, GR>(a1, sW, e, rb + stride, lr, lg, n0);
     if (rb + 3 * stride < M) rows_load<T, KS, MODE>(a1, A, M, rb + 3 * stride, lr, lg, e.geom);
   }
 }
@@ -1024,11 +1032,16 @@ static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
   // persistent: two workgroups per CU when one takes <= 80 KiB of LDS, else one; the
   // one-per-CU shape (patch merging) runs 8 wavefronts per workgroup in fp16 (bf16's
   // conversions need a few more registers than 8 wavefronts leave: 4 wavefronts there)
+  // An output wider than the NF * 16 columns whose weights one workgroup holds runs as
+  // column slices (grid y), each reading every token row once: N / (NF * 16) reads of the
+  // token matrix instead of one, still far below a tiled kernel's.
   const int per_cu = rows_lds_bytes<T, NF, KS, true>() <= 80 * 1024 ? 2 : 1;
   constexpr int NTH = (NF == 12 && KS == 12 && std::is_same<T, f16>::value) ? 512 : 256;
   const int rows_wg = NTH / 64 * 16;
   const int blocks = (a.M + rows_wg - 1) / rows_wg;
-  const int grid = std::min(blocks, 256 * per_cu);
+  if (a.N % (NF * 16)) return hipErrorInvalidValue;
+  const int slices = a.N / (NF * 16);
+  const dim3 grid(std::max(1, std::min(blocks, 256 * per_cu / slices)), slices);
 #define TEL_ROWS_LN(EPI, LNA, MODE)                                                          \
   do {                                                                                       \
     EpiArgs<T, T, T> e{a.bias, (const T*)a.resid, (T*)a.C, a.M, a.N, a.heads, a.dq, a.qinv, \
@@ -1068,7 +1081,7 @@ static hipError_t launch_rows_nk(const GemmArgs& a, hipStream_t stream) {
 bool gemm_rows_supported(int dtype, int N, int K) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   return (N == 288 && K == 96) || (N == 96 && K == 96) || (N == 384 && K == 96) ||
-         (N == 96 && K == 384);
+         (N == 96 && K == 384) || (K == 192 && (N == 192 || N == 576 || N == 768));
 }
 
 bool patch_merging_supported(int dtype, int channels) {
@@ -1083,6 +1096,9 @@ static bool launch_rows(const GemmArgs& a, hipStream_t stream, hipError_t* err) 
   else if (a.N == 96 && a.K == 96) *err = launch_rows_nk<T, 6, 3>(a, stream);
   else if (a.N == 384 && a.K == 96) *err = launch_rows_nk<T, 24, 3>(a, stream);
   else if (a.N == 96 && a.K == 384) *err = launch_rows_nk<T, 6, 12>(a, stream);
+  // channels 192 (Swin stage 2): QKV 576, proj 192 and fc1 768 columns as 192-column slices
+  else if (a.K == 192 && (a.N == 192 || a.N == 576 || a.N == 768) && !a.ln_merge)
+    *err = launch_rows_nk<T, 12, 6>(a, stream);
   else if (a.N == 192 && a.K == 384 && a.ln_merge) *err = launch_rows_nk<T, 12, 12>(a, stream);
   else return false;
   return true;
