@@ -110,6 +110,16 @@ int main() {
   EXPECT(tel_layernorm(p, p, (float*)p, (float*)p, 4, 12, 1e-5f, TEL_F16, nullptr) != TEL_OK);
   EXPECT(tel_quantize_i8(odd, (int8_t*)p, 64, 1.f, TEL_F16, nullptr) == TEL_EINVAL);
 
+  // the library's switches: query, set, restore (pure host state)
+  const int pf = tel_weight_prefetch(-1);
+  EXPECT(pf == 0 || pf == 1);
+  EXPECT(tel_weight_prefetch(0) == pf && tel_weight_prefetch(-1) == 0);
+  EXPECT(tel_weight_prefetch(1) == 0 && tel_weight_prefetch(-1) == 1);
+  tel_weight_prefetch(pf);
+  const int gr = tel_graph_cache(-1);
+  EXPECT(gr == 0 || gr == 1);
+  EXPECT(tel_graph_cache(gr) == gr);
+
   // the allocation-free entry point refuses what its scratch array cannot hold
   EXPECT(tel_encoder_layer_forward_noalloc(&d, p, xp, yp, ip, 1, 1 << 20, 128, nullptr) ==
          TEL_EWORKSPACE);
