@@ -819,13 +819,17 @@ constexpr size_t PREFETCH_MIN_STACK_BYTES = size_t(160) << 20;
 std::mutex g_prefetch_mu;
 int g_prefetch_on = -1;           // -1: read TEL_PREFETCH once (on unless it is "0")
 
-bool prefetch_on() {
-  std::lock_guard<std::mutex> lk(g_prefetch_mu);
+bool prefetch_on_locked() {
   if (g_prefetch_on < 0) {
     const char* e = getenv("TEL_PREFETCH");
     g_prefetch_on = (e && e[0] == '0') ? 0 : 1;
   }
   return g_prefetch_on == 1;
+}
+
+bool prefetch_on() {
+  std::lock_guard<std::mutex> lk(g_prefetch_mu);
+  return prefetch_on_locked();
 }
 
 bool prefetch_wanted(const tel_encoder_desc* d, int n_layers, int total_tokens) {
@@ -838,8 +842,8 @@ bool prefetch_wanted(const tel_encoder_desc* d, int n_layers, int total_tokens) 
 }  // namespace
 
 int tel_weight_prefetch(int enable) {
-  const int prev = prefetch_on() ? 1 : 0;
   std::lock_guard<std::mutex> lk(g_prefetch_mu);
+  const int prev = prefetch_on_locked() ? 1 : 0;
   if (enable >= 0) g_prefetch_on = enable ? 1 : 0;
   return prev;
 }
