@@ -258,15 +258,21 @@ int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const v
   void* pre = ws + W.pre;
   void* h1 = ws + W.h1;
   void* f = ws + W.f;
-  const float zeros[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  TEL_TRY(launch_store_f32(amax, zeros, 5, st));   // a kernel, not a memset (graph capture)
+  // this layer's five maxima start at 0: cleared by a kernel (not a memset: graph capture),
+  // or, inside a stack, by the quantise kernel of the layer input, which reads the other
+  // region's slot (the previous layer's LN2 maximum) and so saves a launch per layer
+  if (!link.in_from_prev) {
+    const float zeros[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    TEL_TRY(launch_store_f32(amax, zeros, 5, st));
+  }
   // the layer input's max-abs has its own pass; ctx's, h1's and the GELU output's are folded
   // into the kernels that store them (attention, LN1, the FFN1 epilogue)
   auto quantize = [&](const void* a, size_t n, int8_t* q, int g) {
     return launch_quantize_act(DT_F16, a, q, n, nullptr, 0.f, st, amax + g);
   };
   if (!link.in_from_prev) TEL_TRY(launch_absmax(DT_F16, x, (size_t)T * H, amax + 0, st));
-  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, nullptr, 0.f, st, x_amax));
+  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, nullptr, 0.f, st, x_amax,
+                              link.in_from_prev ? amax : nullptr, link.in_from_prev ? 5 : 0));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.dq = F32(L.sw_qkv);
   g.dyn_amax = x_amax;

@@ -202,10 +202,12 @@ hipError_t launch_quantize_weight(int dtype, const void* w, int8_t* q, float* s_
                                   float act_scale, int N, int K, hipStream_t stream);
 // q[i] = clamp(rne(float(x[i]) * inv), -127, 127); inv is a device scalar when inv_dev is
 // not null, else the host value inv_host; with amax_dev (dynamic scales) inv = 127 / *amax_dev
-// (1 when it is 0).
+// (1 when it is 0). zero[0 .. n_zero) (n_zero <= 256, none of them amax_dev) are set to 0 by
+// the kernel, for maxima a later kernel of the stream folds into.
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
                                float inv_host, hipStream_t stream,
-                               const float* amax_dev = nullptr);
+                               const float* amax_dev = nullptr, float* zero = nullptr,
+                               int n_zero = 0);
 // *out = max(*out, max |x[i]|) (calibration statistic; out is a device float >= 0)
 hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream);
 

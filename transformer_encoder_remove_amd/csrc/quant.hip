@@ -67,7 +67,12 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
                                                            int8_t* __restrict__ q, size_t n,
                                                            const float* __restrict__ inv_dev,
                                                            float inv_host,
-                                                           const float* __restrict__ amax_dev) {
+                                                           const float* __restrict__ amax_dev,
+                                                           float* __restrict__ zero,
+                                                           int n_zero) {
+  // zero: statistics a later kernel folds maxima into, cleared here to save a launch (never
+  // the ones this kernel reads)
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_zero) zero[threadIdx.x] = 0.f;
   // dynamic scale: 1 / s = 127 / max-abs of the tensor (1 for an all-zero tensor)
   float inv = inv_dev ? *inv_dev : inv_host;
   if (amax_dev) {
@@ -95,20 +100,25 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
 }
 
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
-                               float inv_host, hipStream_t stream, const float* amax_dev) {
+                               float inv_host, hipStream_t stream, const float* amax_dev,
+                               float* zero, int n_zero) {
   if (n == 0) return hipSuccess;
+  if (n_zero < 0 || n_zero > 256 || (n_zero && !zero)) return hipErrorInvalidValue;
   size_t blocks = (n / 8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
   switch (dtype) {
     case DT_F16:
-      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host, amax_dev);
+      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host, amax_dev,
+                                                           zero, n_zero);
       break;
     case DT_BF16:
-      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host, amax_dev);
+      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host, amax_dev,
+                                                           zero, n_zero);
       break;
     case DT_F32:
-      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev, inv_host, amax_dev);
+      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev, inv_host, amax_dev,
+                                                           zero, n_zero);
       break;
     default:
       return hipErrorInvalidValue;
