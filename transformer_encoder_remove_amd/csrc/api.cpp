@@ -439,9 +439,8 @@ int layer_forward(const tel_encoder_desc* d, const char* P, const void* x, void*
                            nullptr, false, nullptr, pf.on ? P + L.w_1 : nullptr,
                            pf.on ? L.w_2 - L.w_1 : 0));
   const int pre_dt = f32s ? (int)DT_F32 : dt;
-  // output projection + bias + residual, then LayerNorm; split over k (float32 partials,
-  // or fp16 ones for long-K fp16 shapes; bias + residual + LayerNorm in the reduce kernel)
-  // when the plan says the split pays
+  // output projection + bias + residual, then LayerNorm; split over k (float32 partials;
+  // bias + residual + LayerNorm in the reduce kernel) when the plan says the split pays
   if (sp_o > 1) {
     g = GemmArgs{EPI_PARTIAL, ctx, P + L.w_o, nullptr, nullptr, part, T, H, H, nh};
     g.splits = sp_o;
@@ -818,8 +817,8 @@ size_t tel_encoder_forward_workspace_size(const tel_encoder_desc* d, int batch, 
 // weights a later GEMM needs, once, into that cache: the attention FFN1's, the first
 // reduce-LayerNorm (after the output projection) FFN2's, the second one (end of the layer)
 // the next layer's QKV and output-projection weights, about 8 MB each at BERT-large. Used
-// when the weights cannot all stay cached and dominate what a layer reads, and only on the
-// k-split path.
+// when the weights cannot all stay cached and dominate what a layer reads (few tokens, where
+// the plan splits those GEMMs over k and the reduce kernels run); float layers only.
 namespace {
 constexpr size_t PREFETCH_MIN_STACK_BYTES = size_t(160) << 20;
 std::mutex g_prefetch_mu;
@@ -858,8 +857,8 @@ int tel_weight_prefetch(int enable) {
 // arguments already validated.
 static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_layers,
                            int n_layers, const void* x_pad, void* y_pad,
-                          const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
-                          int max_len, void* workspace, hipStream_t st) {
+                           const int32_t* seq_lens, int batch, int max_seq, int total_tokens,
+                           int max_len, void* workspace, hipStream_t st) {
   const StackWs S = stack_ws(d, batch, max_seq);
   // the layer workspace is laid out for batch * max_seq tokens; a layer at total_tokens
   // (<= batch * max_seq) re-derives its offsets from its own token count and must fit
