@@ -57,6 +57,23 @@ def test_edge_shapes(shape, dtype):
     assert_close(y, _oracle(cfg, lens, x, ws), dtype, f"edge {shape}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bert_base_512_token_sequence(dtype):
+    """BERT's longest sequence (512 tokens, eight 64-key blocks and four 128-query
+    workgroups per head) beside a 300-token and a one-token sequence, at BERT-base width;
+    one layer against the oracle, pads exactly 0."""
+    lens = [512, 300, 1]
+    cfg = ti.custom_encoder_config(len(lens), 512, lens, 768, 12, 3072, dtype=dtype, seed=512,
+                                   layers=1)
+    lens, x = ti.encoder_input(cfg)
+    ws = [ti.encoder_layer_weights(cfg, 0, variant=True)]
+    y = gpu_encoder_forward(tel, cfg, lens, x, ws)
+    ref = _oracle(cfg, lens, x, ws)
+    assert_close(enc.remove_padding(y, lens), enc.remove_padding(ref, lens), dtype, "512 tokens")
+    for b in range(len(lens)):
+        assert not y[b, lens[b]:].any()
+
+
 def test_fp16_ffn2_k2048_ragged_two_layers():
     """H 768, F 2048 (FFN2 at K 2048): two layers with non-trivial LayerNorm parameters over
     1434 ragged tokens (empty and one-token sequences, not a multiple of any tile)."""
