@@ -26,15 +26,15 @@ def switches():
     tel.tel_graph_cache(gr)
 
 
-def _stack(layers):
-    cfg = dict(ti.ENCODER_CONFIGS["bert_large_latency"], dtype="f16", layers=layers)
+def _stack(layers, dtype="f16"):
+    cfg = dict(ti.ENCODER_CONFIGS["bert_large_latency"], dtype=dtype, layers=layers)
     lens, x = ti.encoder_input(cfg)
     ws = [ti.encoder_layer_weights(cfg, i, variant=True) for i in range(layers)]
-    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT["f16"],
+    desc = tel.make_encoder_desc(cfg["hidden"], cfg["heads"], cfg["ffn"], TORCH_DT[dtype],
                                  ti.LN_EPS)
-    packed = prepare_layers(tel, desc, ws, "f16")
+    packed = prepare_layers(tel, desc, ws, dtype)
     B, S, H = x.shape
-    xd = dev(x, "f16")
+    xd = dev(x, dtype)
     yd = torch.empty_like(xd)
     lens_d = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
     wsb = tel.alloc_bytes(tel.tel_encoder_forward_workspace_size(desc, B, S))
@@ -59,8 +59,9 @@ def test_stack_uses_the_prefetch():
     assert LAYERS * packed >= 160 << 20 and act * 8 < packed
 
 
-def test_prefetch_on_off_bit_identical(switches):
-    _, _, _, _, _, run = _stack(LAYERS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefetch_on_off_bit_identical(switches, dtype):
+    _, _, _, _, _, run = _stack(LAYERS, dtype)
     tel.tel_graph_cache(0)
     tel.tel_weight_prefetch(0)
     ref = run()
