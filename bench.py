@@ -74,6 +74,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu() -> str:
+    """The host processor's model name (Linux /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     args = parse()
     if args.summarise_traffic:
@@ -786,6 +798,7 @@ def bench_swin(args):
         tok = n_img * cfg["height"] * cfg["width"]
         cpu = {"value": round(tok / t_cpu, 1), "unit": "tokens/s per block",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "host_cpu": host_cpu(),
                "sample": f"{n_img} image(s) of the same block, float64 NumPy, {t_cpu:.1f} s"}
     out = {
         "metric": "tokens/sec per shifted-window block (Swin-T stage-1 fp16)",
@@ -924,6 +937,7 @@ def bench_swin_stages(args):
         t_cpu = time.perf_counter() - t0
         cpu = {"value": round(H * W / t_cpu, 1), "unit": "stage-1 tokens/s",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "host_cpu": host_cpu(),
                "sample": f"1 image through both stages and the merge, float64 NumPy, {t_cpu:.1f} s"}
     out = {
         "metric": "stage-1 tokens/sec through Swin-T stages 1 and 2 with patch merging (fp16)",
@@ -979,7 +993,7 @@ def cpu_baseline(cfg, lens, x_pad, seconds):
     cores = blas_threads or len(os.sched_getaffinity(0))
     log(f"[bench] cpu oracle: {done} layers x {T} tokens in {elapsed:.1f} s on {cores} threads")
     out = {"value": round(T * done / elapsed, 1), "unit": "valid tokens/s per layer",
-           "cores": cores, "kind": "oracle",
+           "cores": cores, "kind": "oracle", "host_cpu": host_cpu(),
            "sample": f"{done} layer(s) of the same workload on the full batch ({T} valid "
                      f"tokens), float64 NumPy, {elapsed:.1f} s"}
     # the same oracle on one thread: layer 0 on the leading sequences up to ~768 tokens

@@ -37,7 +37,9 @@ def test_host_abi_under_asan_and_ubsan():
     _run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", *HOST_SAN,
           "-I", CSRC, "-I", INCLUDE, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_o])
     lib = os.path.join(OUT, "libtel_hostsan.so")
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_o, *objs, "-o", lib])
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_o, *objs, "-o", lib,
+          "-L", rocm_lib, f"-Wl,-rpath,{rocm_lib}", "-lrocprofiler-sdk-roctx"])
     exe = os.path.join(OUT, "host_abi_driver")
     _run([CLANGXX, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-I", INCLUDE,

@@ -27,6 +27,8 @@ LIB = os.path.join(HERE, "libtel.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+ROCM_LIB = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
+MARKER_LIBS = ["-L", ROCM_LIB, f"-Wl,-rpath,{ROCM_LIB}", "-lrocprofiler-sdk-roctx"]
 
 # Packed-fp32 VALU instructions are disabled for all device code.
 COMMON = [
@@ -107,7 +109,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # the host-timeline markers of api.cpp come from ROCm's marker library
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           *MARKER_LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -11,6 +11,8 @@
 #include <mutex>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "launch.h"
 #include "tel.h"
 
@@ -853,6 +855,24 @@ int tel_weight_prefetch(int enable) {
   return prev;
 }
 
+// Named ranges on the host timeline around a forward and each of its layers (shown by
+// rocprofv3 --marker-trace; a call into the marker library otherwise).
+namespace {
+struct MarkerRange {
+  explicit MarkerRange(const char* name) { roctxRangePushA(name); }
+  ~MarkerRange() { roctxRangePop(); }
+  MarkerRange(const MarkerRange&) = delete;
+  MarkerRange& operator=(const MarkerRange&) = delete;
+};
+const char* const LAYER_NAMES[] = {"tel layer 0", "tel layer 1", "tel layer 2", "tel layer 3",
+                                   "tel layer 4", "tel layer 5", "tel layer 6", "tel layer 7",
+                                   "tel layer 8", "tel layer 9", "tel layer 10", "tel layer 11",
+                                   "tel layer 12", "tel layer 13", "tel layer 14", "tel layer 15",
+                                   "tel layer 16", "tel layer 17", "tel layer 18", "tel layer 19",
+                                   "tel layer 20", "tel layer 21", "tel layer 22", "tel layer 23"};
+constexpr int N_LAYER_NAMES = sizeof(LAYER_NAMES) / sizeof(LAYER_NAMES[0]);
+}  // namespace
+
 // The whole forward (offsets, remove padding, layers, rebuild) enqueued on stream st;
 // arguments already validated.
 static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_layers,
@@ -880,7 +900,9 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
   int8_t* qb = (int8_t*)(ws + S.qb);
   const size_t act_off = d->int8_gemm ? layer_layout(d).act : 0;
   const bool pf = prefetch_wanted(d, n_layers, total_tokens);
+  MarkerRange fwd("tel encoder forward");
   for (int i = 0; i < n_layers; ++i) {
+    MarkerRange layer(i < N_LAYER_NAMES ? LAYER_NAMES[i] : "tel layer");
     int r;
     if (d->int8_gemm && !d->dynamic_scales && total_tokens > 0) {
       // each LN2 writes the codes of its output at the next layer's input scale
