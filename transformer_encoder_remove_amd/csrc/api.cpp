@@ -126,6 +126,8 @@ LayerLayout layer_layout(const tel_encoder_desc* d) {
 // their storage type. When few tokens leave most compute units idle, the output
 // projection and FFN2 run split over k instead: float32 (int32 for int8 operands)
 // partial sums that the reduce-LayerNorm kernel adds with bias and residual.
+constexpr int DYN_STATS = 5;   // dynamic scales: max-abs statistics per layer
+
 struct LayerWs {
   size_t qkv, ctx, pre, part, h1, h1f, f, total;
   size_t xq, ctxq, h1q;   // int8 layer: codes of the inputs of the QKV, O and FFN1 GEMMs
@@ -174,8 +176,10 @@ LayerWs layer_ws(const tel_encoder_desc* d, size_t T) {
   LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
-  // dynamic scales: the four max-abs values first (documented: bytes 0..15 of the workspace)
-  if (d->dynamic_scales) w.dyn = take(16 * 4);   // two regions of 8 maxima (DynLink)
+  // dynamic scales: the four max-abs values first (documented: bytes 0..15 of the workspace):
+  // two regions of 8 folded maxima (DynLink), then from byte 128 each region's five
+  // statistics of AMAX_SLOTS copies (amax_raise)
+  if (d->dynamic_scales) w.dyn = take((32 + 2 * DYN_STATS * AMAX_STAT_FLOATS) * 4);
   w.qkv = take(3 * T * H * es);
   w.ctx = take(T * H * es);
   w.pre = take(T * H * (f32_stream(d) ? 4 : es));
@@ -232,9 +236,12 @@ struct Int8Link {
 // quantise kernel takes 127 / max-abs as its inverse scale, and the GEMM epilogue forms the
 // dequantisation scale (max-abs / 127) * s_w[n] per column. The layer never splits over k.
 //
-// In a stack, layer i uses region i % 2 of the 16 floats at W.dyn: [0..3] its four maxima,
-// [4] the max-abs of its output, which its LN2 folds in and layer i + 1 takes as its input
-// statistic (DynLink), so only the first layer reads its input for the max-abs.
+// Each max-abs is a statistic of AMAX_SLOTS copies that its producer's workgroups raise
+// (amax_raise: one address per copy, so the atomics do not queue on one), and the quantise
+// kernel that reads it folds the copies and stores the value for the GEMM's epilogue.
+// In a stack, layer i uses region i % 2 of W.dyn: folded values [0..3] its four maxima,
+// [4] the max-abs of its output, whose statistic its LN2 raises and layer i + 1 takes as
+// its input statistic (DynLink), so only the first layer reads its input for the max-abs.
 struct DynLink {
   int parity = 0;         // region of this layer
   bool in_from_prev = false;   // input max-abs left by the previous layer's LN2
@@ -249,8 +256,12 @@ int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const v
   const int H = d->hidden, F = d->ffn, nh = d->heads;
   auto F32 = [&](size_t off) { return (const float*)(P + off); };
   float* const dyn = (float*)(ws + W.dyn);
-  float* amax = dyn + 8 * link.parity;
-  const float* x_amax = link.in_from_prev ? dyn + 8 * (1 - link.parity) + 4 : amax + 0;
+  float* amax = dyn + 8 * link.parity;   // folded values
+  auto stat = [&](int parity, int g) {
+    return dyn + 32 + ((size_t)parity * DYN_STATS + g) * AMAX_STAT_FLOATS;
+  };
+  const float* x_stat = link.in_from_prev ? stat(1 - link.parity, 4) : stat(link.parity, 0);
+  float* x_amax = link.in_from_prev ? dyn + 8 * (1 - link.parity) + 4 : amax + 0;
   int8_t* xq = (int8_t*)(ws + W.xq);
   int8_t* ctxq = (int8_t*)(ws + W.ctxq);
   int8_t* h1q = (int8_t*)(ws + W.h1q);
@@ -260,40 +271,40 @@ int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const v
   void* pre = ws + W.pre;
   void* h1 = ws + W.h1;
   void* f = ws + W.f;
-  // this layer's five maxima start at 0: cleared by a kernel (not a memset: graph capture),
-  // or, inside a stack, by the quantise kernel of the layer input, which reads the other
-  // region's slot (the previous layer's LN2 maximum) and so saves a launch per layer
-  if (!link.in_from_prev) {
-    const float zeros[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-    TEL_TRY(launch_store_f32(amax, zeros, 5, st));
-  }
-  // the layer input's max-abs has its own pass; ctx's, h1's and the GELU output's are folded
-  // into the kernels that store them (attention, LN1, the FFN1 epilogue)
+  // this layer's five statistics start at 0: cleared by a kernel (not a memset: graph
+  // capture), or, inside a stack, by the quantise kernel of the layer input, which reads the
+  // other region's statistic (the previous layer's LN2 maximum) and so saves a launch
+  if (!link.in_from_prev) TEL_TRY(launch_clear_amax(stat(link.parity, 0), DYN_STATS, st));
+  // the layer input's max-abs has its own pass; ctx's, h1's and the GELU output's are raised
+  // by the kernels that store them (attention, LN1, the FFN1 epilogue)
   auto quantize = [&](const void* a, size_t n, int8_t* q, int g) {
-    return launch_quantize_act(DT_F16, a, q, n, nullptr, 0.f, st, amax + g);
+    return launch_quantize_act(DT_F16, a, q, n, nullptr, 0.f, st, stat(link.parity, g),
+                               amax + g);
   };
-  if (!link.in_from_prev) TEL_TRY(launch_absmax(DT_F16, x, (size_t)T * H, amax + 0, st));
-  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, nullptr, 0.f, st, x_amax,
-                              link.in_from_prev ? amax : nullptr, link.in_from_prev ? 5 : 0));
+  if (!link.in_from_prev)
+    TEL_TRY(launch_absmax(DT_F16, x, (size_t)T * H, stat(link.parity, 0), st, true));
+  TEL_TRY(launch_quantize_act(DT_F16, x, xq, (size_t)T * H, nullptr, 0.f, st, x_stat, x_amax,
+                              link.in_from_prev ? stat(link.parity, 0) : nullptr,
+                              link.in_from_prev ? DYN_STATS : 0));
   GemmArgs g{EPI_QKV_SPLIT, xq, P + L.w_qkv, F32(L.b_qkv), nullptr, qkv, T, 3 * H, H, nh};
   g.dq = F32(L.sw_qkv);
   g.dyn_amax = x_amax;
   TEL_TRY(launch_gemm(DT_I8, g, st));
   // P split as in the static int8 layer: ctx's codes follow P's rounding closely
   TEL_TRY(launch_attention(DT_F16, qkv, ctx, cu, batch, T, max_len, nh, H / nh, st, nullptr,
-                           nullptr, true, amax + 1));
+                           nullptr, true, stat(link.parity, 1)));
   TEL_TRY(quantize(ctx, (size_t)T * H, ctxq, 1));
   g = GemmArgs{EPI_BIAS_RESID, ctxq, P + L.w_o, F32(L.b_o), x, pre, T, H, H, nh};
   g.dq = F32(L.sw_o);
   g.dyn_amax = amax + 1;
   TEL_TRY(launch_gemm(DT_I8, g, st));
-  TEL_TRY(launch_layernorm_amax(pre, h1, amax + 2, F32(L.ln1_g), F32(L.ln1_b), T, H, d->ln_eps,
-                                st));
+  TEL_TRY(launch_layernorm_amax(pre, h1, stat(link.parity, 2), F32(L.ln1_g), F32(L.ln1_b), T, H,
+                                d->ln_eps, st));
   TEL_TRY(quantize(h1, (size_t)T * H, h1q, 2));
   g = GemmArgs{EPI_BIAS_GELU_AMAX, h1q, P + L.w_1, F32(L.b_1), nullptr, f, T, F, H, nh};
   g.dq = F32(L.sw_1);
   g.dyn_amax = amax + 2;
-  g.out_amax = amax + 3;
+  g.out_amax = stat(link.parity, 3);
   TEL_TRY(launch_gemm(DT_I8, g, st));
   TEL_TRY(quantize(f, (size_t)T * F, fq, 3));
   g = GemmArgs{EPI_BIAS_RESID, fq, P + L.w_2, F32(L.b_2), h1, pre, T, H, F, nh};
@@ -301,7 +312,7 @@ int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const v
   g.dyn_amax = amax + 3;
   TEL_TRY(launch_gemm(DT_I8, g, st));
   if (link.out_to_next)
-    TEL_TRY(launch_layernorm_amax(pre, y, amax + 4, F32(L.ln2_g), F32(L.ln2_b), T, H,
+    TEL_TRY(launch_layernorm_amax(pre, y, stat(link.parity, 4), F32(L.ln2_g), F32(L.ln2_b), T, H,
                                   d->ln_eps, st));
   else
     TEL_TRY(launch_layernorm(DT_F16, DT_F16, pre, y, nullptr, F32(L.ln2_g), F32(L.ln2_b), T, H,

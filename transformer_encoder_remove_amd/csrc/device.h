@@ -112,22 +112,33 @@ template <int G> __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-// One wavefront's share of a tensor's max-abs: the 64 lanes' maxima (each >= 0) reduced in
-// registers, then one atomic max on *out (non-negative floats order like their bit
-// patterns, so the unsigned atomic is exact and independent of arrival order). Every lane
-// of the wavefront must call it.
-__device__ __forceinline__ void wave_atomic_max(float m, float* out) {
-  m = group_max<64>(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+// Max-abs statistics of the dynamically scaled int8 layer. Many workgroups raise one such
+// statistic at the end of a short kernel, nearly at once, and device atomics on one address
+// serialise (a few ns each: ~3 us for the ~360 workgroups of a LayerNorm). So a statistic
+// is kept in AMAX_SLOTS copies 128 bytes apart, workgroup w raises copy w % AMAX_SLOTS, and
+// its reader folds the copies (amax_fold). Non-negative floats order like their bit
+// patterns, so the unsigned atomic max is exact and independent of arrival order.
+constexpr int AMAX_SLOTS = 64, AMAX_STRIDE = 32;              // copies, floats apart
+constexpr size_t AMAX_STAT_FLOATS = (size_t)AMAX_SLOTS * AMAX_STRIDE;
+
+__device__ __forceinline__ void amax_raise(float* stat, float m) {
+  const unsigned int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  atomicMax(reinterpret_cast<unsigned int*>(stat + (wg % AMAX_SLOTS) * AMAX_STRIDE),
+            __float_as_uint(m));
 }
 
-// The same for a workgroup of nw wavefronts with one global atomic: each wavefront folds
-// its maximum into lds[0] with an LDS atomic max, then increments the counter lds[1]; the
-// wavefront that brings the counter to nw (its increment is ordered after every other
-// wavefront's maximum) folds lds[0] into *out. There is no barrier, so wavefronts that
-// have already left (a GEMM's producers) are not waited for. lds[0] and lds[1] must hold 0
+// The statistic's value, in every lane of the calling wavefront (all 64 lanes must call).
+__device__ __forceinline__ float amax_fold(const float* stat) {
+  return group_max<64>(stat[(threadIdx.x & 63) * AMAX_STRIDE]);
+}
+
+// A workgroup of nw wavefronts raises a statistic with one global atomic: each wavefront
+// folds its maximum into lds[0] with an LDS atomic max, then increments the counter lds[1];
+// the wavefront that brings the counter to nw (its increment is ordered after every other
+// wavefront's maximum) raises the statistic. There is no barrier, so wavefronts that have
+// already left (a GEMM's producers) are not waited for. lds[0] and lds[1] must hold 0
 // before any wavefront gets here, and each of the nw wavefronts calls this once.
-__device__ __forceinline__ void wg_atomic_max(float m, float* out, unsigned int* lds, int nw) {
+__device__ __forceinline__ void wg_atomic_max(float m, float* stat, unsigned int* lds, int nw) {
   m = group_max<64>(m);
   if ((threadIdx.x & 63) == 0) {
     __hip_atomic_fetch_max(&lds[0], __float_as_uint(m), __ATOMIC_RELAXED,
@@ -137,7 +148,7 @@ __device__ __forceinline__ void wg_atomic_max(float m, float* out, unsigned int*
     if (n == (unsigned int)nw - 1) {
       const unsigned int v = __hip_atomic_load(&lds[0], __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_WORKGROUP);
-      atomicMax(reinterpret_cast<unsigned int*>(out), v);
+      amax_raise(stat, __uint_as_float(v));
     }
   }
 }

@@ -49,7 +49,8 @@ template <typename T, typename TR, typename TO> struct EpiArgs {
   const float* qinv;   // int8 output: device scalar, 1 / activation scale of the consumer
   SwinGeom geom;       // EPI_SWIN_SCATTER: window order -> image order
   const float* dyn_amax = nullptr;   // int8 operands, dynamic scale: dq = s_w, s_a from max-abs
-  float* out_amax = nullptr;         // EPI_BIAS_GELU_AMAX: max-abs of the stored outputs
+  float* out_amax = nullptr;         // EPI_BIAS_GELU_AMAX: max-abs statistic of the stored
+                                     // outputs (AMAX_SLOTS copies, amax_raise)
 };
 
 constexpr bool epi_gelu(int epi) { return epi == EPI_BIAS_GELU || epi == EPI_BIAS_GELU_AMAX; }

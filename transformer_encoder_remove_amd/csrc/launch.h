@@ -16,8 +16,8 @@ enum Epi {
                          // k-split s at C + s * M * N, or those sums rounded to fp16
                          // (GemmArgs::part16, fp16 operands); a reduce kernel finishes the sum
   EPI_PLAIN = 7,         // C = A W^T in the storage type, no bias (skinny kernel only)
-  EPI_BIAS_GELU_AMAX = 8 // int8 operands, fp16 output: EPI_BIAS_GELU that also folds the
-                         // max-abs of its stored outputs into *out_amax (dynamic scales)
+  EPI_BIAS_GELU_AMAX = 8 // int8 operands, fp16 output: EPI_BIAS_GELU that also raises the
+                         // max-abs statistic out_amax (amax_raise) by its stored outputs
 };
 
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : dt == DT_I8 ? 1 : 2; }
@@ -67,7 +67,8 @@ struct GemmArgs {
   const float* qinv = nullptr;  // int8 output: device scalar 1 / scale (EPI_BIAS_GELU), or
                                 // three of them, for Q, K and V (EPI_QKV_SPLIT)
   int out_i8 = 0;               // int8 operands, EPI_BIAS_GELU / EPI_QKV_SPLIT: int8 codes
-  float* out_amax = nullptr;    // EPI_BIAS_GELU_AMAX: atomic max of |stored output| (>= 0 before)
+  float* out_amax = nullptr;    // EPI_BIAS_GELU_AMAX: max-abs statistic raised by |stored
+                                // output| (AMAX_SLOTS copies, each >= 0 before)
   SwinGeom geom{};              // EPI_SWIN_SCATTER
   int splits = 1;               // pipelined kernel only: K split over this many workgroups
   int part16 = 0;               // EPI_PARTIAL, fp16 operands: partial sums stored as fp16
@@ -119,7 +120,8 @@ bool attention_supported(int dtype, int head_dim);
 // ctxq != nullptr: write only the int8 codes of the stored-type output (scale *qinv);
 // psplit: P enters P V split into two 16-bit parts also for fp16 values (the int8 layers,
 // whose codes of the context are sensitive to P's rounding; always so for bf16 and codes).
-// amax (context stored, no codes): atomic max of |stored context| into *amax (>= 0 before).
+// amax (context stored, no codes): raise the max-abs statistic amax (AMAX_SLOTS copies,
+// amax_raise; each >= 0 before) by |stored context|.
 // ahead (16-byte aligned): extra workgroups read [ahead, ahead + ahead_bytes) once into the
 // cache for a later kernel (read_ahead).
 hipError_t launch_attention(int dtype, const void* qkv, void* ctx, const int32_t* cu, int batch,
@@ -162,8 +164,9 @@ hipError_t launch_layernorm(int dtype_in, int dtype_out, const void* x, void* y,
 hipError_t launch_layernorm_gather(int dtype, const void* x, void* y, const float* gamma,
                                    const float* beta, int rows, int width, float eps,
                                    const SwinGeom& geom, hipStream_t stream);
-// fp16 LayerNorm that also folds the max-abs of its (fp16-rounded) output into *amax
-// (atomic max; *amax must hold a non-negative value, e.g. 0, beforehand).
+// fp16 LayerNorm that also raises the max-abs statistic amax (AMAX_SLOTS copies,
+// amax_raise; each must hold a non-negative value, e.g. 0, beforehand) by its
+// (fp16-rounded) output.
 hipError_t launch_layernorm_amax(const void* x, void* y, float* amax, const float* gamma,
                                  const float* beta, int rows, int width, float eps,
                                  hipStream_t stream);
@@ -201,14 +204,20 @@ hipError_t launch_store_f32(float* dst, const float* vals, int n, hipStream_t st
 hipError_t launch_quantize_weight(int dtype, const void* w, int8_t* q, float* s_w, float* dq,
                                   float act_scale, int N, int K, hipStream_t stream);
 // q[i] = clamp(rne(float(x[i]) * inv), -127, 127); inv is a device scalar when inv_dev is
-// not null, else the host value inv_host; with amax_dev (dynamic scales) inv = 127 / *amax_dev
-// (1 when it is 0). zero[0 .. n_zero) (n_zero <= 256, none of them amax_dev) are set to 0 by
-// the kernel, for maxima a later kernel of the stream folds into.
+// not null, else the host value inv_host. Dynamic scales: amax_stat is a max-abs statistic
+// (AMAX_SLOTS copies), a = its folded value, inv = 127 / a (1 when a is 0), and a is stored
+// to *amax_out (for the GEMM epilogue that dequantises). The n_zero statistics
+// zero + i * AMAX_STAT_FLOATS (n_zero <= 8, none of them amax_stat) are cleared by the
+// kernel, for maxima later kernels of the stream raise.
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
                                float inv_host, hipStream_t stream,
-                               const float* amax_dev = nullptr, float* zero = nullptr,
-                               int n_zero = 0);
-// *out = max(*out, max |x[i]|) (calibration statistic; out is a device float >= 0)
-hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream);
+                               const float* amax_stat = nullptr, float* amax_out = nullptr,
+                               float* zero = nullptr, int n_zero = 0);
+// *out = max(*out, max |x[i]|) (calibration statistic; out is a device float >= 0); with
+// stat, out is a max-abs statistic of AMAX_SLOTS copies raised by amax_raise instead.
+hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream,
+                         bool stat = false);
+// Clears n max-abs statistics stats + i * AMAX_STAT_FLOATS (every copy) with a kernel.
+hipError_t launch_clear_amax(float* stats, int n, hipStream_t stream);
 
 }  // namespace tel

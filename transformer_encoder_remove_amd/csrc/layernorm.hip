@@ -47,10 +47,10 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float* 
 // from the stored (TO-rounded) value: code = clamp(rne(float(y) * inv), -127, 127).
 // GATHER: output row r reads input row geom.src_row(r) (the shifted-window partition:
 // LayerNorm, cyclic shift and window partition in one pass).
-// AMAX: also *amax = max(*amax, max |y|) over the stored (TO-rounded) outputs, the
-// statistic of a dynamically scaled int8 GEMM that reads y: reduced over the workgroup
-// through LDS, then one atomic max per workgroup (non-negative floats order like their
-// bit patterns, so the unsigned atomic is exact and order-independent). Rows past the end
+// AMAX: also raise the max-abs statistic amax by max |y| over the stored (TO-rounded)
+// outputs, the statistic of a dynamically scaled int8 GEMM that reads y: reduced over the
+// workgroup through LDS, then one atomic max per workgroup on one of the statistic's copies
+// (amax_raise). Rows past the end
 // then compute on the last row instead of leaving, so that every lane reaches the barrier.
 template <typename TI, typename TO, bool COPY, int G, int NV, bool Q8 = false, bool GATHER = false,
           bool AMAX = false>
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const TI* __restr
       float m = wave_max[0];
 #pragma unroll
       for (int w = 1; w < LN_THREADS / 64; ++w) m = fmaxf(m, wave_max[w]);
-      atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+      amax_raise(amax, m);
     }
   }
 }

@@ -67,16 +67,21 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
                                                            int8_t* __restrict__ q, size_t n,
                                                            const float* __restrict__ inv_dev,
                                                            float inv_host,
-                                                           const float* __restrict__ amax_dev,
+                                                           const float* __restrict__ amax_stat,
+                                                           float* __restrict__ amax_out,
                                                            float* __restrict__ zero,
                                                            int n_zero) {
-  // zero: statistics a later kernel folds maxima into, cleared here to save a launch (never
-  // the ones this kernel reads)
-  if (blockIdx.x == 0 && (int)threadIdx.x < n_zero) zero[threadIdx.x] = 0.f;
-  // dynamic scale: 1 / s = 127 / max-abs of the tensor (1 for an all-zero tensor)
+  // zero: statistics later kernels raise, cleared here to save a launch (never the one this
+  // kernel reads)
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero * AMAX_SLOTS; i += 256)
+      zero[(size_t)(i / AMAX_SLOTS) * AMAX_STAT_FLOATS + (i % AMAX_SLOTS) * AMAX_STRIDE] = 0.f;
+  // dynamic scale: 1 / s = 127 / max-abs of the tensor (1 for an all-zero tensor); every
+  // wavefront folds the statistic's copies itself (256 threads: four whole wavefronts)
   float inv = inv_dev ? *inv_dev : inv_host;
-  if (amax_dev) {
-    const float a = *amax_dev;
+  if (amax_stat) {
+    const float a = amax_fold(amax_stat);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *amax_out = a;
     inv = a > 0.f ? 127.f / a : 1.f;
   }
   const size_t nv = n / 8;
@@ -100,25 +105,27 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T* __restrict__
 }
 
 hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, const float* inv_dev,
-                               float inv_host, hipStream_t stream, const float* amax_dev,
-                               float* zero, int n_zero) {
+                               float inv_host, hipStream_t stream, const float* amax_stat,
+                               float* amax_out, float* zero, int n_zero) {
   if (n == 0) return hipSuccess;
-  if (n_zero < 0 || n_zero > 256 || (n_zero && !zero)) return hipErrorInvalidValue;
+  if (n_zero < 0 || n_zero > 8 || (n_zero && !zero) || (amax_stat && !amax_out))
+    return hipErrorInvalidValue;
   size_t blocks = (n / 8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) blocks = 1;
   switch (dtype) {
     case DT_F16:
-      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host, amax_dev,
-                                                           zero, n_zero);
+      quantize_act_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, q, n, inv_dev, inv_host,
+                                                           amax_stat, amax_out, zero, n_zero);
       break;
     case DT_BF16:
-      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host, amax_dev,
-                                                           zero, n_zero);
+      quantize_act_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, q, n, inv_dev, inv_host,
+                                                            amax_stat, amax_out, zero, n_zero);
       break;
     case DT_F32:
-      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev, inv_host, amax_dev,
-                                                           zero, n_zero);
+      quantize_act_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, q, n, inv_dev,
+                                                             inv_host, amax_stat, amax_out, zero,
+                                                             n_zero);
       break;
     default:
       return hipErrorInvalidValue;
@@ -134,7 +141,7 @@ hipError_t launch_quantize_act(int dtype, const void* x, int8_t* q, size_t n, co
 // tail of n that does not fill a vector.
 template <typename T>
 __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, size_t n,
-                                                     float* __restrict__ out) {
+                                                     float* __restrict__ out, bool stat) {
   constexpr int VEC = 16 / sizeof(T);
   __shared__ float wave_max[4];
   float m = 0.f;
@@ -153,11 +160,13 @@ __global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, si
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+    if (stat) amax_raise(out, m);
+    else atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
   }
 }
 
-hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream) {
+hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStream_t stream,
+                         bool stat) {
   if (n == 0) return hipSuccess;
   if ((uintptr_t)x & 15u) return hipErrorInvalidValue;   // 16-byte vector loads
   // one workgroup per compute unit at most: atomics to the one address serialise (a few
@@ -166,11 +175,23 @@ hipError_t launch_absmax(int dtype, const void* x, size_t n, float* out, hipStre
   if (blocks > 256) blocks = 256;
   if (blocks == 0) blocks = 1;
   switch (dtype) {
-    case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out); break;
-    case DT_BF16: absmax_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, n, out); break;
-    case DT_F32: absmax_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, n, out); break;
+    case DT_F16: absmax_kernel<f16><<<blocks, 256, 0, stream>>>((const f16*)x, n, out, stat); break;
+    case DT_BF16: absmax_kernel<bf16><<<blocks, 256, 0, stream>>>((const bf16*)x, n, out, stat); break;
+    case DT_F32: absmax_kernel<float><<<blocks, 256, 0, stream>>>((const float*)x, n, out, stat); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// Every copy of n max-abs statistics set to 0 (a kernel, not a memset: graph capture).
+__global__ __launch_bounds__(256) void clear_amax_kernel(float* __restrict__ stats, int n) {
+  for (int i = threadIdx.x; i < n * AMAX_SLOTS; i += 256)
+    stats[(size_t)(i / AMAX_SLOTS) * AMAX_STAT_FLOATS + (i % AMAX_SLOTS) * AMAX_STRIDE] = 0.f;
+}
+
+hipError_t launch_clear_amax(float* stats, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  clear_amax_kernel<<<1, 256, 0, stream>>>(stats, n);
   return hipGetLastError();
 }
 
