@@ -231,7 +231,7 @@ struct Int8Link {
 
 // Int8 layer with dynamic activation scales ("揭秘Transformer模型…", section 3.3: the
 // quantisation parameters follow the data at inference time): each GEMM input is stored as
-// fp16 by its producer, its max-abs over the batch is reduced on the device (folded into
+// fp16 by its producer, its max-abs over the batch is reduced on the device (raised by
 // the producer for ctx, h1 and the GELU output; a pass of its own for the layer input), the
 // quantise kernel takes 127 / max-abs as its inverse scale, and the GEMM epilogue forms the
 // dequantisation scale (max-abs / 127) * s_w[n] per column. The layer never splits over k.
@@ -245,7 +245,7 @@ struct Int8Link {
 struct DynLink {
   int parity = 0;         // region of this layer
   bool in_from_prev = false;   // input max-abs left by the previous layer's LN2
-  bool out_to_next = false;    // fold this layer's output max-abs for the next layer
+  bool out_to_next = false;    // raise this layer's output max-abs for the next layer
 };
 
 int layer_forward_int8_dynamic(const tel_encoder_desc* d, const char* P, const void* x, void* y,
@@ -929,7 +929,7 @@ static int forward_enqueue(const tel_encoder_desc* d, const void* const* packed_
       qa = qb;
       qb = tq;
     } else if (d->int8_gemm && d->dynamic_scales && total_tokens > 0) {
-      // each LN2 folds the max-abs of its output in for the next layer's input scale
+      // each LN2 raises the max-abs statistic of its output for the next layer's input scale
       DynLink dl;
       dl.parity = i & 1;
       dl.in_from_prev = i > 0;
