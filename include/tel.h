@@ -184,7 +184,7 @@ int tel_encoder_layer_forward(const tel_encoder_desc* desc, const void* packed,
  * by the call; the caller still passes inputs, output and packed weights as for
  * tel_encoder_layer_forward (same arguments, same results).
  *   Limit: tel_encoder_workspace_size(desc, total_tokens) must not exceed
- *   TEL_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a BERT-base fp16 layer up to 4,164 tokens),
+ *   TEL_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a BERT-base fp16 layer up to 4,266 tokens),
  *   else TEL_EWORKSPACE and nothing is enqueued.
  *   Every call on one GPU uses that GPU's one array, which keeps the last call's contents:
  *   calls that can overlap on the same GPU (different streams, or host threads without

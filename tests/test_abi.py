@@ -125,7 +125,7 @@ def test_partial_plan_invariants():
     256 workgroups, and then two splits of the 128 x 128 tile that still fill one round."""
     # (BM, BN) of the pipelined tile table, in its order (gemm.hip PIPE_CFGS)
     cfgs = [(128, 256), (128, 192), (128, 128), (64, 128), (64, 64), (128, 256), (256, 128),
-            (128, 128), (64, 128), (192, 192), (96, 128)]
+            (128, 128), (64, 128), (192, 192), (96, 128), (32, 64)]
     assert len(cfgs) == tel.tel_gemm_tile_configs()
     for dt, es in ((tel.TEL_F16, 2), (tel.TEL_BF16, 2), (tel.TEL_F32, 4), (tel.TEL_I8, 1)):
         for M in (1, 17, 128, 640, 2557, 14336, 24576):
@@ -145,9 +145,10 @@ def test_partial_plan_invariants():
                     assert tiles * sp // 2 < 100          # the smallest split that suffices
                 else:
                     assert tiles >= 100 or nk % 2 or nk // 2 < 8
-    # a 128-token batch at BERT-large shape: output projection split in 2, FFN2 in 4
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (4, 2, 4)
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (4, 4, 4)
+    # a 128-token batch at BERT-large shape: 32 x 64 tiles (64 of them), the output
+    # projection and FFN2 each split in 2
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (11, 2, 4)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (11, 2, 4)
     # 2557 tokens at BERT-base shape: output projection and FFN2 (K 3072, one round of
     # 240 tiles of 64 x 128) unsplit, in every type
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 768)[1] == 1
@@ -297,6 +298,11 @@ def test_noalloc_layer_validation():
     assert tel.tel_encoder_workspace_size(desc, ok_T) <= tel.TEL_NOALLOC_SCRATCH_BYTES
     big_T = 5000
     assert tel.tel_encoder_workspace_size(desc, big_T) > tel.TEL_NOALLOC_SCRATCH_BYTES
+    # the limit the header states for this layer is exact
+    limit = 4266
+    assert "up to 4,266 tokens" in open(HEADER).read()
+    assert tel.tel_encoder_workspace_size(desc, limit) <= tel.TEL_NOALLOC_SCRATCH_BYTES
+    assert tel.tel_encoder_workspace_size(desc, limit + 1) > tel.TEL_NOALLOC_SCRATCH_BYTES
     assert F(pd, A256, A256, ctypes.c_void_p((1 << 20) + 4096), A256, 2, big_T, 128, None) == \
         tel.TEL_EWORKSPACE
     assert F(pd, A256, A256, A256, A256, 2, 100, 64, None) == tel.TEL_EINVAL        # x == y

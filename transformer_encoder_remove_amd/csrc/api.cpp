@@ -150,7 +150,7 @@ size_t partial_rows_uncached(const tel_encoder_desc* d, size_t T) {
     return sp > 1 ? (size_t)sp * t : 0;
   };
   // Plans change only where a tile count does, i.e. just past a multiple of some tile
-  // height (64, 96, 128 or 192 rows: all multiples of 32), so the largest need inside each
+  // height (32, 64, 96, 128 or 192 rows: all multiples of 32), so the largest need inside each
   // run of equal plans is at its top, a multiple of 32 (or T itself).
   size_t rows = need(T);
   for (size_t t = 32; t < T; t += 32) rows = std::max(rows, need(t));

@@ -1122,6 +1122,7 @@ constexpr PipeCfg PIPE_CFGS[] = {
     {64, 128, 2, 2, 4},    // 8: 4 waves, wave tile 32x64, 96 KiB
     {192, 192, 2, 4, 3},   // 9: 8 waves, wave tile 96x48, 144 KiB
     {96, 128, 2, 4, 4},    // 10: 8 waves, wave tile 48x32, 112 KiB
+    {32, 64, 2, 2, 4},     // 11: 4 waves, wave tile 16x32, 48 KiB
 };
 constexpr int N_PIPE_CFGS = sizeof(PIPE_CFGS) / sizeof(PIPE_CFGS[0]);
 
@@ -1246,6 +1247,7 @@ static void launch_cfg(int cfg, const GemmArgs& a, hipStream_t stream) {
     case 8: launch_pipe<T, 8, EPI, TR, TO>(a, stream); break;
     case 9: launch_pipe<T, 9, EPI, TR, TO>(a, stream); break;
     case 10: launch_pipe<T, 10, EPI, TR, TO>(a, stream); break;
+    case 11: launch_pipe<T, 11, EPI, TR, TO>(a, stream); break;
     default: launch_one<T, 64, 64, 2, 2, EPI, TR, TO>(a, stream); break;
   }
 }
@@ -1324,10 +1326,12 @@ static hipError_t run_epi_i8(int cfg, const GemmArgs& a, hipStream_t stream) {
 static int pick_cfg(const GemmArgs& a, int elem_bytes) {
   if (((long long)a.K * elem_bytes) % 128) return -1;
   // (tile, loop efficiency relative to the 128x256 tile); 192x192 and 96x128 fill one
-  // round of 256 tiles at token counts where 128x256 or 64x128 would spill into a second
+  // round of 256 tiles at token counts where 128x256 or 64x128 would spill into a second;
+  // 32x64 puts twice the compute units of 64x64 on a 128-token batch (BERT-large at 128
+  // tokens, back to back: QKV 6.2 -> 5.4 us, FFN1 6.2 -> 5.3, unsplit FFN2 13.5 -> 10.6)
   struct Cand { int cfg; double eff; };
   constexpr Cand CANDS[] = {{0, 1.0}, {1, 0.9}, {2, 0.65}, {3, 0.62}, {4, 0.5}, {9, 0.95},
-                            {10, 0.55}};
+                            {10, 0.55}, {11, 0.35}};
   constexpr double FIXED_US = 3.5, CUS = 256;
   const double rate = elem_bytes == 1 ? 6.06e6 : elem_bytes == 2 ? 3.19e6 : 0.2e6;
   int best = 0;
