@@ -184,7 +184,7 @@ int tel_encoder_layer_forward(const tel_encoder_desc* desc, const void* packed,
  * by the call; the caller still passes inputs, output and packed weights as for
  * tel_encoder_layer_forward (same arguments, same results).
  *   Limit: tel_encoder_workspace_size(desc, total_tokens) must not exceed
- *   TEL_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a BERT-base fp16 layer up to 4,266 tokens),
+ *   TEL_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a BERT-base fp16 layer up to 4,241 tokens),
  *   else TEL_EWORKSPACE and nothing is enqueued.
  *   Every call on one GPU uses that GPU's one array, which keeps the last call's contents:
  *   calls that can overlap on the same GPU (different streams, or host threads without
@@ -466,8 +466,9 @@ int tel_gemm_partial(int dtype, int tile_config, int splits, const void* A, cons
 /* [host] The tile configuration, number of k-splits and partial-sum width (4: float32 /
  * int32, 2: fp16) the encoder layer uses for a partial GEMM of this shape. splits > 1 when
  * the unsplit tile grid has fewer than about 100 workgroups (few tokens): the smallest
- * power of two (at most 8) that reaches that many, keeping at least 8 k-slices of 128 bytes
- * per split, 32-bit partials (partial_bytes 4; fp16 partials are never planned). The layer
+ * power of two (at most 8) that reaches that many, then doubled while the grid still fits
+ * one round of 256 workgroups, keeping at least 8 k-slices of 128 bytes per split, 32-bit
+ * partials (partial_bytes 4; fp16 partials are never planned). The layer
  * runs its output projection and FFN2 split (tel_gemm_partial + tel_layernorm_reduce)
  * exactly when splits > 1. No device work. */
 int tel_gemm_partial_plan(int dtype, int M, int N, int K, int* tile_config, int* splits,

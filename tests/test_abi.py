@@ -120,7 +120,8 @@ def test_kernel_entry_validation():
 def test_partial_plan_invariants():
     """The k-split plan of the output projection / FFN2 GEMMs (host logic): 32-bit partial
     sums only when the unsplit tile grid is under 100 workgroups, a power of two up to 8,
-    whole 128-byte slices with at least 8 per split, and never more than needed; fp16
+    whole 128-byte slices with at least 8 per split, the smallest split reaching 100
+    workgroups and then as many doublings as one round of 256 holds; fp16
     partials only for fp16 operands, K >= 2048, a 64-row unsplit tile filling one round of
     256 workgroups, and then two splits of the 128 x 128 tile that still fill one round."""
     # (BM, BN) of the pipelined tile table, in its order (gemm.hip PIPE_CFGS)
@@ -142,13 +143,18 @@ def test_partial_plan_invariants():
                     assert nk % 2 == 0 and nk // 2 >= 8
                 elif sp > 1:
                     assert tiles < 100 and nk % sp == 0 and nk // sp >= 8
-                    assert tiles * sp // 2 < 100          # the smallest split that suffices
+                    # the smallest split that reaches 100 workgroups, then doublings that
+                    # keep the grid within one round of 256
+                    assert tiles * sp // 2 < 100 or tiles * sp <= 256
+                    # and no further doubling was possible
+                    assert (sp == 8 or tiles * sp * 2 > 256 or nk % (2 * sp) or
+                            nk // (2 * sp) < 8)
                 else:
                     assert tiles >= 100 or nk % 2 or nk // 2 < 8
     # a 128-token batch at BERT-large shape: 32 x 64 tiles (64 of them), the output
-    # projection and FFN2 each split in 2
+    # projection split in 2 (8 k-slices each), FFN2 in 4 (one round of 256 workgroups)
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 1024) == (11, 2, 4)
-    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (11, 2, 4)
+    assert tel.tel_gemm_partial_plan(tel.TEL_F16, 128, 1024, 4096) == (11, 4, 4)
     # 2557 tokens at BERT-base shape: output projection and FFN2 (K 3072, one round of
     # 240 tiles of 64 x 128) unsplit, in every type
     assert tel.tel_gemm_partial_plan(tel.TEL_F16, 2557, 768, 768)[1] == 1
@@ -299,8 +305,8 @@ def test_noalloc_layer_validation():
     big_T = 5000
     assert tel.tel_encoder_workspace_size(desc, big_T) > tel.TEL_NOALLOC_SCRATCH_BYTES
     # the limit the header states for this layer is exact
-    limit = 4266
-    assert "up to 4,266 tokens" in open(HEADER).read()
+    limit = 4241
+    assert "up to 4,241 tokens" in open(HEADER).read()
     assert tel.tel_encoder_workspace_size(desc, limit) <= tel.TEL_NOALLOC_SCRATCH_BYTES
     assert tel.tel_encoder_workspace_size(desc, limit + 1) > tel.TEL_NOALLOC_SCRATCH_BYTES
     assert F(pd, A256, A256, ctypes.c_void_p((1 << 20) + 4096), A256, 2, big_T, 128, None) == \

@@ -1352,8 +1352,9 @@ static int pick_cfg(const GemmArgs& a, int elem_bytes) {
 // Partial-sum GEMMs: a shape whose tile grid leaves most compute units idle (few tokens,
 // e.g. one 128-token sequence) is split over k. The tile is the one the unsplit kernel
 // would take; the split count is the smallest power of two that reaches about 100
-// workgroups while every split keeps at least 8 k-slices (fewer make the prologue and the
-// partial-sum traffic dominate). Returns 1 when splitting does not pay.
+// workgroups, then doubled while the grid fits one round of 256, as long as every split
+// keeps at least 8 k-slices (fewer make the prologue and the partial-sum traffic
+// dominate). Returns 1 when splitting does not pay.
 constexpr int SPLIT_MIN_TILES = 100, SPLIT_MIN_SLICES = 8, SPLIT_MAX = 8;
 
 //
@@ -1378,9 +1379,11 @@ int gemm_partial_plan(int dtype, int M, int N, int K, int* cfg, int* part16) {
   if (*cfg < 0) return 1;
   const long tiles = tiles_of(*cfg, M, N);
   const int nk = (int)((long long)K * es / 128);
+  // once split, keep doubling while the grid still fits one round of 256 workgroups: a
+  // long K then streams in shorter runs per compute unit
   int sp = 1;
-  while (sp < SPLIT_MAX && tiles * sp < SPLIT_MIN_TILES && nk % (2 * sp) == 0 &&
-         nk / (2 * sp) >= SPLIT_MIN_SLICES)
+  while (sp < SPLIT_MAX && (tiles * sp < SPLIT_MIN_TILES || (sp > 1 && tiles * sp * 2 <= 256)) &&
+         nk % (2 * sp) == 0 && nk / (2 * sp) >= SPLIT_MIN_SLICES)
     sp *= 2;
   return sp;
 }
